@@ -1,0 +1,65 @@
+"""Integer reference for the persistent tile schedule.  TEST INFRASTRUCTURE.
+
+Only tests/ may use this module; it shares no code with the HIP library.
+
+What the schedule follows ("Optimizing Jagged Flash Attention with TLX",
+"Scheduling jagged tiles across SMs"): in the forward a tile's cost grows
+with its sequence's key length, so work is sorted by K/V workload, longest
+first, and handed to the persistent workers in a zigzag (boustrophedon):
+even passes fill workers left to right, odd passes right to left.  The
+backward's tiles are (batch, head, K/V block) triples of a valid-tile list,
+block-innermost so consecutive tiles reuse the same data.
+
+The rules, in the order they are applied (tile sizes BM, BN and the worker
+count P are parameters; tie-breaks are this library's reading):
+  1. L_b = offsets[b+1] - offsets[b].
+  2. Sequence order: by L_b descending; equal lengths keep ascending b.
+  3. Tiles per sequence:
+       forward, broadcast Q:   H * cdiv(Lq, BM)   (also when L_b == 0: those
+                               tiles write O = 0, lse = -inf)
+       forward, self:          H * cdiv(L_b, BM)
+       backward (both modes):  H * cdiv(L_b, BN)
+  4. The sequences' tiles are concatenated in that order (an exclusive
+     prefix sum of the counts gives each sequence's first tile).  Inside a
+     sequence: heads ascending, and for each head the blocks in cost order,
+     heaviest first -- forward query blocks descending (a causal query
+     block sees more keys the later it is), backward key blocks ascending
+     (a causal key block is seen by more query blocks the earlier it is).
+  5. Tile t goes to worker slot: pass p = t // P, s = t % P,
+     slot = s if p is even else P - 1 - s.
+"""
+from __future__ import annotations
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def sequence_order(lengths) -> list:
+    return sorted(range(len(lengths)), key=lambda b: (-int(lengths[b]), b))
+
+
+def tiles_of_sequence(L: int, H: int, Lq: int, broadcast_q: bool, pass_: int, BM: int, BN: int):
+    """(h, block) pairs of one sequence, in schedule order."""
+    if pass_ == 0:
+        nblk = cdiv(Lq, BM) if broadcast_q else cdiv(L, BM)
+        blocks = list(range(nblk - 1, -1, -1))
+    else:
+        nblk = cdiv(L, BN)
+        blocks = list(range(nblk))
+    return [(h, blk) for h in range(H) for blk in blocks]
+
+
+def zigzag_slot(t: int, P: int) -> int:
+    p, s = divmod(t, P)
+    return s if p % 2 == 0 else P - 1 - s
+
+
+def schedule(lengths, H: int, Lq: int, broadcast_q: bool, pass_: int, BM: int, BN: int, P: int):
+    """Full tile list: [(b, h, block, slot), ...] in tile order t = 0, 1, ..."""
+    out = []
+    for b in sequence_order(lengths):
+        for (h, blk) in tiles_of_sequence(int(lengths[b]), H, Lq, broadcast_q, pass_, BM, BN):
+            t = len(out)
+            out.append((b, h, blk, zigzag_slot(t, P)))
+    return out

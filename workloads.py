@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs for jagged attention: the one module both sides share.
+
+This module draws sequence lengths and bf16 tensors and nothing else: it holds
+no attention arithmetic.  The oracle (CPU, fp64) and the HIP library are both
+fed from what it returns.
+
+The five workloads stand in for the production shapes of "Optimizing Jagged
+Flash Attention with TLX" (Performance section: a dense broadcast Q against
+jagged K/V at varying sparsity), whose data is not public.  Each is given by
+its sizes and length distribution:
+
+  tiny_bcast      broadcast Q, B=4,    H=2,  d=64,  Lq=32,  L ~ U[1,64]
+  self_causal_1k  self-attn, causal, B=32,  H=8,  d=128,        L ~ U[1,1024]
+  prod_bcast      broadcast Q, B=1024, H=4,  d=128, Lq=256, L ~ U[64,2048]
+  long_causal_8k  self-attn, causal, B=64,  H=16, d=128,        L ~ logU[128,8192]
+  skew_bcast      broadcast Q, B=4096, H=8,  d=128, Lq=512,
+                  90% L ~ U[1,32], 10% L ~ U[4096,16384], values N(0, 0.5)
+
+Lengths are drawn with numpy's PCG64 from the seed; integer draws are
+inclusive.  Log-uniform lengths are round(exp(U(ln lo, ln hi))) clipped to
+[lo, hi].  In skew_bcast exactly round(0.1*B) sequences, at seeded random
+positions, are long.  Tensor values are fp32 normal draws times the
+workload's standard deviation, rounded to bf16 (round to nearest even), made
+with a torch generator on the target device so large inputs never pass
+through host memory.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+try:  # torch is only needed to materialise tensors
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    broadcast_q: bool
+    causal: bool
+    B: int
+    H: int
+    d: int
+    Lq: int  # query rows of the shared Q (broadcast mode); 0 in self mode
+    lengths: tuple  # ("uniform", lo, hi) | ("loguniform", lo, hi) | ("mix", frac_long, (lo,hi), (lo,hi))
+    std: float = 1.0
+    tags: tuple = field(default_factory=tuple)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+WORKLOADS = [
+    Workload("tiny_bcast", True, False, 4, 2, 64, 32, ("uniform", 1, 64)),
+    Workload("self_causal_1k", False, True, 32, 8, 128, 0, ("uniform", 1, 1024)),
+    Workload("prod_bcast", True, False, 1024, 4, 128, 256, ("uniform", 64, 2048)),
+    Workload("long_causal_8k", False, True, 64, 16, 128, 0, ("loguniform", 128, 8192)),
+    Workload("skew_bcast", True, False, 4096, 8, 128, 512,
+             ("mix", 0.1, (1, 32), (4096, 16384)), std=0.5),
+]
+
+
+def workload(index_or_name) -> Workload:
+    if isinstance(index_or_name, int):
+        return WORKLOADS[index_or_name]
+    for w in WORKLOADS:
+        if w.name == index_or_name:
+            return w
+    raise KeyError(index_or_name)
+
+
+def draw_lengths(spec: tuple, B: int, seed: int) -> np.ndarray:
+    """Sequence lengths (int64 [B]) for a length spec, from numpy PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kind = spec[0]
+    if kind == "uniform":
+        lo, hi = spec[1], spec[2]
+        return rng.integers(lo, hi + 1, size=B, dtype=np.int64)
+    if kind == "loguniform":
+        lo, hi = spec[1], spec[2]
+        u = rng.uniform(math.log(lo), math.log(hi), size=B)
+        return np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int64)
+    if kind == "mix":
+        frac, (slo, shi), (llo, lhi) = spec[1], spec[2], spec[3]
+        n_long = int(round(frac * B))
+        lengths = rng.integers(slo, shi + 1, size=B, dtype=np.int64)
+        pos = rng.choice(B, size=n_long, replace=False)
+        lengths[pos] = rng.integers(llo, lhi + 1, size=n_long, dtype=np.int64)
+        return lengths
+    raise ValueError(f"unknown length spec {spec!r}")
+
+
+def offsets_from_lengths(lengths) -> np.ndarray:
+    """int64 [B+1]: offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b]."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = np.zeros(lengths.size + 1, dtype=np.int64)
+    np.cumsum(lengths, out=off[1:])
+    return off
+
+
+def _normal_bf16(shape, std, gen, device, chunk_elems=1 << 28):
+    """bf16 tensor of fp32 N(0,1)*std draws, produced in chunks on `device`."""
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk_elems):
+        e = min(n, s + chunk_elems)
+        tmp = torch.randn(e - s, generator=gen, device=device, dtype=torch.float32)
+        if std != 1.0:
+            tmp.mul_(std)
+        flat[s:e].copy_(tmp)  # fp32 -> bf16, round to nearest even
+        del tmp
+    return out
+
+
+def make_tensors(lengths, H: int, d: int, Lq: int, broadcast_q: bool, std: float = 1.0,
+                 seed: int = 0, device="cpu", with_dout: bool = True):
+    """Seeded q, k, v, dout (bf16) and offsets (int64) for one jagged batch.
+
+    Layouts: k, v [T, H, d] with T = sum(lengths).  Broadcast mode: q [H, Lq, d],
+    dout [B, H, Lq, d].  Self mode: q, dout [T, H, d].
+    """
+    if torch is None:  # pragma: no cover
+        raise RuntimeError("torch is required to build tensors")
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    B = lengths.size
+    dev = torch.device(device)
+    gens = []
+    for i in range(4):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed * 7919 + 104729 * (i + 1))
+        gens.append(g)
+    q_shape = (H, Lq, d) if broadcast_q else (T, H, d)
+    o_shape = (B, H, Lq, d) if broadcast_q else (T, H, d)
+    t = {
+        "offsets": torch.from_numpy(off).to(dev),
+        "q": _normal_bf16(q_shape, std, gens[0], dev),
+        "k": _normal_bf16((T, H, d), std, gens[1], dev),
+        "v": _normal_bf16((T, H, d), std, gens[2], dev),
+    }
+    if with_dout:
+        t["dout"] = _normal_bf16(o_shape, std, gens[3], dev)
+    t["lengths"] = lengths
+    t["total_len"] = T
+    return t
+
+
+def make_workload(w, seed: int | None = None, device="cpu", with_dout: bool = True):
+    """Tensors for a named workload (seed defaults to the workload's index)."""
+    if not isinstance(w, Workload):
+        w = workload(w)
+    if seed is None:
+        seed = WORKLOADS.index(w)
+    lengths = draw_lengths(w.lengths, w.B, seed)
+    t = make_tensors(lengths, w.H, w.d, w.Lq, w.broadcast_q, w.std, seed, device, with_dout)
+    t["workload"] = w
+    return t
