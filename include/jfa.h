@@ -1,0 +1,111 @@
+/*
+ * jfa.h -- C-ABI of the gfx950 (MI355X) jagged flash-attention library,
+ * libjfa.so.
+ *
+ * The operation.  For every sequence b of a packed batch and every head h,
+ *     O = softmax(scale * Q K^T) V,   lse = log sum_j exp(scale * (Q K^T)_ij)
+ * ("cuTile Kernels -- FMHA Implementation", "Attention Basics"), computed
+ * with the online-softmax recurrence ("Flash Attention Algorithm") directly
+ * on packed, padding-free K/V addressed through an offsets tensor
+ * ("Optimizing Jagged Flash Attention with TLX", "Introduction"), plus the
+ * backward pass.  Two modes:
+ *   broadcast_q = 1: one dense Q [H, Lq, d] is shared by every sequence, so
+ *                    dQ is the sum of the per-sequence dQ over the whole
+ *                    batch ("1. The Challenge").
+ *   broadcast_q = 0: self-attention; Q is packed like K/V.
+ * causal = 1 masks future keys ("Attention Basics"): query i of a sequence
+ * sees keys j <= i, positions counted from the start of the sequence
+ * (top-left aligned, also when Lq differs from the sequence length).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers on the current HIP device, and
+ *     16-byte aligned.  The caller owns all memory; the library keeps no
+ *     pointer after a call returns and never allocates or frees.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns without synchronising.  Results are valid once the
+ *     stream has executed the work.  Calls that share a workspace must not
+ *     overlap.
+ *   - bf16 tensors are passed as raw 16-bit storage.  Supported head dims:
+ *     d = 64 and d = 128.  B <= 8192 sequences.
+ *   - offsets: int64 [B+1], offsets[0] = 0, non-decreasing,
+ *     offsets[B] = total_len.  Sequence b owns packed rows
+ *     offsets[b] .. offsets[b+1]-1.  It is read on the device only; values
+ *     outside [0, total_len] are clamped (the results are then meaningless
+ *     but no memory outside the tensors is touched).
+ *   - Layouts (row-major, contiguous):
+ *       k, v            bf16 [total_len, H, d]
+ *       broadcast:  q   bf16 [H, Lq, d]
+ *                   out, dout bf16 [B, H, Lq, d];  lse fp32 [B, H, Lq]
+ *                   dq  fp32 [H, Lq, d]  (sum over all sequences)
+ *       self:       q, out, dout bf16 [total_len, H, d]; lse fp32 [total_len, H]
+ *                   dq  fp32 [total_len, H, d]; Lq is ignored
+ *       dk, dv          fp32 [total_len, H, d]
+ *   - lse is the natural-log log-sum-exp.  A sequence with no keys yields
+ *     O = 0, lse = -inf (broadcast mode) and no gradient contribution.
+ *   - Every call returns a jfa_status.  Argument errors are detected on the
+ *     host before anything is enqueued; JFA_ERR_HIP reports a failed HIP
+ *     runtime call or kernel launch.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, non-finite scale */
+  JFA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, B above the supported maximum */
+  JFA_ERR_WORKSPACE = 3,   /* workspace_bytes smaller than jfa_workspace_size() */
+  JFA_ERR_HIP = 4          /* HIP runtime error or failed launch */
+} jfa_status;
+
+/* Workspace bytes needed by jfa_fwd (pass = 0) or jfa_bwd (pass = 1) for
+ * these sizes, written to *bytes.  The size depends on the current device's
+ * compute-unit count (the backward keeps one fp32 dQ partial [H, Lq, d] per
+ * persistent workgroup in broadcast mode).  No work is enqueued. */
+int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q,
+                       int pass, size_t* bytes);
+
+/* Forward.  Writes out (bf16) and lse (fp32) in the layouts above.
+ * Scheduling (sequence sort by length, tile list) runs on the device. */
+int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
+            int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward.  `out` and `lse` must come from jfa_fwd with identical
+ * arguments; `dout` is dL/dO.  Writes dq, dk, dv (fp32) in the layouts
+ * above.  The result is bitwise reproducible for a given device: every
+ * reduction runs in a fixed order (broadcast-mode dQ is summed from
+ * per-workgroup partials by a fixed pairwise tree, never by atomics). */
+int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
+            int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
+            const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
+            size_t workspace_bytes, void* stream);
+
+/* Tile geometry the library uses on the current device for a pass:
+ * *block_rows = query rows per forward tile (pass 0) or key rows per
+ * backward tile (pass 1); *workers = persistent workgroups that share the
+ * tile list.  Host-only. */
+int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block_rows, int* workers);
+
+/* Test hook: builds the tile list of a pass exactly as jfa_fwd / jfa_bwd do
+ * and copies it to `tiles` (device int32 [cap][4]: b, h, block, worker slot),
+ * in list order; *n_tiles (device int64) receives the full tile count.  At
+ * most `cap` tiles are written.  Uses the workspace of that pass. */
+int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q,
+                       int pass, int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a jfa_status value. */
+const char* jfa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H */

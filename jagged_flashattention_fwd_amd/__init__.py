@@ -1,0 +1,163 @@
+"""Python binding of libjfa.so, the gfx950 jagged flash-attention library.
+
+Argument marshalling only: every step of the computation runs in the
+library's HIP kernels.  torch provides device memory and the current stream.
+The C functions keep their names (jfa_fwd, jfa_bwd, ...); `attention_fwd` and
+`attention_bwd` additionally allocate outputs and the workspace with torch.
+If the library is missing, or no GPU is present, calls raise RuntimeError;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libjfa.so")
+
+JFA_OK = 0
+STATUS_NAMES = {0: "JFA_OK", 1: "JFA_ERR_INVALID_ARG", 2: "JFA_ERR_UNSUPPORTED",
+                3: "JFA_ERR_WORKSPACE", 4: "JFA_ERR_HIP"}
+
+# Symbols declared in include/jfa.h, with their ctypes signatures.
+_c = ctypes
+_SIGS = {
+    "jfa_workspace_size": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                      _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
+    "jfa_fwd": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                           _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
+                           _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_bwd": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                           _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
+                           _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                           _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_schedule_params": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_int),
+                                       _c.POINTER(_c.c_int)]),
+    "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                      _c.c_int, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                      _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_status_string": (_c.c_char_p, [_c.c_int]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m jagged_flashattention_fwd_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(rc: int) -> str:
+    return lib().jfa_status_string(rc).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != JFA_OK:
+        raise RuntimeError(f"{what}: {status_string(rc)}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------- C names ---------
+def jfa_workspace_size(total_len, B, H, Lq, d, causal, broadcast_q, pass_) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jfa_workspace_size(int(total_len), B, H, Lq, d, int(causal), int(broadcast_q), pass_,
+                                    ctypes.byref(out)), "jfa_workspace_size")
+    return out.value
+
+
+def jfa_schedule_params(pass_, causal, broadcast_q, d):
+    br, w = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().jfa_schedule_params(pass_, int(causal), int(broadcast_q), d, ctypes.byref(br),
+                                     ctypes.byref(w)), "jfa_schedule_params")
+    return br.value, w.value
+
+
+def jfa_fwd(q, k, v, offsets, B, H, Lq, d, scale, causal, broadcast_q, out, lse, total_len,
+            workspace, stream=None):
+    _check(lib().jfa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, Lq, d, float(scale),
+                         int(causal), int(broadcast_q), _ptr(out), _ptr(lse), int(total_len),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream(stream)), "jfa_fwd")
+
+
+def jfa_bwd(q, k, v, offsets, B, H, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
+            total_len, workspace, stream=None):
+    _check(lib().jfa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, Lq, d, float(scale),
+                         int(causal), int(broadcast_q), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                         _ptr(dk), _ptr(dv), int(total_len), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_bwd")
+
+
+def jfa_debug_schedule(offsets, B, H, Lq, causal, broadcast_q, pass_, total_len, tiles, n_tiles,
+                       workspace, stream=None):
+    _check(lib().jfa_debug_schedule(_ptr(offsets), B, H, Lq, int(causal), int(broadcast_q), pass_,
+                                    int(total_len), _ptr(tiles), tiles.shape[0], _ptr(n_tiles),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "jfa_debug_schedule")
+
+
+# --------------------------------------------- allocating helpers --------
+def _shape_args(q, k, offsets, broadcast_q):
+    T, H, d = k.shape
+    B = offsets.numel() - 1
+    Lq = q.shape[1] if broadcast_q else 0
+    return B, H, Lq, d, T
+
+
+def workspace(total_len, B, H, Lq, d, causal, broadcast_q, pass_, device):
+    import torch
+    n = jfa_workspace_size(total_len, B, H, Lq, d, causal, broadcast_q, pass_)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def attention_fwd(q, k, v, offsets, scale, causal=False, broadcast_q=True, ws=None):
+    """(out bf16, lse fp32) of jagged attention; see include/jfa.h for layouts."""
+    import torch
+    B, H, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
+    if broadcast_q:
+        out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=k.device)
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=k.device)
+    else:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=k.device)
+        lse = torch.empty((T, H), dtype=torch.float32, device=k.device)
+    if ws is None:
+        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 0, k.device)
+    jfa_fwd(q, k, v, offsets, B, H, Lq, d, scale, causal, broadcast_q, out, lse, T, ws)
+    return out, lse
+
+
+def attention_bwd(q, k, v, offsets, scale, causal, broadcast_q, out, lse, dout, ws=None):
+    """(dq, dk, dv) fp32 of jagged attention; see include/jfa.h for layouts."""
+    import torch
+    B, H, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=k.device)
+    dk = torch.empty((T, H, d), dtype=torch.float32, device=k.device)
+    dv = torch.empty((T, H, d), dtype=torch.float32, device=k.device)
+    if ws is None:
+        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 1, k.device)
+    jfa_bwd(q, k, v, offsets, B, H, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv, T,
+            ws)
+    return dq, dk, dv

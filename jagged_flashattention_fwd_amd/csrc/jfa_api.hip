@@ -1,0 +1,285 @@
+// Host side of the C-ABI (include/jfa.h): argument checks, workspace
+// carving, template dispatch and launches on the caller's stream.  Nothing
+// here allocates, frees or synchronises.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "jfa.h"
+#include "jfa_internal.hpp"
+
+namespace jfa {
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+int g_cu_count[MAX_DEVICES];
+std::once_flag g_cu_once[MAX_DEVICES];
+
+// Compute units of the current device (cached per device).
+int cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return JFA_ERR_HIP;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    g_cu_count[dev] = n;
+  });
+  if (g_cu_count[dev] <= 0) return JFA_ERR_HIP;
+  *out = g_cu_count[dev];
+  return JFA_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int fwd_block_rows(int broadcast_q) { return broadcast_q ? FWD_BM_BCAST : FWD_BM_SELF; }
+
+// Upper bound on a pass's tile count that needs only host-known sizes:
+// sum_b cdiv(L_b, blk) <= cdiv(total_len, blk) + B.
+int64_t max_tiles(int pass, int64_t total_len, int B, int H, int Lq, int broadcast_q) {
+  if (pass == 0) {
+    const int bm = fwd_block_rows(broadcast_q);
+    if (broadcast_q) return (int64_t)B * H * cdiv(Lq, bm);
+    return (int64_t)H * (cdiv(total_len, bm) + B);
+  }
+  return (int64_t)H * (cdiv(total_len, BWD_BN) + B);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t sched_a[4];  // order, cum, n_tiles, tiles
+  size_t sched_b[4];
+  int64_t cap_a = 0, cap_b = 0;
+  size_t delta = 0, dq_part = 0;
+  size_t total = 0;
+};
+
+void place_schedule(size_t* at, size_t off[4], int B, int64_t cap) {
+  off[0] = *at; *at = align256(*at + sizeof(int) * (size_t)B);
+  off[1] = *at; *at = align256(*at + sizeof(int64_t) * ((size_t)B + 1));
+  off[2] = *at; *at = align256(*at + sizeof(int64_t));
+  off[3] = *at; *at = align256(*at + sizeof(TileRec) * (size_t)cap);
+}
+
+Layout layout(int pass, int64_t total_len, int B, int H, int Lq, int d, int broadcast_q, int P) {
+  Layout L;
+  size_t at = 0;
+  if (pass == 0) {
+    L.cap_a = max_tiles(0, total_len, B, H, Lq, broadcast_q);
+    place_schedule(&at, L.sched_a, B, L.cap_a);
+  } else {
+    L.cap_a = max_tiles(1, total_len, B, H, Lq, broadcast_q);
+    place_schedule(&at, L.sched_a, B, L.cap_a);
+    if (!broadcast_q) {
+      L.cap_b = max_tiles(0, total_len, B, H, Lq, broadcast_q);
+      place_schedule(&at, L.sched_b, B, L.cap_b);
+    }
+    const size_t rows = broadcast_q ? (size_t)B * H * Lq : (size_t)total_len * H;
+    L.delta = at; at = align256(at + sizeof(float) * rows);
+    if (broadcast_q) {
+      L.dq_part = at;
+      at = align256(at + sizeof(float) * (size_t)P * H * Lq * d);
+    }
+  }
+  L.total = at;
+  return L;
+}
+
+Schedule schedule_at(char* ws, const size_t off[4], int64_t cap) {
+  Schedule s;
+  s.order = reinterpret_cast<int*>(ws + off[0]);
+  s.cum = reinterpret_cast<int64_t*>(ws + off[1]);
+  s.n_tiles = reinterpret_cast<int64_t*>(ws + off[2]);
+  s.tiles = reinterpret_cast<TileRec*>(ws + off[3]);
+  s.max_tiles = cap;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_sizes(int64_t total_len, int B, int H, int Lq, int d, int broadcast_q) {
+  if (B < 1 || H < 1 || total_len < 0) return JFA_ERR_INVALID_ARG;
+  if (broadcast_q && Lq < 1) return JFA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return JFA_ERR_UNSUPPORTED;
+  if (B > MAX_B) return JFA_ERR_UNSUPPORTED;
+  // Row and element indices inside a sequence are 32-bit.
+  if (total_len > (int64_t)INT32_MAX || (broadcast_q && (int64_t)Lq * H > (int64_t)INT32_MAX))
+    return JFA_ERR_UNSUPPORTED;
+  if (H > 65535) return JFA_ERR_UNSUPPORTED;
+  return JFA_OK;
+}
+
+int workers(int pass, int* P) {
+  int cus = 0;
+  const int rc = cu_count(&cus);
+  if (rc != JFA_OK) return rc;
+  (void)pass;
+  *P = cus;  // one persistent workgroup (4 waves) per compute unit
+  return JFA_OK;
+}
+
+}  // namespace
+}  // namespace jfa
+
+using namespace jfa;
+
+extern "C" {
+
+const char* jfa_status_string(int status) {
+  switch (status) {
+    case JFA_OK: return "JFA_OK";
+    case JFA_ERR_INVALID_ARG: return "JFA_ERR_INVALID_ARG: invalid argument";
+    case JFA_ERR_UNSUPPORTED: return "JFA_ERR_UNSUPPORTED: unsupported size or head dim";
+    case JFA_ERR_WORKSPACE: return "JFA_ERR_WORKSPACE: workspace too small";
+    case JFA_ERR_HIP: return "JFA_ERR_HIP: HIP runtime error";
+    default: return "JFA: unknown status";
+  }
+}
+
+int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block_rows, int* workers_out) {
+  (void)causal;
+  if (!block_rows || !workers_out || (pass != 0 && pass != 1)) return JFA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return JFA_ERR_UNSUPPORTED;
+  *block_rows = pass == 0 ? fwd_block_rows(broadcast_q) : BWD_BN;
+  return workers(pass, workers_out);
+}
+
+int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q,
+                       int pass, size_t* bytes) {
+  (void)causal;
+  if (!bytes || (pass != 0 && pass != 1)) return JFA_ERR_INVALID_ARG;
+  int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
+  if (rc != JFA_OK) return rc;
+  int P = 0;
+  rc = workers(pass, &P);
+  if (rc != JFA_OK) return rc;
+  *bytes = layout(pass, total_len, B, H, Lq, d, broadcast_q, P).total;
+  return JFA_OK;
+}
+
+int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
+            int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !offsets || !out || !lse || !workspace) return JFA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 7))
+    return JFA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
+  int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
+  if (rc != JFA_OK) return rc;
+  if (!broadcast_q) Lq = 0;
+  int P = 0;
+  rc = workers(0, &P);
+  if (rc != JFA_OK) return rc;
+  const Layout lay = layout(0, total_len, B, H, Lq, d, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const Schedule s = schedule_at(ws, lay.sched_a, lay.cap_a);
+
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows(broadcast_q)};
+  if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
+
+  FwdArgs fa;
+  fa.q = static_cast<const uint16_t*>(q);
+  fa.k = static_cast<const uint16_t*>(k);
+  fa.v = static_cast<const uint16_t*>(v);
+  fa.offsets = offsets;
+  fa.out = static_cast<uint16_t*>(out);
+  fa.lse = lse;
+  fa.tiles = s.tiles;
+  fa.n_tiles = s.n_tiles;
+  fa.total_len = total_len;
+  fa.B = B; fa.H = H; fa.Lq = Lq; fa.d = d;
+  fa.scale_log2 = scale * 1.4426950408889634f;
+  fa.causal = causal ? 1 : 0;
+  fa.broadcast_q = broadcast_q ? 1 : 0;
+  fa.P = P;
+  if (launch_fwd(fa, st) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
+}
+
+int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
+            int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
+            const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return JFA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 7))
+    return JFA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
+  int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
+  if (rc != JFA_OK) return rc;
+  if (!broadcast_q) Lq = 0;
+  int P = 0;
+  rc = workers(1, &P);
+  if (rc != JFA_OK) return rc;
+  const Layout lay = layout(1, total_len, B, H, Lq, d, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const Schedule sk = schedule_at(ws, lay.sched_a, lay.cap_a);
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 1, BWD_BN};
+  if (launch_schedule(sa, sk, st) != hipSuccess) return JFA_ERR_HIP;
+  Schedule sq{};
+  if (!broadcast_q) {
+    sq = schedule_at(ws, lay.sched_b, lay.cap_b);
+    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, fwd_block_rows(0)};
+    if (launch_schedule(sb, sq, st) != hipSuccess) return JFA_ERR_HIP;
+  }
+  BwdArgs ba;
+  ba.q = static_cast<const uint16_t*>(q);
+  ba.k = static_cast<const uint16_t*>(k);
+  ba.v = static_cast<const uint16_t*>(v);
+  ba.offsets = offsets;
+  ba.out = static_cast<const uint16_t*>(out);
+  ba.lse = lse;
+  ba.dout = static_cast<const uint16_t*>(dout);
+  ba.dq = dq; ba.dk = dk; ba.dv = dv;
+  ba.delta = reinterpret_cast<float*>(ws + lay.delta);
+  ba.dq_part = broadcast_q ? reinterpret_cast<float*>(ws + lay.dq_part) : nullptr;
+  ba.ktiles = sk.tiles;
+  ba.n_ktiles = sk.n_tiles;
+  ba.qtiles = broadcast_q ? nullptr : sq.tiles;
+  ba.n_qtiles = broadcast_q ? nullptr : sq.n_tiles;
+  ba.B = B; ba.H = H; ba.Lq = Lq; ba.d = d;
+  ba.total_len = total_len;
+  ba.scale = scale;
+  ba.scale_log2 = scale * 1.4426950408889634f;
+  ba.causal = causal ? 1 : 0;
+  ba.broadcast_q = broadcast_q ? 1 : 0;
+  ba.P = P;
+  ba.P_dq = P;
+  if (launch_bwd(ba, st) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
+}
+
+int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q, int pass,
+                       int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  (void)causal;
+  if (!offsets || !tiles || !n_tiles || !workspace || cap < 0 || (pass != 0 && pass != 1))
+    return JFA_ERR_INVALID_ARG;
+  // The fwd check_sizes needs some d; the schedule does not depend on it.
+  int rc = check_sizes(total_len, B, H, Lq, 128, broadcast_q);
+  if (rc != JFA_OK) return rc;
+  if (!broadcast_q) Lq = 0;
+  int P = 0;
+  rc = workers(pass, &P);
+  if (rc != JFA_OK) return rc;
+  const Layout lay = layout(pass, total_len, B, H, Lq, 64, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Schedule s = schedule_at(static_cast<char*>(workspace), lay.sched_a, lay.cap_a);
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, pass,
+               pass == 0 ? fwd_block_rows(broadcast_q) : BWD_BN};
+  if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
+  if (launch_schedule_dump(s, P, tiles, cap, n_tiles, st) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+// Device-side building blocks for the gfx950 (CDNA4) jagged attention kernels.
+//
+// Everything here is written for one wave of 64 lanes and the bf16 matrix
+// core instruction v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, C 32x32 fp32).
+// Operand lane layouts of that instruction (checked on the device):
+//   A:  lane l holds A[l % 32][8*(l/32) + 0..7]
+//   B:  lane l holds B[8*(l/32) + 0..7][l % 32]
+//   C:  lane l, register i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
+// LDS tiles are row-major bf16 with no padding; the 16-byte chunks of each
+// row are XOR-swizzled so that both access patterns the kernels use are free
+// of bank conflicts within 16 lanes: 16-byte reads of 16 rows at one chunk,
+// and the transposing read ds_read_b64_tr_b16 (4 rows x 32 bytes per 16
+// lanes).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) short lds_short;
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- math --
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Full-row reductions for the transposed score layout, where lanes l and
+// l+32 hold the two halves of one row: after the swap every lane sees both.
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float min_across_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// ------------------------------------------------------------- LDS tiles --
+// Swizzle of the 16-byte chunk index for a row: 16 distinct values over 16
+// consecutive rows when a row has 16 chunks (D = 128), 8 when it has 8; any
+// 4 consecutive rows starting at a multiple of 4 map an aligned chunk pair to
+// 4 disjoint pairs.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  int x = ((row & 3) << 1) | ((row >> 2) & 1);
+  if (D >= 128) x |= ((row >> 3) & 1) << 3;
+  return x;
+}
+// Byte offset of (row, 16-byte chunk) in a row-major [rows][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ chunk_swizzle<D>(row)) << 4);
+}
+// Byte offset of element column `col` (multiple of 4) of `row`.
+template <int D>
+__device__ __forceinline__ int tile_off_col4(int row, int col) {
+  return tile_off<D>(row, col >> 3) + ((col & 4) << 1);
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const char* lds, int off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + off));
+}
+__device__ __forceinline__ void lds_write16(char* lds, int off, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(lds + off) = v;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, source lane s = 4j + q
+// supplies 4 consecutive 16-bit values of row j at columns 4q..4q+3; lane i of
+// the group receives column i of rows 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const char* lds, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((lds_short*)((__attribute__((address_space(3))) char*)(lds + off))));
+}
+
+// MFMA operand with the k index running along the rows of a row-major LDS
+// tile X[k][n] (e.g. V^T from V[key][d]): lane l receives X[k][n0 + l%32] for
+// its 8 k-slots.  `krow(r, g)` gives the first of the 4 rows delivered by read
+// r (0 or 1) to lane group g = l/32; rows krow..krow+3 fill k-slots 4r..4r+3.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_operand_tr(const char* lds, int krow0, int krow1, int n0) {
+  const int l = lane_id();
+  const int s = l & 15, j = s >> 2, q = s & 3, G = l >> 4;
+  const int col = n0 + ((G & 1) << 4) + (q << 2);
+  i16x4 a = lds_read_tr(lds, tile_off_col4<D>(krow0 + j, col));
+  i16x4 b = lds_read_tr(lds, tile_off_col4<D>(krow1 + j, col));
+  struct P { i16x4 x, y; } p = {a, b};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+// ------------------------------------------------------ global <-> LDS ----
+// A tile of R rows x D bf16 columns is copied by NT threads, 16 bytes each
+// per step; row r of the tile is global row (base + r * ld) and rows at or
+// beyond `nrows` read as zero.
+template <int R, int D, int NT>
+struct TileLoader {
+  static constexpr int CPR = D / 8;              // chunks per row
+  static constexpr int N = R * CPR / NT;         // chunks per thread
+  static_assert(R * CPR % NT == 0, "tile must split evenly");
+  u32x4 v[N];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / CPR, c = idx % CPR;
+      if (r < nrows) {
+        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)r * ld + c * 8);
+      } else {
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / CPR, c = idx % CPR;
+      lds_write16(lds, tile_off<D>(r, c), v[i]);
+    }
+  }
+};
+
+// ------------------------------------------------------------ sequences --
+// Rows [s0, s0 + L) of the packed tensors belong to sequence b.  Offsets are
+// clamped into [0, total] so that malformed offsets can never address memory
+// outside the packed tensors (results are then meaningless, but in bounds).
+__device__ __forceinline__ int64_t seq_range(const int64_t* __restrict__ off, int b, int64_t total,
+                                             int64_t* s0_out) {
+  int64_t s0 = off[b], e = off[b + 1];
+  s0 = s0 < 0 ? 0 : (s0 > total ? total : s0);
+  e = e < s0 ? s0 : (e > total ? total : e);
+  *s0_out = s0;
+  return e - s0;
+}
+
+// ----------------------------------------------------------- schedule ----
+// Tile t of the concatenated list goes to worker slot zigzag_slot(t, P):
+// pass t / P fills slots left to right when even, right to left when odd.
+__device__ __forceinline__ int64_t zigzag_tile(int64_t pass, int slot, int P) {
+  return pass * P + ((pass & 1) ? (P - 1 - slot) : slot);
+}
+__device__ __forceinline__ int zigzag_slot(int64_t t, int P) {
+  const int64_t p = t / P;
+  const int s = (int)(t - p * P);
+  return (p & 1) ? (P - 1 - s) : s;
+}
+// Persistent workgroup w runs worker slot logical_slot(w): hardware places
+// workgroup w on XCD w % 8, so consecutive slots (which receive consecutive
+// tiles, often of the same sequence) are packed onto the same XCD and its L2.
+__device__ __forceinline__ int logical_slot(int w, int P) {
+  const int per = P / 8;
+  if (per * 8 != P) return w;
+  return (w & 7) * per + (w >> 3);
+}
+
+}  // namespace jfa

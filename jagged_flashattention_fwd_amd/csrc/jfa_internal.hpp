@@ -1,0 +1,87 @@
+// Internal (library-private) launch interface shared by the host API and the
+// kernel translation units.  Not part of the C-ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+struct TileRec {
+  int b, h, blk, pad;
+};
+
+// Tile sizes.  Forward: a tile is BM query rows of one (sequence, head),
+// streamed against K/V in steps of KV_STEP keys.  Backward: a tile is BN key
+// rows of one (sequence, head), streamed against query blocks of QB rows.
+constexpr int FWD_KV_STEP = 64;
+constexpr int FWD_BM_BCAST = 256;  // 4 waves x 64 query rows
+constexpr int FWD_BM_SELF = 128;   // 4 waves x 32 query rows
+constexpr int BWD_BN = 128;        // 4 waves x 32 key rows
+constexpr int BWD_QB = 64;         // query rows per step of the dK/dV kernel
+constexpr int DQ_BM = 128;         // self-attention dQ kernel: 4 waves x 32 query rows
+constexpr int DQ_KV_STEP = 64;
+constexpr int MAX_B = 8192;        // single-workgroup sequence sort
+
+struct Schedule {
+  int* order;         // [B]
+  int64_t* cum;       // [B+1]
+  TileRec* tiles;     // [max_tiles]
+  int64_t* n_tiles;   // [1]
+  int64_t max_tiles;  // capacity of `tiles`
+};
+
+struct SchedArgs {
+  const int64_t* offsets;
+  int64_t total_len;
+  int B, H, Lq, broadcast_q, pass, blk;
+};
+
+hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out,
+                                hipStream_t stream);
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int64_t* offsets;
+  uint16_t* out;
+  float* lse;
+  const TileRec* tiles;
+  const int64_t* n_tiles;
+  int64_t total_len;
+  int B, H, Lq, d;
+  float scale_log2;  // softmax scale times log2(e)
+  int causal, broadcast_q;
+  int P;             // persistent workgroups
+};
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int64_t* offsets;
+  const uint16_t* out;
+  const float* lse;
+  const uint16_t* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;           // [rows] scratch
+  float* dq_part;         // [P][H][Lq][d] broadcast-mode partials
+  const TileRec* ktiles;  // key-block tiles (dK/dV kernel)
+  const int64_t* n_ktiles;
+  const TileRec* qtiles;  // query-block tiles (self-attention dQ kernel)
+  const int64_t* n_qtiles;
+  int B, H, Lq, d;
+  int64_t total_len;
+  float scale;
+  float scale_log2;
+  int causal, broadcast_q;
+  int P;       // persistent workgroups of the dK/dV kernel (== number of partials)
+  int P_dq;    // persistent workgroups of the self-attention dQ kernel
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace jfa

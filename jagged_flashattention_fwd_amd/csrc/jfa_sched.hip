@@ -1,0 +1,157 @@
+// On-device tile scheduler for the persistent kernels.
+//
+// "Optimizing Jagged Flash Attention with TLX", "Scheduling jagged tiles
+// across SMs", sorts the forward's tiles by K/V workload, longest first, and
+// hands them to the persistent workers in a zigzag; the backward walks a list
+// of valid (batch, head, K/V block) tiles, block-innermost.  That page does
+// the sorting on the host.  Here it runs on the device from the offsets
+// tensor, so no length ever crosses to the host and nothing synchronises:
+//   1. one workgroup sorts the sequences by length, descending (ties: lower
+//      index first), counts each sequence's tiles and takes an exclusive
+//      prefix sum of the counts in sorted order;
+//   2. one workgroup per sequence writes that sequence's tiles -- heads
+//      ascending, blocks heaviest first -- at its prefix-sum position.
+// The persistent kernels then take tile t in zigzag order (jfa_device.hpp).
+#include "jfa_device.hpp"
+#include "jfa_internal.hpp"
+
+namespace jfa {
+
+namespace {
+
+constexpr int SORT_THREADS = 1024;
+
+__device__ __forceinline__ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ int64_t tiles_of(int64_t L, int H, int Lq, int broadcast_q, int pass, int blk) {
+  if (pass == 0) return (int64_t)H * cdiv64(broadcast_q ? Lq : L, blk);
+  return (int64_t)H * cdiv64(L, blk);
+}
+
+// Single workgroup: bitonic sort of N = 2^k keys in LDS, then a chunked
+// exclusive scan of the per-sequence tile counts.
+__global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Schedule s, int N) {
+  extern __shared__ __attribute__((aligned(16))) unsigned long long keys[];
+  __shared__ int64_t part[SORT_THREADS];
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  for (int i = tid; i < N; i += SORT_THREADS) {
+    unsigned long long k = ~0ull;
+    if (i < B) {
+      int64_t s0;
+      const int64_t L = seq_range(a.offsets, i, a.total_len, &s0);
+      unsigned long long Lc = L > 0xffffffffll ? 0xffffffffull : (unsigned long long)L;
+      k = ((0xffffffffull - Lc) << 32) | (unsigned long long)i;
+    }
+    keys[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += SORT_THREADS) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = keys[i], y = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Chunked exclusive scan over ranks 0..B-1.
+  const int per = (B + SORT_THREADS - 1) / SORT_THREADS;
+  const int r0 = tid * per, r1 = min(B, r0 + per);
+  int64_t local = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int b = (int)(keys[r] & 0xffffffffull);
+    s.order[r] = b;
+    int64_t s0;
+    local += tiles_of(seq_range(a.offsets, b, a.total_len, &s0), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < SORT_THREADS; off <<= 1) {
+    const int64_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  // Positions are clamped to the list's capacity, which well-formed offsets
+  // never reach.
+  int64_t run = part[tid] - local;  // exclusive prefix of this chunk
+  for (int r = r0; r < r1; ++r) {
+    s.cum[r] = run < s.max_tiles ? run : s.max_tiles;
+    const int b = (int)(keys[r] & 0xffffffffull);
+    int64_t s0;
+    run += tiles_of(seq_range(a.offsets, b, a.total_len, &s0), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
+  }
+  if (tid == SORT_THREADS - 1) {
+    const int64_t T = part[tid] < s.max_tiles ? part[tid] : s.max_tiles;
+    s.cum[B] = T;
+    *s.n_tiles = T;
+  }
+}
+
+// One workgroup per sorted rank: write that sequence's tiles.
+__global__ __launch_bounds__(256) void sched_expand(SchedArgs a, Schedule s) {
+  const int r = blockIdx.x;
+  const int b = s.order[r];
+  const int64_t start = s.cum[r];
+  const int64_t n = s.cum[r + 1] - start;
+  if (n <= 0) return;
+  int64_t s0;
+  const int64_t L = seq_range(a.offsets, b, a.total_len, &s0);
+  const int64_t nblk = a.pass == 0 ? cdiv64(a.broadcast_q ? a.Lq : L, a.blk) : cdiv64(L, a.blk);
+  if (nblk <= 0) return;
+  for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
+    const int h = (int)(j / nblk);
+    const int64_t i = j - (int64_t)h * nblk;
+    const int blk = (int)(a.pass == 0 ? nblk - 1 - i : i);
+    s.tiles[start + j] = TileRec{b, h, blk, 0};
+  }
+}
+
+__global__ __launch_bounds__(256) void sched_dump(Schedule s, int P, int32_t* out, int64_t cap, int64_t* n_out) {
+  const int64_t T = *s.n_tiles;
+  const int64_t n = T < cap ? T : cap;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const TileRec r = s.tiles[t];
+    out[4 * t + 0] = r.b;
+    out[4 * t + 1] = r.h;
+    out[4 * t + 2] = r.blk;
+    out[4 * t + 3] = zigzag_slot(t, P);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_out = T;
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t stream) {
+  int N = 1;
+  while (N < a.B) N <<= 1;
+  static bool attr_set = false;
+  if (!attr_set) {
+    // Sorting MAX_B keys needs 64 KiB of dynamic LDS.
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sched_sort_scan),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, MAX_B * 8);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(sched_sort_scan, dim3(1), dim3(SORT_THREADS), (size_t)N * 8, stream, a, s, N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sched_expand, dim3(a.B), dim3(256), 0, stream, a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(sched_dump, dim3(256), dim3(256), 0, stream, s, P, out, cap, n_out);
+  return hipGetLastError();
+}
+
+}  // namespace jfa

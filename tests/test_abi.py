@@ -1,0 +1,85 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function
+include/jfa.h declares, and rejects bad arguments on the host before any
+HIP call (no compute is attempted here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import jagged_flashattention_fwd_amd as jfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(jfa.LIB_PATH):
+        from jagged_flashattention_fwd_amd import build
+        build.build()
+    return jfa.lib()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "jfa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jfa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_calls():
+    assert _declared_functions() == sorted([
+        "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_schedule_params", "jfa_status_string",
+        "jfa_workspace_size"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(jfa.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+    assert set(jfa._SIGS) == set(_declared_functions())
+
+
+def test_status_strings(lib):
+    for code, name in jfa.STATUS_NAMES.items():
+        assert jfa.status_string(code).startswith(name)
+    assert "unknown" in jfa.status_string(99)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _fwd(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, off=FAKE, B=2, H=2, Lq=8, d=128, scale=0.1, causal=0, bq=1,
+                out=FAKE, lse=FAKE, T=10, ws=FAKE, wsb=1 << 30)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.jfa_fwd(vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["off"]), args["B"],
+                       args["H"], args["Lq"], args["d"], args["scale"], args["causal"], args["bq"],
+                       vp(args["out"]), vp(args["lse"]), args["T"], vp(args["ws"]), args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(off=0), 1), (dict(out=0), 1), (dict(ws=0), 1),
+    (dict(q=FAKE + 2), 1), (dict(lse=FAKE + 1), 1), (dict(off=FAKE + 4), 1),
+    (dict(scale=math.inf), 1), (dict(scale=math.nan), 1),
+    (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1), (dict(Lq=0), 1),
+    (dict(d=96), 2), (dict(d=256), 2), (dict(B=8193), 2),
+])
+def test_fwd_rejects_bad_arguments_before_any_hip_call(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+def test_bwd_rejects_null_gradient(lib):
+    vp = ctypes.c_void_p
+    rc = lib.jfa_bwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 2, 8, 128, 0.1, 0, 1, vp(FAKE),
+                     vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), 10, vp(FAKE), 1 << 30, None)
+    assert rc == 1
+
+
+def test_workspace_size_argument_checks(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.jfa_workspace_size(10, 2, 2, 8, 96, 0, 1, 0, ctypes.byref(out)) == 2
+    assert lib.jfa_workspace_size(10, 0, 2, 8, 128, 0, 1, 0, ctypes.byref(out)) == 1
+    assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 7, ctypes.byref(out)) == 1
+    assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 0, None) == 1

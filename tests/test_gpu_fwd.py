@@ -1,0 +1,115 @@
+"""GPU parity of jfa_fwd (called through the C-ABI) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import jfa_oracle as jo
+from oracle import schedule_ref as sr
+from tests._parity import compare, compare_lse, to64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# Tile geometry this test expects of the library (checked against the
+# library's own report before use).
+FWD_BM = {True: 256, False: 128}
+BWD_BN = 128
+
+
+@pytest.fixture(scope="module")
+def jfa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import jagged_flashattention_fwd_amd as m
+    m.lib()
+    return m
+
+
+def _run_case(jfa, lengths, H, d, Lq, bq, causal, seed, std=1.0, scale=None):
+    t = wl.make_tensors(lengths, H, d, Lq, bq, std=std, seed=seed, device="cuda", with_dout=False)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    print(f"fwd case lengths={list(lengths)[:8]}.. H={H} d={d} Lq={Lq} bq={bq} causal={causal}",
+          flush=True)
+    out, lse = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], scale, causal, bq)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = jo.jagged_forward(to64(t["q"]), to64(t["k"]), to64(t["v"]),
+                                       t["offsets"].cpu().numpy(), scale, causal, bq)
+    compare("O", to64(out), ref_o)
+    compare_lse("lse", to64(lse), ref_lse)
+    return t, out, lse
+
+
+EDGE = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 0, 255, 256, 257, 300]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bq,causal", [(True, False), (True, True), (False, False), (False, True)])
+def test_fwd_edge_lengths(jfa, d, bq, causal):
+    _run_case(jfa, EDGE, 2, d, 70 if bq else 0, bq, causal, seed=11)
+
+
+@pytest.mark.parametrize("Lq", [1, 32, 255, 256, 257, 512])
+def test_fwd_broadcast_lq(jfa, Lq):
+    _run_case(jfa, [5, 130, 1, 64, 700], 3, 128, Lq, True, False, seed=Lq)
+
+
+def test_fwd_negative_and_zero_scale(jfa):
+    _run_case(jfa, [3, 77, 130], 2, 64, 40, True, False, seed=5, scale=-0.3)
+    _run_case(jfa, [3, 77, 130], 2, 128, 0, False, True, seed=6, scale=0.0)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_fwd_workloads_full(jfa, idx):
+    w = wl.workload(idx)
+    lengths = wl.draw_lengths(w.lengths, w.B, idx)
+    _run_case(jfa, lengths, w.H, w.d, w.Lq, w.broadcast_q, w.causal, seed=idx, std=w.std)
+
+
+def test_single_key_sequences_return_v_bitwise(jfa):
+    lengths = [1, 1, 5, 1]
+    H, d, Lq = 2, 128, 33
+    t = wl.make_tensors(lengths, H, d, Lq, True, seed=3, device="cuda", with_dout=False)
+    out, _ = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], 0.1, False, True)
+    off = t["offsets"].cpu().numpy()
+    for b in (0, 1, 3):
+        v = t["v"][off[b]]  # [H, d]
+        assert torch.equal(out[b], v[:, None, :].expand(H, Lq, d))
+    # causal self-attention: row 0 of every sequence returns V row 0
+    t = wl.make_tensors([7, 1, 130], H, d, 0, False, seed=4, device="cuda", with_dout=False)
+    out, _ = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], 0.1, True, False)
+    for s in t["offsets"].cpu().numpy()[:-1]:
+        assert torch.equal(out[s], t["v"][s])
+
+
+def test_fwd_deterministic(jfa):
+    t = wl.make_tensors([300, 17, 900, 64], 4, 128, 256, True, seed=9, device="cuda", with_dout=False)
+    a = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], 0.08, False, True)
+    b = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], 0.08, False, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("pass_", [0, 1])
+@pytest.mark.parametrize("bq", [True, False])
+def test_schedule_bit_exact(jfa, pass_, bq):
+    lengths = wl.draw_lengths(("mix", 0.1, (0, 40), (300, 3000)), 777, 21)
+    H, Lq = 3, 300
+    block, P = jfa.jfa_schedule_params(pass_, 0, int(bq), 128)
+    props = torch.cuda.get_device_properties(0)
+    expect_block = FWD_BM[bq] if pass_ == 0 else BWD_BN
+    assert (block, P) == (expect_block, props.multi_processor_count)
+    off = torch.from_numpy(wl.offsets_from_lengths(lengths)).cuda()
+    T = int(off[-1])
+    ws = jfa.workspace(T, len(lengths), H, Lq if bq else 0, 128, 0, bq, pass_, "cuda")
+    ref = sr.schedule(lengths, H, Lq if bq else 0, bq, pass_, expect_block, expect_block,
+                      props.multi_processor_count)
+    cap = len(ref) + 5
+    tiles = torch.full((cap, 4), -7, dtype=torch.int32, device="cuda")
+    n = torch.zeros(1, dtype=torch.int64, device="cuda")
+    jfa.jfa_debug_schedule(off, len(lengths), H, Lq if bq else 0, 0, bq, pass_, T, tiles, n, ws)
+    torch.cuda.synchronize()
+    assert int(n.item()) == len(ref)
+    got = tiles.cpu().numpy()
+    assert np.array_equal(got[:len(ref)], np.array(ref, dtype=np.int32))
+    assert np.all(got[len(ref):] == -7)
