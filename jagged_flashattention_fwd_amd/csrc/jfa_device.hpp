@@ -49,6 +49,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 r = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, r);
 }
+// Two-term bf16 split of a pair: hi = the values truncated to bf16, lo = the
+// remainders rounded to bf16, so hi + lo carries about 16 significant bits.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t* hi, uint32_t* lo) {
+  const uint32_t ua = __float_as_uint(a) & 0xffff0000u, ub = __float_as_uint(b) & 0xffff0000u;
+  *hi = (ua >> 16) | ub;
+  f32x2 r = {a - __uint_as_float(ua), b - __uint_as_float(ub)};
+  *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
