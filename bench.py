@@ -1,0 +1,300 @@
+"""Benchmark of the jagged flash-attention hot path on one MI355X.
+
+One step = jfa_fwd + jfa_bwd over one synthetic batch already resident in
+HBM.  Default workload: prod_bcast (broadcast Q [4, 256, 128], B = 1024
+sequences with lengths U[64, 2048], bf16, non-causal).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prod_bcast]
+
+Useful FLOPs count visible (query, key) pairs only, no padding: 4*d per pair
+and head in the forward (two GEMMs), 10*d in the backward (five GEMMs).  The
+same convention reproduces the FMHA guide's printed TFLOPS
+("cuTile Kernels -- FMHA Implementation", "Performance Results").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_FLOP_PER_CLK_PER_CU = 4096   # dense bf16
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E
+PEAK_SCLK_GHZ = 2.4               # MI355X peak engine clock
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+# ------------------------------------------------------------ counting ----
+def visible_pairs(lengths, Lq: int, causal: bool, broadcast_q: bool) -> int:
+    """Number of (query, key) pairs the mask leaves visible, per head."""
+    L = np.asarray(lengths, dtype=np.int64)
+    if broadcast_q:
+        if not causal:
+            return int(Lq * L.sum())
+        # query i sees min(i + 1, L) keys
+        i = np.arange(Lq, dtype=np.int64)[:, None]
+        return int(np.minimum(i + 1, L[None, :]).sum())
+    if causal:
+        return int((L * (L + 1) // 2).sum())
+    return int((L * L).sum())
+
+
+def useful_flops(lengths, H: int, d: int, Lq: int, causal: bool, broadcast_q: bool):
+    n = visible_pairs(lengths, Lq, causal, broadcast_q)
+    return 4 * d * H * n, 10 * d * H * n
+
+
+def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q: bool, P: int) -> int:
+    """Bytes a kernel must move between HBM and the chip for one launch:
+    every input element read once and every output element written once."""
+    T = int(np.asarray(lengths).sum())
+    B = len(lengths)
+    kv = T * H * d * 2                    # one bf16 [T, H, d] tensor
+    rows = B * H * Lq if broadcast_q else T * H
+    row_bf16 = rows * d * 2               # out / dout, bf16
+    q_bytes = H * Lq * d * 2 if broadcast_q else T * H * d * 2
+    if kernel == "fwd_kernel":
+        return 2 * kv + q_bytes + row_bf16 + rows * 4
+    if kernel == "delta_kernel":
+        return 2 * row_bf16 + rows * 4
+    if kernel == "dkdv_kernel":
+        # K, V, Q, dO, lse, delta in; dK, dV (fp32) out; broadcast dQ partials out
+        b = 2 * kv + q_bytes + row_bf16 + 2 * rows * 4 + 2 * T * H * d * 4
+        if broadcast_q:
+            b += P * H * Lq * d * 4
+        return b
+    if kernel == "dq_reduce":
+        return (P + 1) * H * Lq * d * 4
+    if kernel == "dq_self_kernel":
+        return 2 * kv + q_bytes + row_bf16 + 2 * rows * 4 + T * H * d * 4
+    return 0
+
+
+def kernel_flops(kernel: str, fwd_flops: int, bwd_flops: int, broadcast_q: bool) -> int:
+    if kernel == "fwd_kernel":
+        return fwd_flops
+    if kernel == "dkdv_kernel":
+        return bwd_flops if broadcast_q else bwd_flops * 8 // 10   # 4 of 5 GEMMs
+    if kernel == "dq_self_kernel":
+        return bwd_flops * 2 // 10 + fwd_flops   # dQ GEMM + recomputed S, dP
+    return 0
+
+
+# ---------------------------------------------------------- traffic -------
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "jagged_flashattention_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------- cpu baseline ----
+def cpu_baseline(t, w, scale, seconds: float):
+    """The fp64 oracle, as it stands, on the first sequences of the same
+    workload until `seconds` of CPU time are spent."""
+    from oracle import jfa_oracle as jo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    off = t["offsets"].cpu().numpy()
+    q = t["q"].float().cpu().numpy().astype(np.float64) if w.broadcast_q else None
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    while done < w.B and time.perf_counter() - t0 < seconds:
+        s0, s1 = int(off[done]), int(off[done + 1])
+        k = t["k"][s0:s1].float().cpu().numpy().astype(np.float64)
+        v = t["v"][s0:s1].float().cpu().numpy().astype(np.float64)
+        if w.broadcast_q:
+            qb = q
+            dob = t["dout"][done:done + 1].float().cpu().numpy().astype(np.float64)
+        else:
+            qb = t["q"][s0:s1].float().cpu().numpy().astype(np.float64)
+            dob = t["dout"][s0:s1].float().cpu().numpy().astype(np.float64)
+        o1 = np.array([0, s1 - s0], dtype=np.int64)
+        jo.jagged_forward(qb, k, v, o1, scale, w.causal, w.broadcast_q)
+        jo.jagged_backward(qb, k, v, o1, scale, w.causal, w.broadcast_q, dob)
+        f, b = useful_flops([s1 - s0], w.H, w.d, w.Lq, w.causal, w.broadcast_q)
+        flops += f + b
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of the first {done} of {w.B} sequences "
+                      f"({w.H} heads) of the same workload, {el:.1f} s",
+            "seconds": round(el, 2), "sequences": done}
+
+
+# ---------------------------------------------------------------- main ----
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prod_bcast")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library runs on a single MI355X).", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as wl
+    import jagged_flashattention_fwd_amd as jfa
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    clock_ghz = PEAK_SCLK_GHZ  # published peak engine clock; the reported current clock varies
+    peak_tflops = cus * MFMA_FLOP_PER_CLK_PER_CU * clock_ghz * 1e9 / 1e12
+
+    w = wl.workload(args.workload)
+    seed = wl.WORKLOADS.index(w)
+    t = wl.make_workload(w, seed=seed, device=dev)
+    lengths = t["lengths"]
+    T = t["total_len"]
+    scale = w.scale
+    H, d, Lq, B = w.H, w.d, w.Lq, w.B
+    bq, causal = w.broadcast_q, w.causal
+    q, k, v, off, dout = t["q"], t["k"], t["v"], t["offsets"], t["dout"]
+
+    if bq:
+        out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    ws_f = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, dev)
+    ws_b = jfa.workspace(T, B, H, Lq, d, causal, bq, 1, dev)
+    _, P = jfa.jfa_schedule_params(1, causal, bq, d)
+
+    def step():
+        jfa.jfa_fwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, T, ws_f)
+        jfa.jfa_bwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, dout, dq, dk, dv, T, ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, kernel events recorded on the launch stream.
+    jfa.jfa_timing_enable(16 * args.steps + 16)
+    jfa.jfa_timing_reset()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        jfa.jfa_fwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, T, ws_f)
+        ev[i][1].record(stream)
+        jfa.jfa_bwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, dout, dq, dk, dv, T, ws_b)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ktimes = jfa.kernel_times()
+    jfa.jfa_timing_enable(0)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+    fwd_fl, bwd_fl = useful_flops(lengths, H, d, Lq, causal, bq)
+    value = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
+    fwd_tf = fwd_fl / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_fl / (bwd_ms * 1e-3) / 1e12
+
+    # Dominant kernel: largest device time per step.
+    per_kernel = {}
+    for name, (n, ms) in ktimes.items():
+        if n:
+            per_kernel[name] = {"launches": n, "avg_ms": ms / n,
+                                "ms_per_step": ms / args.steps}
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["ms_per_step"])
+    avg_s = per_kernel[dom]["avg_ms"] * 1e-3
+    nbytes = algorithmic_bytes(dom, lengths, H, d, Lq, bq, P)
+    kfl = kernel_flops(dom, fwd_fl, bwd_fl, bq)
+    gbs = nbytes / avg_s / 1e9
+    tfl = kfl / avg_s / 1e12 if kfl else 0.0
+    # bound: whichever of HBM time and MFMA time at peak is larger
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= kfl / (peak_tflops * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfl, 1), "peak": round(peak_tflops, 1),
+                "unit": "TFLOP/s", "frac": round(tfl / peak_tflops, 4)}
+    roof["traffic"] = measured_traffic(dom, w.name)
+    roof.update({"kernel": dom, "avg_launch_ms": round(per_kernel[dom]["avg_ms"], 4),
+                 "algorithmic_bytes": nbytes, "kernel_useful_flops": kfl,
+                 "kernel_tflops": round(tfl, 1), "kernel_gbs": round(gbs, 1)})
+    for name, rec in per_kernel.items():
+        b = algorithmic_bytes(name, lengths, H, d, Lq, bq, P)
+        rec["avg_ms"] = round(rec["avg_ms"], 4)
+        rec["ms_per_step"] = round(rec["ms_per_step"], 4)
+        if b:
+            rec["gbs"] = round(b / (rec["avg_ms"] * 1e-3) / 1e9, 1)
+
+    res = {
+        "metric": "useful TFLOP/s fwd & bwd (no padding) + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "d": d, "Lq": Lq,
+                   "lengths": list(w.lengths), "causal": causal, "broadcast_q": bq,
+                   "total_len": T, "seed": seed, "accumulate": "fp32", "grad_dtype": "fp32"},
+        "pct_of_peak": round(value / peak_tflops, 4),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 1),
+                "pct_of_peak": round(fwd_tf / peak_tflops, 4), "useful_flops": fwd_fl},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 1),
+                "pct_of_peak": round(bwd_tf / peak_tflops, 4), "useful_flops": bwd_fl},
+        "device": {"name": props.name, "cus": cus, "clock_ghz": clock_ghz,
+                   "bf16_peak_tflops": round(peak_tflops, 1)},
+        "kernels": per_kernel,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(t, w, scale, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

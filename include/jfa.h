@@ -101,6 +101,20 @@ int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal,
                        int pass, int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-kernel timing for measurement tools (not thread-safe; host-only
+ * bookkeeping).  jfa_timing_enable(capacity) creates 2*capacity hipEvents and
+ * from then on brackets every kernel launch of the library with two events
+ * on the launch stream (capacity 0 turns timing off and frees the events).
+ * At most `capacity` launches are recorded between two reads; later ones are
+ * not timed.  jfa_timing_read(kernel, ...) waits for the recorded events,
+ * then returns the number of completed launches of kernel number `kernel`
+ * (0 <= kernel < the count at which jfa_kernel_name returns NULL) and their
+ * summed device time in milliseconds since the last jfa_timing_reset. */
+int jfa_timing_enable(int capacity);
+int jfa_timing_reset(void);
+int jfa_timing_read(int kernel, int64_t* launches, double* total_ms);
+const char* jfa_kernel_name(int kernel);
+
 /* Static, human-readable name of a jfa_status value. */
 const char* jfa_status_string(int status);
 

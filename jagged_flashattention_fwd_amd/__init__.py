@@ -37,6 +37,10 @@ _SIGS = {
                                       _c.c_int, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                       _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "jfa_status_string": (_c.c_char_p, [_c.c_int]),
+    "jfa_timing_enable": (_c.c_int, [_c.c_int]),
+    "jfa_timing_reset": (_c.c_int, []),
+    "jfa_timing_read": (_c.c_int, [_c.c_int, _c.POINTER(_c.c_int64), _c.POINTER(_c.c_double)]),
+    "jfa_kernel_name": (_c.c_char_p, [_c.c_int]),
 }
 
 _lib = None
@@ -117,6 +121,37 @@ def jfa_debug_schedule(offsets, B, H, Lq, causal, broadcast_q, pass_, total_len,
                                     int(total_len), _ptr(tiles), tiles.shape[0], _ptr(n_tiles),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "jfa_debug_schedule")
+
+
+def jfa_timing_enable(capacity: int):
+    _check(lib().jfa_timing_enable(int(capacity)), "jfa_timing_enable")
+
+
+def jfa_timing_reset():
+    _check(lib().jfa_timing_reset(), "jfa_timing_reset")
+
+
+def jfa_timing_read(kernel: int):
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(lib().jfa_timing_read(int(kernel), ctypes.byref(n), ctypes.byref(ms)), "jfa_timing_read")
+    return n.value, ms.value
+
+
+def jfa_kernel_name(kernel: int):
+    r = lib().jfa_kernel_name(int(kernel))
+    return None if r is None else r.decode()
+
+
+def kernel_times():
+    """{kernel name: (launches, total ms)} of every kernel timed since the last reset."""
+    out = {}
+    k = 0
+    while True:
+        name = jfa_kernel_name(k)
+        if name is None:
+            return out
+        out[name] = jfa_timing_read(k)
+        k += 1
 
 
 # --------------------------------------------- allocating helpers --------

@@ -29,6 +29,7 @@
 // masked path, the rest do not.
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
+#include "jfa_timing.hpp"
 
 namespace jfa {
 
@@ -579,32 +580,32 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const int64_t work = rows * (D / 8);
     const int64_t want = (work + 255) / 256;
     const int blocks = (int)(want < 4096 ? want : 4096);
-    hipLaunchKernelGGL((delta_kernel<D>), dim3(blocks), dim3(256), 0, st, a.out, a.dout, a.delta, rows);
+    JFA_TIMED_LAUNCH(K_DELTA, st, (delta_kernel<D>), dim3(blocks), dim3(256), 0, st, a.out, a.dout, a.delta, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.broadcast_q) {
     if (a.causal)
-      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a);
+      JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a);
+      JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)a.H * a.Lq * D;
-    hipLaunchKernelGGL(dq_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dq_part, a.dq, n,
+    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dq_part, a.dq, n,
                        a.P, a.scale);
     return hipGetLastError();
   }
   if (a.causal)
-    hipLaunchKernelGGL((dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a);
+    JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a);
+    JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.causal)
-    hipLaunchKernelGGL((dq_self_kernel<D, true>), dim3(a.P_dq), dim3(256), 0, st, a);
+    JFA_TIMED_LAUNCH(K_DQ_SELF, st, (dq_self_kernel<D, true>), dim3(a.P_dq), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((dq_self_kernel<D, false>), dim3(a.P_dq), dim3(256), 0, st, a);
+    JFA_TIMED_LAUNCH(K_DQ_SELF, st, (dq_self_kernel<D, false>), dim3(a.P_dq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@
 // most rescaling of the accumulator.
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
+#include "jfa_timing.hpp"
 
 namespace jfa {
 
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 
 template <int D, int QW, bool CAUSAL, bool BCAST>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, QW, CAUSAL, BCAST>), dim3(a.P), dim3(256), 0, stream, a);
+  JFA_TIMED_LAUNCH(K_FWD, stream, (fwd_kernel<D, QW, CAUSAL, BCAST>), dim3(a.P), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

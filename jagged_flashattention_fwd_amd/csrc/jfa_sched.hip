@@ -14,6 +14,7 @@
 // The persistent kernels then take tile t in zigzag order (jfa_device.hpp).
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
+#include "jfa_timing.hpp"
 
 namespace jfa {
 
@@ -141,16 +142,16 @@ hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t st
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(sched_sort_scan, dim3(1), dim3(SORT_THREADS), (size_t)N * 8, stream, a, s, N);
+  JFA_TIMED_LAUNCH(K_SCHED_SORT, stream, sched_sort_scan, dim3(1), dim3(SORT_THREADS), (size_t)N * 8, stream, a, s, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sched_expand, dim3(a.B), dim3(256), 0, stream, a, s);
+  JFA_TIMED_LAUNCH(K_SCHED_EXPAND, stream, sched_expand, dim3(a.B), dim3(256), 0, stream, a, s);
   return hipGetLastError();
 }
 
 hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(sched_dump, dim3(256), dim3(256), 0, stream, s, P, out, cap, n_out);
+  JFA_TIMED_LAUNCH(K_SCHED_DUMP, stream, sched_dump, dim3(256), dim3(256), 0, stream, s, P, out, cap, n_out);
   return hipGetLastError();
 }
 

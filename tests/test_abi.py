@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_header_declares_expected_calls():
     assert _declared_functions() == sorted([
-        "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_schedule_params", "jfa_status_string",
+        "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_kernel_name", "jfa_schedule_params",
+        "jfa_status_string", "jfa_timing_enable", "jfa_timing_read", "jfa_timing_reset",
         "jfa_workspace_size"])
 
 
@@ -83,3 +84,13 @@ def test_workspace_size_argument_checks(lib):
     assert lib.jfa_workspace_size(10, 0, 2, 8, 128, 0, 1, 0, ctypes.byref(out)) == 1
     assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 7, ctypes.byref(out)) == 1
     assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 0, None) == 1
+
+
+def test_kernel_names(lib):
+    names = []
+    k = 0
+    while jfa.jfa_kernel_name(k) is not None:
+        names.append(jfa.jfa_kernel_name(k))
+        k += 1
+    assert "fwd_kernel" in names and "dkdv_kernel" in names and len(names) == len(set(names))
+    assert lib.jfa_timing_read(-1, None, None) == 1

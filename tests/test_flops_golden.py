@@ -1,0 +1,51 @@
+"""The useful-FLOP convention of bench.py against the numbers the FMHA guide
+prints ("cuTile Kernels -- FMHA Implementation", "Performance Results"):
+dense attention, 4*head_dim flops per (query, key) pair and head, over the
+full S x S, with batch*heads*head_dim = 8192 behind every printed row."""
+import os
+
+import numpy as np
+import pytest
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        if line.strip() and not line.startswith("#"):
+            out.append([float(x) for x in line.split()])
+    return out
+
+
+def test_b300_sweep_matches_flop_convention():
+    # batch*heads = 64, head_dim = 128: 64 equal-length dense sequences, one head
+    # each, i.e. per the library's count 4*d*H*pairs with pairs = sum L^2.
+    for seq, ms, tflops in _rows("cutile_b300_fmha_sweep.txt"):
+        S = int(seq)
+        fwd, _ = bench.useful_flops([S] * 64, 1, 128, 0, False, False)
+        assert fwd == 4 * S * S * 8192
+        got = fwd / (ms * 1e-3) / 1e12
+        assert got == pytest.approx(tflops, rel=0.006), (S, got, tflops)
+
+
+def test_spark_steps_match_flop_convention():
+    fwd, _ = bench.useful_flops([2048] * 64, 1, 128, 0, False, False)
+    for _, ms, tflops in _rows("cutile_spark_fmha_steps.txt"):
+        assert fwd / (ms * 1e-3) / 1e12 == pytest.approx(tflops, rel=0.015)
+
+
+def test_visible_pairs_closed_forms():
+    L = [1, 5, 64]
+    assert bench.visible_pairs(L, 0, True, False) == 1 + 15 + 64 * 65 // 2
+    assert bench.visible_pairs(L, 0, False, False) == 1 + 25 + 64 * 64
+    assert bench.visible_pairs(L, 7, False, True) == 7 * 70
+    # broadcast causal: query i sees min(i+1, L) keys
+    assert bench.visible_pairs([3], 5, True, True) == 1 + 2 + 3 + 3 + 3
+    assert bench.useful_flops(L, 2, 64, 7, False, True) == (4 * 64 * 2 * 490, 10 * 64 * 2 * 490)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    assert bench.main(["--gpus", "2"]) == 2
