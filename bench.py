@@ -166,6 +166,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="prod_bcast")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(reference kernel for scaling hardware byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -290,6 +293,14 @@ def main(argv=None):
         "kernels": per_kernel,
         "roofline": roof,
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(t, w, scale, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -74,18 +74,18 @@ template <int D, bool CAUSAL, bool BCAST>
 struct DkdvSmem {
   static constexpr int QB = BWD_QB;
   static constexpr int BN = BWD_BN;
-  static constexpr int QTILE = QB * D * 2;
+  static constexpr int QTILE = tile_bytes<QB, D>();
   char q[2][QTILE];
   char dout[2][QTILE];
   float lse2[2][QB];
   float delta[2][QB];
   float dpart[4][QB];  // per-wave partial row sums of P o dP
   int split[4];        // per-wave: dS carried as two bf16 terms
-  char k[BCAST ? BN * D * 2 : 16];
+  char k[BCAST ? tile_bytes<BN, D>() : 16];
   union {
     struct {
-      char hi[BN * QB * 2];  // dS as [key][query], bf16 high terms
-      char lo[BN * QB * 2];  // bf16 remainders (zero where not split)
+      char hi[BN * TR_ONLY_ROW_BYTES_64];  // dS as [key][query], bf16 high terms
+      char lo[BN * TR_ONLY_ROW_BYTES_64];  // bf16 remainders (zero where not split)
     } ds;
     float pdp[BN][QB + PDP_PAD];  // P o dP as [key][query]
   } u;
@@ -205,18 +205,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       const char* Ds = sm.dout[buf];
       const bool diag = CAUSAL && m < m_nomask;
 
-      // ---- S = Q K^T, dP = dO V^T; P.  C layout: lane owns key kw;
-      // register i is query row m*QB + s*32 + 8*(i/4) + 4g + i%4.
-      float pf[2][16], dpf[2][16];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // S = Q K^T and dP = dO V^T for query subtile s (32 rows) of the block.
+      // C layout: lane owns key kw; register i is query row
+      // m*QB + s*32 + 8*(i/4) + 4g + i%4.
+      auto scores = [&](int s, f32x16& sacc, f32x16& dpacc) {
+        sacc = f32x16{};
+        dpacc = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int off = tile_off<D>(s * 32 + lc, ks * 2 + g);
           sacc = mfma32(lds_read16(Qs, off), kreg[ks], sacc);
           dpacc = mfma32(lds_read16(Ds, off), vreg[ks], dpacc);
         }
+      };
+      auto probs = [&](int s, const f32x16& sacc, float* pf) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r = s * 32 + i4 * 8 + g * 4;
@@ -224,24 +226,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = i4 * 4 + e;
-            float pv = fast_exp2(sacc[i] * c2 - ls[e]);
+            const float pv = fast_exp2(sacc[i] * c2 - ls[e]);
             bool ok = key_ok;
             if (diag) ok = ok && (kw <= m * QB + r + e);
-            pf[s][i] = ok ? pv : 0.f;
-            dpf[s][i] = dpacc[i];
+            pf[i] = ok ? pv : 0.f;
           }
         }
-      }
+      };
+
       if (exact_delta) {
+        // delta = rowsum(P o dP) over every key of the sequence (all in this
+        // tile); S and dP are recomputed below.
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s) {
+          f32x16 sacc, dpacc;
+          scores(s, sacc, dpacc);
+          float pf[16];
+          probs(s, sacc, pf);
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             f32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = pf[s][i4 * 4 + e] * dpf[s][i4 * 4 + e];
+            for (int e = 0; e < 4; ++e) v[e] = pf[i4 * 4 + e] * dpacc[i4 * 4 + e];
             *reinterpret_cast<f32x4*>(&sm.u.pdp[wave * 32 + lc][s * 32 + i4 * 8 + g * 4]) = v;
           }
+        }
         __syncthreads();
         {
           const int q = tid & (QB - 1), kq = tid >> 6;  // 4 ranges of 32 keys
@@ -259,59 +268,59 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         }
         __syncthreads();
       }
-      // ---- dS = P o (dP - delta)
-      float dsf[2][16];
-      float pmax = 0.f, dsmax = 0.f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
+
+      bool split_ds_any = false;
+#pragma unroll 1
+      for (int s = 0; s < 2; ++s) {
+        f32x16 sacc, dpacc;
+        scores(s, sacc, dpacc);
+        float pf[16], dsf[16];
+        probs(s, sacc, pf);
+        float pmax = 0.f, dsmax = 0.f;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 dl = *reinterpret_cast<const f32x4*>(&sm.delta[buf][s * 32 + i4 * 8 + g * 4]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = i4 * 4 + e;
-            const float dsv = pf[s][i] * (dpf[s][i] - dl[e]);
-            dsf[s][i] = dsv;
-            pmax = fmaxf(pmax, pf[s][i]);
-            dsmax = fmaxf(dsmax, fabsf(dsv));
+            dsf[i] = pf[i] * (dpacc[i] - dl[e]);
+            pmax = fmaxf(pmax, pf[i]);
+            dsmax = fmaxf(dsmax, fabsf(dsf[i]));
           }
         }
-      // Rounding P or dS to bf16 costs up to 2^-9 of each value, and dV / dK
-      // / dQ sum that error over many queries or keys.  Where a value is
-      // large (short or sharply peaked sequences) the operand is split into a
-      // truncated bf16 high part and a rounded bf16 remainder and the product
-      // is taken twice; elsewhere one rounded bf16 operand is used.
-      const bool split_p = __any(pmax > SPLIT_P);
-      const bool split_ds = __any(dsmax > SPLIT_DS);
-      uint32_t pp[2][2][4], dsp[2][2][4], plo[2][2][4], dslo[2][2][4];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
+        // Rounding P or dS to bf16 costs up to 2^-9 of each value, and dV /
+        // dK / dQ sum that error over many queries or keys.  Where a value is
+        // large (short or sharply peaked sequences) the operand is split into
+        // a truncated bf16 high part and a rounded bf16 remainder and the
+        // product is taken twice; elsewhere one rounded bf16 operand is used.
+        const bool split_p = __any(pmax > SPLIT_P);
+        const bool split_ds = __any(dsmax > SPLIT_DS);
+        split_ds_any = split_ds_any || split_ds;
+        uint32_t pp[2][4], dsp[2][4], plo[2][4], dslo[2][4];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const int hh = i >> 3, e = (i & 7) >> 1;
           if (split_p) {
-            split_bf16x2(pf[s][i], pf[s][i + 1], &pp[s][hh][e], &plo[s][hh][e]);
+            split_bf16x2(pf[i], pf[i + 1], &pp[hh][e], &plo[hh][e]);
           } else {
-            pp[s][hh][e] = pack_bf16x2(pf[s][i], pf[s][i + 1]);
-            plo[s][hh][e] = 0u;
+            pp[hh][e] = pack_bf16x2(pf[i], pf[i + 1]);
+            plo[hh][e] = 0u;
           }
           if (split_ds) {
-            split_bf16x2(dsf[s][i], dsf[s][i + 1], &dsp[s][hh][e], &dslo[s][hh][e]);
+            split_bf16x2(dsf[i], dsf[i + 1], &dsp[hh][e], &dslo[hh][e]);
           } else {
-            dsp[s][hh][e] = pack_bf16x2(dsf[s][i], dsf[s][i + 1]);
-            dslo[s][hh][e] = 0u;
+            dsp[hh][e] = pack_bf16x2(dsf[i], dsf[i + 1]);
+            dslo[hh][e] = 0u;
           }
         }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS: A operands are transposed
-      // reads of the query-major tiles; k-slots = the query rows of the
-      // P / dS register pairs.
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
+        // dV^T += dO^T P and dK^T += Q^T dS: A operands are transposed reads
+        // of the query-major tiles; k-slots = the query rows of the P / dS
+        // register pairs.
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int r0 = s * 32 + hh * 16 + g * 4;
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[s][hh][0], pp[s][hh][1], pp[s][hh][2], pp[s][hh][3]});
-          const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dsp[s][hh][0], dsp[s][hh][1], dsp[s][hh][2], dsp[s][hh][3]});
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]});
+          const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dsp[hh][0], dsp[hh][1], dsp[hh][2], dsp[hh][3]});
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
             const bf16x8 doa = lds_operand_tr<D>(Ds, r0, r0 + 8, dt * 32);
@@ -319,29 +328,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
             dv[dt] = mfma32(doa, pb, dv[dt]);
             dk[dt] = mfma32(qa, db, dk[dt]);
             if (split_p) {
-              const bf16x8 pl = __builtin_bit_cast(bf16x8, u32x4{plo[s][hh][0], plo[s][hh][1], plo[s][hh][2], plo[s][hh][3]});
+              const bf16x8 pl = __builtin_bit_cast(bf16x8, u32x4{plo[hh][0], plo[hh][1], plo[hh][2], plo[hh][3]});
               dv[dt] = mfma32(doa, pl, dv[dt]);
             }
             if (split_ds) {
-              const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{dslo[s][hh][0], dslo[s][hh][1], dslo[s][hh][2], dslo[s][hh][3]});
+              const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{dslo[hh][0], dslo[hh][1], dslo[hh][2], dslo[hh][3]});
               dk[dt] = mfma32(qa, dl, dk[dt]);
             }
           }
         }
-
-      if (BCAST) {
-        // dS (two bf16 terms) to LDS as [key][query]: this wave's 32 key rows.
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
+        if (BCAST) {
+          // dS (two bf16 terms) to LDS as [key][query]: this wave's 32 key rows.
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             const int col = s * 32 + i4 * 8 + g * 4;
-            const int off = tile_off_col4<QB>(wave * 32 + lc, col);
+            const int off = tile_off_col4<QB, TR_ONLY_ROW_BYTES_64>(wave * 32 + lc, col);
             const int hh = i4 >> 1, e0 = (i4 & 1) * 2;
-            *reinterpret_cast<u32x2*>(sm.u.ds.hi + off) = u32x2{dsp[s][hh][e0], dsp[s][hh][e0 + 1]};
-            *reinterpret_cast<u32x2*>(sm.u.ds.lo + off) = u32x2{dslo[s][hh][e0], dslo[s][hh][e0 + 1]};
+            *reinterpret_cast<u32x2*>(sm.u.ds.hi + off) = u32x2{dsp[hh][e0], dsp[hh][e0 + 1]};
+            *reinterpret_cast<u32x2*>(sm.u.ds.lo + off) = u32x2{dslo[hh][e0], dslo[hh][e0 + 1]};
           }
-        if (l == 0) sm.split[wave] = split_ds ? 1 : 0;
+        }
+      }
+
+      if (BCAST) {
+        if (l == 0) sm.split[wave] = split_ds_any ? 1 : 0;
+        if (m == m_first) __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const bool any_split = (sm.split[0] | sm.split[1] | sm.split[2] | sm.split[3]) != 0;
         // dQ[q][d] (block) = sum over the tile's 128 keys of dS[q][key] K[key][d].
@@ -354,9 +365,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < BN / 16; ++kk) {
           const int kr0 = kk * 16 + g * 8;
-          const bf16x8 ahi = lds_operand_tr<QB>(sm.u.ds.hi, kr0, kr0 + 4, qs * 32);
+          const bf16x8 ahi = lds_operand_tr<QB, TR_ONLY_ROW_BYTES_64>(sm.u.ds.hi, kr0, kr0 + 4, qs * 32);
           bf16x8 alo = ahi;
-          if (any_split) alo = lds_operand_tr<QB>(sm.u.ds.lo, kr0, kr0 + 4, qs * 32);
+          if (any_split) alo = lds_operand_tr<QB, TR_ONLY_ROW_BYTES_64>(sm.u.ds.lo, kr0, kr0 + 4, qs * 32);
 #pragma unroll
           for (int x = 0; x < DTW; ++x) {
             const int dt = (wave >> 1) * DTW + x;
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
             const int q = m * QB + qs * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
             if (q < Lq) {
               float* dst = part + ((int64_t)h * Lq + q) * D + dcol;
-              *dst += dqa[x][i];
+              unsafeAtomicAdd(dst, dqa[x][i]);
             }
           }
         }
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part,
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dq_self_kernel(BwdArgs a) {
   constexpr int BN = DQ_KV_STEP, KS = D / 16, DT = D / 32, BM = DQ_BM;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][BN * D * 2];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char smem[2][2][tile_bytes<BN, D>()];  // [buffer][K, V]
   const int tid = threadIdx.x;
   const int wave = tid / WAVE, l = tid % WAVE, g = l / 32, lc = l % 32;
   const int slot = logical_slot(blockIdx.x, a.P_dq);

@@ -6,11 +6,10 @@
 //   A:  lane l holds A[l % 32][8*(l/32) + 0..7]
 //   B:  lane l holds B[8*(l/32) + 0..7][l % 32]
 //   C:  lane l, register i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
-// LDS tiles are row-major bf16 with no padding; the 16-byte chunks of each
-// row are XOR-swizzled so that both access patterns the kernels use are free
-// of bank conflicts within 16 lanes: 16-byte reads of 16 rows at one chunk,
-// and the transposing read ds_read_b64_tr_b16 (4 rows x 32 bytes per 16
-// lanes).
+// LDS tiles are row-major bf16 with padded rows (TileGeom) so that both
+// access patterns the kernels use are free of bank conflicts within 16
+// lanes: 16-byte reads of 16 rows at one chunk, and the transposing read
+// ds_read_b64_tr_b16 (4 rows x 32 bytes per 16 lanes).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,26 +75,34 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 }
 
 // ------------------------------------------------------------- LDS tiles --
-// Swizzle of the 16-byte chunk index for a row: 16 distinct values over 16
-// consecutive rows when a row has 16 chunks (D = 128), 8 when it has 8; any
-// 4 consecutive rows starting at a multiple of 4 map an aligned chunk pair to
-// 4 disjoint pairs.
+// Row-major bf16 tile with D columns, rows padded to ROW_BYTES.  The padding
+// is chosen so that (a) 16-byte reads of 16 consecutive rows at one column
+// hit 16 distinct 16-byte bank groups (ROW_BYTES / 16 is odd), and (b) the
+// transpose read, which takes 32 bytes from each of 4 consecutive rows per
+// 16 lanes, touches 4 disjoint 32-byte ranges modulo 256 bytes.  Because the
+// layout is affine in (row, column), every operand address is one per-lane
+// base plus a compile-time constant, which the LDS instructions take as an
+// immediate offset.
 template <int D>
-__device__ __forceinline__ int chunk_swizzle(int row) {
-  int x = ((row & 3) << 1) | ((row >> 2) & 1);
-  if (D >= 128) x |= ((row >> 3) & 1) << 3;
-  return x;
-}
-// Byte offset of (row, 16-byte chunk) in a row-major [rows][D] bf16 tile.
+struct TileGeom {
+  static_assert(D == 64 || D == 128, "tile width");
+  static constexpr int ROW_BYTES = D == 128 ? 304 : 208;
+};
+// Row bytes of a 64-column tile that is only ever read with the transpose
+// read (condition (b) alone).
+constexpr int TR_ONLY_ROW_BYTES_64 = 160;
+// Byte offset of (row, 16-byte chunk).
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * (D * 2) + ((chunk ^ chunk_swizzle<D>(row)) << 4);
+  return row * TileGeom<D>::ROW_BYTES + (chunk << 4);
 }
-// Byte offset of element column `col` (multiple of 4) of `row`.
-template <int D>
+// Byte offset of element column `col` of `row`.
+template <int D, int RB = TileGeom<D>::ROW_BYTES>
 __device__ __forceinline__ int tile_off_col4(int row, int col) {
-  return tile_off<D>(row, col >> 3) + ((col & 4) << 1);
+  return row * RB + (col << 1);
 }
+template <int R, int D>
+constexpr int tile_bytes() { return R * TileGeom<D>::ROW_BYTES; }
 
 __device__ __forceinline__ bf16x8 lds_read16(const char* lds, int off) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + off));
@@ -116,13 +123,13 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* lds, int off) {
 // tile X[k][n] (e.g. V^T from V[key][d]): lane l receives X[k][n0 + l%32] for
 // its 8 k-slots.  `krow(r, g)` gives the first of the 4 rows delivered by read
 // r (0 or 1) to lane group g = l/32; rows krow..krow+3 fill k-slots 4r..4r+3.
-template <int D>
+template <int D, int RB = TileGeom<D>::ROW_BYTES>
 __device__ __forceinline__ bf16x8 lds_operand_tr(const char* lds, int krow0, int krow1, int n0) {
   const int l = lane_id();
   const int s = l & 15, j = s >> 2, q = s & 3, G = l >> 4;
   const int col = n0 + ((G & 1) << 4) + (q << 2);
-  i16x4 a = lds_read_tr(lds, tile_off_col4<D>(krow0 + j, col));
-  i16x4 b = lds_read_tr(lds, tile_off_col4<D>(krow1 + j, col));
+  i16x4 a = lds_read_tr(lds, tile_off_col4<D, RB>(krow0 + j, col));
+  i16x4 b = lds_read_tr(lds, tile_off_col4<D, RB>(krow1 + j, col));
   struct P { i16x4 x, y; } p = {a, b};
   return __builtin_bit_cast(bf16x8, p);
 }

@@ -47,7 +47,7 @@ struct Fwd {
   static constexpr int BM = NW * QW;
   static constexpr int KS = D / 16;    // MFMA k-steps over the head dim
   static constexpr int DT = D / 32;    // 32-wide head-dim tiles of O^T
-  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int TILE_BYTES = tile_bytes<BN, D>();
 };
 
 template <int D, int QW, bool CAUSAL, bool BCAST>
