@@ -134,6 +134,39 @@ __device__ __forceinline__ bf16x8 lds_operand_tr(const char* lds, int krow0, int
   return __builtin_bit_cast(bf16x8, p);
 }
 
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// Four MFMA A operands of a transposed 128-wide tile (head-dim tiles 0..3)
+// from one key group, with the transpose read issued directly: a0 / a1 are
+// this lane's LDS addresses for the group's first and second 4-row read.
+// The builtin form of the instruction makes the compiler drain every
+// outstanding direct-to-LDS copy before it; this form waits only for its
+// own reads (lgkmcnt), and its results depend on that wait.
+__device__ __forceinline__ void lds_operand_tr_x4(uint32_t a0, uint32_t a1, bf16x8 out[4]) {
+  i16x4 x0, y0, x1, y1, x2, y2, x3, y3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:64\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:128\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(y0), "=&v"(x1), "=&v"(y1), "=&v"(x2), "=&v"(y2), "=&v"(x3), "=&v"(y3)
+      : "v"(a0), "v"(a1)
+      : "memory");
+  struct P { i16x4 x, y; };
+  out[0] = __builtin_bit_cast(bf16x8, P{x0, y0});
+  out[1] = __builtin_bit_cast(bf16x8, P{x1, y1});
+  out[2] = __builtin_bit_cast(bf16x8, P{x2, y2});
+  out[3] = __builtin_bit_cast(bf16x8, P{x3, y3});
+}
+
 // ------------------------------------------------------ global <-> LDS ----
 // A tile of R rows x D bf16 columns is copied by NT threads, 16 bytes each
 // per step; row r of the tile is global row (base + r * ld) and rows at or
@@ -177,6 +210,31 @@ __device__ __forceinline__ int64_t seq_range(const int64_t* __restrict__ off, in
   e = e < s0 ? s0 : (e > total ? total : e);
   *s0_out = s0;
   return e - s0;
+}
+
+// ------------------------------------------------- direct global -> LDS --
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 256-byte row (D = 128 bf16) copied by the 64 lanes of a wave straight
+// into LDS (global_load_lds_dword): lane l moves bytes 4l..4l+3.  The LDS
+// destination must be the same for every lane of the wave.
+__device__ __forceinline__ void dma_row256(const uint16_t* __restrict__ src_row, char* lds_row) {
+  __builtin_amdgcn_global_load_lds(src_row + 2 * lane_id(), (lds_void*)lds_row, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (at most n
+// operations of this wave still outstanding; n <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that also orders this wave's earlier LDS reads before
+// it (lgkmcnt(0)), without waiting for outstanding global loads: the
+// direct-to-LDS pipelines account for those with wait_vmcnt.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ----------------------------------------------------------- schedule ----

@@ -12,7 +12,7 @@
 // Work unit: a tile = BM query rows of one (sequence, head).  The kernel is
 // persistent ("2.1 Structural changes"): P workgroups walk a device-built,
 // longest-first tile list in zigzag order ("Scheduling jagged tiles across
-// SMs").  Each workgroup is 4 waves; wave w owns QW consecutive query rows.
+// SMs").  Wave w of a workgroup owns QW consecutive query rows.
 //
 // Per K/V step of 64 keys the math is done transposed, S^T = K Q^T, so a lane
 // owns one query column: the row max and row sum of the online softmax are
@@ -28,6 +28,8 @@
 // than 2^8 (in exp2 units); until then exponentials are taken against the
 // stale maximum, which leaves O and lse unchanged up to rounding and skips
 // most rescaling of the accumulator.
+#include <type_traits>
+
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
 #include "jfa_timing.hpp"
@@ -38,9 +40,8 @@ namespace {
 
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
-template <int D, int QW, bool CAUSAL, bool BCAST>
+template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
 struct Fwd {
-  static constexpr int NW = 4;
   static constexpr int NT = NW * WAVE;
   static constexpr int BN = FWD_KV_STEP;
   static constexpr int QS = QW / 32;   // 32-row query subtiles per wave
@@ -48,13 +49,23 @@ struct Fwd {
   static constexpr int KS = D / 16;    // MFMA k-steps over the head dim
   static constexpr int DT = D / 32;    // 32-wide head-dim tiles of O^T
   static constexpr int TILE_BYTES = tile_bytes<BN, D>();
+  // d = 128: K/V rows go straight from global memory to LDS, DEP steps
+  // ahead of the one being computed, in a ring of DEP + 1 buffers.  Each
+  // wave issues IPS row copies per step; the vector-memory counter can hold
+  // at most 63 outstanding operations, which bounds DEP.
+  // d = 64: rows are staged through registers one step ahead.
+  static constexpr bool DMA = D == 128;
+  static constexpr int IPS = 2 * BN / NW;
+  static constexpr int DEP = DMA ? ((2 * IPS <= 63) ? 3 : 2) : 1;
+  static constexpr int NBUF = DEP + 1;
 };
 
-template <int D, int QW, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
-  using C = Fwd<D, QW, CAUSAL, BCAST>;
+template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
+  using C = Fwd<D, NW, QW, CAUSAL, BCAST>;
   constexpr int BN = C::BN, QS = C::QS, BM = C::BM, KS = C::KS, DT = C::DT, NT = C::NT;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][C::TILE_BYTES];  // [buffer][K, V]
+  constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::TILE_BYTES];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int wave = tid / WAVE, l = tid % WAVE, g = l / 32, lc = l % 32;
@@ -109,31 +120,68 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
     const uint16_t* kbase = a.k + (s0 * H + h) * (int64_t)D;
     const uint16_t* vbase = a.v + (s0 * H + h) * (int64_t)D;
     TileLoader<BN, D, NT> kl, vl;
+    // Copies K/V step j into ring buffer j % NBUF (d = 128 path).  Rows past
+    // the sequence end repeat its last row: finite values that the mask
+    // discards, and never an address outside the tensor.
+    auto issue = [&](int j) {
+      char* Kd = smem[j % NBUF][0];
+      char* Vd = smem[j % NBUF][1];
+      const int k0 = j * BN;
+#pragma unroll
+      for (int i = 0; i < BN / NW; ++i) {
+        const int row = wave * (BN / NW) + i;
+        const int src = min(k0 + row, L - 1);
+        dma_row256(kbase + (int64_t)src * ld, Kd + row * TileGeom<D>::ROW_BYTES);
+        dma_row256(vbase + (int64_t)src * ld, Vd + row * TileGeom<D>::ROW_BYTES);
+      }
+    };
 
     __syncthreads();  // the previous tile's readers are done with LDS
-    if (n_kv > 0) {
-      kl.load(kbase, ld, min(BN, L), tid);
-      vl.load(vbase, ld, min(BN, L), tid);
-      kl.store(smem[0][0], tid);
-      vl.store(smem[0][1], tid);
+    if constexpr (C::DMA) {
+      wait_vmcnt<0>();  // Q rows (and the last tile's stores) are not counted below
+      for (int jj = 0; jj < DEP && jj < n_kv; ++jj) issue(jj);
+    } else {
+      if (n_kv > 0) {
+        kl.load(kbase, ld, min(BN, L), tid);
+        vl.load(vbase, ld, min(BN, L), tid);
+        kl.store(smem[0][0], tid);
+        vl.store(smem[0][1], tid);
+      }
+      __syncthreads();
     }
-    __syncthreads();
 
-    for (int j = 0; j < n_kv; ++j) {
-      const int buf = j & 1;
+    // One K/V step of BN keys.  MASKED is a compile-time constant: the
+    // bulk steps carry no mask code at all; only the tail step and the
+    // causal diagonal steps take the masked body.
+    auto kv_step = [&](int j, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const int buf = j % NBUF;
       const int k0 = j * BN;
-      if (j + 1 < n_kv) {
+      if constexpr (C::DMA) {
+        // Wait for this wave's copies of step j (later steps may still be in
+        // flight), then for every wave's; step j-1's buffer is then free.
+        const int ahead = min(DEP, n_kv - j) - 1;
+        if constexpr (DEP >= 3) {
+          if (ahead >= 2) wait_vmcnt<2 * IPS>();
+          else if (ahead == 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        } else {
+          if (ahead >= 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        }
+        barrier_lds();
+        if (j + DEP < n_kv) issue(j + DEP);
+      } else if (j + 1 < n_kv) {
         const int nxt = k0 + BN;
         kl.load(kbase + (int64_t)nxt * ld, ld, min(BN, L - nxt), tid);
         vl.load(vbase + (int64_t)nxt * ld, ld, min(BN, L - nxt), tid);
       }
       // Causal: a wave whose last query row precedes this step's first key
       // sees none of it.
-      const bool active = !CAUSAL || (k0 <= wq0 + QS * 32 - 1);
+      const bool active = !(CAUSAL && MASKED) || (k0 <= wq0 + QS * 32 - 1);
       if (active) {
         const char* Ks = smem[buf][0];
         const char* Vs = smem[buf][1];
-        const bool masked = j >= n_bulk;
         // ---- S^T = K Q^T : two 32-key subtiles x QS query subtiles.
         f32x16 sacc[2][QS];
 #pragma unroll
@@ -160,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               float x = sacc[kt][s][i] * c2;
-              if (masked) {
+              if (MASKED) {
                 const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
                 const bool ok = key < L && (!CAUSAL || key <= qi);
                 x = ok ? x : -INFINITY;
@@ -170,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
             }
           mt = max_across_halves(mt);
           const bool need = mt > m2[s] + RESCALE_SLACK;
-          if (__any(need)) {
+          if (__builtin_expect(__any(need), 0)) {
             const float alpha = need ? fast_exp2(m2[s] - mt) : 1.f;
             m2[s] = need ? mt : m2[s];
             lsum[s] *= alpha;
@@ -201,24 +249,38 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int r0 = kt * 32 + hh * 16 + g * 4;
+            bf16x8 va[DT];
+            if constexpr (C::DMA) {
+              // lane's transpose-read address: row r0 + j, column 16*(G&1) + 4q
+              const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
+              const uint32_t a0 = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
+              lds_operand_tr_x4(a0, a0 + 8 * TileGeom<D>::ROW_BYTES, va);
+            } else {
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) va[dt] = lds_operand_tr<D>(Vs, r0, r0 + 8, dt * 32);
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-              const bf16x8 va = lds_operand_tr<D>(Vs, r0, r0 + 8, dt * 32);
 #pragma unroll
               for (int s = 0; s < QS; ++s) {
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[kt][hh][s][0], pk[kt][hh][s][1],
                                                                     pk[kt][hh][s][2], pk[kt][hh][s][3]});
-                oacc[dt][s] = mfma32(va, pb, oacc[dt][s]);
+                oacc[dt][s] = mfma32(va[dt], pb, oacc[dt][s]);
               }
             }
           }
       }
-      if (j + 1 < n_kv) {
-        kl.store(smem[buf ^ 1][0], tid);
-        vl.store(smem[buf ^ 1][1], tid);
+      if constexpr (!C::DMA) {
+        if (j + 1 < n_kv) {
+          kl.store(smem[buf ^ 1][0], tid);
+          vl.store(smem[buf ^ 1][1], tid);
+        }
+        __syncthreads();
       }
-      __syncthreads();
-    }
+    };
+    const int n_plain = min(n_bulk, n_kv);
+    for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
+    for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
 
     // ---- epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2.
 #pragma unroll
@@ -251,20 +313,23 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int QW, bool CAUSAL, bool BCAST>
+template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  JFA_TIMED_LAUNCH(K_FWD, stream, (fwd_kernel<D, QW, CAUSAL, BCAST>), dim3(a.P), dim3(256), 0, stream, a);
+  JFA_TIMED_LAUNCH(K_FWD, stream, (fwd_kernel<D, NW, QW, CAUSAL, BCAST>), dim3(a.P), dim3(NW * WAVE), 0,
+                   stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+  // 32 query rows per wave; broadcast tiles of 256 rows use 8 waves (two
+  // per SIMD, so one wave's matrix ops overlap the other's softmax).
   if (a.broadcast_q) {
-    return a.causal ? launch_fwd_t<D, FWD_BM_BCAST / 4, true, true>(a, stream)
-                    : launch_fwd_t<D, FWD_BM_BCAST / 4, false, true>(a, stream);
+    return a.causal ? launch_fwd_t<D, FWD_BM_BCAST / 32, 32, true, true>(a, stream)
+                    : launch_fwd_t<D, FWD_BM_BCAST / 32, 32, false, true>(a, stream);
   }
-  return a.causal ? launch_fwd_t<D, FWD_BM_SELF / 4, true, false>(a, stream)
-                  : launch_fwd_t<D, FWD_BM_SELF / 4, false, false>(a, stream);
+  return a.causal ? launch_fwd_t<D, FWD_BM_SELF / 32, 32, true, false>(a, stream)
+                  : launch_fwd_t<D, FWD_BM_SELF / 32, 32, false, false>(a, stream);
 }
 
 }  // namespace
