@@ -120,6 +120,56 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, kernel: str, copy_bytes: int) -> str:
+    """Write profiles/traffic_<kernel>_<workload>.txt from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each counter is scaled
+    by bytes-moved / counter-reading of the plain device copy of copy_bytes
+    that bench.py --copy-calibration-mib runs in the same process."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for name, vs in d.items() if key in name for v in vs]
+        return sum(vals) / len(vals), len(vals), sum(vals)
+
+    _, _, copy_fetch = pick(fetch, "copyBuffer")
+    _, _, copy_write = pick(write, "copyBuffer")
+    f_scale = copy_bytes / copy_fetch
+    w_scale = copy_bytes / copy_write
+    kf, nf, _ = pick(fetch, kernel)
+    kw, nw, _ = pick(write, kernel)
+    total = kf * f_scale + kw * w_scale
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.txt")
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of {kernel} on {workload}, from rocprofv3 FETCH_SIZE and WRITE_SIZE\n")
+        f.write("# commands (MI355X; one counter per run):\n")
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            f.write(f"#   cd /tmp && rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/pmc_{ctr} "
+                    f"-o pmc -- python -u $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
+                    f"--no-cpu-baseline --copy-calibration-mib {copy_bytes >> 20}\n")
+        f.write(f"#   python bench.py --summarize-pmc <fetch csv> <write csv> --workload {workload}\n")
+        f.write(f"# calibration: plain copy of {copy_bytes} bytes read {copy_fetch:.0f} FETCH bytes and "
+                f"{copy_write:.0f} WRITE bytes\n")
+        f.write(f"fetch_scale: {f_scale:.4f}\n")
+        f.write(f"write_scale: {w_scale:.4f}\n")
+        f.write(f"dispatches: {nf} / {nw}\n")
+        f.write(f"fetch_bytes_per_launch_raw: {kf:.0f}\n")
+        f.write(f"write_bytes_per_launch_raw: {kw:.0f}\n")
+        f.write(f"hbm_bytes_per_launch: {total:.0f}\n")
+        f.write(f"source_digest: {kernel_source_digest()}\n")
+    return path
+
+
 # ------------------------------------------------------- cpu baseline ----
 def cpu_baseline(t, w, scale, seconds: float):
     """The fp64 oracle, as it stands, on the first sequences of the same
@@ -169,7 +219,14 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference kernel for scaling hardware byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary under profiles/ from two counter runs and exit")
+    ap.add_argument("--kernel", default="dkdv_kernel", help="kernel for --summarize-pmc")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.kernel,
+                            (args.copy_calibration_mib or 1024) << 20))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library runs on a single MI355X).", file=sys.stderr)
