@@ -48,6 +48,18 @@ int64_t max_tiles(int pass, int64_t total_len, int B, int H, int Lq, int broadca
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Broadcast-mode dQ work split: n_qb query blocks of DQ_BM_BCAST rows per
+// head, and nc sequence chunks, so that H * n_qb * nc fills but does not
+// exceed the P compute units (at most 256 chunks, at most B).
+void dq_split(int B, int H, int Lq, int P, int* n_qb, int* nc) {
+  *n_qb = (int)cdiv(Lq, DQ_BM_BCAST);
+  int c = P / (H * *n_qb);
+  if (c > B) c = B;
+  if (c > 256) c = 256;
+  if (c < 1) c = 1;
+  *nc = c;
+}
+
 struct Layout {
   size_t sched_a[4];  // order, cum, n_tiles, tiles
   size_t sched_b[4];
@@ -79,8 +91,10 @@ Layout layout(int pass, int64_t total_len, int B, int H, int Lq, int d, int broa
     const size_t rows = broadcast_q ? (size_t)B * H * Lq : (size_t)total_len * H;
     L.delta = at; at = align256(at + sizeof(float) * rows);
     if (broadcast_q) {
+      int n_qb, nc;
+      dq_split(B, H, Lq, P, &n_qb, &nc);
       L.dq_part = at;
-      at = align256(at + sizeof(float) * (size_t)P * H * Lq * d);
+      at = align256(at + sizeof(float) * (size_t)H * n_qb * nc * DQ_BM_BCAST * d);
     }
   }
   L.total = at;
@@ -242,6 +256,10 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   ba.dq = dq; ba.dk = dk; ba.dv = dv;
   ba.delta = reinterpret_cast<float*>(ws + lay.delta);
   ba.dq_part = broadcast_q ? reinterpret_cast<float*>(ws + lay.dq_part) : nullptr;
+  ba.seq_order = sk.order;
+  ba.dq_qblocks = 0;
+  ba.dq_chunks = 0;
+  if (broadcast_q) dq_split(B, H, Lq, P, &ba.dq_qblocks, &ba.dq_chunks);
   ba.ktiles = sk.tiles;
   ba.n_ktiles = sk.n_tiles;
   ba.qtiles = broadcast_q ? nullptr : sq.tiles;

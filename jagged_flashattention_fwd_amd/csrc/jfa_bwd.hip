@@ -27,6 +27,8 @@
 //                  dQ^T += K^T dS^T.  No atomics.
 // Loops are peeled ("Loop peeling"): the causal diagonal blocks take the
 // masked path, the rest do not.
+#include <type_traits>
+
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
 #include "jfa_timing.hpp"
@@ -79,16 +81,8 @@ struct DkdvSmem {
   char dout[2][QTILE];
   float lse2[2][QB];
   float delta[2][QB];
-  float dpart[4][QB];  // per-wave partial row sums of P o dP
-  int split[4];        // per-wave: dS carried as two bf16 terms
-  char k[BCAST ? tile_bytes<BN, D>() : 16];
-  union {
-    struct {
-      char hi[BN * TR_ONLY_ROW_BYTES_64];  // dS as [key][query], bf16 high terms
-      char lo[BN * TR_ONLY_ROW_BYTES_64];  // bf16 remainders (zero where not split)
-    } ds;
-    float pdp[BN][QB + PDP_PAD];  // P o dP as [key][query]
-  } u;
+  float dpart[4][QB];            // per-wave partial row sums of P o dP
+  float pdp[BN][QB + PDP_PAD];   // P o dP as [key][query]
 };
 
 template <int D, bool CAUSAL, bool BCAST>
@@ -104,15 +98,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const int H = a.H, Lq = a.Lq;
   const int64_t ld = (int64_t)H * D;
   const float c2 = a.scale_log2;
-
-  float* part = nullptr;
-  if (BCAST) {
-    // This workgroup's private dQ partial [H][Lq][D], cleared first.
-    const int64_t n = (int64_t)H * Lq * D;
-    part = a.dq_part + (int64_t)slot * n;
-    for (int64_t i = (int64_t)tid * 4; i < n; i += NT * 4)
-      *reinterpret_cast<f32x4*>(part + i) = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
 
   for (int64_t pass = 0;; ++pass) {
     const int64_t t = zigzag_tile(pass, slot, a.P);
@@ -191,11 +176,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       load_block(m_first);
       store_block(0);
     }
-    if (BCAST) {
-      TileLoader<BN, D, NT> kl;
-      kl.load(a.k + (s0 * H + h) * (int64_t)D + (int64_t)k0 * ld, ld, min(BN, L - k0), tid);
-      kl.store(sm.k, tid);
-    }
     __syncthreads();
 
     for (int m = m_first; m < m_end; ++m) {
@@ -248,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = pf[i4 * 4 + e] * dpacc[i4 * 4 + e];
-            *reinterpret_cast<f32x4*>(&sm.u.pdp[wave * 32 + lc][s * 32 + i4 * 8 + g * 4]) = v;
+            *reinterpret_cast<f32x4*>(&sm.pdp[wave * 32 + lc][s * 32 + i4 * 8 + g * 4]) = v;
           }
         }
         __syncthreads();
@@ -256,20 +236,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           const int q = tid & (QB - 1), kq = tid >> 6;  // 4 ranges of 32 keys
           float acc = 0.f;
 #pragma unroll 8
-          for (int kk = 0; kk < 32; ++kk) acc += sm.u.pdp[kq * 32 + kk][q];
+          for (int kk = 0; kk < 32; ++kk) acc += sm.pdp[kq * 32 + kk][q];
           sm.dpart[kq][q] = acc;
         }
         __syncthreads();
         if (tid < QB) {
           const float dsum = (sm.dpart[0][tid] + sm.dpart[1][tid]) + (sm.dpart[2][tid] + sm.dpart[3][tid]);
           sm.delta[buf][tid] = dsum;
-          // the self-attention dQ kernel runs next and reads it
-          if (!BCAST && m * QB + tid < nq) del_base[(int64_t)(m * QB + tid) * sld] = dsum;
+          // the dQ kernel runs next and reads it (this tile is the only one
+          // of its sequence and head)
+          if (m * QB + tid < nq) del_base[(int64_t)(m * QB + tid) * sld] = dsum;
         }
         __syncthreads();
       }
 
-      bool split_ds_any = false;
 #pragma unroll 1
       for (int s = 0; s < 2; ++s) {
         f32x16 sacc, dpacc;
@@ -295,7 +275,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         // product is taken twice; elsewhere one rounded bf16 operand is used.
         const bool split_p = __any(pmax > SPLIT_P);
         const bool split_ds = __any(dsmax > SPLIT_DS);
-        split_ds_any = split_ds_any || split_ds;
         uint32_t pp[2][4], dsp[2][4], plo[2][4], dslo[2][4];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -337,59 +316,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
             }
           }
         }
-        if (BCAST) {
-          // dS (two bf16 terms) to LDS as [key][query]: this wave's 32 key rows.
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int col = s * 32 + i4 * 8 + g * 4;
-            const int off = tile_off_col4<QB, TR_ONLY_ROW_BYTES_64>(wave * 32 + lc, col);
-            const int hh = i4 >> 1, e0 = (i4 & 1) * 2;
-            *reinterpret_cast<u32x2*>(sm.u.ds.hi + off) = u32x2{dsp[hh][e0], dsp[hh][e0 + 1]};
-            *reinterpret_cast<u32x2*>(sm.u.ds.lo + off) = u32x2{dslo[hh][e0], dslo[hh][e0 + 1]};
-          }
-        }
       }
 
-      if (BCAST) {
-        if (l == 0) sm.split[wave] = split_ds_any ? 1 : 0;
-        if (m == m_first) __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const bool any_split = (sm.split[0] | sm.split[1] | sm.split[2] | sm.split[3]) != 0;
-        // dQ[q][d] (block) = sum over the tile's 128 keys of dS[q][key] K[key][d].
-        // Wave w: query subtile (w & 1), head-dim tiles of half (w >> 1).
-        constexpr int DTW = DT / 2;
-        const int qs = wave & 1;
-        f32x16 dqa[DTW];
-#pragma unroll
-        for (int x = 0; x < DTW; ++x) dqa[x] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < BN / 16; ++kk) {
-          const int kr0 = kk * 16 + g * 8;
-          const bf16x8 ahi = lds_operand_tr<QB, TR_ONLY_ROW_BYTES_64>(sm.u.ds.hi, kr0, kr0 + 4, qs * 32);
-          bf16x8 alo = ahi;
-          if (any_split) alo = lds_operand_tr<QB, TR_ONLY_ROW_BYTES_64>(sm.u.ds.lo, kr0, kr0 + 4, qs * 32);
-#pragma unroll
-          for (int x = 0; x < DTW; ++x) {
-            const int dt = (wave >> 1) * DTW + x;
-            const bf16x8 kb = lds_operand_tr<D>(sm.k, kr0, kr0 + 4, dt * 32);
-            dqa[x] = mfma32(ahi, kb, dqa[x]);
-            if (any_split) dqa[x] = mfma32(alo, kb, dqa[x]);
-          }
-        }
-        // C layout: lane -> head-dim column, registers -> query rows.
-#pragma unroll
-        for (int x = 0; x < DTW; ++x) {
-          const int dcol = ((wave >> 1) * DTW + x) * 32 + lc;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = m * QB + qs * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-            if (q < Lq) {
-              float* dst = part + ((int64_t)h * Lq + q) * D + dcol;
-              unsafeAtomicAdd(dst, dqa[x][i]);
-            }
-          }
-        }
-      }
       if (m + 1 < m_end) store_block(buf ^ 1);
       __syncthreads();
     }
@@ -418,18 +346,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------- dQ reduce ----
-// dq[e] = scale * sum_{w < P} part[w][e], summed as a perfect binary tree
-// over MAXP leaves (leaves w >= P are zero), left operand first.
+// dq[h][q][:] = scale * sum over the NC partials of (h, q-block), summed as a
+// perfect binary tree over MAXP leaves (leaves c >= NC are zero), left
+// operand first.  Partials: [H][n_qb][NC][BM][d].
 constexpr int MAXP = 256;
 
 __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part, float* __restrict__ dq,
-                                                 int64_t n, int P, float scale) {
+                                                 int H, int Lq, int d, int BM, int n_qb, int NC, float scale) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)H * Lq * d;
   if (e >= n) return;
+  const int col = (int)(e % d);
+  const int64_t hq = e / d;
+  const int q = (int)(hq % Lq), h = (int)(hq / Lq);
+  const int qb = q / BM, r = q - qb * BM;
+  const int64_t stride = (int64_t)BM * d;  // between the partials of consecutive chunks
+  const float* p0 = part + (((int64_t)h * n_qb + qb) * NC) * stride + (int64_t)r * d + col;
   float s[9];
 #pragma unroll
   for (int w = 0; w < MAXP; ++w) {
-    float x = w < P ? part[(int64_t)w * n + e] : 0.f;
+    float x = w < NC ? p0[(int64_t)w * stride] : 0.f;
     // Leaf w closes one subtree per trailing one bit of w: merge them.
     int lvl = 0;
 #pragma unroll
@@ -444,143 +380,267 @@ __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part,
   dq[e] = s[8] * scale;
 }
 
-// ------------------------------------------------ self-attention dQ ----
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dq_self_kernel(BwdArgs a) {
-  constexpr int BN = DQ_KV_STEP, KS = D / 16, DT = D / 32, BM = DQ_BM;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][tile_bytes<BN, D>()];  // [buffer][K, V]
+// ------------------------------------------------------------------ dQ ----
+// dQ for a block of BM = NW*32 query rows: loop over the K/V rows it sees,
+// recompute S^T = K Q^T and dP^T = V dO^T, form dS^T = P^T o (dP^T - delta)
+// and accumulate dQ^T += K^T dS^T in registers.  One lane owns one query
+// row (the forward's layout), so lse and delta are per-lane scalars.
+//   self mode:      persistent over the query-block tile list; a tile sees
+//                   its own sequence and writes its dQ rows.
+//   broadcast mode: one workgroup per (head, query block, chunk); chunk c
+//                   takes every NC-th sequence of the length-sorted order
+//                   (so chunks get alike mixes of lengths), and writes its
+//                   fp32 partial for dq_reduce.
+template <int D, int NW, bool CAUSAL, bool BCAST>
+struct DqCfg {
+  static constexpr int NT = NW * WAVE;
+  static constexpr int BN = DQ_KV_STEP;
+  static constexpr int BM = NW * 32;
+  static constexpr int KS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int TILE_BYTES = tile_bytes<BN, D>();
+  static constexpr bool DMA = D == 128;
+  static constexpr int IPS = 2 * BN / NW;  // row copies per wave per step
+  static constexpr int DEP = DMA ? ((2 * IPS <= 63) ? 3 : 2) : 1;
+  static constexpr int NBUF = DEP + 1;
+};
+
+template <int D, int NW, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
+  using C = DqCfg<D, NW, CAUSAL, BCAST>;
+  constexpr int BN = C::BN, BM = C::BM, KS = C::KS, DT = C::DT, NT = C::NT;
+  constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::TILE_BYTES];  // [buffer][K, V]
   const int tid = threadIdx.x;
   const int wave = tid / WAVE, l = tid % WAVE, g = l / 32, lc = l % 32;
-  const int slot = logical_slot(blockIdx.x, a.P_dq);
-  const int64_t T = *a.n_qtiles;
   const int H = a.H;
   const int64_t ld = (int64_t)H * D;
   const float c2 = a.scale_log2;
 
-  for (int64_t pass = 0;; ++pass) {
-    const int64_t t = zigzag_tile(pass, slot, a.P_dq);
-    if (t >= T) break;
-    const TileRec tile = a.qtiles[t];
-    int64_t s0;
-    const int L = (int)seq_range(a.offsets, tile.b, a.total_len, &s0);
-    const int h = tile.h;
-    const int q0 = tile.blk * BM;
-    const int wq0 = q0 + wave * 32;
-    const int qi = wq0 + lc;
-    const bool q_ok = qi < L;
+  bf16x8 qreg[KS], doreg[KS];
+  float lse2 = INFINITY, del = 0.f;
+  f32x16 dqa[DT];
+  TileLoader<BN, D, NT> kl, vl;
 
-    bf16x8 qreg[KS], doreg[KS];
-    {
-      const uint16_t* qr = a.q + ((s0 + qi) * H + h) * (int64_t)D;
-      const uint16_t* dr = a.dout + ((s0 + qi) * H + h) * (int64_t)D;
+  // Rows of Q (B operand Q^T) for this wave's query rows.
+  auto load_rows = [&](const uint16_t* rowp, bool ok, bf16x8* dst) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (ok) x = *reinterpret_cast<const u32x4*>(rowp + ks * 16 + g * 8);
+      dst[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  };
+
+  // One K/V step: S^T, dP^T, dS^T, dQ^T += K^T dS^T, two 32-key halves in turn.
+  auto step_math = [&](const char* Ks, const char* Vs, int k0, int L, int qi, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-        if (q_ok) {
-          x = *reinterpret_cast<const u32x4*>(qr + ks * 16 + g * 8);
-          y = *reinterpret_cast<const u32x4*>(dr + ks * 16 + g * 8);
+        const int off = tile_off<D>(kt * 32 + lc, ks * 2 + g);
+        sacc = mfma32(lds_read16(Ks, off), qreg[ks], sacc);
+        dpacc = mfma32(lds_read16(Vs, off), doreg[ks], dpacc);
+      }
+      // C layout: lane owns query qi; register i is key
+      // k0 + kt*32 + 8*(i/4) + 4g + i%4.
+      float dsf[16];
+      float dsmax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(sacc[i] * c2 - lse2);
+        if (MASKED) {
+          const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          const bool ok = key < L && (!CAUSAL || key <= qi);
+          pv = ok ? pv : 0.f;
         }
-        qreg[ks] = __builtin_bit_cast(bf16x8, x);
-        doreg[ks] = __builtin_bit_cast(bf16x8, y);
+        dsf[i] = pv * (dpacc[i] - del);
+        dsmax = fmaxf(dsmax, fabsf(dsf[i]));
+      }
+      // dQ sums dS over many keys (all keys of a chunk of sequences in
+      // broadcast mode): large dS values are carried as two bf16 terms.
+      const bool split = __any(dsmax > SPLIT_DS);
+      uint32_t hi[2][4], lo[2][4];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const int hh = i >> 3, e = (i & 7) >> 1;
+        if (split) {
+          split_bf16x2(dsf[i], dsf[i + 1], &hi[hh][e], &lo[hh][e]);
+        } else {
+          hi[hh][e] = pack_bf16x2(dsf[i], dsf[i + 1]);
+          lo[hh][e] = 0u;
+        }
+      }
+      // dQ^T += K^T dS^T; K^T by transpose read, keys in the order of the
+      // dS^T registers.
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r0 = kt * 32 + hh * 16 + g * 4;
+        bf16x8 ka[DT];
+        if constexpr (C::DMA) {
+          const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
+          const uint32_t a0 = lds_addr(Ks + tile_off_col4<D>(r0 + jj, cq));
+          lds_operand_tr_x4(a0, a0 + 8 * TileGeom<D>::ROW_BYTES, ka);
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) ka[dt] = lds_operand_tr<D>(Ks, r0, r0 + 8, dt * 32);
+        }
+        const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{hi[hh][0], hi[hh][1], hi[hh][2], hi[hh][3]});
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], db, dqa[dt]);
+        if (split) {
+          const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{lo[hh][0], lo[hh][1], lo[hh][2], lo[hh][3]});
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], dl, dqa[dt]);
+        }
       }
     }
-    const float lse2 = q_ok ? a.lse[(s0 + qi) * H + h] * LOG2E : INFINITY;
-    const float del = q_ok ? a.delta[(s0 + qi) * H + h] : 0.f;
+  };
 
-    f32x16 dqa[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
-
+  // All K/V steps of one sequence (rows s0.. of head h), with the same ring
+  // discipline as the forward.  `after_prologue` runs once the first copies
+  // are in flight (loads of per-sequence rows go there).
+  auto sequence = [&](int64_t s0, int L, int h, int q0, int wq0, int qi, auto after_prologue) {
     int kv_end = L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     const int n_bulk = CAUSAL ? min(q0 / BN, L / BN) : L / BN;
-
     const uint16_t* kbase = a.k + (s0 * H + h) * (int64_t)D;
     const uint16_t* vbase = a.v + (s0 * H + h) * (int64_t)D;
-    TileLoader<BN, D, NT> kl, vl;
-    __syncthreads();
-    if (n_kv > 0) {
-      kl.load(kbase, ld, min(BN, L), tid);
-      vl.load(vbase, ld, min(BN, L), tid);
-      kl.store(smem[0][0], tid);
-      vl.store(smem[0][1], tid);
-    }
-    __syncthreads();
-
-    for (int j = 0; j < n_kv; ++j) {
-      const int buf = j & 1;
+    auto issue = [&](int j) {
+      char* Kd = smem[j % NBUF][0];
+      char* Vd = smem[j % NBUF][1];
       const int k0 = j * BN;
-      if (j + 1 < n_kv) {
+#pragma unroll
+      for (int i = 0; i < BN / NW; ++i) {
+        const int row = wave * (BN / NW) + i;
+        const int src = min(k0 + row, L - 1);
+        dma_row256(kbase + (int64_t)src * ld, Kd + row * TileGeom<D>::ROW_BYTES);
+        dma_row256(vbase + (int64_t)src * ld, Vd + row * TileGeom<D>::ROW_BYTES);
+      }
+    };
+    __syncthreads();  // earlier readers of the ring are done
+    if constexpr (C::DMA) {
+      wait_vmcnt<0>();
+      for (int jj = 0; jj < DEP && jj < n_kv; ++jj) issue(jj);
+      after_prologue();
+    } else {
+      after_prologue();
+      if (n_kv > 0) {
+        kl.load(kbase, ld, min(BN, L), tid);
+        vl.load(vbase, ld, min(BN, L), tid);
+        kl.store(smem[0][0], tid);
+        vl.store(smem[0][1], tid);
+      }
+      __syncthreads();
+    }
+    auto kv_step = [&](int j, auto masked_tag) {
+      const int buf = j % NBUF;
+      const int k0 = j * BN;
+      if constexpr (C::DMA) {
+        const int ahead = min(DEP, n_kv - j) - 1;
+        if constexpr (DEP >= 3) {
+          if (ahead >= 2) wait_vmcnt<2 * IPS>();
+          else if (ahead == 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        } else {
+          if (ahead >= 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        }
+        barrier_lds();
+        if (j + DEP < n_kv) issue(j + DEP);
+      } else if (j + 1 < n_kv) {
         const int nxt = k0 + BN;
         kl.load(kbase + (int64_t)nxt * ld, ld, min(BN, L - nxt), tid);
         vl.load(vbase + (int64_t)nxt * ld, ld, min(BN, L - nxt), tid);
       }
-      const bool active = !CAUSAL || (k0 <= wq0 + 31);
-      if (active) {
-        const char* Ks = smem[buf][0];
-        const char* Vs = smem[buf][1];
-        const bool masked = j >= n_bulk;
-        uint32_t dsp[2][2][4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int off = tile_off<D>(kt * 32 + lc, ks * 2 + g);
-            sacc = mfma32(lds_read16(Ks, off), qreg[ks], sacc);
-            dpacc = mfma32(lds_read16(Vs, off), doreg[ks], dpacc);
-          }
-          // C layout: lane owns query qi; register i is key
-          // k0 + kt*32 + 8*(i/4) + 4g + i%4.
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            float dsv[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              float pv = fast_exp2(sacc[i + e] * c2 - lse2);
-              if (masked) {
-                const int key = k0 + kt * 32 + ((i + e) >> 2) * 8 + g * 4 + ((i + e) & 3);
-                const bool ok = key < L && (!CAUSAL || key <= qi);
-                pv = ok ? pv : 0.f;
-              }
-              dsv[e] = pv * (dpacc[i + e] - del);
-            }
-            dsp[kt][i >> 3][(i & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
-          }
+      const bool active = !(CAUSAL && decltype(masked_tag)::value) || (k0 <= wq0 + 31);
+      if (active) step_math(smem[buf][0], smem[buf][1], k0, L, qi, masked_tag);
+      if constexpr (!C::DMA) {
+        if (j + 1 < n_kv) {
+          kl.store(smem[buf ^ 1][0], tid);
+          vl.store(smem[buf ^ 1][1], tid);
         }
-        // dQ^T += K^T dS^T; K^T through the transpose read, keys in the
-        // order of the dS^T registers.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r0 = kt * 32 + hh * 16 + g * 4;
-            const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dsp[kt][hh][0], dsp[kt][hh][1], dsp[kt][hh][2], dsp[kt][hh][3]});
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-              dqa[dt] = mfma32(lds_operand_tr<D>(Ks, r0, r0 + 8, dt * 32), db, dqa[dt]);
-          }
+        __syncthreads();
       }
-      if (j + 1 < n_kv) {
-        kl.store(smem[buf ^ 1][0], tid);
-        vl.store(smem[buf ^ 1][1], tid);
-      }
-      __syncthreads();
-    }
+    };
+    const int n_plain = min(n_bulk, n_kv);
+    for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
+    for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+  };
 
-    if (q_ok) {
-      float* dst = a.dq + ((s0 + qi) * H + h) * (int64_t)D;
+  if constexpr (!BCAST) {
+    const int slot = logical_slot(blockIdx.x, a.P_dq);
+    const int64_t T = *a.n_qtiles;
+    for (int64_t pass = 0;; ++pass) {
+      const int64_t t = zigzag_tile(pass, slot, a.P_dq);
+      if (t >= T) break;
+      const TileRec tile = a.qtiles[t];
+      int64_t s0;
+      const int L = (int)seq_range(a.offsets, tile.b, a.total_len, &s0);
+      const int h = tile.h;
+      const int q0 = tile.blk * BM;
+      const int wq0 = q0 + wave * 32;
+      const int qi = wq0 + lc;
+      const bool q_ok = qi < L;
+      load_rows(a.q + ((s0 + qi) * H + h) * (int64_t)D, q_ok, qreg);
+      load_rows(a.dout + ((s0 + qi) * H + h) * (int64_t)D, q_ok, doreg);
+      lse2 = q_ok ? a.lse[(s0 + qi) * H + h] * LOG2E : INFINITY;
+      del = q_ok ? a.delta[(s0 + qi) * H + h] : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
+      sequence(s0, L, h, q0, wq0, qi, [] {});
+      if (q_ok) {
+        float* dst = a.dq + ((s0 + qi) * H + h) * (int64_t)D;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 v;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = dqa[dt][i4 * 4 + e] * a.scale;
-          *reinterpret_cast<f32x4*>(dst + dt * 32 + i4 * 8 + g * 4) = v;
-        }
+          for (int i4 = 0; i4 < 4; ++i4) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = dqa[dt][i4 * 4 + e] * a.scale;
+            *reinterpret_cast<f32x4*>(dst + dt * 32 + i4 * 8 + g * 4) = v;
+          }
+      }
     }
+  } else {
+    const int NC = a.dq_chunks, n_qb = a.dq_qblocks, Lq = a.Lq;
+    const int item = blockIdx.x;
+    const int h = item / (n_qb * NC);
+    const int rem = item - h * n_qb * NC;
+    const int qb = rem / NC, c = rem - qb * NC;
+    const int q0 = qb * BM;
+    const int wq0 = q0 + wave * 32;
+    const int qi = wq0 + lc;
+    const bool q_ok = qi < Lq;
+    load_rows(a.q + ((int64_t)h * Lq + qi) * D, q_ok, qreg);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
+    for (int r = c; r < a.B; r += NC) {
+      const int b = a.seq_order[r];
+      int64_t s0;
+      const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
+      if (L <= 0) continue;
+      const int64_t row = ((int64_t)b * H + h) * Lq + qi;
+      sequence(s0, L, h, q0, wq0, qi, [&] {
+        load_rows(a.dout + row * D, q_ok, doreg);
+        lse2 = q_ok ? a.lse[row] * LOG2E : INFINITY;
+        del = q_ok ? a.delta[row] : 0.f;
+      });
+    }
+    // this chunk's fp32 partial, rows q0.. of (h, qb): [BM][D]
+    float* dst = a.dq_part + (int64_t)item * BM * D + (int64_t)(wave * 32 + lc) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dqa[dt][i4 * 4 + e];
+        *reinterpret_cast<f32x4*>(dst + dt * 32 + i4 * 8 + g * 4) = v;
+      }
   }
 }
 
@@ -595,35 +655,40 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  hipError_t e;
   if (a.broadcast_q) {
     if (a.causal)
       JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a);
     else
       JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int items = a.H * a.dq_qblocks * a.dq_chunks;
+    if (a.causal)
+      JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, true, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+    else
+      JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, false, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = (int64_t)a.H * a.Lq * D;
-    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dq_part, a.dq, n,
-                       a.P, a.scale);
+    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dq_part,
+                     a.dq, a.H, a.Lq, D, DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale);
     return hipGetLastError();
   }
   if (a.causal)
     JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a);
   else
     JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.causal)
-    JFA_TIMED_LAUNCH(K_DQ_SELF, st, (dq_self_kernel<D, true>), dim3(a.P_dq), dim3(256), 0, st, a);
+    JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM / 32, true, false>), dim3(a.P_dq), dim3(DQ_BM * 2), 0, st, a);
   else
-    JFA_TIMED_LAUNCH(K_DQ_SELF, st, (dq_self_kernel<D, false>), dim3(a.P_dq), dim3(256), 0, st, a);
+    JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM / 32, false, false>), dim3(a.P_dq), dim3(DQ_BM * 2), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  if (a.broadcast_q && a.P > MAXP) return hipErrorInvalidValue;
+  if (a.broadcast_q && a.dq_chunks > MAXP) return hipErrorInvalidValue;
   if (a.d == 64) return launch_bwd_d<64>(a, stream);
   return launch_bwd_d<128>(a, stream);
 }

@@ -19,6 +19,7 @@ constexpr int FWD_BM_SELF = 128;   // 4 waves x 32 query rows
 constexpr int BWD_BN = 128;        // 4 waves x 32 key rows
 constexpr int BWD_QB = 64;         // query rows per step of the dK/dV kernel
 constexpr int DQ_BM = 128;         // self-attention dQ kernel: 4 waves x 32 query rows
+constexpr int DQ_BM_BCAST = 256;   // broadcast dQ kernel: 8 waves x 32 query rows
 constexpr int DQ_KV_STEP = 64;
 constexpr int MAX_B = 8192;        // single-workgroup sequence sort
 
@@ -69,7 +70,10 @@ struct BwdArgs {
   float* dk;
   float* dv;
   float* delta;           // [rows] scratch
-  float* dq_part;         // [P][H][Lq][d] broadcast-mode partials
+  float* dq_part;         // [H][n_qb][NC][DQ_BM_BCAST][d] broadcast-mode partials
+  const int* seq_order;   // sequences sorted by length (broadcast dQ chunks)
+  int dq_qblocks;         // n_qb = cdiv(Lq, DQ_BM_BCAST)
+  int dq_chunks;          // NC
   const TileRec* ktiles;  // key-block tiles (dK/dV kernel)
   const int64_t* n_ktiles;
   const TileRec* qtiles;  // query-block tiles (self-attention dQ kernel)

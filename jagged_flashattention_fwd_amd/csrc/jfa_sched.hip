@@ -10,7 +10,8 @@
 //      index first), counts each sequence's tiles and takes an exclusive
 //      prefix sum of the counts in sorted order;
 //   2. one workgroup per sequence writes that sequence's tiles -- heads
-//      ascending, blocks heaviest first -- at its prefix-sum position.
+//      ascending, blocks heaviest first -- at its prefix-sum position
+//      (broadcast-Q backward: head-major, see sched_expand).
 // The persistent kernels then take tile t in zigzag order (jfa_device.hpp).
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
@@ -108,11 +109,19 @@ __global__ __launch_bounds__(256) void sched_expand(SchedArgs a, Schedule s) {
   const int64_t L = seq_range(a.offsets, b, a.total_len, &s0);
   const int64_t nblk = a.pass == 0 ? cdiv64(a.broadcast_q ? a.Lq : L, a.blk) : cdiv64(L, a.blk);
   if (nblk <= 0) return;
+  // Broadcast-Q backward: the list is head-major (all tiles of head 0, then
+  // head 1, ...), so at any time the persistent workgroups work on one head
+  // and their dQ partials for that head stay cache-resident.  Every
+  // sequence has the same tile count in every head, so head h's part of the
+  // list starts at h * (T / H) and this sequence's tiles at cum[r] / H.
+  const bool head_major = a.pass == 1 && a.broadcast_q;
+  const int64_t T = s.cum[a.B];
   for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
     const int h = (int)(j / nblk);
     const int64_t i = j - (int64_t)h * nblk;
     const int blk = (int)(a.pass == 0 ? nblk - 1 - i : i);
-    s.tiles[start + j] = TileRec{b, h, blk, 0};
+    const int64_t pos = head_major ? h * (T / a.H) + start / a.H + i : start + j;
+    if (pos < s.max_tiles) s.tiles[pos] = TileRec{b, h, blk, 0};
   }
 }
 

@@ -12,7 +12,7 @@ enum KernelId {
   K_DELTA,
   K_DKDV,
   K_DQ_REDUCE,
-  K_DQ_SELF,
+  K_DQ,
   K_COUNT
 };
 

@@ -25,6 +25,9 @@ count P are parameters; tie-breaks are this library's reading):
      heaviest first -- forward query blocks descending (a causal query
      block sees more keys the later it is), backward key blocks ascending
      (a causal key block is seen by more query blocks the earlier it is).
+     Broadcast-Q backward only: the list is head-major instead -- all of
+     head 0's tiles (sequences in the order of rule 2, blocks ascending),
+     then head 1's, and so on.
   5. Tile t goes to worker slot: pass p = t // P, s = t % P,
      slot = s if p is even else P - 1 - s.
 """
@@ -57,9 +60,10 @@ def zigzag_slot(t: int, P: int) -> int:
 
 def schedule(lengths, H: int, Lq: int, broadcast_q: bool, pass_: int, BM: int, BN: int, P: int):
     """Full tile list: [(b, h, block, slot), ...] in tile order t = 0, 1, ..."""
-    out = []
+    triples = []
     for b in sequence_order(lengths):
         for (h, blk) in tiles_of_sequence(int(lengths[b]), H, Lq, broadcast_q, pass_, BM, BN):
-            t = len(out)
-            out.append((b, h, blk, zigzag_slot(t, P)))
-    return out
+            triples.append((b, h, blk))
+    if pass_ == 1 and broadcast_q:
+        triples = [x for h in range(H) for x in triples if x[1] == h]
+    return [(b, h, blk, zigzag_slot(t, P)) for t, (b, h, blk) in enumerate(triples)]

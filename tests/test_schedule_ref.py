@@ -78,3 +78,16 @@ def test_zigzag(P):
     # a slot's tile count differs by at most one from any other slot's
     counts = np.bincount(slots, minlength=P)
     assert counts.max() - counts.min() <= 1
+
+
+def test_broadcast_backward_is_head_major():
+    lengths = [300, 5, 129]
+    tiles = sr.schedule(lengths, 3, 16, True, 1, 64, 128, P=4)
+    heads = [t[1] for t in tiles]
+    assert heads == sorted(heads)
+    # within a head: sequences longest first, blocks ascending
+    h0 = [(t[0], t[2]) for t in tiles if t[1] == 0]
+    assert h0 == [(0, 0), (0, 1), (0, 2), (2, 0), (2, 1), (1, 0)]
+    # self-attention backward keeps the sequence-major order
+    tiles = sr.schedule(lengths, 3, 0, False, 1, 64, 128, P=4)
+    assert [t[:3] for t in tiles[:4]] == [(0, 0, 0), (0, 0, 1), (0, 0, 2), (0, 1, 0)]
