@@ -53,6 +53,14 @@ def useful_flops(lengths, H: int, d: int, Lq: int, causal: bool, broadcast_q: bo
     return 4 * d * H * n, 10 * d * H * n
 
 
+def dq_split(B: int, H: int, Lq: int, P: int):
+    """Broadcast dQ work split of the library: (query blocks of 256 rows,
+    sequence chunks)."""
+    n_qb = -(-Lq // 256)
+    nc = max(1, min(P // (H * n_qb), B, 256))
+    return n_qb, nc
+
+
 def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q: bool, P: int) -> int:
     """Bytes a kernel must move between HBM and the chip for one launch:
     every input element read once and every output element written once."""
@@ -65,27 +73,33 @@ def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q
     if kernel == "fwd_kernel":
         return 2 * kv + q_bytes + row_bf16 + rows * 4
     if kernel == "delta_kernel":
-        return 2 * row_bf16 + rows * 4
+        # O, dO, lse in; delta, lse*log2(e) out
+        return 2 * row_bf16 + 3 * rows * 4
     if kernel == "dkdv_kernel":
-        # K, V, Q, dO, lse, delta in; dK, dV (fp32) out; broadcast dQ partials out
-        b = 2 * kv + q_bytes + row_bf16 + 2 * rows * 4 + 2 * T * H * d * 4
+        # K, V, Q, dO, lse*log2(e), delta in; dK, dV (fp32) out
+        return 2 * kv + q_bytes + row_bf16 + 2 * rows * 4 + 2 * T * H * d * 4
+    if kernel == "dq_kernel":
+        # K, V, Q, dO, lse, delta in; dQ (self) or the fp32 partials (broadcast) out
+        b = 2 * kv + q_bytes + row_bf16 + 2 * rows * 4
         if broadcast_q:
-            b += P * H * Lq * d * 4
-        return b
+            n_qb, nc = dq_split(B, H, Lq, P)
+            return b + H * n_qb * nc * 256 * d * 4
+        return b + T * H * d * 4
     if kernel == "dq_reduce":
-        return (P + 1) * H * Lq * d * 4
-    if kernel == "dq_self_kernel":
-        return 2 * kv + q_bytes + row_bf16 + 2 * rows * 4 + T * H * d * 4
+        n_qb, nc = dq_split(B, H, Lq, P)
+        return H * n_qb * nc * 256 * d * 4 + H * Lq * d * 4
     return 0
 
 
 def kernel_flops(kernel: str, fwd_flops: int, bwd_flops: int, broadcast_q: bool) -> int:
+    """Useful (unpadded) flops of one launch.  dK/dV: S, dP, dV, dK (4 of
+    the 5 backward products); dQ: the dQ product plus S and dP recomputed."""
     if kernel == "fwd_kernel":
         return fwd_flops
     if kernel == "dkdv_kernel":
-        return bwd_flops if broadcast_q else bwd_flops * 8 // 10   # 4 of 5 GEMMs
-    if kernel == "dq_self_kernel":
-        return bwd_flops * 2 // 10 + fwd_flops   # dQ GEMM + recomputed S, dP
+        return bwd_flops * 8 // 10
+    if kernel == "dq_kernel":
+        return bwd_flops * 2 // 10 + fwd_flops
     return 0
 
 

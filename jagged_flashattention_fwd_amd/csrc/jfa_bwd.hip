@@ -7,24 +7,20 @@
 // ("Optimizing Jagged Flash Attention with TLX", "1. The Challenge").
 //
 // Kernels, in launch order:
-//   delta_kernel   streaming pre-pass, delta = rowsum(dO o O) (O as stored).
-//   dkdv_kernel    persistent; a tile is 128 keys of one (sequence, head), its
-//                  K/V held in registers while query blocks of 64 rows stream
-//                  through LDS -- the K/V-outer, dense-Q-inner loop of
-//                  "Scheduling jagged tiles across SMs".  Per query block:
-//                  S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q
-//                  and, in broadcast mode, the fifth product dQ += dS K
-//                  ("2-CTA collaborative MMA (backward)" counts five GEMMs per
-//                  K/V block).  Broadcast dQ goes to a private fp32 partial
-//                  per workgroup instead of a contended reduce-add into one
-//                  buffer ("Multi-stage dQ staging" names that reduce-add the
-//                  main backward bottleneck); the tile list is handed out
-//                  statically, so each partial sums in a fixed order.
-//   dq_reduce      sums the partials with a fixed pairwise tree (bitwise
-//                  reproducible), times scale.
-//   dq_self_kernel self-attention dQ: a tile is 128 query rows; loops over
-//                  K/V steps recomputing S^T, dP^T, dS^T and accumulating
-//                  dQ^T += K^T dS^T.  No atomics.
+//   delta_kernel        streaming pre-pass: delta = rowsum(dO o O) (O as
+//                       stored) and lse * log2(e), per query row.
+//   delta_exact_kernel  delta again, exactly, for sequences of at most 128
+//                       keys (jfa_dkdv.hip).
+//   dkdv_kernel         dK and dV (jfa_dkdv.hip).
+//   dq_kernel           dQ.  Self-attention: persistent, a tile is 128 query
+//                       rows, looping over K/V steps recomputing S^T, dP^T,
+//                       dS^T and accumulating dQ^T += K^T dS^T.  Broadcast Q:
+//                       one workgroup per (head, 256-row query block, chunk of
+//                       sequences) writes a private fp32 partial, summed by
+//   dq_reduce           with a fixed pairwise tree (bitwise reproducible) --
+//                       per-workgroup partials instead of a contended
+//                       reduce-add into one buffer, which "Multi-stage dQ
+//                       staging" names the main backward bottleneck.
 // Loops are peeled ("Loop peeling"): the causal diagonal blocks take the
 // masked path, the rest do not.
 #include <type_traits>
@@ -37,18 +33,20 @@ namespace jfa {
 
 namespace {
 
-constexpr int NW = 4;
-constexpr int NT = NW * WAVE;
-// Split thresholds of the two-term bf16 operands in dV and dK (see dkdv_kernel).
-constexpr float SPLIT_P = 1.0f / 16.0f;
+// Threshold of the two-term bf16 dS operand in dQ: rounding dS to bf16 costs
+// up to 2^-9 of each value, summed over many keys; where a subtile holds a
+// value above this, the rounded remainder is multiplied in as well.
 constexpr float SPLIT_DS = 0.25f;
 
 // ------------------------------------------------------------- delta ----
-// Rows of d elements; D/8 threads per row, 16 bytes each.
+// Rows of d elements; D/8 threads per row, 16 bytes each.  Also writes the
+// row's lse in base-2 units (lse * log2(e)), the form the dK/dV kernel reads.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
-                                                    float* __restrict__ delta, int64_t rows) {
+                                                    const float* __restrict__ lse,
+                                                    float* __restrict__ delta, float* __restrict__ lse2,
+                                                    int64_t rows) {
   constexpr int TPR = D / 8;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -65,282 +63,9 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
     }
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
-    if (c == 0) delta[row] = acc;
-  }
-}
-
-// ------------------------------------------------------------- dK / dV ----
-constexpr int PDP_PAD = 4;  // fp32 row padding of the P o dP staging tile
-
-template <int D, bool CAUSAL, bool BCAST>
-struct DkdvSmem {
-  static constexpr int QB = BWD_QB;
-  static constexpr int BN = BWD_BN;
-  static constexpr int QTILE = tile_bytes<QB, D>();
-  char q[2][QTILE];
-  char dout[2][QTILE];
-  float lse2[2][QB];
-  float delta[2][QB];
-  float dpart[4][QB];            // per-wave partial row sums of P o dP
-  float pdp[BN][QB + PDP_PAD];   // P o dP as [key][query]
-};
-
-template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
-  constexpr int QB = BWD_QB, BN = BWD_BN, KS = D / 16, DT = D / 32;
-  using Smem = DkdvSmem<D, CAUSAL, BCAST>;
-  __shared__ __attribute__((aligned(16))) Smem sm;
-
-  const int tid = threadIdx.x;
-  const int wave = tid / WAVE, l = tid % WAVE, g = l / 32, lc = l % 32;
-  const int slot = logical_slot(blockIdx.x, a.P);
-  const int64_t T = *a.n_ktiles;
-  const int H = a.H, Lq = a.Lq;
-  const int64_t ld = (int64_t)H * D;
-  const float c2 = a.scale_log2;
-
-  for (int64_t pass = 0;; ++pass) {
-    const int64_t t = zigzag_tile(pass, slot, a.P);
-    if (t >= T) break;
-    const TileRec tile = a.ktiles[t];
-    int64_t s0;
-    const int L = (int)seq_range(a.offsets, tile.b, a.total_len, &s0);
-    const int h = tile.h;
-    const int k0 = tile.blk * BN;         // first key of the tile
-    const int kw = k0 + wave * 32 + lc;   // this lane's key
-    const bool key_ok = kw < L;
-    const int nq = BCAST ? Lq : L;
-    // When the tile holds every key of its sequence, delta is recomputed
-    // here as rowsum(P o dP) from fp32 P and dP, instead of rowsum(dO o O)
-    // from the bf16-rounded O: for short sequences P is large and the O
-    // rounding would otherwise dominate the dK and dQ error.
-    const bool exact_delta = L <= BN;
-
-    // K and V rows of this lane's key as B operands (B[d][key] = K[key][d]).
-    bf16x8 kreg[KS], vreg[KS];
-    {
-      const uint16_t* kr = a.k + ((s0 + kw) * H + h) * (int64_t)D;
-      const uint16_t* vr = a.v + ((s0 + kw) * H + h) * (int64_t)D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-        if (key_ok) {
-          x = *reinterpret_cast<const u32x4*>(kr + ks * 16 + g * 8);
-          y = *reinterpret_cast<const u32x4*>(vr + ks * 16 + g * 8);
-        }
-        kreg[ks] = __builtin_bit_cast(bf16x8, x);
-        vreg[ks] = __builtin_bit_cast(bf16x8, y);
-      }
-    }
-    f32x16 dk[DT], dv[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
-
-    // Query blocks that can see a key of this tile.
-    const int m_first = CAUSAL ? k0 / QB : 0;
-    const int m_end = (nq + QB - 1) / QB;        // exclusive
-    // Blocks whose rows all lie at or after the tile's last key need no causal mask.
-    const int m_nomask = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
-
-    const uint16_t* qbase = BCAST ? a.q + (int64_t)h * Lq * D : a.q + (s0 * H + h) * (int64_t)D;
-    const int64_t qld = BCAST ? D : ld;
-    const uint16_t* dobase = BCAST ? a.dout + ((int64_t)tile.b * H + h) * Lq * D
-                                   : a.dout + (s0 * H + h) * (int64_t)D;
-    const float* lse_base = BCAST ? a.lse + ((int64_t)tile.b * H + h) * Lq : a.lse + s0 * H + h;
-    float* del_base = BCAST ? a.delta + ((int64_t)tile.b * H + h) * Lq : a.delta + s0 * H + h;
-    const int64_t sld = BCAST ? 1 : H;  // stride between rows of lse / delta
-
-    TileLoader<QB, D, NT> ql, dol;
-    float sv = 0.f;  // lse2 (threads 0..63) or delta (64..127) of the next block
-    auto load_block = [&](int m) {
-      const int r0 = m * QB;
-      const int nr = min(QB, nq - r0);
-      ql.load(qbase + (int64_t)r0 * qld, qld, nr, tid);
-      dol.load(dobase + (int64_t)r0 * qld, qld, nr, tid);
-      if (tid < QB) {
-        sv = tid < nr ? lse_base[(int64_t)(r0 + tid) * sld] * LOG2E : INFINITY;
-      } else if (tid < 2 * QB) {
-        const int r = tid - QB;
-        sv = r < nr ? del_base[(int64_t)(r0 + r) * sld] : 0.f;
-      }
-    };
-    auto store_block = [&](int buf) {
-      ql.store(sm.q[buf], tid);
-      dol.store(sm.dout[buf], tid);
-      if (tid < QB) sm.lse2[buf][tid] = sv;
-      else if (tid < 2 * QB) sm.delta[buf][tid - QB] = sv;
-    };
-
-    __syncthreads();  // the previous tile's readers are done with LDS
-    if (m_first < m_end) {
-      load_block(m_first);
-      store_block(0);
-    }
-    __syncthreads();
-
-    for (int m = m_first; m < m_end; ++m) {
-      const int buf = (m - m_first) & 1;
-      if (m + 1 < m_end) load_block(m + 1);
-      const char* Qs = sm.q[buf];
-      const char* Ds = sm.dout[buf];
-      const bool diag = CAUSAL && m < m_nomask;
-
-      // S = Q K^T and dP = dO V^T for query subtile s (32 rows) of the block.
-      // C layout: lane owns key kw; register i is query row
-      // m*QB + s*32 + 8*(i/4) + 4g + i%4.
-      auto scores = [&](int s, f32x16& sacc, f32x16& dpacc) {
-        sacc = f32x16{};
-        dpacc = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = tile_off<D>(s * 32 + lc, ks * 2 + g);
-          sacc = mfma32(lds_read16(Qs, off), kreg[ks], sacc);
-          dpacc = mfma32(lds_read16(Ds, off), vreg[ks], dpacc);
-        }
-      };
-      auto probs = [&](int s, const f32x16& sacc, float* pf) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int r = s * 32 + i4 * 8 + g * 4;
-          const f32x4 ls = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][r]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i4 * 4 + e;
-            const float pv = fast_exp2(sacc[i] * c2 - ls[e]);
-            bool ok = key_ok;
-            if (diag) ok = ok && (kw <= m * QB + r + e);
-            pf[i] = ok ? pv : 0.f;
-          }
-        }
-      };
-
-      if (exact_delta) {
-        // delta = rowsum(P o dP) over every key of the sequence (all in this
-        // tile); S and dP are recomputed below.
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          f32x16 sacc, dpacc;
-          scores(s, sacc, dpacc);
-          float pf[16];
-          probs(s, sacc, pf);
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = pf[i4 * 4 + e] * dpacc[i4 * 4 + e];
-            *reinterpret_cast<f32x4*>(&sm.pdp[wave * 32 + lc][s * 32 + i4 * 8 + g * 4]) = v;
-          }
-        }
-        __syncthreads();
-        {
-          const int q = tid & (QB - 1), kq = tid >> 6;  // 4 ranges of 32 keys
-          float acc = 0.f;
-#pragma unroll 8
-          for (int kk = 0; kk < 32; ++kk) acc += sm.pdp[kq * 32 + kk][q];
-          sm.dpart[kq][q] = acc;
-        }
-        __syncthreads();
-        if (tid < QB) {
-          const float dsum = (sm.dpart[0][tid] + sm.dpart[1][tid]) + (sm.dpart[2][tid] + sm.dpart[3][tid]);
-          sm.delta[buf][tid] = dsum;
-          // the dQ kernel runs next and reads it (this tile is the only one
-          // of its sequence and head)
-          if (m * QB + tid < nq) del_base[(int64_t)(m * QB + tid) * sld] = dsum;
-        }
-        __syncthreads();
-      }
-
-#pragma unroll 1
-      for (int s = 0; s < 2; ++s) {
-        f32x16 sacc, dpacc;
-        scores(s, sacc, dpacc);
-        float pf[16], dsf[16];
-        probs(s, sacc, pf);
-        float pmax = 0.f, dsmax = 0.f;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(&sm.delta[buf][s * 32 + i4 * 8 + g * 4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i4 * 4 + e;
-            dsf[i] = pf[i] * (dpacc[i] - dl[e]);
-            pmax = fmaxf(pmax, pf[i]);
-            dsmax = fmaxf(dsmax, fabsf(dsf[i]));
-          }
-        }
-        // Rounding P or dS to bf16 costs up to 2^-9 of each value, and dV /
-        // dK / dQ sum that error over many queries or keys.  Where a value is
-        // large (short or sharply peaked sequences) the operand is split into
-        // a truncated bf16 high part and a rounded bf16 remainder and the
-        // product is taken twice; elsewhere one rounded bf16 operand is used.
-        const bool split_p = __any(pmax > SPLIT_P);
-        const bool split_ds = __any(dsmax > SPLIT_DS);
-        uint32_t pp[2][4], dsp[2][4], plo[2][4], dslo[2][4];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const int hh = i >> 3, e = (i & 7) >> 1;
-          if (split_p) {
-            split_bf16x2(pf[i], pf[i + 1], &pp[hh][e], &plo[hh][e]);
-          } else {
-            pp[hh][e] = pack_bf16x2(pf[i], pf[i + 1]);
-            plo[hh][e] = 0u;
-          }
-          if (split_ds) {
-            split_bf16x2(dsf[i], dsf[i + 1], &dsp[hh][e], &dslo[hh][e]);
-          } else {
-            dsp[hh][e] = pack_bf16x2(dsf[i], dsf[i + 1]);
-            dslo[hh][e] = 0u;
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS: A operands are transposed reads
-        // of the query-major tiles; k-slots = the query rows of the P / dS
-        // register pairs.
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int r0 = s * 32 + hh * 16 + g * 4;
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]});
-          const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dsp[hh][0], dsp[hh][1], dsp[hh][2], dsp[hh][3]});
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 doa = lds_operand_tr<D>(Ds, r0, r0 + 8, dt * 32);
-            const bf16x8 qa = lds_operand_tr<D>(Qs, r0, r0 + 8, dt * 32);
-            dv[dt] = mfma32(doa, pb, dv[dt]);
-            dk[dt] = mfma32(qa, db, dk[dt]);
-            if (split_p) {
-              const bf16x8 pl = __builtin_bit_cast(bf16x8, u32x4{plo[hh][0], plo[hh][1], plo[hh][2], plo[hh][3]});
-              dv[dt] = mfma32(doa, pl, dv[dt]);
-            }
-            if (split_ds) {
-              const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{dslo[hh][0], dslo[hh][1], dslo[hh][2], dslo[hh][3]});
-              dk[dt] = mfma32(qa, dl, dk[dt]);
-            }
-          }
-        }
-      }
-
-      if (m + 1 < m_end) store_block(buf ^ 1);
-      __syncthreads();
-    }
-
-    // dK = scale * dS^T Q, dV = P^T dO for this lane's key; C layout: lane ->
-    // key, registers -> head-dim rows 8*(i/4) + 4g + i%4 of each 32-wide tile.
-    if (key_ok) {
-      float* dkr = a.dk + ((s0 + kw) * H + h) * (int64_t)D;
-      float* dvr = a.dv + ((s0 + kw) * H + h) * (int64_t)D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = dt * 32 + i4 * 8 + g * 4;
-          f32x4 kv, vv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv[e] = dk[dt][i4 * 4 + e] * a.scale;
-            vv[e] = dv[dt][i4 * 4 + e];
-          }
-          *reinterpret_cast<f32x4*>(dkr + d0) = kv;
-          *reinterpret_cast<f32x4*>(dvr + d0) = vv;
-        }
+    if (c == 0) {
+      delta[row] = acc;
+      lse2[row] = lse[row] * LOG2E;
     }
   }
 }
@@ -651,17 +376,14 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const int64_t work = rows * (D / 8);
     const int64_t want = (work + 255) / 256;
     const int blocks = (int)(want < 4096 ? want : 4096);
-    JFA_TIMED_LAUNCH(K_DELTA, st, (delta_kernel<D>), dim3(blocks), dim3(256), 0, st, a.out, a.dout, a.delta, rows);
+    JFA_TIMED_LAUNCH(K_DELTA, st, (delta_kernel<D>), dim3(blocks), dim3(256), 0, st, a.out, a.dout, a.lse, a.delta,
+                     a.lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipError_t e;
+  hipError_t e = launch_dkdv(a, st);
+  if (e != hipSuccess) return e;
   if (a.broadcast_q) {
-    if (a.causal)
-      JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a);
-    else
-      JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int items = a.H * a.dq_qblocks * a.dq_chunks;
     if (a.causal)
       JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, true, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
@@ -673,11 +395,6 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
                      a.dq, a.H, a.Lq, D, DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale);
     return hipGetLastError();
   }
-  if (a.causal)
-    JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a);
-  else
-    JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.causal)
     JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM / 32, true, false>), dim3(a.P_dq), dim3(DQ_BM * 2), 0, st, a);
   else

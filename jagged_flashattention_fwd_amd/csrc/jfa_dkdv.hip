@@ -1,0 +1,684 @@
+// dK / dV of jagged flash attention on gfx950, and the exact-delta pre-pass.
+//
+// dV = P^T dO and dK = scale dS^T Q with P recomputed from the forward's lse
+// and dS = P o (dO V^T - delta) ("Optimizing Jagged Flash Attention with TLX",
+// "2-CTA collaborative MMA (backward)"; the tiles follow the K/V-outer,
+// dense-Q-inner loop of "Scheduling jagged tiles across SMs").
+//
+// dkdv_kernel is persistent.  A tile is 128 keys of one (sequence, head); each
+// of the 4 waves keeps its 32 keys' K and V rows in registers as MFMA
+// operands and accumulates their dK^T / dV^T.  Query blocks of 64 rows (Q, dO,
+// lse*log2(e), delta) stream through a ring of 3 LDS buffers, copied straight
+// from global memory two blocks ahead of use.  Each block is two 32-row
+// subtiles, ordered so that the vector-ALU work of a subtile (P and dS) sits
+// beside matrix-core work of the other (S and dP of subtile 1, dV and dK of
+// subtile 0) in one basic block; with one wave per SIMD that overlap is the
+// only latency hiding there is.
+//
+// Masks are compile-time variants chosen per block: blocks that cross the
+// causal diagonal, the key tile at a sequence end and the last (partial)
+// query block take the masked body; every other block carries no mask code.
+#include <type_traits>
+
+#include "jfa_device.hpp"
+#include "jfa_internal.hpp"
+#include "jfa_timing.hpp"
+
+namespace jfa {
+
+namespace {
+
+// Two-term bf16 operands: rounding P or dS to bf16 costs up to 2^-9 of each
+// value, and dV / dK sum that error over many queries.  Where a subtile holds
+// a large value (short or sharply peaked sequences) the rounded remainder
+// x - bf16(x) is multiplied in as well.
+constexpr float SPLIT_P = 1.0f / 16.0f;
+constexpr float SPLIT_DS = 0.25f;
+
+template <int D>
+struct Dkdv {
+  static constexpr int NW = 4;
+  static constexpr int QB = BWD_QB;  // query rows per block (two subtiles)
+  static constexpr int BN = BWD_BN;  // keys per tile (32 per wave)
+  static constexpr int KS = D / 16, DT = D / 32;
+  static constexpr int RB = TileGeom<D>::ROW_BYTES;
+  static constexpr int TILE = QB * RB;
+  // d = 128 rows are 256 bytes, one direct-to-LDS copy per wave instruction.
+  static constexpr bool DMA = D == 128;
+  static constexpr int NBUF = 3;
+  // One ring buffer: Q tile, dO tile, then four 64-float rows: lse*log2(e),
+  // delta and two spares (waves 2 and 3 copy a duplicate row there, which
+  // keeps the number of copies equal across waves).
+  static constexpr int OFF_DO = TILE;
+  static constexpr int OFF_LSE = 2 * TILE;
+  static constexpr int OFF_DEL = OFF_LSE + QB * 4;
+  static constexpr int BUF = OFF_LSE + 4 * QB * 4;
+  static constexpr int IPS = 2 * (QB / NW) + 1;  // copies per wave per block
+  static_assert(IPS <= 63, "one block of copies must fit the vector-memory counter");
+  static_assert(NBUF * BUF <= 160 * 1024, "LDS");
+};
+
+// Issue the transposed reads of DT head-dim operand tiles for the 8 k-slots at
+// rows (row0 .. row0+3) and (row0+8 .. row0+11), where `addr` already holds
+// this lane's row and column and OFF is the byte offset of row0.  Nothing
+// waits here: tr_wait<N> below makes the values available.
+template <int OFF, int RB>
+__device__ __forceinline__ void tr_issue4(uint32_t addr, i16x4 (&x)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:%16"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+        "=&v"(x[7])
+      : "v"(addr), "i"(OFF), "i"(OFF + 8 * RB), "i"(OFF + 64), "i"(OFF + 8 * RB + 64), "i"(OFF + 128),
+        "i"(OFF + 8 * RB + 128), "i"(OFF + 192), "i"(OFF + 8 * RB + 192));
+}
+template <int OFF, int RB>
+__device__ __forceinline__ void tr_issue2(uint32_t addr, i16x4 (&x)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:%8"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(addr), "i"(OFF), "i"(OFF + 8 * RB), "i"(OFF + 64), "i"(OFF + 8 * RB + 64));
+  x[4] = x[5] = x[6] = x[7] = i16x4{0, 0, 0, 0};
+}
+template <int D, int OFF, int RB>
+__device__ __forceinline__ void tr_issue(uint32_t addr, i16x4 (&x)[8]) {
+  if constexpr (D == 128) tr_issue4<OFF, RB>(addr, x);
+  else tr_issue2<OFF, RB>(addr, x);
+}
+// Wait until at most N LDS reads of this wave are outstanding; the values in
+// x become defined by this statement, so their users are ordered after it.
+template <int N>
+__device__ __forceinline__ void tr_wait(i16x4 (&x)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7])
+               : "i"(N));
+}
+__device__ __forceinline__ bf16x8 tr_operand(const i16x4 (&x)[8], int dt) {
+  struct P { i16x4 a, b; } p = {x[2 * dt], x[2 * dt + 1]};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+// Direct global -> LDS copies (global_load_lds_dword: 4 bytes per lane into
+// LDS at M0 + 4 * lane), written as asm so that the compiler does not treat
+// them as pending writes to every LDS buffer and drain them before each LDS
+// read; completion is tracked with wait_vmcnt instead.  Nothing else in these
+// kernels uses M0, and each statement sets it before its copy.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 256 contiguous bytes: row base (uniform) + 4 * lane.
+__device__ __forceinline__ void copy_row256(const void* row, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"(row), "s"(lds) : "m0");
+}
+// One dword per lane from a per-lane address.
+__device__ __forceinline__ void copy_gather(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "m0");
+}
+#pragma clang diagnostic pop
+
+// f(integral_constant<int, i>) for i = B .. E-1, at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x2;
+constexpr int SG_MFMA = 0x8;
+constexpr int SG_DS_READ = 0x100;
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// Operand reads of S = Q K^T and dP = dO V^T for one subtile: for each
+// k-step ks the 16-byte chunk (2ks + g) of this lane's query row, of Q and
+// of dO, issued in the order q0 d0 q1 d1 ... (`addr` holds this lane's row
+// and chunk g; OFF is the subtile's row offset).  With d = 128 the 16 reads
+// are two statements; qd_wait<N> then makes pair ks available with N = the
+// number of reads issued after it.
+template <int OFF, int OFFD>
+__device__ __forceinline__ void qd_issue4(uint32_t addr, u32x4* q, u32x4* d) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16"
+      : "=&v"(q[0]), "=&v"(d[0]), "=&v"(q[1]), "=&v"(d[1]), "=&v"(q[2]), "=&v"(d[2]), "=&v"(q[3]), "=&v"(d[3])
+      : "v"(addr), "i"(OFF), "i"(OFFD), "i"(OFF + 32), "i"(OFFD + 32), "i"(OFF + 64), "i"(OFFD + 64),
+        "i"(OFF + 96), "i"(OFFD + 96));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait2(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+// lse*log2(e) and delta of rows OFF/4 + 8 i4 + 4g + 0..3 (i4 = 0..3), issued
+// as l0 d0 l1 d1 l2 d2 l3 d3 (`addr` holds this lane's 16 * g).
+template <int OFFL, int OFFD>
+__device__ __forceinline__ void ld_issue(uint32_t addr, f32x4 (&l)[4], f32x4 (&d)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16"
+      : "=&v"(l[0]), "=&v"(d[0]), "=&v"(l[1]), "=&v"(d[1]), "=&v"(l[2]), "=&v"(d[2]), "=&v"(l[3]), "=&v"(d[3])
+      : "v"(addr), "i"(OFFL), "i"(OFFD), "i"(OFFL + 32), "i"(OFFD + 32), "i"(OFFL + 64), "i"(OFFD + 64),
+        "i"(OFFL + 96), "i"(OFFD + 96));
+}
+template <int N>
+__device__ __forceinline__ void ld_wait(f32x4 (&l)[4], f32x4 (&d)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(l[0]), "+v"(d[0]), "+v"(l[1]), "+v"(d[1]), "+v"(l[2]), "+v"(d[2]), "+v"(l[3]), "+v"(d[3])
+               : "i"(N));
+}
+
+// Residual of a packed bf16 pair: bf16(a - hi.a), bf16(b - hi.b).
+__device__ __forceinline__ uint32_t bf16x2_residual(float a, float b, uint32_t hi) {
+  return pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
+}
+
+template <int D, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+  using C = Dkdv<D>;
+  constexpr int QB = C::QB, BN = C::BN, KS = C::KS, DT = C::DT, NBUF = C::NBUF, RB = C::RB;
+  constexpr int NT = C::NW * WAVE;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][C::BUF];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int l = tid % WAVE, g = l / 32, lc = l % 32;
+  const int slot = logical_slot(blockIdx.x, a.P);
+  const int64_t T = *a.n_ktiles;
+  const int H = a.H, Lq = a.Lq;
+  const int64_t ld = (int64_t)H * D;
+  const float c2 = a.scale_log2;
+
+  // This lane's part of a transposed read (see lds_operand_tr): row j of the
+  // 4-row group, 4 columns at 16 * (G & 1) + 4 q.
+  const int trs = l & 15;
+  const uint32_t tr_lane = (uint32_t)((g * 4 + (trs >> 2)) * RB + (((((l >> 4) & 1) << 4) + ((trs & 3) << 2)) << 1));
+
+  // The next tile's record is loaded one tile ahead.
+  TileRec nxt = TileRec{};
+  if (zigzag_tile(0, slot, a.P) < T) nxt = a.ktiles[zigzag_tile(0, slot, a.P)];
+  for (int64_t pass = 0;; ++pass) {
+    const int64_t t = zigzag_tile(pass, slot, a.P);
+    if (t >= T) break;
+    const TileRec tile = nxt;
+    if (zigzag_tile(pass + 1, slot, a.P) < T) nxt = a.ktiles[zigzag_tile(pass + 1, slot, a.P)];
+    const int64_t s0 = tile.s0;
+    const int L = tile.L;
+    const int h = tile.h;
+    const int k0 = tile.blk * BN;         // first key of the tile
+    const int kw = k0 + wave * 32 + lc;   // this lane's key
+    const bool key_ok = kw < L;
+    const int nq = BCAST ? Lq : L;
+
+    // Query blocks that can see a key of this tile.
+    const int m_first = CAUSAL ? k0 / QB : 0;
+    const int m_end = (nq + QB - 1) / QB;  // exclusive
+    const int nb = m_end > m_first ? m_end - m_first : 0;
+    // Blocks m < m_diag hold a row before the tile's last key.
+    const int m_diag = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
+    const bool tile_partial = k0 + BN > L;
+    const int m_full = nq / QB;  // blocks m < m_full have all QB rows
+
+    const uint16_t* qbase = BCAST ? a.q + (int64_t)h * Lq * D : a.q + (s0 * H + h) * (int64_t)D;
+    const int64_t qld = BCAST ? D : ld;
+    const uint16_t* dobase = BCAST ? a.dout + ((int64_t)tile.b * H + h) * Lq * D
+                                   : a.dout + (s0 * H + h) * (int64_t)D;
+    const int64_t rbase = BCAST ? ((int64_t)tile.b * H + h) * Lq : s0 * H + h;  // lse / delta row 0
+    const int64_t sld = BCAST ? 1 : H;
+
+    // Copies query block j into ring buffer bj.  Rows past the last query
+    // repeat it: finite values the masked body discards.
+    auto issue = [&](int j, int bj) {
+      char* buf = smem[bj];
+      const int r0 = j * QB;
+      if constexpr (C::DMA) {
+        const uint32_t lb = lds_addr(buf);
+#pragma unroll
+        for (int i = 0; i < QB / C::NW; ++i) {
+          const int row = wave * (QB / C::NW) + i;
+          const int64_t src = (int64_t)min(r0 + row, nq - 1) * qld;
+          copy_row256(qbase + src, 4u * l, lb + row * RB);
+          copy_row256(dobase + src, 4u * l, lb + C::OFF_DO + row * RB);
+        }
+        const float* vec = (wave & 1) ? a.delta : a.lse2;
+        const int64_t r = rbase + (int64_t)min(r0 + l, nq - 1) * sld;
+        copy_gather(vec + r, lb + C::OFF_LSE + wave * QB * 4);
+      } else {
+        TileLoader<QB, D, NT> ql, dol;
+        const int nr = min(QB, nq - r0);
+        ql.load(qbase + (int64_t)r0 * qld, qld, nr, tid);
+        dol.load(dobase + (int64_t)r0 * qld, qld, nr, tid);
+        float v = 0.f;
+        if (tid < 2 * QB) {
+          const int r = tid & (QB - 1);
+          const int64_t ri = rbase + (int64_t)min(r0 + r, nq - 1) * sld;
+          v = tid < QB ? a.lse2[ri] : a.delta[ri];
+        }
+        ql.store(buf, tid);
+        dol.store(buf + C::OFF_DO, tid);
+        if (tid < 2 * QB) reinterpret_cast<float*>(buf + C::OFF_LSE)[tid] = v;
+      }
+    };
+    // Block j is in its buffer for every wave once this returns; block j+1
+    // may still be in flight.
+    auto wait_block = [&](int j) {
+      if constexpr (C::DMA) {
+        if (j + 1 < m_end) wait_vmcnt<C::IPS>();
+        else wait_vmcnt<0>();
+      }
+      barrier_lds();
+    };
+
+    __syncthreads();  // the previous tile's readers are done with the ring
+
+    // K and V rows of this lane's key as B operands (B[d][key] = K[key][d]).
+    // Lanes past the sequence end read its last key (finite values; those
+    // keys are masked and never stored).  The loads are issued ahead of the
+    // first query block's copies, and the wait for that block covers them.
+    u32x4 kraw[KS], vraw[KS];
+    {
+      const int kc = min(kw, L - 1);
+      const uint16_t* kr = a.k + ((s0 + kc) * H + h) * (int64_t)D + g * 8;
+      const uint16_t* vr = a.v + ((s0 + kc) * H + h) * (int64_t)D + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kraw[ks] = *reinterpret_cast<const u32x4*>(kr + ks * 16);
+        vraw[ks] = *reinterpret_cast<const u32x4*>(vr + ks * 16);
+      }
+    }
+    bf16x8 kreg[KS], vreg[KS];
+    f32x16 dk[DT], dv[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
+
+    // Lane bases of the LDS reads (the buffer address is added per block).
+    const uint32_t qd_lane = (uint32_t)(lc * RB + g * 16);
+    const uint32_t ld_lane = (uint32_t)(g * 16);
+
+    // S = Q K^T and dP = dO V^T of subtile S_ from the operand reads q / d
+    // (issued by qd_issue; W0 = reads issued after the last pair, so pair ks
+    // waits for W0 + 2 (KS - 1 - ks)).  C layout: lane owns key kw; register
+    // i is query row S_*32 + 8*(i/4) + 4g + i%4.
+    // After each k-step, hook(ks) runs vector work beside it, and a
+    // scheduling barrier keeps that order.
+    auto mma_scores = [&](auto w_tag, auto lo_tag, auto hi_tag, u32x4* q, u32x4* d, f32x16& sacc, f32x16& dpacc,
+                          auto&& hook) {
+      constexpr int W0 = decltype(w_tag)::value;
+      static_for<decltype(lo_tag)::value, decltype(hi_tag)::value>([&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        lgkm_wait2<W0 + 2 * (KS - 1 - ks)>(q[ks], d[ks]);
+        sacc = mfma32(__builtin_bit_cast(bf16x8, q[ks]), kreg[ks], sacc);
+        dpacc = mfma32(__builtin_bit_cast(bf16x8, d[ks]), vreg[ks], dpacc);
+        hook(ks_tag);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    auto qd_issue = [&](auto s_tag, uint32_t base, u32x4* q, u32x4* d) {
+      constexpr int S_ = decltype(s_tag)::value;
+      qd_issue4<S_ * 32 * RB, S_ * 32 * RB + C::OFF_DO>(base, q, d);
+      if constexpr (KS == 8) qd_issue4<S_ * 32 * RB + 128, S_ * 32 * RB + C::OFF_DO + 128>(base, q + 4, d + 4);
+    };
+    auto ldv_issue = [&](auto s_tag, uint32_t base, f32x4 (&l)[4], f32x4 (&d)[4]) {
+      constexpr int S_ = decltype(s_tag)::value;
+      ld_issue<C::OFF_LSE + S_ * 128, C::OFF_DEL + S_ * 128>(base, l, d);
+    };
+
+    // P and dS of registers 4*i4 .. 4*i4+3 (query rows s*32 + 8*i4 + 4g + e)
+    // of subtile s of block m, from its S / dP and the rows' lse*log2(e) /
+    // delta.
+    auto pds = [&](auto masked_tag, int m, int s, const f32x16& sc, const f32x16& dc, int i4, const f32x4& ls,
+                   const f32x4& dl, float (&p4)[4], float (&d4)[4]) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const int r = s * 32 + i4 * 8 + g * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i4 * 4 + e;
+        float pv = fast_exp2(sc[i] * c2 - ls[e]);
+        if constexpr (MASKED) {
+          const int row = m * QB + r + e;
+          bool ok = key_ok && row < nq;
+          if constexpr (CAUSAL) ok = ok && kw <= row;
+          pv = ok ? pv : 0.f;
+        }
+        p4[e] = pv;
+        d4[e] = pv * (dc[i] - dl[e]);
+      }
+    };
+
+    // P and dS of subtile s as packed bf16 MFMA B operands pp / dsp (pair
+    // hh: query rows s*32 + hh*16 + 4g + {0..3, 8..11}); pmax / dsmax
+    // collect max |value|.
+    auto probs = [&](auto masked_tag, int m, int s, const f32x16& sc, const f32x16& dc, const f32x4 (&l)[4],
+                     const f32x4 (&dl)[4], uint32_t (&pp)[2][4], uint32_t (&dsp)[2][4], float& pmax, float& dsmax,
+                     int i4) {
+      {
+        float p4[4], d4[4];
+        pds(masked_tag, m, s, sc, dc, i4, l[i4], dl[i4], p4, d4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pmax = fmaxf(pmax, p4[e]);
+          dsmax = fmaxf(dsmax, fabsf(d4[e]));
+        }
+        pp[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(p4[0], p4[1]);
+        pp[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(p4[2], p4[3]);
+        dsp[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(d4[0], d4[1]);
+        dsp[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(d4[2], d4[3]);
+      }
+    };
+
+    // dV^T += dO^T P and dK^T += Q^T dS for subtile s: the A operands are
+    // transposed reads of the query-major dO / Q tiles at the same query rows
+    // as the k-slots of the P / dS register pairs.  Reads: dO(hh0) Q(hh0)
+    // dO(hh1) Q(hh1), each group waited with the later ones in flight.
+    auto dvdk = [&](auto s_tag, uint32_t tb, const uint32_t (&pp)[2][4], const uint32_t (&dsp)[2][4],
+                    auto&& hook) {
+      constexpr int s = decltype(s_tag)::value;
+      constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
+      constexpr int NR = 2 * DT;  // reads per group
+      const bf16x8 p0 = __builtin_bit_cast(bf16x8, u32x4{pp[0][0], pp[0][1], pp[0][2], pp[0][3]});
+      const bf16x8 p1 = __builtin_bit_cast(bf16x8, u32x4{pp[1][0], pp[1][1], pp[1][2], pp[1][3]});
+      const bf16x8 d0 = __builtin_bit_cast(bf16x8, u32x4{dsp[0][0], dsp[0][1], dsp[0][2], dsp[0][3]});
+      const bf16x8 d1 = __builtin_bit_cast(bf16x8, u32x4{dsp[1][0], dsp[1][1], dsp[1][2], dsp[1][3]});
+      i16x4 xo0[8], xq0[8], xo1[8], xq1[8];
+      tr_issue<D, OF0 + C::OFF_DO, RB>(tb, xo0);
+      tr_issue<D, OF0, RB>(tb, xq0);
+      tr_wait<NR>(xo0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dv[dt] = mfma32(tr_operand(xo0, dt), p0, dv[dt]);
+      hook(std::integral_constant<int, 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      tr_issue<D, OF1 + C::OFF_DO, RB>(tb, xo1);
+      tr_wait<NR>(xq0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dk[dt] = mfma32(tr_operand(xq0, dt), d0, dk[dt]);
+      hook(std::integral_constant<int, 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      tr_issue<D, OF1, RB>(tb, xq1);
+      tr_wait<NR>(xo1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dv[dt] = mfma32(tr_operand(xo1, dt), p1, dv[dt]);
+      hook(std::integral_constant<int, 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      tr_wait<0>(xq1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dk[dt] = mfma32(tr_operand(xq1, dt), d1, dk[dt]);
+      hook(std::integral_constant<int, 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Remainder products of subtile s where a P (dV) or dS (dK) value is
+    // large: P / dS are recomputed from S / dP and their residuals against
+    // the packed operands multiplied in.
+    auto fixup = [&](auto masked_tag, auto s_tag, int m, const char* buf, const f32x16& sc, const f32x16& dc,
+                     const uint32_t (&pp)[2][4], const uint32_t (&dsp)[2][4], bool fix_p, bool fix_ds) {
+      constexpr int s = decltype(s_tag)::value;
+      // Opaque copies: the values below are recomputed here rather than
+      // kept alive from the main path through the whole block.
+      f32x16 sc2 = sc, dc2 = dc;
+      asm volatile("" : "+v"(sc2), "+v"(dc2));
+      const uint32_t tb = lds_addr(buf) + tr_lane;
+      auto half = [&](auto hh_tag) {
+        constexpr int hh = decltype(hh_tag)::value;
+        u32x4 plo, dlo;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int i4 = 2 * hh + k;
+          const int r = s * 32 + i4 * 8 + g * 4;
+          const f32x4 ls = *reinterpret_cast<const f32x4*>(buf + C::OFF_LSE + r * 4);
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(buf + C::OFF_DEL + r * 4);
+          float p4[4], d4[4];
+          pds(masked_tag, m, s, sc2, dc2, i4, ls, dl, p4, d4);
+          plo[2 * k] = bf16x2_residual(p4[0], p4[1], pp[hh][2 * k]);
+          plo[2 * k + 1] = bf16x2_residual(p4[2], p4[3], pp[hh][2 * k + 1]);
+          dlo[2 * k] = bf16x2_residual(d4[0], d4[1], dsp[hh][2 * k]);
+          dlo[2 * k + 1] = bf16x2_residual(d4[2], d4[3], dsp[hh][2 * k + 1]);
+        }
+        if (fix_p) {
+          i16x4 xo[8];
+          tr_issue<D, (s * 32 + hh * 16) * RB + C::OFF_DO, RB>(tb, xo);
+          tr_wait<0>(xo);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) dv[dt] = mfma32(tr_operand(xo, dt), __builtin_bit_cast(bf16x8, plo), dv[dt]);
+        }
+        if (fix_ds) {
+          i16x4 xq[8];
+          tr_issue<D, (s * 32 + hh * 16) * RB, RB>(tb, xq);
+          tr_wait<0>(xq);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) dk[dt] = mfma32(tr_operand(xq, dt), __builtin_bit_cast(bf16x8, dlo), dk[dt]);
+        }
+      };
+      half(std::integral_constant<int, 0>{});
+      half(std::integral_constant<int, 1>{});
+    };
+
+    // One query block, every LDS read issued explicitly so that its latency
+    // overlaps other work:
+    //   1. lse/delta(0), Q/dO(0) reads; S0, dP0.
+    //   2. Q/dO(1) reads; P0, dS0 (vector ALU) beside S1, dP1; lse/delta(1)
+    //      reads once half of Q/dO(1) is consumed (the wait counter counts at
+    //      most 15 later reads).
+    //   3. dV/dK of subtile 0 beside P1, dS1.
+    //   4. dV/dK of subtile 1.
+    auto block = [&](auto masked_tag, int m, const char* buf) {
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using W0 = std::integral_constant<int, 0>;
+      using W8 = std::integral_constant<int, 8>;
+      using K0 = std::integral_constant<int, 0>;
+      using KH = std::integral_constant<int, KS / 2>;
+      using KE = std::integral_constant<int, KS>;
+      const uint32_t lb = lds_addr(buf);
+      const uint32_t qb = lb + qd_lane, lsb = lb + ld_lane, tb = lb + tr_lane;
+      f32x16 sa = f32x16{}, da = f32x16{}, sb = f32x16{}, db = f32x16{};
+      uint32_t pa[2][4], dsa[2][4], pb[2][4], dsb[2][4];
+      f32x4 l0[4], e0[4], l1[4], e1[4];
+      u32x4 q[KS], d[KS];
+      auto none = [](auto) {};
+      ldv_issue(S0{}, lsb, l0, e0);
+      qd_issue(S0{}, qb, q, d);
+      mma_scores(W0{}, K0{}, KE{}, q, d, sa, da, none);
+
+      // P0 / dS0 in four row groups, one after every KS/4 k-steps of S1 / dP1.
+      qd_issue(S1{}, qb, q, d);
+      ld_wait<15>(l0, e0);
+      float pmax = 0.f, dsmax = 0.f;
+      auto p0_hook = [&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        if constexpr (ks % (KS / 4) == KS / 4 - 1) probs(masked_tag, m, 0, sa, da, l0, e0, pa, dsa, pmax, dsmax, ks / (KS / 4));
+      };
+      mma_scores(W0{}, K0{}, KH{}, q, d, sb, db, p0_hook);
+      ldv_issue(S1{}, lsb, l1, e1);
+      mma_scores(W8{}, KH{}, KE{}, q, d, sb, db, p0_hook);
+
+      // P1 / dS1 beside dV / dK of subtile 0.
+      ld_wait<0>(l1, e1);
+      float pmax1 = 0.f, dsmax1 = 0.f;
+      auto p1_hook = [&](auto g_tag) {
+        probs(masked_tag, m, 1, sb, db, l1, e1, pb, dsb, pmax1, dsmax1, decltype(g_tag)::value);
+      };
+      dvdk(S0{}, tb, pa, dsa, p1_hook);
+      dvdk(S1{}, tb, pb, dsb, none);
+      const bool f0p = pmax > SPLIT_P, f0d = dsmax > SPLIT_DS;
+      const bool f1p = pmax1 > SPLIT_P, f1d = dsmax1 > SPLIT_DS;
+      if (__builtin_expect(__any(f0p || f0d || f1p || f1d), 0)) {
+        fixup(masked_tag, S0{}, m, buf, sa, da, pa, dsa, __any(f0p), __any(f0d));
+        fixup(masked_tag, S1{}, m, buf, sb, db, pb, dsb, __any(f1p), __any(f1d));
+      }
+    };
+
+    if (nb > 0) {
+      // Ring buffer bi holds block m; block m + 2 goes to the buffer block
+      // m - 1 used, which every wave has left once block m's wait returns.
+      issue(m_first, 0);
+      if (nb > 1) issue(m_first + 1, 1);
+      wait_block(m_first);
+      if (nb > 2) issue(m_first + 2, 2);
+      // The K / V registers are consumed here, outside the loops, so that the
+      // compiler's wait for those loads (it cannot see the copies above and
+      // waits for everything) happens once per tile rather than in a loop.
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        asm volatile("" : "+v"(kraw[ks]), "+v"(vraw[ks]));
+        kreg[ks] = __builtin_bit_cast(bf16x8, kraw[ks]);
+        vreg[ks] = __builtin_bit_cast(bf16x8, vraw[ks]);
+      }
+      int bi = 0;
+      // Blocks [m0, m1) with one body (a loop per mask variant, rather than
+      // a branch per block, keeps register allocation to one body at a time).
+      auto run = [&](auto masked_tag, int m0, int m1) {
+        for (int m = m0; m < m1; ++m) {
+          if (m != m_first) {
+            wait_block(m);
+            if (m + 2 < m_end) issue(m + 2, bi == 0 ? NBUF - 1 : bi - 1);
+          }
+          block(masked_tag, m, smem[bi]);
+          bi = bi == NBUF - 1 ? 0 : bi + 1;
+        }
+      };
+      if (tile_partial) {
+        run(std::true_type{}, m_first, m_end);
+      } else {
+        // masked: causal diagonal blocks, then the partial last block
+        const int u0 = CAUSAL ? min(max(m_diag, m_first), m_end) : m_first;
+        const int u1 = max(u0, min(m_full, m_end));
+        run(std::true_type{}, m_first, u0);
+        run(std::false_type{}, u0, u1);
+        run(std::true_type{}, u1, m_end);
+      }
+    }
+
+    // dK = scale * dS^T Q, dV = P^T dO for this lane's key; C layout: lane ->
+    // key, registers -> head-dim rows 8*(i/4) + 4g + i%4 of each 32-wide tile.
+    if (key_ok) {
+      float* dkr = a.dk + ((s0 + kw) * H + h) * (int64_t)D;
+      float* dvr = a.dv + ((s0 + kw) * H + h) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = dt * 32 + i4 * 8 + g * 4;
+          f32x4 kv, vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[e] = dk[dt][i4 * 4 + e] * a.scale;
+            vv[e] = dv[dt][i4 * 4 + e];
+          }
+          *reinterpret_cast<f32x4*>(dkr + d0) = kv;
+          *reinterpret_cast<f32x4*>(dvr + d0) = vv;
+        }
+    }
+  }
+}
+
+// ----------------------------------------------------------- exact delta --
+// For a sequence with at most BWD_BN keys, delta_i = sum_k P_ik dP_ik from
+// fp32 P and dP (the same quantity as rowsum(dO o O), without the bf16
+// rounding of the stored O, which dominates the dK and dQ error when P is
+// large).  One workgroup: 128 query rows of one (sequence, head); wave w takes
+// rows 32w .. 32w+31 with the transposed score layout S^T = K Q^T (lane ->
+// query, registers -> keys), so each lane sums its registers and the two
+// halves of the wave are added.
+template <int D, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  const int b = blockIdx.x, h = blockIdx.y;
+  int64_t s0;
+  const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
+  if (L == 0 || L > BWD_BN) return;
+  const int H = a.H, Lq = a.Lq;
+  const int nq = BCAST ? Lq : L;
+  const int wave = threadIdx.x / WAVE, l = threadIdx.x % WAVE, g = l / 32, lc = l % 32;
+  const int qw = blockIdx.z * 128 + wave * 32;
+  if (qw >= nq) return;
+  const int q = qw + lc;
+  const int qc = min(q, nq - 1);
+  const uint16_t* qrow = BCAST ? a.q + ((int64_t)h * Lq + qc) * D : a.q + ((s0 + qc) * H + h) * (int64_t)D;
+  const int64_t ri = BCAST ? ((int64_t)b * H + h) * Lq + qc : (s0 + qc) * H + h;
+  const uint16_t* dorow = a.dout + ri * D;
+  bf16x8 qr[KS], dr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8));
+    dr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dorow + ks * 16 + g * 8));
+  }
+  const float ls2 = a.lse2[ri];
+  const float c2 = a.scale_log2;
+  float acc = 0.f;
+  for (int kt = 0; kt * 32 < L; ++kt) {
+    const int key = min(kt * 32 + lc, L - 1);
+    const uint16_t* kr = a.k + ((s0 + key) * H + h) * (int64_t)D;
+    const uint16_t* vr = a.v + ((s0 + key) * H + h) * (int64_t)D;
+    f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + ks * 16 + g * 8));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vr + ks * 16 + g * 8));
+      st = mfma32(ka, qr[ks], st);
+      dpt = mfma32(va, dr[ks], dpt);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = kt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+      bool ok = kk < L;
+      if (CAUSAL) ok = ok && kk <= q;
+      const float p = ok ? fast_exp2(st[i] * c2 - ls2) : 0.f;
+      acc += p * dpt[i];
+    }
+  }
+  acc = sum_across_halves(acc);
+  if (g == 0 && q < nq) a.delta[ri] = acc;
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
+  const int nqb = a.broadcast_q ? (a.Lq + 127) / 128 : 1;
+  const dim3 eg((unsigned)a.B, (unsigned)a.H, (unsigned)nqb);
+  if (a.broadcast_q) {
+    if (a.causal) JFA_TIMED_LAUNCH(K_DELTA_EXACT, st, (delta_exact_kernel<D, true, true>), eg, dim3(256), 0, st, a);
+    else JFA_TIMED_LAUNCH(K_DELTA_EXACT, st, (delta_exact_kernel<D, false, true>), eg, dim3(256), 0, st, a);
+  } else {
+    if (a.causal) JFA_TIMED_LAUNCH(K_DELTA_EXACT, st, (delta_exact_kernel<D, true, false>), eg, dim3(256), 0, st, a);
+    else JFA_TIMED_LAUNCH(K_DELTA_EXACT, st, (delta_exact_kernel<D, false, false>), eg, dim3(256), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.broadcast_q) {
+    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a);
+    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a);
+  } else {
+    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a);
+    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 64) return launch_d<64>(a, stream);
+  return launch_d<128>(a, stream);
+}
+
+}  // namespace jfa

@@ -6,9 +6,15 @@
 
 namespace jfa {
 
+// One tile of a persistent kernel's work list: sequence b, head h, block blk,
+// and the sequence's (clamped) packed row range [s0, s0 + L), so that a
+// kernel needs no second dependent load to find its rows.
 struct TileRec {
-  int b, h, blk, pad;
+  int b, h, blk, L;
+  int64_t s0;
+  int64_t pad;
 };
+static_assert(sizeof(TileRec) == 32, "tile record layout");
 
 // Tile sizes.  Forward: a tile is BM query rows of one (sequence, head),
 // streamed against K/V in steps of KV_STEP keys.  Backward: a tile is BN key
@@ -69,7 +75,8 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;           // [rows] scratch
+  float* delta;           // [rows] scratch: delta per query row
+  float* lse2;            // [rows] scratch: lse * log2(e) per query row
   float* dq_part;         // [H][n_qb][NC][DQ_BM_BCAST][d] broadcast-mode partials
   const int* seq_order;   // sequences sorted by length (broadcast dQ chunks)
   int dq_qblocks;         // n_qb = cdiv(Lq, DQ_BM_BCAST)
@@ -87,5 +94,8 @@ struct BwdArgs {
   int P_dq;    // persistent workgroups of the self-attention dQ kernel
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// Exact delta for short sequences, then dK / dV (delta and lse2 must hold the
+// pre-pass values).
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace jfa

@@ -13,6 +13,7 @@ enum KernelId {
   K_DKDV,
   K_DQ_REDUCE,
   K_DQ,
+  K_DELTA_EXACT,
   K_COUNT
 };
 
