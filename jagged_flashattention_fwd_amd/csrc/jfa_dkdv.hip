@@ -9,7 +9,11 @@
 // of the 4 waves keeps its 32 keys' K and V rows in registers as MFMA
 // operands and accumulates their dK^T / dV^T.  Query blocks of 64 rows (Q, dO,
 // lse*log2(e), delta) stream through a ring of 3 LDS buffers, copied straight
-// from global memory two blocks ahead of use.  Each block is two 32-row
+// from global memory (16 bytes per lane, 3 rows per copy) two blocks ahead of
+// use; the stream runs on across tile boundaries, and the copies are issued
+// from inside the previous block's first products.  The dK / dV stores go
+// through a per-wave LDS transpose into whole 128-byte segments, after the
+// next tile's K / V loads, and drain while that tile computes.  Each block is two 32-row
 // subtiles, ordered so that the vector-ALU work of a subtile (P and dS) sits
 // beside matrix-core work of the other (S and dP of subtile 1, dV and dK of
 // subtile 0) in one basic block; with one wave per SIMD that overlap is the
@@ -43,17 +47,25 @@ struct Dkdv {
   static constexpr int KS = D / 16, DT = D / 32;
   static constexpr int RB = TileGeom<D>::ROW_BYTES;
   static constexpr int TILE = QB * RB;
-  // d = 128 rows are 256 bytes, one direct-to-LDS copy per wave instruction.
+  // d = 128: rows are copied straight from global memory into LDS.
   static constexpr bool DMA = D == 128;
   static constexpr int NBUF = 3;
   // One ring buffer: Q tile, dO tile, then four 64-float rows: lse*log2(e),
   // delta and two spares (waves 2 and 3 copy a duplicate row there, which
-  // keeps the number of copies equal across waves).
-  static constexpr int OFF_DO = TILE;
-  static constexpr int OFF_LSE = 2 * TILE;
+  // keeps the number of copies equal across waves).  Each tile is followed by
+  // a 128-byte gap that absorbs the overhang of the last row copy (below).
+  static constexpr int GAP = 128;
+  static constexpr int OFF_DO = TILE + GAP;
+  static constexpr int OFF_LSE = OFF_DO + TILE + GAP;
   static constexpr int OFF_DEL = OFF_LSE + QB * 4;
   static constexpr int BUF = OFF_LSE + 4 * QB * 4;
-  static constexpr int IPS = 2 * (QB / NW) + 1;  // copies per wave per block
+  // A 16-byte-per-lane copy writes 1 KB of consecutive LDS: with 304-byte
+  // rows (19 chunks) that is 3 whole rows and 7 chunks of a fourth, so a
+  // wave's 16 rows of a tile take 6 copies starting at rows 0, 3, .., 12, 13.
+  static constexpr int RPW = QB / NW;    // rows per wave per tile
+  static constexpr int CPT = 6;          // copies per wave per tile
+  static_assert(D != 128 || (RB == 19 * 16 && RPW == 16), "copy geometry");
+  static constexpr int IPS = 2 * CPT + 1;  // copies per wave per block
   static_assert(IPS <= 63, "one block of copies must fit the vector-memory counter");
   static_assert(NBUF * BUF <= 160 * 1024, "LDS");
 };
@@ -115,13 +127,32 @@ __device__ __forceinline__ bf16x8 tr_operand(const i16x4 (&x)[8], int dt) {
 // kernels uses M0, and each statement sets it before its copy.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 256 contiguous bytes: row base (uniform) + 4 * lane.
+// 256 contiguous bytes: row base (uniform) + 4 * lane.  Both addresses are
+// wave-uniform; readfirstlane states it for the compiler where it cannot
+// prove it, and costs nothing when they already sit in scalar registers.
 __device__ __forceinline__ void copy_row256(const void* row, uint32_t lane_off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"(row), "s"(lds) : "m0");
+  const uint64_t r = (uint64_t)(uintptr_t)row;
+  const uint64_t ru = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
+  const uint32_t lu = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off),
+               "s"((const void*)(uintptr_t)ru), "s"(lu)
+               : "m0");
 }
 // One dword per lane from a per-lane address.
 __device__ __forceinline__ void copy_gather(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "m0");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "m0");
+}
+// 16 bytes per lane from base (uniform) + voff (per lane), into LDS at
+// lds + 16 * lane.
+__device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t r = (uint64_t)(uintptr_t)base;
+  const uint64_t ru = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"((const void*)(uintptr_t)ru), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -195,7 +226,7 @@ __device__ __forceinline__ uint32_t bf16x2_residual(float a, float b, uint32_t h
 }
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* __restrict__ tiles) {
   using C = Dkdv<D>;
   constexpr int QB = C::QB, BN = C::BN, KS = C::KS, DT = C::DT, NBUF = C::NBUF, RB = C::RB;
   constexpr int NT = C::NW * WAVE;
@@ -215,98 +246,225 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const int trs = l & 15;
   const uint32_t tr_lane = (uint32_t)((g * 4 + (trs >> 2)) * RB + (((((l >> 4) & 1) << 4) + ((trs & 3) << 2)) << 1));
 
-  // The next tile's record is loaded one tile ahead.
-  TileRec nxt = TileRec{};
-  if (zigzag_tile(0, slot, a.P) < T) nxt = a.ktiles[zigzag_tile(0, slot, a.P)];
+  // Work flows across tile boundaries.  Query blocks form one stream over
+  // this workgroup's tiles and are copied two blocks ahead of the compute,
+  // into the next tile's first blocks while the current tile finishes.  The
+  // next tile's K / V rows are loaded into registers before the current
+  // tile's dK / dV are stored, so that the stores drain while the next tile
+  // computes.
+  const int64_t t0 = zigzag_tile(0, slot, a.P);
+  if (t0 >= T) return;
+
+  struct Tp {
+    int64_t s0;
+    int L, h, b, k0, m_first, m_end;
+  };
+  auto tparams = [&](const TileRec& r) {
+    Tp p;
+    p.s0 = r.s0;
+    p.L = r.L;
+    p.h = r.h;
+    p.b = r.b;
+    p.k0 = r.blk * BN;
+    const int nq = BCAST ? Lq : r.L;
+    p.m_first = CAUSAL ? p.k0 / QB : 0;                 // query blocks that can see a key of the tile
+    p.m_end = max((nq + QB - 1) / QB, p.m_first);       // exclusive
+    return p;
+  };
+  const int64_t qs = BCAST ? (int64_t)D : ld;          // row stride of Q / dO
+  const int64_t sld = BCAST ? 1 : H;                    // row stride of lse / delta
+
+  // One query block's copies into a ring buffer.  With d = 128 they are
+  // prepared before the block (which block, source rows, buffer) and issued
+  // from inside the block's first matrix-core phase (issue_rows / issue_vec),
+  // where their scalar address work overlaps the products.  Rows past the
+  // last query repeat it: finite values the masked body discards.
+  // The prepared job: this wave's first Q / dO source rows of the block, this
+  // lane's lse*log2(e) (even waves) or delta (odd waves) source, the ring
+  // buffer's LDS address, rows i > j_last repeat row j_last, and the number
+  // of vector-memory operations the job issues (0: none).
+  const uint16_t* j_q = a.q;
+  const uint16_t* j_d = a.q;
+  const float* j_v = a.lse2;
+  uint32_t j_lds = 0;  // ring buffer
+  uint32_t j_ldw = 0;  // this wave's first row in it
+  int j_last = 0, j_n = 0;
+  // Copies [k0, k1) of this wave's 2 * CPT for the prepared block: copy k
+  // (Q for k < CPT, dO after) starts at row R = min(3 (k mod CPT), 13) of the
+  // wave's rows; lane i fills chunk i % 19 of row R + i / 19 (chunks 16..18
+  // are row padding, and lanes past the third row write the first chunks of
+  // the row after, with the same values its own copy writes, or into the
+  // gap after the tile).
+  const int cp_row = l / 19, cp_chunk = l % 19;
+  const uint32_t cp_byte = cp_chunk < 16 ? (uint32_t)cp_chunk * 16u : 0u;
+  auto issue_rows = [&](int k0, int k1) {
+    if constexpr (C::DMA) {
+      if (j_n == 0) return;
+#pragma unroll
+      for (int k = k0; k < k1; ++k) {
+        const int kk = k % C::CPT;
+        const int R = min(3 * kk, C::RPW - 3);
+        const uint32_t voff = (uint32_t)min(R + cp_row, j_last) * (uint32_t)(qs * 2) + cp_byte;
+        if (k < C::CPT) copy16(j_q, voff, j_ldw + R * RB);
+        else copy16(j_d, voff, j_ldw + C::OFF_DO + R * RB);
+      }
+    }
+  };
+  auto issue_vec = [&]() {
+    if constexpr (C::DMA) {
+      if (j_n == 0) return;
+      copy_gather(j_v, j_lds + C::OFF_LSE + wave * QB * 4);
+    }
+  };
+  // d = 64: the block is staged through registers right away (the job then
+  // issues nothing).
+  auto stage_now = [&](const uint16_t* qbase, const uint16_t* dobase, int64_t rbase, int nq, int j, char* buf) {
+    const int r0 = j * QB;
+    TileLoader<QB, D, NT> ql, dol;
+    const int nr = min(QB, nq - r0);
+    ql.load(qbase + (int64_t)r0 * qs, qs, nr, tid);
+    dol.load(dobase + (int64_t)r0 * qs, qs, nr, tid);
+    float v = 0.f;
+    if (tid < 2 * QB) {
+      const int r = tid & (QB - 1);
+      const int64_t ri = rbase + (int64_t)min(r0 + r, nq - 1) * sld;
+      v = tid < QB ? a.lse2[ri] : a.delta[ri];
+    }
+    ql.store(buf, tid);
+    dol.store(buf + C::OFF_DO, tid);
+    if (tid < 2 * QB) reinterpret_cast<float*>(buf + C::OFF_LSE)[tid] = v;
+  };
+
+  // Issue state of the block stream.
+  int ring_iss = 0, ring_cmp = 0;  // ring buffers of the next issued / computed block
+  int iss_cur = 0, iss_nxt = 0;    // blocks of the current / next tile issued so far
+  // Prepares the next block of the stream (the current tile's, then the next
+  // tile's), if there is one, and advances the stream.
+  auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
+    j_n = 0;
+    const int nbc = cp.m_end - cp.m_first;
+    const int nbn = has_nxt ? np.m_end - np.m_first : 0;
+    const bool cur = iss_cur < nbc;
+    if (!cur && iss_nxt >= nbn) return;
+    const int64_t s0_ = cur ? cp.s0 : np.s0;
+    const int h_ = cur ? cp.h : np.h, b_ = cur ? cp.b : np.b;
+    const int nq_ = BCAST ? Lq : (cur ? cp.L : np.L);
+    const int j = cur ? cp.m_first + iss_cur : np.m_first + iss_nxt;
+    const uint16_t* qbase = BCAST ? a.q + (int64_t)h_ * Lq * D : a.q + (s0_ * H + h_) * (int64_t)D;
+    const uint16_t* dobase = BCAST ? a.dout + ((int64_t)b_ * H + h_) * Lq * D : a.dout + (s0_ * H + h_) * (int64_t)D;
+    const int64_t rbase = BCAST ? ((int64_t)b_ * H + h_) * Lq : s0_ * H + h_;  // lse / delta row 0
+    if constexpr (C::DMA) {
+      const int base_row = min(j * QB + wave * C::RPW, nq_ - 1);
+      j_q = qbase + (int64_t)base_row * qs;
+      j_d = dobase + (int64_t)base_row * qs;
+      j_v = ((wave & 1) ? a.delta : a.lse2) + rbase + (int64_t)min(j * QB + l, nq_ - 1) * sld;
+      j_lds = lds_addr(smem[ring_iss]);
+      j_ldw = j_lds + wave * C::RPW * RB;
+      j_last = nq_ - 1 - base_row;
+      j_n = C::IPS;
+    } else {
+      stage_now(qbase, dobase, rbase, nq_, j, smem[ring_iss]);
+    }
+    if (cur) ++iss_cur;
+    else ++iss_nxt;
+    ring_iss = ring_iss == NBUF - 1 ? 0 : ring_iss + 1;
+  };
+  auto issue_now = [&]() {
+    issue_rows(0, 2 * C::CPT);
+    issue_vec();
+  };
+
+  // Waits until at most n vector-memory operations of this wave are
+  // outstanding, for n one of the counts the block stream produces.
+  auto wait_n = [&](int n) {
+    if constexpr (C::DMA) {
+      if (n >= C::IPS) wait_vmcnt<C::IPS>();
+      else wait_vmcnt<0>();
+    }
+  };
+
+  // K and V rows of this lane's key of tile p as B operands (B[d][key] =
+  // K[key][d]).  Lanes past the sequence end read its last key (finite
+  // values; those keys are masked and never stored).
+  u32x4 kraw[KS], vraw[KS];
+  auto load_kv = [&](const Tp& p) {
+    const int kc = min(p.k0 + wave * 32 + lc, p.L - 1);
+    const uint16_t* kr = a.k + ((p.s0 + kc) * H + p.h) * (int64_t)D + g * 8;
+    const uint16_t* vr = a.v + ((p.s0 + kc) * H + p.h) * (int64_t)D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kraw[ks] = *reinterpret_cast<const u32x4*>(kr + ks * 16);
+      vraw[ks] = *reinterpret_cast<const u32x4*>(vr + ks * 16);
+    }
+  };
+
+  // dK = scale * dS^T Q and dV = P^T dO of this lane's keys.  The C layout
+  // (lane -> key, registers -> head-dim rows 8*(i/4) + 4g + i%4 of each
+  // 32-wide tile) gives 32-byte pieces of 32 rows per register group; each
+  // 32 x 32 chunk is transposed through a per-wave LDS area so that every
+  // store writes whole 128-byte segments of 8 rows.  Buffer stores bounded to
+  // the tile's first nvalid keys: every wave issues exactly 8 * DT of them
+  // whatever its keys, and stores past the bound are dropped, so the K / V
+  // wait at the next tile start has a fixed count.
+  constexpr int SRS = 36;  // staging row stride in floats
+  __shared__ __attribute__((aligned(16))) float stage[C::NW][32 * SRS];
+  auto store_dkdv = [&](const Tp& p, int nvalid, const f32x16 (&dk)[DT], const f32x16 (&dv)[DT]) {
+    const int64_t row0 = (p.s0 + p.k0) * H + p.h;
+    const int nrec = nvalid * H * D * 4;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(a.dk + row0 * D, (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(a.dv + row0 * D, (short)0, nrec, 0x00020000);
+    float* st = stage[wave];
+    const int rk8 = l >> 3, rc = (l & 7) * 4;  // read side: key 8r + rk8, columns rc .. rc+3
+    auto chunk = [&](const f32x16& acc, float mul, const __amdgpu_buffer_rsrc_t& rs, int dt) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i4 * 4 + e] * mul;
+        *reinterpret_cast<f32x4*>(st + lc * SRS + i4 * 8 + g * 4) = v;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + (r * 8 + rk8) * SRS + rc);
+        const int off = ((wave * 32 + r * 8 + rk8) * H * D + dt * 32 + rc) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) chunk(dk[dt], a.scale, rk, dt);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) chunk(dv[dt], 1.0f, rv, dt);
+  };
+
+  Tp cp = tparams(tiles[t0]);
+  load_kv(cp);
+  {
+    // Stores that write nothing: the first tile start sees the same
+    // operations after its K / V loads as every later one.
+    f32x16 z[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
+    store_dkdv(cp, 0, z, z);
+  }
+
   for (int64_t pass = 0;; ++pass) {
-    const int64_t t = zigzag_tile(pass, slot, a.P);
-    if (t >= T) break;
-    const TileRec tile = nxt;
-    if (zigzag_tile(pass + 1, slot, a.P) < T) nxt = a.ktiles[zigzag_tile(pass + 1, slot, a.P)];
-    const int64_t s0 = tile.s0;
-    const int L = tile.L;
-    const int h = tile.h;
-    const int k0 = tile.blk * BN;         // first key of the tile
+    const int64_t tn = zigzag_tile(pass + 1, slot, a.P);
+    const bool has_nxt = tn < T;
+    const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
+    const int64_t s0 = cp.s0;
+    const int L = cp.L;
+    const int h = cp.h;
+    const int k0 = cp.k0;                 // first key of the tile
     const int kw = k0 + wave * 32 + lc;   // this lane's key
     const bool key_ok = kw < L;
     const int nq = BCAST ? Lq : L;
-
-    // Query blocks that can see a key of this tile.
-    const int m_first = CAUSAL ? k0 / QB : 0;
-    const int m_end = (nq + QB - 1) / QB;  // exclusive
-    const int nb = m_end > m_first ? m_end - m_first : 0;
+    const int m_first = cp.m_first, m_end = cp.m_end;
+    const int nb = m_end - m_first;
     // Blocks m < m_diag hold a row before the tile's last key.
     const int m_diag = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
     const bool tile_partial = k0 + BN > L;
     const int m_full = nq / QB;  // blocks m < m_full have all QB rows
 
-    const uint16_t* qbase = BCAST ? a.q + (int64_t)h * Lq * D : a.q + (s0 * H + h) * (int64_t)D;
-    const int64_t qld = BCAST ? D : ld;
-    const uint16_t* dobase = BCAST ? a.dout + ((int64_t)tile.b * H + h) * Lq * D
-                                   : a.dout + (s0 * H + h) * (int64_t)D;
-    const int64_t rbase = BCAST ? ((int64_t)tile.b * H + h) * Lq : s0 * H + h;  // lse / delta row 0
-    const int64_t sld = BCAST ? 1 : H;
-
-    // Copies query block j into ring buffer bj.  Rows past the last query
-    // repeat it: finite values the masked body discards.
-    auto issue = [&](int j, int bj) {
-      char* buf = smem[bj];
-      const int r0 = j * QB;
-      if constexpr (C::DMA) {
-        const uint32_t lb = lds_addr(buf);
-#pragma unroll
-        for (int i = 0; i < QB / C::NW; ++i) {
-          const int row = wave * (QB / C::NW) + i;
-          const int64_t src = (int64_t)min(r0 + row, nq - 1) * qld;
-          copy_row256(qbase + src, 4u * l, lb + row * RB);
-          copy_row256(dobase + src, 4u * l, lb + C::OFF_DO + row * RB);
-        }
-        const float* vec = (wave & 1) ? a.delta : a.lse2;
-        const int64_t r = rbase + (int64_t)min(r0 + l, nq - 1) * sld;
-        copy_gather(vec + r, lb + C::OFF_LSE + wave * QB * 4);
-      } else {
-        TileLoader<QB, D, NT> ql, dol;
-        const int nr = min(QB, nq - r0);
-        ql.load(qbase + (int64_t)r0 * qld, qld, nr, tid);
-        dol.load(dobase + (int64_t)r0 * qld, qld, nr, tid);
-        float v = 0.f;
-        if (tid < 2 * QB) {
-          const int r = tid & (QB - 1);
-          const int64_t ri = rbase + (int64_t)min(r0 + r, nq - 1) * sld;
-          v = tid < QB ? a.lse2[ri] : a.delta[ri];
-        }
-        ql.store(buf, tid);
-        dol.store(buf + C::OFF_DO, tid);
-        if (tid < 2 * QB) reinterpret_cast<float*>(buf + C::OFF_LSE)[tid] = v;
-      }
-    };
-    // Block j is in its buffer for every wave once this returns; block j+1
-    // may still be in flight.
-    auto wait_block = [&](int j) {
-      if constexpr (C::DMA) {
-        if (j + 1 < m_end) wait_vmcnt<C::IPS>();
-        else wait_vmcnt<0>();
-      }
-      barrier_lds();
-    };
-
-    __syncthreads();  // the previous tile's readers are done with the ring
-
-    // K and V rows of this lane's key as B operands (B[d][key] = K[key][d]).
-    // Lanes past the sequence end read its last key (finite values; those
-    // keys are masked and never stored).  The loads are issued ahead of the
-    // first query block's copies, and the wait for that block covers them.
-    u32x4 kraw[KS], vraw[KS];
-    {
-      const int kc = min(kw, L - 1);
-      const uint16_t* kr = a.k + ((s0 + kc) * H + h) * (int64_t)D + g * 8;
-      const uint16_t* vr = a.v + ((s0 + kc) * H + h) * (int64_t)D + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kraw[ks] = *reinterpret_cast<const u32x4*>(kr + ks * 16);
-        vraw[ks] = *reinterpret_cast<const u32x4*>(vr + ks * 16);
-      }
-    }
     bf16x8 kreg[KS], vreg[KS];
     f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -498,7 +656,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       auto none = [](auto) {};
       ldv_issue(S0{}, lsb, l0, e0);
       qd_issue(S0{}, qb, q, d);
-      mma_scores(W0{}, K0{}, KE{}, q, d, sa, da, none);
+      // The next block's copies, spread over the k-steps.
+      auto copy_hook = [&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        constexpr int PER = (2 * C::CPT + KS - 1) / KS;
+        issue_rows(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
+        if constexpr (ks == KS - 1) issue_vec();
+      };
+      mma_scores(W0{}, K0{}, KE{}, q, d, sa, da, copy_hook);
 
       // P0 / dS0 in four row groups, one after every KS/4 k-steps of S1 / dP1.
       qd_issue(S1{}, qb, q, d);
@@ -528,33 +693,48 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       }
     };
 
-    if (nb > 0) {
-      // Ring buffer bi holds block m; block m + 2 goes to the buffer block
-      // m - 1 used, which every wave has left once block m's wait returns.
-      issue(m_first, 0);
-      if (nb > 1) issue(m_first + 1, 1);
-      wait_block(m_first);
-      if (nb > 2) issue(m_first + 2, 2);
-      // The K / V registers are consumed here, outside the loops, so that the
-      // compiler's wait for those loads (it cannot see the copies above and
-      // waits for everything) happens once per tile rather than in a loop.
+    // The K / V registers are consumed here, on every path and outside the
+    // loops, so that the compiler's own wait for those loads (it sees the 8 *
+    // DT stores after them) happens once per tile.
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        asm volatile("" : "+v"(kraw[ks]), "+v"(vraw[ks]));
-        kreg[ks] = __builtin_bit_cast(bf16x8, kraw[ks]);
-        vreg[ks] = __builtin_bit_cast(bf16x8, vraw[ks]);
+    for (int ks = 0; ks < KS; ++ks) {
+      asm volatile("" : "+v"(kraw[ks]), "+v"(vraw[ks]));
+      kreg[ks] = __builtin_bit_cast(bf16x8, kraw[ks]);
+      vreg[ks] = __builtin_bit_cast(bf16x8, vraw[ks]);
+    }
+    if (nb > 0) {
+      // Tile start.  Normally the first two blocks were issued during the
+      // previous tile, before its K / V loads for this tile, and only the
+      // previous tile's 8 * DT stores may be outstanding after those.
+      int vm_last;
+      {
+        const int need = min(nb, 2);
+        if (iss_cur < need) {
+          while (iss_cur < need) {
+            prep_next(cp, np, has_nxt);
+            issue_now();
+          }
+          wait_vmcnt<0>();
+        } else {
+          static_assert(8 * DT <= 63, "store count");
+          wait_vmcnt<8 * DT>();
+        }
+        barrier_lds();  // the block's copies landed for every wave; the previous block's readers are done
       }
-      int bi = 0;
       // Blocks [m0, m1) with one body (a loop per mask variant, rather than
       // a branch per block, keeps register allocation to one body at a time).
+      // Block m + 2 goes to the ring buffer block m - 1 used, which every
+      // wave has left once block m's barrier returns.
       auto run = [&](auto masked_tag, int m0, int m1) {
         for (int m = m0; m < m1; ++m) {
           if (m != m_first) {
-            wait_block(m);
-            if (m + 2 < m_end) issue(m + 2, bi == 0 ? NBUF - 1 : bi - 1);
+            wait_n(vm_last);
+            barrier_lds();
           }
-          block(masked_tag, m, smem[bi]);
-          bi = bi == NBUF - 1 ? 0 : bi + 1;
+          prep_next(cp, np, has_nxt);
+          vm_last = j_n;
+          block(masked_tag, m, smem[ring_cmp]);
+          ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
         }
       };
       if (tile_partial) {
@@ -569,26 +749,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       }
     }
 
-    // dK = scale * dS^T Q, dV = P^T dO for this lane's key; C layout: lane ->
-    // key, registers -> head-dim rows 8*(i/4) + 4g + i%4 of each 32-wide tile.
-    if (key_ok) {
-      float* dkr = a.dk + ((s0 + kw) * H + h) * (int64_t)D;
-      float* dvr = a.dv + ((s0 + kw) * H + h) * (int64_t)D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = dt * 32 + i4 * 8 + g * 4;
-          f32x4 kv, vv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv[e] = dk[dt][i4 * 4 + e] * a.scale;
-            vv[e] = dv[dt][i4 * 4 + e];
-          }
-          *reinterpret_cast<f32x4*>(dkr + d0) = kv;
-          *reinterpret_cast<f32x4*>(dvr + d0) = vv;
-        }
-    }
+    // Tile end: the next tile's K / V loads, then this tile's stores.
+    if (has_nxt) load_kv(np);
+    store_dkdv(cp, min(L - k0, BN), dk, dv);
+    if (!has_nxt) break;
+    cp = np;
+    iss_cur = iss_nxt;
+    iss_nxt = 0;
   }
 }
 
@@ -665,11 +832,11 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.broadcast_q) {
-    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a);
-    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a);
+    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
   } else {
-    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a);
-    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a);
+    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
   }
   return hipGetLastError();
 }
