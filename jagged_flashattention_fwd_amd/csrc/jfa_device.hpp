@@ -215,12 +215,50 @@ __device__ __forceinline__ int64_t seq_range(const int64_t* __restrict__ off, in
 // ------------------------------------------------- direct global -> LDS --
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One 256-byte row (D = 128 bf16) copied by the 64 lanes of a wave straight
-// into LDS (global_load_lds_dword): lane l moves bytes 4l..4l+3.  The LDS
-// destination must be the same for every lane of the wave.
-__device__ __forceinline__ void dma_row256(const uint16_t* __restrict__ src_row, char* lds_row) {
-  __builtin_amdgcn_global_load_lds(src_row + 2 * lane_id(), (lds_void*)lds_row, 4, 0, 0);
+
+// 16 bytes per lane from base (wave-uniform) + voff (per lane) straight into
+// LDS at lds + 16 * lane (global_load_lds_dwordx4, 1 KB per wave).  Written
+// as asm so that the compiler does not treat it as a pending write to every
+// LDS buffer and drain it before each LDS read; completion is tracked with
+// wait_vmcnt.  readfirstlane states the uniformity of the addresses where
+// the compiler cannot prove it, and costs nothing where they already sit in
+// scalar registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_copy16(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t r = (uint64_t)(uintptr_t)base;
+  const uint64_t ru = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"((const void*)(uintptr_t)ru), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "m0");
 }
+#pragma clang diagnostic pop
+
+// Rows of 256 data bytes padded to 304 in LDS (19 chunks of 16 bytes), copied
+// with dma_copy16: one copy fills 3 whole rows and the first 7 chunks of a
+// fourth.  Lane l moves chunk l % 19 of row l / 19; chunks 16..18 are padding
+// (those lanes re-read chunk 0 into it).  A run of n >= 3 rows takes
+// ceil(n / 3) copies starting at rows min(3 k, n - 3); the overhang into the
+// row after the run writes the values that row's own copy writes, or lands
+// in a gap of at least 112 bytes after the tile.
+struct PadRowCopy {
+  static constexpr int GAP = 128;
+  uint32_t row;   // row of this lane within a copy (0..3)
+  uint32_t byte;  // byte offset of its chunk within the row
+  __device__ __forceinline__ PadRowCopy() {
+    const int l = lane_id();
+    row = (uint32_t)(l / 19);
+    byte = (l % 19) < 16 ? (uint32_t)(l % 19) * 16u : 0u;
+  }
+  static constexpr int copies(int n) { return (n + 2) / 3; }
+  static constexpr int start(int k, int n) { return 3 * k < n - 3 ? 3 * k : n - 3; }
+  // Per-lane source offset of copy k of a run whose rows past `last` repeat
+  // row `last`; stride = global row stride in bytes.
+  __device__ __forceinline__ uint32_t voff(int R, int last, uint32_t stride) const {
+    return (uint32_t)min(R + (int)row, last) * stride + byte;
+  }
+};
 
 // s_waitcnt with only the vector-memory counter constrained (at most n
 // operations of this wave still outstanding; n <= 63).

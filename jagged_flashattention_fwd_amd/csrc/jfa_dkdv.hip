@@ -47,24 +47,22 @@ struct Dkdv {
   static constexpr int KS = D / 16, DT = D / 32;
   static constexpr int RB = TileGeom<D>::ROW_BYTES;
   static constexpr int TILE = QB * RB;
-  // d = 128: rows are copied straight from global memory into LDS.
+  // d = 128: rows are copied straight from global memory into LDS, three
+  // padded rows per copy (PadRowCopy); a wave's 16 rows of a tile take 6.
   static constexpr bool DMA = D == 128;
   static constexpr int NBUF = 3;
   // One ring buffer: Q tile, dO tile, then four 64-float rows: lse*log2(e),
   // delta and two spares (waves 2 and 3 copy a duplicate row there, which
   // keeps the number of copies equal across waves).  Each tile is followed by
-  // a 128-byte gap that absorbs the overhang of the last row copy (below).
-  static constexpr int GAP = 128;
+  // the gap that absorbs the overhang of its last row copy.
+  static constexpr int GAP = PadRowCopy::GAP;
   static constexpr int OFF_DO = TILE + GAP;
   static constexpr int OFF_LSE = OFF_DO + TILE + GAP;
   static constexpr int OFF_DEL = OFF_LSE + QB * 4;
   static constexpr int BUF = OFF_LSE + 4 * QB * 4;
-  // A 16-byte-per-lane copy writes 1 KB of consecutive LDS: with 304-byte
-  // rows (19 chunks) that is 3 whole rows and 7 chunks of a fourth, so a
-  // wave's 16 rows of a tile take 6 copies starting at rows 0, 3, .., 12, 13.
-  static constexpr int RPW = QB / NW;    // rows per wave per tile
-  static constexpr int CPT = 6;          // copies per wave per tile
-  static_assert(D != 128 || (RB == 19 * 16 && RPW == 16), "copy geometry");
+  static constexpr int RPW = QB / NW;                  // rows per wave per tile
+  static constexpr int CPT = PadRowCopy::copies(RPW);  // copies per wave per tile
+  static_assert(!DMA || (RB == 19 * 16 && RPW >= 3), "copy geometry");
   static constexpr int IPS = 2 * CPT + 1;  // copies per wave per block
   static_assert(IPS <= 63, "one block of copies must fit the vector-memory counter");
   static_assert(NBUF * BUF <= 160 * 1024, "LDS");
@@ -127,31 +125,9 @@ __device__ __forceinline__ bf16x8 tr_operand(const i16x4 (&x)[8], int dt) {
 // kernels uses M0, and each statement sets it before its copy.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 256 contiguous bytes: row base (uniform) + 4 * lane.  Both addresses are
-// wave-uniform; readfirstlane states it for the compiler where it cannot
-// prove it, and costs nothing when they already sit in scalar registers.
-__device__ __forceinline__ void copy_row256(const void* row, uint32_t lane_off, uint32_t lds) {
-  const uint64_t r = (uint64_t)(uintptr_t)row;
-  const uint64_t ru = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
-  const uint32_t lu = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off),
-               "s"((const void*)(uintptr_t)ru), "s"(lu)
-               : "m0");
-}
 // One dword per lane from a per-lane address.
 __device__ __forceinline__ void copy_gather(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "m0");
-}
-// 16 bytes per lane from base (uniform) + voff (per lane), into LDS at
-// lds + 16 * lane.
-__device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t lds) {
-  const uint64_t r = (uint64_t)(uintptr_t)base;
-  const uint64_t ru = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"((const void*)(uintptr_t)ru), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
 }
 #pragma clang diagnostic pop
@@ -289,24 +265,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   uint32_t j_lds = 0;  // ring buffer
   uint32_t j_ldw = 0;  // this wave's first row in it
   int j_last = 0, j_n = 0;
-  // Copies [k0, k1) of this wave's 2 * CPT for the prepared block: copy k
-  // (Q for k < CPT, dO after) starts at row R = min(3 (k mod CPT), 13) of the
-  // wave's rows; lane i fills chunk i % 19 of row R + i / 19 (chunks 16..18
-  // are row padding, and lanes past the third row write the first chunks of
-  // the row after, with the same values its own copy writes, or into the
-  // gap after the tile).
-  const int cp_row = l / 19, cp_chunk = l % 19;
-  const uint32_t cp_byte = cp_chunk < 16 ? (uint32_t)cp_chunk * 16u : 0u;
+  // Copies [k0, k1) of this wave's 2 * CPT for the prepared block (Q for
+  // k < CPT, dO after), three padded rows each (PadRowCopy).
+  const PadRowCopy pc;
   auto issue_rows = [&](int k0, int k1) {
     if constexpr (C::DMA) {
       if (j_n == 0) return;
 #pragma unroll
       for (int k = k0; k < k1; ++k) {
-        const int kk = k % C::CPT;
-        const int R = min(3 * kk, C::RPW - 3);
-        const uint32_t voff = (uint32_t)min(R + cp_row, j_last) * (uint32_t)(qs * 2) + cp_byte;
-        if (k < C::CPT) copy16(j_q, voff, j_ldw + R * RB);
-        else copy16(j_d, voff, j_ldw + C::OFF_DO + R * RB);
+        const int R = PadRowCopy::start(k % C::CPT, C::RPW);
+        const uint32_t voff = pc.voff(R, j_last, (uint32_t)(qs * 2));
+        if (k < C::CPT) dma_copy16(j_q, voff, j_ldw + R * RB);
+        else dma_copy16(j_d, voff, j_ldw + C::OFF_DO + R * RB);
       }
     }
   };

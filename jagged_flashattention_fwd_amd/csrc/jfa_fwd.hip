@@ -49,15 +49,20 @@ struct Fwd {
   static constexpr int KS = D / 16;    // MFMA k-steps over the head dim
   static constexpr int DT = D / 32;    // 32-wide head-dim tiles of O^T
   static constexpr int TILE_BYTES = tile_bytes<BN, D>();
-  // d = 128: K/V rows go straight from global memory to LDS, DEP steps
-  // ahead of the one being computed, in a ring of DEP + 1 buffers.  Each
-  // wave issues IPS row copies per step; the vector-memory counter can hold
-  // at most 63 outstanding operations, which bounds DEP.
+  // d = 128: K/V rows go straight from global memory to LDS (three padded
+  // rows per copy), DEP steps ahead of the one being computed, in a ring of
+  // DEP + 1 buffers.  Each wave copies RPW rows of K and of V per step, IPS
+  // copies; the vector-memory counter can hold at most 63 outstanding
+  // operations, which bounds DEP.
   // d = 64: rows are staged through registers one step ahead.
   static constexpr bool DMA = D == 128;
-  static constexpr int IPS = 2 * BN / NW;
+  static constexpr int RPW = BN / NW;
+  static constexpr int CPT = PadRowCopy::copies(RPW);
+  static constexpr int IPS = 2 * CPT;
   static constexpr int DEP = DMA ? ((2 * IPS <= 63) ? 3 : 2) : 1;
   static constexpr int NBUF = DEP + 1;
+  static constexpr int BUF_BYTES = TILE_BYTES + PadRowCopy::GAP;
+  static_assert(!DMA || (TileGeom<D>::ROW_BYTES == 19 * 16 && RPW >= 3), "copy geometry");
 };
 
 template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
   using C = Fwd<D, NW, QW, CAUSAL, BCAST>;
   constexpr int BN = C::BN, QS = C::QS, BM = C::BM, KS = C::KS, DT = C::DT, NT = C::NT;
   constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS;
-  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::TILE_BYTES];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::BUF_BYTES];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int wave = tid / WAVE, l = tid % WAVE, g = l / 32, lc = l % 32;
@@ -123,16 +128,21 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
     // Copies K/V step j into ring buffer j % NBUF (d = 128 path).  Rows past
     // the sequence end repeat its last row: finite values that the mask
     // discards, and never an address outside the tensor.
+    const PadRowCopy pc;
     auto issue = [&](int j) {
-      char* Kd = smem[j % NBUF][0];
-      char* Vd = smem[j % NBUF][1];
-      const int k0 = j * BN;
+      constexpr int RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
+      const int base_row = min(j * BN + wave * RPW, L - 1);
+      const int last = L - 1 - base_row;
+      const uint16_t* kb = kbase + (int64_t)base_row * ld;
+      const uint16_t* vb = vbase + (int64_t)base_row * ld;
+      const uint32_t kd = lds_addr(smem[j % NBUF][0]) + wave * RPW * RB;
+      const uint32_t vd = lds_addr(smem[j % NBUF][1]) + wave * RPW * RB;
 #pragma unroll
-      for (int i = 0; i < BN / NW; ++i) {
-        const int row = wave * (BN / NW) + i;
-        const int src = min(k0 + row, L - 1);
-        dma_row256(kbase + (int64_t)src * ld, Kd + row * TileGeom<D>::ROW_BYTES);
-        dma_row256(vbase + (int64_t)src * ld, Vd + row * TileGeom<D>::ROW_BYTES);
+      for (int k = 0; k < C::CPT; ++k) {
+        const int R = PadRowCopy::start(k, RPW);
+        const uint32_t vo = pc.voff(R, last, (uint32_t)(ld * 2));
+        dma_copy16(kb, vo, kd + R * RB);
+        dma_copy16(vb, vo, vd + R * RB);
       }
     };
 
