@@ -380,6 +380,268 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
   }
 }
 
+// Broadcast dQ, d = 128.  One workgroup per (head, 256-row query block,
+// chunk); its K/V steps form one stream over the chunk's sequences, copied DEP
+// steps ahead across sequence boundaries and issued from inside the S^T / dP^T
+// products of the step DEP before.  The next sequence's dO rows, lse and
+// delta are loaded at the start of the current one.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a) {
+  constexpr int NW = DQ_BM_BCAST / 32;
+  using C = DqCfg<D, NW, CAUSAL, true>;
+  static_assert(C::DMA, "direct-copy form");
+  constexpr int BN = C::BN, BM = C::BM, KS = C::KS, DT = C::DT;
+  constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS, RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::BUF_BYTES];  // [buffer][K, V]
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int l = tid % WAVE, g = l / 32, lc = l % 32;
+  const PadRowCopy pc;
+  const int H = a.H, Lq = a.Lq, B = a.B;
+  const int64_t ld = (int64_t)H * D;
+  const float c2 = a.scale_log2;
+
+  const int NC = a.dq_chunks, n_qb = a.dq_qblocks;
+  const int item = blockIdx.x;
+  const int h = item / (n_qb * NC);
+  const int rem = item - h * n_qb * NC;
+  const int qb = rem / NC, c = rem - qb * NC;
+  const int q0 = qb * BM;
+  const int wq0 = q0 + wave * 32;
+  const int qi = wq0 + lc;
+  const bool q_ok = qi < Lq;
+
+  // Q^T operand (B) of this lane's query row; rows past Lq are zero.
+  bf16x8 qreg[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)h * Lq + (q_ok ? qi : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8);
+      if (!q_ok) x = u32x4{0u, 0u, 0u, 0u};
+      qreg[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  f32x16 dqa[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
+
+  // A sequence of the chunk: packed rows [s0, s0 + L), its dO / lse / delta
+  // rows, and its K/V step counts.
+  struct Sq {
+    int64_t s0, row;
+    int L, n_kv, n_bulk, r;
+  };
+  auto seq_at = [&](int r) {
+    Sq q;
+    q.r = r;
+    const int b = a.seq_order[r];
+    q.L = (int)seq_range(a.offsets, b, a.total_len, &q.s0);
+    q.row = ((int64_t)b * H + h) * Lq;
+    int kv_end = q.L;
+    if (CAUSAL) kv_end = min(kv_end, q0 + BM);
+    q.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    q.n_bulk = min(CAUSAL ? min(q0 / BN, q.L / BN) : q.L / BN, q.n_kv);
+    return q;
+  };
+  // The first sequence of the chunk at or after position r with keys to
+  // visit (r >= B: none).
+  auto next_valid = [&](int r) {
+    Sq q;
+    q.r = B;
+    q.n_kv = 0;
+    for (; r < B; r += NC) {
+      q = seq_at(r);
+      if (q.n_kv > 0) break;
+      q.r = B;
+    }
+    return q;
+  };
+
+  // ---- the step stream (as in the forward).
+  int g_iss = 0, g_cmp = 0, iss_cur = 0, iss_nxt = 0;
+  const uint16_t* j_k = a.k;
+  const uint16_t* j_v = a.v;
+  uint32_t j_kd = 0, j_vd = 0;
+  int j_last = 0;
+  bool j_on = false;
+  auto prep_next = [&](const Sq& cp, const Sq& np, bool has_nxt) {
+    const int nn = has_nxt ? np.n_kv : 0;
+    const bool cur = iss_cur < cp.n_kv;
+    j_on = cur || iss_nxt < nn;
+    if (!j_on) return;
+    const int64_t s0_ = cur ? cp.s0 : np.s0;
+    const int L_ = cur ? cp.L : np.L;
+    const int j = cur ? iss_cur : iss_nxt;
+    const int base_row = min(j * BN + wave * RPW, L_ - 1);
+    j_k = a.k + ((s0_ + base_row) * H + h) * (int64_t)D;
+    j_v = a.v + ((s0_ + base_row) * H + h) * (int64_t)D;
+    j_last = L_ - 1 - base_row;
+    const int buf = g_iss % NBUF;
+    j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
+    j_vd = lds_addr(smem[buf][1]) + wave * RPW * RB;
+    if (cur) ++iss_cur;
+    else ++iss_nxt;
+    ++g_iss;
+  };
+  auto issue_copies = [&](int k0, int k1) {
+    if (!j_on) return;
+#pragma unroll
+    for (int k = k0; k < k1; ++k) {
+      const int R = PadRowCopy::start(k % C::CPT, RPW);
+      const uint32_t vo = pc.voff(R, j_last, (uint32_t)(ld * 2));
+      if (k < C::CPT) dma_copy16(j_k, vo, j_kd + R * RB);
+      else dma_copy16(j_v, vo, j_vd + R * RB);
+    }
+  };
+
+  // Per-sequence operands of this lane's query row: dO (A operand of dP^T's
+  // B side), lse * log2(e) and delta; the next sequence's are loaded ahead.
+  bf16x8 doreg[KS], don[KS];
+  float lse2 = INFINITY, del = 0.f, lse2n = INFINITY, deln = 0.f;
+  auto load_seq = [&](const Sq& q) {
+    const int64_t row = q.row + (q_ok ? qi : 0);
+    const uint16_t* dr = a.dout + row * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) don[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dr + ks * 16 + g * 8));
+    lse2n = a.lse2[row];
+    deln = a.delta[row];
+  };
+
+  Sq cp = next_valid(c);
+  if (cp.r < B) load_seq(cp);
+  while (cp.r < B) {
+    const Sq np = next_valid(cp.r + NC);
+    const bool has_nxt = np.r < B;
+    // This sequence's operands (loaded during the previous one, so only the
+    // copies issued since, which the prefetched steps need anyway, are
+    // waited for with them).
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 x = __builtin_bit_cast(u32x4, don[ks]);
+      asm volatile("" : "+v"(x));
+      doreg[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+    asm volatile("" : "+v"(lse2n), "+v"(deln));
+    lse2 = q_ok ? lse2n : INFINITY;
+    del = q_ok ? deln : 0.f;
+    if (has_nxt) load_seq(np);
+    const int L = cp.L, n_kv = cp.n_kv;
+    {
+      const int need = min(DEP, n_kv);
+      if (iss_cur < need) {
+        while (iss_cur < need) {
+          prep_next(cp, np, has_nxt);
+          issue_copies(0, 2 * C::CPT);
+        }
+      }
+    }
+    auto kv_step = [&](int j, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const int buf = g_cmp % NBUF;
+      const int k0 = j * BN;
+      // Wait for this wave's copies of the step: the copies issued after it
+      // may stay in flight.  (Copies issued before this sequence's operand
+      // loads were already waited for with them, and the next sequence's
+      // operand loads, issued before any later copy, need no wait here.)
+      {
+        const int after = g_iss - 1 - g_cmp;
+        if constexpr (DEP >= 3) {
+          if (after >= 2) wait_vmcnt<2 * IPS>();
+          else if (after == 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        } else {
+          if (after >= 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        }
+      }
+      barrier_lds();
+      prep_next(cp, np, has_nxt);
+      const bool active = !(CAUSAL && MASKED) || (k0 <= wq0 + 31);
+      if (!active) {
+        issue_copies(0, 2 * C::CPT);
+      } else {
+        const char* Ks = smem[buf][0];
+        const char* Vs = smem[buf][1];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          f32x16 sacc = f32x16{}, dpacc = f32x16{};
+          static_for<0, KS>([&](auto ks_tag) {
+            constexpr int ks = decltype(ks_tag)::value;
+            const int off = tile_off<D>(kt * 32 + lc, ks * 2 + g);
+            sacc = mfma32(lds_read16(Ks, off), qreg[ks], sacc);
+            dpacc = mfma32(lds_read16(Vs, off), doreg[ks], dpacc);
+            if (kt == 0) {
+              constexpr int PER = (2 * C::CPT + KS - 1) / KS;
+              issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
+            }
+          });
+          // C layout: lane owns query qi; register i is key
+          // k0 + kt*32 + 8*(i/4) + 4g + i%4.
+          float dsf[16];
+          float dsmax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(sacc[i] * c2 - lse2);
+            if (MASKED) {
+              const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+              const bool ok = key < L && (!CAUSAL || key <= qi);
+              pv = ok ? pv : 0.f;
+            }
+            dsf[i] = pv * (dpacc[i] - del);
+            dsmax = fmaxf(dsmax, fabsf(dsf[i]));
+          }
+          const bool split = __any(dsmax > SPLIT_DS);
+          uint32_t hi[2][4], lo[2][4];
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const int hh = i >> 3, e = (i & 7) >> 1;
+            if (split) {
+              split_bf16x2(dsf[i], dsf[i + 1], &hi[hh][e], &lo[hh][e]);
+            } else {
+              hi[hh][e] = pack_bf16x2(dsf[i], dsf[i + 1]);
+              lo[hh][e] = 0u;
+            }
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r0 = kt * 32 + hh * 16 + g * 4;
+            bf16x8 ka[DT];
+            const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
+            const uint32_t a0 = lds_addr(Ks + tile_off_col4<D>(r0 + jj, cq));
+            lds_operand_tr_x4(a0, a0 + 8 * RB, ka);
+            const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{hi[hh][0], hi[hh][1], hi[hh][2], hi[hh][3]});
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], db, dqa[dt]);
+            if (split) {
+              const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{lo[hh][0], lo[hh][1], lo[hh][2], lo[hh][3]});
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], dl, dqa[dt]);
+            }
+          }
+        }
+      }
+      ++g_cmp;
+    };
+    for (int j = 0; j < cp.n_bulk; ++j) kv_step(j, std::false_type{});
+    for (int j = cp.n_bulk; j < n_kv; ++j) kv_step(j, std::true_type{});
+    cp = np;
+    iss_cur = iss_nxt;
+    iss_nxt = 0;
+  }
+  // this chunk's fp32 partial, rows q0.. of (h, qb): [BM][D]
+  float* dst = a.dq_part + (int64_t)item * BM * D + (int64_t)(wave * 32 + lc) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = dqa[dt][i4 * 4 + e];
+      *reinterpret_cast<f32x4*>(dst + dt * 32 + i4 * 8 + g * 4) = v;
+    }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   const int64_t rows = a.broadcast_q ? (int64_t)a.B * a.H * a.Lq : a.total_len * a.H;
@@ -396,10 +658,17 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (a.broadcast_q) {
     const int items = a.H * a.dq_qblocks * a.dq_chunks;
-    if (a.causal)
-      JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, true, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
-    else
-      JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, false, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+    if constexpr (D == 128) {
+      if (a.causal)
+        JFA_TIMED_LAUNCH(K_DQ, st, (dq_bcast_kernel<D, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+      else
+        JFA_TIMED_LAUNCH(K_DQ, st, (dq_bcast_kernel<D, false>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+    } else {
+      if (a.causal)
+        JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, true, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+      else
+        JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, false, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = (int64_t)a.H * a.Lq * D;
     JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dq_part,

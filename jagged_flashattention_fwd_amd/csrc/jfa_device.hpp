@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace jfa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -32,6 +34,15 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// f(integral_constant<int, i>) for i = B .. E-1, at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------- math --
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -234,6 +245,18 @@ __device__ __forceinline__ void dma_copy16(const void* base, uint32_t voff, uint
                : "m0");
 }
 #pragma clang diagnostic pop
+
+// Buffer resource over [base, base + nbytes): buffer stores at byte offsets
+// past nbytes are dropped by the hardware, which bounds-checks them per lane.
+// Both values are wave-uniform; readfirstlane keeps the descriptor in scalar
+// registers where the compiler cannot prove that.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  const uint64_t r = (uint64_t)(uintptr_t)base;
+  const uint64_t ru = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)ru, (short)0, __builtin_amdgcn_readfirstlane(nbytes),
+                                           0x00020000);
+}
 
 // Rows of 256 data bytes padded to 304 in LDS (19 chunks of 16 bytes), copied
 // with dma_copy16: one copy fills 3 whole rows and the first 7 chunks of a

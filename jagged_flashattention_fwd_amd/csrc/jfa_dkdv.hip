@@ -132,14 +132,6 @@ __device__ __forceinline__ void copy_gather(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// f(integral_constant<int, i>) for i = B .. E-1, at compile time.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_VALU = 0x2;
@@ -381,8 +373,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   auto store_dkdv = [&](const Tp& p, int nvalid, const f32x16 (&dk)[DT], const f32x16 (&dv)[DT]) {
     const int64_t row0 = (p.s0 + p.k0) * H + p.h;
     const int nrec = nvalid * H * D * 4;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(a.dk + row0 * D, (short)0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(a.dv + row0 * D, (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.dk + row0 * D, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.dv + row0 * D, nrec);
     float* st = stage[wave];
     const int rk8 = l >> 3, rc = (l & 7) * 4;  // read side: key 8r + rk8, columns rc .. rc+3
     auto chunk = [&](const f32x16& acc, float mul, const __amdgpu_buffer_rsrc_t& rs, int dt) {

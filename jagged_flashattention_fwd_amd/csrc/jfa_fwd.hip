@@ -323,10 +323,349 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// d = 128 form of the kernel.  K/V steps form one stream over this
+// workgroup's tiles: copies run DEP steps ahead across tile boundaries, and a
+// step's copies are issued from inside the S^T products of the step DEP
+// before it.  The next tile's Q rows are loaded before the current tile's O /
+// lse are stored, and the stores are bounded buffer stores of a fixed count
+// per wave, so the wait at the next tile start covers exactly the copies and
+// Q loads and lets the stores drain.
+template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const TileRec* __restrict__ tiles) {
+  using C = Fwd<D, NW, QW, CAUSAL, BCAST>;
+  static_assert(C::DMA, "direct-copy form");
+  constexpr int BN = C::BN, QS = C::QS, BM = C::BM, KS = C::KS, DT = C::DT;
+  constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS, RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
+  // Stores per wave at a tile end: O (DT * 4 pieces of 8 bytes) and lse, per subtile.
+  constexpr int NST = QS * (4 * DT + 1);
+  static_assert(DEP * IPS + NST <= 63, "vector-memory counter");
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::BUF_BYTES];  // [buffer][K, V]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int l = tid % WAVE, g = l / 32, lc = l % 32;
+  const int slot = logical_slot(blockIdx.x, a.P);
+  const int64_t T = *a.n_tiles;
+  const int H = a.H, Lq = a.Lq;
+  const int64_t ld = (int64_t)H * D;  // packed row stride (elements)
+  const float c2 = a.scale_log2;
+  const PadRowCopy pc;
+
+  const int64_t t0 = zigzag_tile(0, slot, a.P);
+  if (t0 >= T) return;
+
+  struct Tp {
+    int64_t s0;
+    int L, h, b, q0, n_kv, n_bulk;
+  };
+  auto tparams = [&](const TileRec& r) {
+    Tp p;
+    p.s0 = r.s0;
+    p.L = r.L;
+    p.h = r.h;
+    p.b = r.b;
+    p.q0 = r.blk * BM;
+    const int nq = BCAST ? Lq : r.L;
+    int kv_end = r.L;
+    if (CAUSAL) kv_end = min(kv_end, min(p.q0 + BM, nq));
+    p.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    p.n_bulk = min(CAUSAL ? min(p.q0 / BN, r.L / BN) : r.L / BN, p.n_kv);
+    return p;
+  };
+
+  // ---- the step stream.  g_iss / g_cmp: steps issued / computed so far
+  // over the whole stream; iss_cur / iss_nxt: steps of the current / next
+  // tile issued.
+  int g_iss = 0, g_cmp = 0, iss_cur = 0, iss_nxt = 0;
+  // The prepared step: this wave's first K and V source rows, rows past
+  // j_last repeat row j_last, its ring buffer, and whether there is one.
+  const uint16_t* j_k = a.k;
+  const uint16_t* j_v = a.v;
+  uint32_t j_kd = 0, j_vd = 0;
+  int j_last = 0;
+  bool j_on = false;
+  auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
+    const int nn = has_nxt ? np.n_kv : 0;
+    const bool cur = iss_cur < cp.n_kv;
+    j_on = cur || iss_nxt < nn;
+    if (!j_on) return;
+    const int64_t s0_ = cur ? cp.s0 : np.s0;
+    const int L_ = cur ? cp.L : np.L, h_ = cur ? cp.h : np.h;
+    const int j = cur ? iss_cur : iss_nxt;
+    const int base_row = min(j * BN + wave * RPW, L_ - 1);
+    j_k = a.k + ((s0_ + base_row) * H + h_) * (int64_t)D;
+    j_v = a.v + ((s0_ + base_row) * H + h_) * (int64_t)D;
+    j_last = L_ - 1 - base_row;
+    const int buf = g_iss % NBUF;
+    j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
+    j_vd = lds_addr(smem[buf][1]) + wave * RPW * RB;
+    if (cur) ++iss_cur;
+    else ++iss_nxt;
+    ++g_iss;
+  };
+  // Copies [k0, k1) of the prepared step (K for k < CPT, V after).
+  auto issue_copies = [&](int k0, int k1) {
+    if (!j_on) return;
+#pragma unroll
+    for (int k = k0; k < k1; ++k) {
+      const int R = PadRowCopy::start(k % C::CPT, RPW);
+      const uint32_t vo = pc.voff(R, j_last, (uint32_t)(ld * 2));
+      if (k < C::CPT) dma_copy16(j_k, vo, j_kd + R * RB);
+      else dma_copy16(j_v, vo, j_vd + R * RB);
+    }
+  };
+
+  // ---- Q^T operand (B): lane (lc, g) holds Q[row][8*(2ks+g) .. +7].
+  // Rows past the last query read row 0 of the block (finite, never stored).
+  bf16x8 qreg[QS][KS];
+  auto load_q = [&](const Tp& p) {
+    const int nq = BCAST ? Lq : p.L;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      int qi = p.q0 + wave * (QS * 32) + s * 32 + lc;
+      qi = qi < nq ? qi : p.q0 < nq ? p.q0 : 0;
+      const uint16_t* qrow = BCAST ? a.q + ((int64_t)p.h * Lq + qi) * D : a.q + ((p.s0 + qi) * H + p.h) * (int64_t)D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qreg[s][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8));
+    }
+  };
+
+  // ---- O = acc / l (bf16) and lse = (m + log2 l) * ln 2 of a tile: NST
+  // buffer stores per wave, bounded to the tile's rows (nrows = 0 stores
+  // nothing).
+  f32x16 oacc[DT][QS];
+  float m2[QS], lsum[QS];
+  auto store_out = [&](const Tp& p, int nrows) {
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      const int r0 = p.q0 + wave * (QS * 32) + s * 32;  // first row of the subtile
+      const int nv = max(0, min(nrows - r0, 32));        // its valid rows
+      const int64_t orow0 = BCAST ? ((int64_t)p.b * H + p.h) * Lq + r0 : (p.s0 + r0) * H + p.h;
+      const int ostride = BCAST ? D : H * D;             // elements between rows
+      const int lstride = BCAST ? 1 : H;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + orow0 * D, nv * ostride * 2);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + orow0, nv * lstride * 4);
+      const float lt = sum_across_halves(lsum[s]);
+      const float inv = lt > 0.f ? fast_rcp(lt) : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = dt * 32 + i4 * 8 + g * 4;
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[dt][s][i4 * 4 + 0] * inv, oacc[dt][s][i4 * 4 + 1] * inv);
+          w[1] = pack_bf16x2(oacc[dt][s][i4 * 4 + 2] * inv, oacc[dt][s][i4 * 4 + 3] * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(w, ro, (lc * ostride + d0) * 2, 0, 0);
+        }
+      const float lse = lt > 0.f ? (m2[s] + fast_log2(lt)) * LN2 : -INFINITY;
+      // lanes of the second half hold the same row: their store is dropped
+      const uint32_t loff = g == 0 ? (uint32_t)(lc * lstride * 4) : 0xfffffff0u;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, loff, 0, 0);
+    }
+  };
+
+  Tp cp = tparams(tiles[t0]);
+  load_q(cp);
+  {
+    // Stores that write nothing: the first tile start sees the same
+    // operations after its Q loads as every later one.
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      lsum[s] = 0.f;
+      m2[s] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt][s] = f32x16{};
+    }
+    store_out(cp, 0);
+  }
+
+  for (int64_t pass = 0;; ++pass) {
+    const int64_t tn = zigzag_tile(pass + 1, slot, a.P);
+    const bool has_nxt = tn < T;
+    const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
+    const int64_t s0 = cp.s0;
+    const int L = cp.L, h = cp.h, q0 = cp.q0, n_kv = cp.n_kv;
+    const int nq = BCAST ? Lq : L;
+    const int wq0 = q0 + wave * (QS * 32);  // first query row of this wave
+    (void)s0;
+    (void)h;
+
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int s = 0; s < QS; ++s) oacc[dt][s] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < QS; ++s) { m2[s] = -INFINITY; lsum[s] = 0.f; }
+
+    // Tile start: normally its first min(DEP, n_kv) steps were issued during
+    // the previous tile, before its Q loads for this tile, and only the
+    // previous tile's NST stores may be outstanding after those.
+    {
+      const int need = min(DEP, n_kv);
+      if (iss_cur < need) {
+        while (iss_cur < need) {
+          prep_next(cp, np, has_nxt);
+          issue_copies(0, 2 * C::CPT);
+        }
+        wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<NST>();
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < QS; ++s)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = __builtin_bit_cast(u32x4, qreg[s][ks]);
+        asm volatile("" : "+v"(x));
+        qreg[s][ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    const int g_first = g_cmp;  // stream index of this tile's step 0
+
+    // One K/V step of BN keys.  MASKED is a compile-time constant: the
+    // bulk steps carry no mask code at all; only the tail step and the
+    // causal diagonal steps take the masked body.
+    auto kv_step = [&](int j, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const int buf = g_cmp % NBUF;
+      const int k0 = j * BN;
+      // Wait for this wave's copies of step j (steps issued after it may
+      // still be in flight), then for every wave's; the ring buffer of the
+      // step before is then free.  Steps issued before the tile start were
+      // waited for there.
+      if (g_cmp != g_first) {
+        const int after = g_iss - 1 - g_cmp;
+        if constexpr (DEP >= 3) {
+          if (after >= 2) wait_vmcnt<2 * IPS>();
+          else if (after == 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        } else {
+          if (after >= 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        }
+      }
+      barrier_lds();
+      prep_next(cp, np, has_nxt);
+      // Causal: a wave whose last query row precedes this step's first key
+      // sees none of it.
+      const bool active = !(CAUSAL && MASKED) || (k0 <= wq0 + QS * 32 - 1);
+      if (!active) {
+        issue_copies(0, 2 * C::CPT);
+      } else {
+        const char* Ks = smem[buf][0];
+        const char* Vs = smem[buf][1];
+        // ---- S^T = K Q^T : two 32-key subtiles x QS query subtiles; the
+        // next step's copies are issued between the k-steps.
+        f32x16 sacc[2][QS];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s = 0; s < QS; ++s) sacc[kt][s] = f32x16{};
+        static_for<0, KS>([&](auto ks_tag) {
+          constexpr int ks = decltype(ks_tag)::value;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const bf16x8 ka = lds_read16(Ks, tile_off<D>(kt * 32 + lc, ks * 2 + g));
+#pragma unroll
+            for (int s = 0; s < QS; ++s) sacc[kt][s] = mfma32(ka, qreg[s][ks], sacc[kt][s]);
+          }
+          constexpr int PER = (2 * C::CPT + KS - 1) / KS;
+          issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
+        });
+        // ---- online softmax, one query per lane (both halves of a row agree).
+        uint32_t pk[2][2][QS][4];  // [kt][k-half][s][bf16 pairs]
+#pragma unroll
+        for (int s = 0; s < QS; ++s) {
+          const int qi = wq0 + s * 32 + lc;
+          float mt = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              float x = sacc[kt][s][i] * c2;
+              if (MASKED) {
+                const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+                const bool ok = key < L && (!CAUSAL || key <= qi);
+                x = ok ? x : -INFINITY;
+              }
+              sacc[kt][s][i] = x;
+              mt = fmaxf(mt, x);
+            }
+          mt = max_across_halves(mt);
+          const bool need = mt > m2[s] + RESCALE_SLACK;
+          if (__builtin_expect(__any(need), 0)) {
+            const float alpha = need ? fast_exp2(m2[s] - mt) : 1.f;
+            m2[s] = need ? mt : m2[s];
+            lsum[s] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][s] *= alpha;
+          }
+          const float mref = m2[s] == -INFINITY ? 0.f : m2[s];
+          float ls = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int i = hh * 8 + e * 2;
+                const float p0 = fast_exp2(sacc[kt][s][i] - mref);
+                const float p1 = fast_exp2(sacc[kt][s][i + 1] - mref);
+                ls += p0 + p1;
+                pk[kt][hh][s][e] = pack_bf16x2(p0, p1);
+              }
+          lsum[s] += ls;
+        }
+        // ---- O^T += V^T P^T.  k-slots of P^T (B operand) for k-half hh of
+        // key subtile kt are keys kt*32 + hh*16 + {4g..4g+3, 8+4g..8+4g+3}; the
+        // transpose read of V delivers the same keys.
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r0 = kt * 32 + hh * 16 + g * 4;
+            bf16x8 va[DT];
+            // lane's transpose-read address: row r0 + j, column 16*(G&1) + 4q
+            const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
+            const uint32_t a0 = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
+            lds_operand_tr_x4(a0, a0 + 8 * RB, va);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+              for (int s = 0; s < QS; ++s) {
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[kt][hh][s][0], pk[kt][hh][s][1],
+                                                                    pk[kt][hh][s][2], pk[kt][hh][s][3]});
+                oacc[dt][s] = mfma32(va[dt], pb, oacc[dt][s]);
+              }
+            }
+          }
+      }
+      ++g_cmp;
+    };
+    const int n_plain = cp.n_bulk;
+    for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
+    for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+
+    // Tile end: the next tile's Q rows, then this tile's O and lse.
+    if (has_nxt) load_q(np);
+    store_out(cp, nq);
+    if (!has_nxt) break;
+    cp = np;
+    iss_cur = iss_nxt;
+    iss_nxt = 0;
+  }
+}
+
 template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  JFA_TIMED_LAUNCH(K_FWD, stream, (fwd_kernel<D, NW, QW, CAUSAL, BCAST>), dim3(a.P), dim3(NW * WAVE), 0,
-                   stream, a);
+  if constexpr (D == 128) {
+    JFA_TIMED_LAUNCH(K_FWD, stream, (fwd_kernel_dma<D, NW, QW, CAUSAL, BCAST>), dim3(a.P), dim3(NW * WAVE), 0,
+                     stream, a, a.tiles);
+  } else {
+    JFA_TIMED_LAUNCH(K_FWD, stream, (fwd_kernel<D, NW, QW, CAUSAL, BCAST>), dim3(a.P), dim3(NW * WAVE), 0,
+                     stream, a);
+  }
   return hipGetLastError();
 }
 
