@@ -336,8 +336,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   static_assert(C::DMA, "direct-copy form");
   constexpr int BN = C::BN, QS = C::QS, BM = C::BM, KS = C::KS, DT = C::DT;
   constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS, RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
-  // Stores per wave at a tile end: O (DT * 4 pieces of 8 bytes) and lse, per subtile.
-  constexpr int NST = QS * (4 * DT + 1);
+  // Stores per wave at a tile end: O (DT * 2 pieces of 16 bytes) and lse, per subtile.
+  constexpr int NST = QS * (2 * DT + 1);
   static_assert(DEP * IPS + NST <= 63, "vector-memory counter");
   __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::BUF_BYTES];  // [buffer][K, V]
 
@@ -448,15 +448,30 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + orow0, nv * lstride * 4);
       const float lt = sum_across_halves(lsum[s]);
       const float inv = lt > 0.f ? fast_rcp(lt) : 0.f;
+      // Register group i4 of lane (row, g) holds columns dt*32 + 8 i4 + 4g
+      // + 0..3.  Lanes l and l + 32 trade one group of each pair (2p, 2p+1)
+      // so that each then holds 8 consecutive columns, 16 + 8g .. of 16p:
+      // one 16-byte store per lane and pair.
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = dt * 32 + i4 * 8 + g * 4;
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[dt][s][i4 * 4 + 0] * inv, oacc[dt][s][i4 * 4 + 1] * inv);
-          w[1] = pack_bf16x2(oacc[dt][s][i4 * 4 + 2] * inv, oacc[dt][s][i4 * 4 + 3] * inv);
-          __builtin_amdgcn_raw_buffer_store_b64(w, ro, (lc * ostride + d0) * 2, 0, 0);
+        for (int p2 = 0; p2 < 2; ++p2) {
+          uint32_t w[2][2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int i4 = 2 * p2 + k;
+            w[k][0] = pack_bf16x2(oacc[dt][s][i4 * 4 + 0] * inv, oacc[dt][s][i4 * 4 + 1] * inv);
+            w[k][1] = pack_bf16x2(oacc[dt][s][i4 * 4 + 2] * inv, oacc[dt][s][i4 * 4 + 3] * inv);
+          }
+          // g = 0 sends group 2p+1 and receives the partner's group 2p;
+          // g = 1 sends group 2p and receives the partner's group 2p+1.
+          const uint32_t s0w = g ? w[0][0] : w[1][0], s1w = g ? w[0][1] : w[1][1];
+          const uint32_t r0w = (uint32_t)__shfl_xor((int)s0w, 32), r1w = (uint32_t)__shfl_xor((int)s1w, 32);
+          u32x4 v;
+          if (g == 0) v = u32x4{w[0][0], w[0][1], r0w, r1w};
+          else v = u32x4{r0w, r1w, w[1][0], w[1][1]};
+          const int d0 = dt * 32 + p2 * 16 + g * 8;
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (lc * ostride + d0) * 2, 0, 0);
         }
       const float lse = lt > 0.f ? (m2[s] + fast_log2(lt)) * LN2 : -INFINITY;
       // lanes of the second half hold the same row: their store is dropped
@@ -578,21 +593,42 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
 #pragma unroll
         for (int s = 0; s < QS; ++s) {
           const int qi = wq0 + s * 32 + lc;
-          float mt = -INFINITY;
+          // Row maximum in exp2 units.  Unmasked steps reduce the raw
+          // scores (the maximum for a non-negative scale, the minimum for a
+          // negative one) and fold the scale into the exponent's fma below;
+          // masked steps scale first and set masked scores to -inf.
+          float mt;
+          if constexpr (MASKED) {
+            mt = -INFINITY;
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float x = sacc[kt][s][i] * c2;
-              if (MASKED) {
+              for (int i = 0; i < 16; ++i) {
+                float x = sacc[kt][s][i] * c2;
                 const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
                 const bool ok = key < L && (!CAUSAL || key <= qi);
                 x = ok ? x : -INFINITY;
+                sacc[kt][s][i] = x;
+                mt = fmaxf(mt, x);
               }
-              sacc[kt][s][i] = x;
-              mt = fmaxf(mt, x);
+            mt = max_across_halves(mt);
+          } else {
+            if (c2 >= 0.f) {
+              float r = -INFINITY;
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) r = fmaxf(r, sacc[kt][s][i]);
+              mt = max_across_halves(r) * c2;
+            } else {
+              float r = INFINITY;
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) r = fminf(r, sacc[kt][s][i]);
+              mt = min_across_halves(r) * c2;
             }
-          mt = max_across_halves(mt);
+          }
           const bool need = mt > m2[s] + RESCALE_SLACK;
           if (__builtin_expect(__any(need), 0)) {
             const float alpha = need ? fast_exp2(m2[s] - mt) : 1.f;
@@ -610,8 +646,14 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int i = hh * 8 + e * 2;
-                const float p0 = fast_exp2(sacc[kt][s][i] - mref);
-                const float p1 = fast_exp2(sacc[kt][s][i + 1] - mref);
+                float p0, p1;
+                if constexpr (MASKED) {
+                  p0 = fast_exp2(sacc[kt][s][i] - mref);
+                  p1 = fast_exp2(sacc[kt][s][i + 1] - mref);
+                } else {
+                  p0 = fast_exp2(__builtin_fmaf(sacc[kt][s][i], c2, -mref));
+                  p1 = fast_exp2(__builtin_fmaf(sacc[kt][s][i + 1], c2, -mref));
+                }
                 ls += p0 + p1;
                 pk[kt][hh][s][e] = pack_bf16x2(p0, p1);
               }
