@@ -36,8 +36,8 @@ namespace {
 // value, and dV / dK sum that error over many queries.  Where a subtile holds
 // a large value (short or sharply peaked sequences) the rounded remainder
 // x - bf16(x) is multiplied in as well.
-constexpr float SPLIT_P = 1.0f / 16.0f;
-constexpr float SPLIT_DS = 0.25f;
+constexpr float SPLIT_P = 0.25f;
+constexpr float SPLIT_DS = 1.0f;
 
 template <int D>
 struct Dkdv {

@@ -37,9 +37,9 @@ def _check_case(jfa, lengths, H, d, Lq, bq, causal, seed, std=1.0, scale=None):
     dq, dk, dv = _run(jfa, t, bq, causal, scale)
     rq, rk, rv = jo.jagged_backward(to64(t["q"]), to64(t["k"]), to64(t["v"]),
                                     t["offsets"].cpu().numpy(), scale, causal, bq, to64(t["dout"]))
-    compare("dQ", to64(dq), rq)
-    compare("dK", to64(dk), rk)
-    compare("dV", to64(dv), rv)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        ma, rl = compare(name, to64(got), ref)
+        print(f"  {name}: max abs {ma:.2e}  rel L2 {rl:.2e}", flush=True)
 
 
 EDGE = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 0, 255, 256, 257, 300]
@@ -54,6 +54,14 @@ def test_bwd_edge_lengths(jfa, d, bq, causal):
 @pytest.mark.parametrize("Lq", [1, 32, 63, 64, 65, 256, 300])
 def test_bwd_broadcast_lq(jfa, Lq):
     _check_case(jfa, [5, 130, 1, 64, 700, 129], 3, 128, Lq, True, False, seed=100 + Lq)
+
+
+# Short sequences against many broadcast queries (the regime of skew_bcast's
+# short sequences): P and dS are large, and dV / dK sum their rounding over
+# all 512 queries.
+@pytest.mark.parametrize("std", [0.5, 1.0])
+def test_bwd_short_sequences_many_queries(jfa, std):
+    _check_case(jfa, [2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 1, 7], 2, 128, 512, True, False, seed=31, std=std)
 
 
 @pytest.mark.parametrize("idx", [0, 1])
