@@ -223,9 +223,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   const int64_t t0 = zigzag_tile(0, slot, a.P);
   if (t0 >= T) return;
 
+  const int64_t qs = BCAST ? (int64_t)D : ld;          // row stride of Q / dO
+  const int64_t sld = BCAST ? 1 : H;                    // row stride of lse / delta
+  // Per-tile values, with the tile's row-0 addresses of Q, dO and this
+  // wave's lse*log2(e) (even waves) or delta (odd waves) rows.
   struct Tp {
     int64_t s0;
-    int L, h, b, k0, m_first, m_end;
+    int L, h, b, k0, m_first, m_end, nq;
+    const uint16_t* qb;
+    const uint16_t* db;
+    const float* vb;
   };
   auto tparams = [&](const TileRec& r) {
     Tp p;
@@ -234,13 +241,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     p.h = r.h;
     p.b = r.b;
     p.k0 = r.blk * BN;
-    const int nq = BCAST ? Lq : r.L;
+    p.nq = BCAST ? Lq : r.L;
     p.m_first = CAUSAL ? p.k0 / QB : 0;                 // query blocks that can see a key of the tile
-    p.m_end = max((nq + QB - 1) / QB, p.m_first);       // exclusive
+    p.m_end = max((p.nq + QB - 1) / QB, p.m_first);     // exclusive
+    p.qb = BCAST ? a.q + (int64_t)r.h * Lq * D : a.q + (r.s0 * H + r.h) * (int64_t)D;
+    p.db = BCAST ? a.dout + ((int64_t)r.b * H + r.h) * Lq * D : a.dout + (r.s0 * H + r.h) * (int64_t)D;
+    p.vb = ((wave & 1) ? a.delta : a.lse2) + (BCAST ? ((int64_t)r.b * H + r.h) * Lq : r.s0 * H + r.h);
     return p;
   };
-  const int64_t qs = BCAST ? (int64_t)D : ld;          // row stride of Q / dO
-  const int64_t sld = BCAST ? 1 : H;                    // row stride of lse / delta
 
   // One query block's copies into a ring buffer.  With d = 128 they are
   // prepared before the block (which block, source rows, buffer) and issued
@@ -308,24 +316,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     const int nbn = has_nxt ? np.m_end - np.m_first : 0;
     const bool cur = iss_cur < nbc;
     if (!cur && iss_nxt >= nbn) return;
-    const int64_t s0_ = cur ? cp.s0 : np.s0;
-    const int h_ = cur ? cp.h : np.h, b_ = cur ? cp.b : np.b;
-    const int nq_ = BCAST ? Lq : (cur ? cp.L : np.L);
+    const int nq_ = cur ? cp.nq : np.nq;
     const int j = cur ? cp.m_first + iss_cur : np.m_first + iss_nxt;
-    const uint16_t* qbase = BCAST ? a.q + (int64_t)h_ * Lq * D : a.q + (s0_ * H + h_) * (int64_t)D;
-    const uint16_t* dobase = BCAST ? a.dout + ((int64_t)b_ * H + h_) * Lq * D : a.dout + (s0_ * H + h_) * (int64_t)D;
-    const int64_t rbase = BCAST ? ((int64_t)b_ * H + h_) * Lq : s0_ * H + h_;  // lse / delta row 0
     if constexpr (C::DMA) {
       const int base_row = min(j * QB + wave * C::RPW, nq_ - 1);
-      j_q = qbase + (int64_t)base_row * qs;
-      j_d = dobase + (int64_t)base_row * qs;
-      j_v = ((wave & 1) ? a.delta : a.lse2) + rbase + (int64_t)min(j * QB + l, nq_ - 1) * sld;
+      j_q = (cur ? cp.qb : np.qb) + (int64_t)base_row * qs;
+      j_d = (cur ? cp.db : np.db) + (int64_t)base_row * qs;
+      j_v = (cur ? cp.vb : np.vb) + (int64_t)min(j * QB + l, nq_ - 1) * sld;
       j_lds = lds_addr(smem[ring_iss]);
       j_ldw = j_lds + wave * C::RPW * RB;
       j_last = nq_ - 1 - base_row;
       j_n = C::IPS;
     } else {
-      stage_now(qbase, dobase, rbase, nq_, j, smem[ring_iss]);
+      const int64_t rbase = BCAST ? ((int64_t)(cur ? cp.b : np.b) * H + (cur ? cp.h : np.h)) * Lq
+                                  : (cur ? cp.s0 : np.s0) * H + (cur ? cp.h : np.h);
+      stage_now(cur ? cp.qb : np.qb, cur ? cp.db : np.db, rbase, nq_, j, smem[ring_iss]);
     }
     if (cur) ++iss_cur;
     else ++iss_nxt;
