@@ -657,6 +657,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
       if (__builtin_expect(__any(f0p || f0d || f1p || f1d), 0)) {
         fixup(masked_tag, S0{}, m, buf, sa, da, pa, dsa, __any(f0p), __any(f0d));
         fixup(masked_tag, S1{}, m, buf, sb, db, pb, dsb, __any(f1p), __any(f1d));
+        // The fixup's lse / delta reads are consumed only where a product
+        // needed them; waiting for the rest here (a wait the compiler sees)
+        // keeps it from assuming them outstanding in every later block.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       }
     };
 

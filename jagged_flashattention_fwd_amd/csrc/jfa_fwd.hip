@@ -330,6 +330,28 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
 // lse are stored, and the stores are bounded buffer stores of a fixed count
 // per wave, so the wait at the next tile start covers exactly the copies and
 // Q loads and lets the stores drain.
+// Four transposed reads (rows a0 / a1, column byte offsets OFF and OFF +
+// 64) issued without waiting: two MFMA operands.  tr4_wait<N> makes them
+// available once at most N later LDS reads of this wave are outstanding.
+template <int OFF>
+__device__ __forceinline__ void tr4_issue(uint32_t a0, uint32_t a1, i16x4 (&x)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 64));
+}
+template <int N>
+__device__ __forceinline__ void tr4_wait(i16x4 (&x)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(N));
+}
+__device__ __forceinline__ bf16x8 tr4_operand(const i16x4 (&x)[4], int k) {
+  struct P { i16x4 a, b; } p = {x[2 * k], x[2 * k + 1]};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
 template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const TileRec* __restrict__ tiles) {
   using C = Fwd<D, NW, QW, CAUSAL, BCAST>;
@@ -354,9 +376,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   const int64_t t0 = zigzag_tile(0, slot, a.P);
   if (t0 >= T) return;
 
+  // Per-tile values, with the addresses of the tile's row 0 of K and V.
   struct Tp {
     int64_t s0;
     int L, h, b, q0, n_kv, n_bulk;
+    const uint16_t* kb;
+    const uint16_t* vb;
   };
   auto tparams = [&](const TileRec& r) {
     Tp p;
@@ -364,6 +389,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     p.L = r.L;
     p.h = r.h;
     p.b = r.b;
+    p.kb = a.k + (r.s0 * H + r.h) * (int64_t)D;
+    p.vb = a.v + (r.s0 * H + r.h) * (int64_t)D;
     p.q0 = r.blk * BM;
     const int nq = BCAST ? Lq : r.L;
     int kv_end = r.L;
@@ -389,12 +416,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     const bool cur = iss_cur < cp.n_kv;
     j_on = cur || iss_nxt < nn;
     if (!j_on) return;
-    const int64_t s0_ = cur ? cp.s0 : np.s0;
-    const int L_ = cur ? cp.L : np.L, h_ = cur ? cp.h : np.h;
+    const int L_ = cur ? cp.L : np.L;
     const int j = cur ? iss_cur : iss_nxt;
     const int base_row = min(j * BN + wave * RPW, L_ - 1);
-    j_k = a.k + ((s0_ + base_row) * H + h_) * (int64_t)D;
-    j_v = a.v + ((s0_ + base_row) * H + h_) * (int64_t)D;
+    const int64_t roff = (int64_t)base_row * ld;
+    j_k = (cur ? cp.kb : np.kb) + roff;
+    j_v = (cur ? cp.vb : np.vb) + roff;
     j_last = L_ - 1 - base_row;
     const int buf = g_iss % NBUF;
     j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
@@ -685,9 +712,231 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       }
       ++g_cmp;
     };
-    const int n_plain = cp.n_bulk;
-    for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
-    for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+    if constexpr (CAUSAL) {
+      const int n_plain = cp.n_bulk;
+      for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
+      for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+    } else if (n_kv > 0) {
+      // Software-pipelined steps: the S products of step j + 1 run beside
+      // the softmax of step j (split into pieces between their k-steps), then
+      // the PV products of step j.  Only the last step of a tile can be
+      // masked (keys past the sequence end); it runs after the loop.
+      // Step j's V stays in use until its PV products, so the copies issued
+      // after the barrier of iteration j go to the buffer of step j - 1 (the
+      // stream's next step is j + 3); the tile's last step issues one more
+      // after a barrier of its own, and the stream stays DEP steps ahead.
+      auto wait_step = [&](int gi) {  // this wave's copies of stream step gi landed
+        const int after = g_iss - 1 - gi;
+        if constexpr (DEP >= 3) {
+          if (after >= 2) wait_vmcnt<2 * IPS>();
+          else if (after == 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        } else {
+          if (after >= 1) wait_vmcnt<IPS>();
+          else wait_vmcnt<0>();
+        }
+      };
+      // S^T = K Q^T of stream step gi into sacc; the K operand of k-step
+      // ks + 1 is read before the products of k-step ks, and hook(ks) runs
+      // after them.
+      auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook) {
+        const char* Ks = smem[gi % NBUF][0];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s = 0; s < QS; ++s) sacc[kt][s] = f32x16{};
+        bf16x8 ka[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) ka[kt] = lds_read16(Ks, tile_off<D>(kt * 32 + lc, g));
+        static_for<0, KS>([&](auto ks_tag) {
+          constexpr int ks = decltype(ks_tag)::value;
+          bf16x8 kn[2];
+          if constexpr (ks + 1 < KS) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) kn[kt] = lds_read16(Ks, tile_off<D>(kt * 32 + lc, (ks + 1) * 2 + g));
+          }
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int s = 0; s < QS; ++s) sacc[kt][s] = mfma32(ka[kt], qreg[s][ks], sacc[kt][s]);
+          constexpr int PER = (2 * C::CPT + KS - 1) / KS;
+          issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
+          hook(ks_tag);
+          if constexpr (ks + 1 < KS) {
+            ka[0] = kn[0];
+            ka[1] = kn[1];
+          }
+        });
+      };
+      // Softmax of one step in pieces: sm_max (row maximum; the masked form
+      // scales and masks the scores in place), sm_rescale (lazy rescale of
+      // the running state; returns the reference exponent), sm_exp (P of key
+      // subtile kt, k-half hh, as packed bf16) and sm_sum.
+      float rmax[QS], mref[QS], lsp[QS];
+      auto sm_max = [&](auto masked_tag, int k0, f32x16 (&sacc)[2][QS], int kt) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+        for (int s = 0; s < QS; ++s) {
+          float r;
+          if constexpr (MASKED) {
+            r = kt == 0 ? -INFINITY : rmax[s];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              float x = sacc[kt][s][i] * c2;
+              const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+              x = key < L ? x : -INFINITY;
+              sacc[kt][s][i] = x;
+              r = fmaxf(r, x);
+            }
+          } else if (c2 >= 0.f) {
+            r = kt == 0 ? -INFINITY : rmax[s];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r = fmaxf(r, sacc[kt][s][i]);
+          } else {
+            r = kt == 0 ? INFINITY : rmax[s];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r = fminf(r, sacc[kt][s][i]);
+          }
+          rmax[s] = r;
+        }
+      };
+      auto sm_rescale = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+        for (int s = 0; s < QS; ++s) {
+          float mt;
+          if constexpr (MASKED) mt = max_across_halves(rmax[s]);
+          else mt = (c2 >= 0.f ? max_across_halves(rmax[s]) : min_across_halves(rmax[s])) * c2;
+          const bool need = mt > m2[s] + RESCALE_SLACK;
+          if (__builtin_expect(__any(need), 0)) {
+            const float alpha = need ? fast_exp2(m2[s] - mt) : 1.f;
+            m2[s] = need ? mt : m2[s];
+            lsum[s] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][s] *= alpha;
+          }
+          mref[s] = m2[s] == -INFINITY ? 0.f : m2[s];
+          lsp[s] = 0.f;
+        }
+      };
+      auto sm_exp = [&](auto masked_tag, const f32x16 (&sacc)[2][QS], int kt, int hh, uint32_t (&pk)[2][2][QS][4]) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = hh * 8 + e * 2;
+            float p0, p1;
+            if constexpr (MASKED) {
+              p0 = fast_exp2(sacc[kt][s][i] - mref[s]);
+              p1 = fast_exp2(sacc[kt][s][i + 1] - mref[s]);
+            } else {
+              p0 = fast_exp2(__builtin_fmaf(sacc[kt][s][i], c2, -mref[s]));
+              p1 = fast_exp2(__builtin_fmaf(sacc[kt][s][i + 1], c2, -mref[s]));
+            }
+            lsp[s] += p0 + p1;
+            pk[kt][hh][s][e] = pack_bf16x2(p0, p1);
+          }
+      };
+      auto sm_sum = [&]() {
+#pragma unroll
+        for (int s = 0; s < QS; ++s) lsum[s] += lsp[s];
+      };
+      // O^T += V^T P^T of stream step gi, in 8 pieces (key group (kt, hh) x
+      // head-dim tiles 2 h, 2 h + 1); the transposed V reads of each piece
+      // are issued before the products of the piece before.
+      const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
+      auto pv_phase = [&](int gi, const uint32_t (&pk)[2][2][QS][4]) {
+        const char* Vs = smem[gi % NBUF][1];
+        uint32_t va[4];
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int r0 = (grp >> 1) * 32 + (grp & 1) * 16 + g * 4;
+          va[grp] = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
+        }
+        i16x4 xv[2][4];
+        static_assert(DT == 4, "two pieces of two head-dim tiles per key group");
+        tr4_issue<0>(va[0], va[0] + 8 * RB, xv[0]);
+        static_for<0, 8>([&](auto pc_tag) {
+          constexpr int pc = decltype(pc_tag)::value;
+          constexpr int grp = pc >> 1, hf = pc & 1;
+          constexpr int kt = grp >> 1, hh = grp & 1;
+          if constexpr (pc + 1 < 8) {
+            constexpr int ng = (pc + 1) >> 1, nh = (pc + 1) & 1;
+            tr4_issue<nh * 128>(va[ng], va[ng] + 8 * RB, xv[(pc + 1) & 1]);
+            tr4_wait<4>(xv[pc & 1]);
+          } else {
+            tr4_wait<0>(xv[pc & 1]);
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int s = 0; s < QS; ++s) {
+              const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[kt][hh][s][0], pk[kt][hh][s][1],
+                                                                  pk[kt][hh][s][2], pk[kt][hh][s][3]});
+              oacc[2 * hf + k][s] = mfma32(tr4_operand(xv[pc & 1], k), pb, oacc[2 * hf + k][s]);
+            }
+        });
+      };
+      // One pipelined iteration: step j's softmax (scores in sa) and PV,
+      // beside step j + 1's S products (into sb).
+      uint32_t pk[2][2][QS][4];
+      auto iter = [&](int j, f32x16 (&sa)[2][QS], f32x16 (&sb)[2][QS]) {
+        const int gj = g_first + j;
+        wait_step(gj + 1);
+        barrier_lds();
+        prep_next(cp, np, has_nxt);
+        using F = std::false_type;
+        s_phase(gj + 1, sb, [&](auto ks_tag) {
+          constexpr int ks = decltype(ks_tag)::value;
+          if constexpr (ks == 0) sm_max(F{}, 0, sa, 0);
+          if constexpr (ks == 1) {
+            sm_max(F{}, 0, sa, 1);
+            sm_rescale(F{});
+          }
+          if constexpr (ks >= 2 && ks < 6) sm_exp(F{}, sa, (ks - 2) >> 1, (ks - 2) & 1, pk);
+          if constexpr (ks == 6) sm_sum();
+        });
+        pv_phase(gj, pk);
+        ++g_cmp;
+      };
+      auto last = [&](auto masked_tag, int j, f32x16 (&sa)[2][QS]) {
+        barrier_lds();  // every wave has left the buffer of step j - 1
+        prep_next(cp, np, has_nxt);
+        issue_copies(0, 2 * C::CPT);
+        sm_max(masked_tag, j * BN, sa, 0);
+        sm_max(masked_tag, j * BN, sa, 1);
+        sm_rescale(masked_tag);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) sm_exp(masked_tag, sa, kt, hh, pk);
+        sm_sum();
+        pv_phase(g_first + j, pk);
+        ++g_cmp;
+      };
+      f32x16 sa[2][QS], sb[2][QS];
+      // prologue: step 0's S products, with no copies (each tile issues
+      // one copy step per iteration and one in its last step)
+      barrier_lds();
+      j_on = false;
+      s_phase(g_first, sa, [](auto) {});
+      int j = 0;
+      for (; j + 2 < n_kv; j += 2) {
+        iter(j, sa, sb);
+        iter(j + 1, sb, sa);
+      }
+      if (j + 1 < n_kv) {
+        iter(j, sa, sb);
+        ++j;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s = 0; s < QS; ++s) sa[kt][s] = sb[kt][s];
+      }
+      if (cp.n_bulk < n_kv) last(std::true_type{}, j, sa);
+      else last(std::false_type{}, j, sa);
+    }
 
     // Tile end: the next tile's Q rows, then this tile's O and lse.
     if (has_nxt) load_q(np);
