@@ -178,6 +178,28 @@ __device__ __forceinline__ void lds_operand_tr_x4(uint32_t a0, uint32_t a1, bf16
   out[3] = __builtin_bit_cast(bf16x8, P{x3, y3});
 }
 
+// Four transposed reads (rows a0 / a1, column byte offsets OFF and OFF +
+// 64) issued without waiting: two MFMA operands.  tr4_wait<N> makes them
+// available once at most N later LDS reads of this wave are outstanding.
+template <int OFF>
+__device__ __forceinline__ void tr4_issue(uint32_t a0, uint32_t a1, i16x4 (&x)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 64));
+}
+template <int N>
+__device__ __forceinline__ void tr4_wait(i16x4 (&x)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(N));
+}
+__device__ __forceinline__ bf16x8 tr4_operand(const i16x4 (&x)[4], int k) {
+  struct P { i16x4 a, b; } p = {x[2 * k], x[2 * k + 1]};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
 // ------------------------------------------------------ global <-> LDS ----
 // A tile of R rows x D bf16 columns is copied by NT threads, 16 bytes each
 // per step; row r of the tile is global row (base + r * ld) and rows at or
