@@ -616,13 +616,12 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
           uint32_t hi[2][4], lo[2][4];
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const int hh = i >> 3, e = (i & 7) >> 1;
-            if (split) {
-              split_bf16x2(dsf[i], dsf[i + 1], &hi[hh][e], &lo[hh][e]);
-            } else {
-              hi[hh][e] = pack_bf16x2(dsf[i], dsf[i + 1]);
-              lo[hh][e] = 0u;
-            }
+            hi[i >> 3][(i & 7) >> 1] = pack_bf16x2(dsf[i], dsf[i + 1]);
+            lo[i >> 3][(i & 7) >> 1] = 0u;
+          }
+          if (split) {
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) split_bf16x2(dsf[i], dsf[i + 1], &hi[i >> 3][(i & 7) >> 1], &lo[i >> 3][(i & 7) >> 1]);
           }
           // dQ^T += K^T dS^T in 4 pieces (k-half hh x head-dim tiles 2 hf,
           // 2 hf + 1); each piece's transposed reads are issued before the
