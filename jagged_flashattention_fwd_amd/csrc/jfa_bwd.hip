@@ -167,14 +167,38 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
   // One K/V step: S^T, dP^T, dS^T, dQ^T += K^T dS^T, two 32-key halves in turn.
   auto step_math = [&](const char* Ks, const char* Vs, int k0, int L, int qi, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // K / V operands of k-step ks + 1 are read before the products of
+      // k-step ks.
+      bf16x8 kc = lds_read16(Ks, tile_off<D>(kt * 32 + lc, g));
+      bf16x8 vc = lds_read16(Vs, tile_off<D>(kt * 32 + lc, g));
+      static_for<0, KS>([&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        bf16x8 kn, vn;
+        if constexpr (ks + 1 < KS) {
+          const int off = tile_off<D>(kt * 32 + lc, (ks + 1) * 2 + g);
+          kn = lds_read16(Ks, off);
+          vn = lds_read16(Vs, off);
+        }
+        sacc = mfma32(kc, qreg[ks], sacc);
+        dpacc = mfma32(vc, doreg[ks], dpacc);
+        if constexpr (ks + 1 < KS) {
+          kc = kn;
+          vc = vn;
+        }
+      });
+      uint32_t ta[2];
+      i16x4 xk[2][4];
+      if constexpr (C::DMA) {
+        // The first transposed K reads of dQ^T's products go out before
+        // the dS arithmetic.
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = tile_off<D>(kt * 32 + lc, ks * 2 + g);
-        sacc = mfma32(lds_read16(Ks, off), qreg[ks], sacc);
-        dpacc = mfma32(lds_read16(Vs, off), doreg[ks], dpacc);
+        for (int hh = 0; hh < 2; ++hh)
+          ta[hh] = lds_addr(Ks + tile_off_col4<D>(kt * 32 + hh * 16 + g * 4 + jj, cq));
+        tr4_issue<0>(ta[0], ta[0] + 8 * TileGeom<D>::ROW_BYTES, xk[0]);
       }
       // C layout: lane owns query qi; register i is key
       // k0 + kt*32 + 8*(i/4) + 4g + i%4.
@@ -197,35 +221,53 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
       uint32_t hi[2][4], lo[2][4];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const int hh = i >> 3, e = (i & 7) >> 1;
-        if (split) {
-          split_bf16x2(dsf[i], dsf[i + 1], &hi[hh][e], &lo[hh][e]);
-        } else {
-          hi[hh][e] = pack_bf16x2(dsf[i], dsf[i + 1]);
-          lo[hh][e] = 0u;
-        }
+        hi[i >> 3][(i & 7) >> 1] = pack_bf16x2(dsf[i], dsf[i + 1]);
+        lo[i >> 3][(i & 7) >> 1] = 0u;
+      }
+      if (split) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) split_bf16x2(dsf[i], dsf[i + 1], &hi[i >> 3][(i & 7) >> 1], &lo[i >> 3][(i & 7) >> 1]);
       }
       // dQ^T += K^T dS^T; K^T by transpose read, keys in the order of the
       // dS^T registers.
+      if constexpr (C::DMA) {
+        // 4 pieces (k-half hh x head-dim tiles 2 hf, 2 hf + 1), each
+        // piece's reads issued before the products of the piece before.
+        static_assert(DT == 4, "two pieces of two head-dim tiles per k-half");
+        static_for<0, 4>([&](auto pc_tag) {
+          constexpr int pc = decltype(pc_tag)::value;
+          constexpr int hh = pc >> 1, hf = pc & 1;
+          if constexpr (pc + 1 < 4) {
+            constexpr int nh = (pc + 1) >> 1, nf = (pc + 1) & 1;
+            tr4_issue<nf * 128>(ta[nh], ta[nh] + 8 * TileGeom<D>::ROW_BYTES, xk[(pc + 1) & 1]);
+            tr4_wait<4>(xk[pc & 1]);
+          } else {
+            tr4_wait<0>(xk[pc & 1]);
+          }
+          const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{hi[hh][0], hi[hh][1], hi[hh][2], hi[hh][3]});
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = kt * 32 + hh * 16 + g * 4;
-        bf16x8 ka[DT];
-        if constexpr (C::DMA) {
-          const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
-          const uint32_t a0 = lds_addr(Ks + tile_off_col4<D>(r0 + jj, cq));
-          lds_operand_tr_x4(a0, a0 + 8 * TileGeom<D>::ROW_BYTES, ka);
-        } else {
+          for (int k = 0; k < 2; ++k) dqa[2 * hf + k] = mfma32(tr4_operand(xk[pc & 1], k), db, dqa[2 * hf + k]);
+          if (split) {
+            const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{lo[hh][0], lo[hh][1], lo[hh][2], lo[hh][3]});
+#pragma unroll
+            for (int k = 0; k < 2; ++k) dqa[2 * hf + k] = mfma32(tr4_operand(xk[pc & 1], k), dl, dqa[2 * hf + k]);
+          }
+        });
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r0 = kt * 32 + hh * 16 + g * 4;
+          bf16x8 ka[DT];
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) ka[dt] = lds_operand_tr<D>(Ks, r0, r0 + 8, dt * 32);
-        }
-        const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{hi[hh][0], hi[hh][1], hi[hh][2], hi[hh][3]});
+          const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{hi[hh][0], hi[hh][1], hi[hh][2], hi[hh][3]});
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], db, dqa[dt]);
-        if (split) {
-          const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{lo[hh][0], lo[hh][1], lo[hh][2], lo[hh][3]});
+          for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], db, dqa[dt]);
+          if (split) {
+            const bf16x8 dl = __builtin_bit_cast(bf16x8, u32x4{lo[hh][0], lo[hh][1], lo[hh][2], lo[hh][3]});
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], dl, dqa[dt]);
+            for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma32(ka[dt], dl, dqa[dt]);
+          }
         }
       }
     }
