@@ -546,6 +546,74 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // One K/V step of BN keys.  MASKED is a compile-time constant: the
     // bulk steps carry no mask code at all; only the tail step and the
     // causal diagonal steps take the masked body.
+    // S^T = K Q^T of stream step gi into sacc; the K operand of k-step
+    // ks + 1 is read before the products of k-step ks, and hook(ks) runs
+    // after them.
+    auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook) {
+      const char* Ks = smem[gi % NBUF][0];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s = 0; s < QS; ++s) sacc[kt][s] = f32x16{};
+      bf16x8 ka[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) ka[kt] = lds_read16(Ks, tile_off<D>(kt * 32 + lc, g));
+      static_for<0, KS>([&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        bf16x8 kn[2];
+        if constexpr (ks + 1 < KS) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) kn[kt] = lds_read16(Ks, tile_off<D>(kt * 32 + lc, (ks + 1) * 2 + g));
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s = 0; s < QS; ++s) sacc[kt][s] = mfma32(ka[kt], qreg[s][ks], sacc[kt][s]);
+        constexpr int PER = (2 * C::CPT + KS - 1) / KS;
+        issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
+        hook(ks_tag);
+        if constexpr (ks + 1 < KS) {
+          ka[0] = kn[0];
+          ka[1] = kn[1];
+        }
+      });
+    };
+    // O^T += V^T P^T of stream step gi, in 8 pieces (key group (kt, hh) x
+    // head-dim tiles 2 h, 2 h + 1); the transposed V reads of each piece
+    // are issued before the products of the piece before.
+    const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
+    auto pv_phase = [&](int gi, const uint32_t (&pk)[2][2][QS][4]) {
+      const char* Vs = smem[gi % NBUF][1];
+      uint32_t va[4];
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int r0 = (grp >> 1) * 32 + (grp & 1) * 16 + g * 4;
+        va[grp] = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
+      }
+      i16x4 xv[2][4];
+      static_assert(DT == 4, "two pieces of two head-dim tiles per key group");
+      tr4_issue<0>(va[0], va[0] + 8 * RB, xv[0]);
+      static_for<0, 8>([&](auto pc_tag) {
+        constexpr int pc = decltype(pc_tag)::value;
+        constexpr int grp = pc >> 1, hf = pc & 1;
+        constexpr int kt = grp >> 1, hh = grp & 1;
+        if constexpr (pc + 1 < 8) {
+          constexpr int ng = (pc + 1) >> 1, nh = (pc + 1) & 1;
+          tr4_issue<nh * 128>(va[ng], va[ng] + 8 * RB, xv[(pc + 1) & 1]);
+          tr4_wait<4>(xv[pc & 1]);
+        } else {
+          tr4_wait<0>(xv[pc & 1]);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int s = 0; s < QS; ++s) {
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[kt][hh][s][0], pk[kt][hh][s][1],
+                                                                pk[kt][hh][s][2], pk[kt][hh][s][3]});
+            oacc[2 * hf + k][s] = mfma32(tr4_operand(xv[pc & 1], k), pb, oacc[2 * hf + k][s]);
+          }
+      });
+    };
     auto kv_step = [&](int j, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       const int buf = g_cmp % NBUF;
@@ -573,26 +641,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       if (!active) {
         issue_copies(0, 2 * C::CPT);
       } else {
-        const char* Ks = smem[buf][0];
-        const char* Vs = smem[buf][1];
         // ---- S^T = K Q^T : two 32-key subtiles x QS query subtiles; the
         // next step's copies are issued between the k-steps.
         f32x16 sacc[2][QS];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int s = 0; s < QS; ++s) sacc[kt][s] = f32x16{};
-        static_for<0, KS>([&](auto ks_tag) {
-          constexpr int ks = decltype(ks_tag)::value;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const bf16x8 ka = lds_read16(Ks, tile_off<D>(kt * 32 + lc, ks * 2 + g));
-#pragma unroll
-            for (int s = 0; s < QS; ++s) sacc[kt][s] = mfma32(ka, qreg[s][ks], sacc[kt][s]);
-          }
-          constexpr int PER = (2 * C::CPT + KS - 1) / KS;
-          issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
-        });
+        s_phase(g_cmp, sacc, [](auto) {});
         // ---- online softmax, one query per lane (both halves of a row agree).
         uint32_t pk[2][2][QS][4];  // [kt][k-half][s][bf16 pairs]
 #pragma unroll
@@ -667,26 +719,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
         // ---- O^T += V^T P^T.  k-slots of P^T (B operand) for k-half hh of
         // key subtile kt are keys kt*32 + hh*16 + {4g..4g+3, 8+4g..8+4g+3}; the
         // transpose read of V delivers the same keys.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r0 = kt * 32 + hh * 16 + g * 4;
-            bf16x8 va[DT];
-            // lane's transpose-read address: row r0 + j, column 16*(G&1) + 4q
-            const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
-            const uint32_t a0 = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
-            lds_operand_tr_x4(a0, a0 + 8 * RB, va);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-              for (int s = 0; s < QS; ++s) {
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[kt][hh][s][0], pk[kt][hh][s][1],
-                                                                    pk[kt][hh][s][2], pk[kt][hh][s][3]});
-                oacc[dt][s] = mfma32(va[dt], pb, oacc[dt][s]);
-              }
-            }
-          }
+        pv_phase(g_cmp, pk);
       }
       ++g_cmp;
     };
@@ -713,38 +746,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
           if (after >= 1) wait_vmcnt<IPS>();
           else wait_vmcnt<0>();
         }
-      };
-      // S^T = K Q^T of stream step gi into sacc; the K operand of k-step
-      // ks + 1 is read before the products of k-step ks, and hook(ks) runs
-      // after them.
-      auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook) {
-        const char* Ks = smem[gi % NBUF][0];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int s = 0; s < QS; ++s) sacc[kt][s] = f32x16{};
-        bf16x8 ka[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) ka[kt] = lds_read16(Ks, tile_off<D>(kt * 32 + lc, g));
-        static_for<0, KS>([&](auto ks_tag) {
-          constexpr int ks = decltype(ks_tag)::value;
-          bf16x8 kn[2];
-          if constexpr (ks + 1 < KS) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) kn[kt] = lds_read16(Ks, tile_off<D>(kt * 32 + lc, (ks + 1) * 2 + g));
-          }
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int s = 0; s < QS; ++s) sacc[kt][s] = mfma32(ka[kt], qreg[s][ks], sacc[kt][s]);
-          constexpr int PER = (2 * C::CPT + KS - 1) / KS;
-          issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
-          hook(ks_tag);
-          if constexpr (ks + 1 < KS) {
-            ka[0] = kn[0];
-            ka[1] = kn[1];
-          }
-        });
       };
       // Softmax of one step in pieces: sm_max (row maximum; the masked form
       // scales and masks the scores in place), sm_rescale (lazy rescale of
@@ -819,42 +820,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       auto sm_sum = [&]() {
 #pragma unroll
         for (int s = 0; s < QS; ++s) lsum[s] += lsp[s];
-      };
-      // O^T += V^T P^T of stream step gi, in 8 pieces (key group (kt, hh) x
-      // head-dim tiles 2 h, 2 h + 1); the transposed V reads of each piece
-      // are issued before the products of the piece before.
-      const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
-      auto pv_phase = [&](int gi, const uint32_t (&pk)[2][2][QS][4]) {
-        const char* Vs = smem[gi % NBUF][1];
-        uint32_t va[4];
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int r0 = (grp >> 1) * 32 + (grp & 1) * 16 + g * 4;
-          va[grp] = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
-        }
-        i16x4 xv[2][4];
-        static_assert(DT == 4, "two pieces of two head-dim tiles per key group");
-        tr4_issue<0>(va[0], va[0] + 8 * RB, xv[0]);
-        static_for<0, 8>([&](auto pc_tag) {
-          constexpr int pc = decltype(pc_tag)::value;
-          constexpr int grp = pc >> 1, hf = pc & 1;
-          constexpr int kt = grp >> 1, hh = grp & 1;
-          if constexpr (pc + 1 < 8) {
-            constexpr int ng = (pc + 1) >> 1, nh = (pc + 1) & 1;
-            tr4_issue<nh * 128>(va[ng], va[ng] + 8 * RB, xv[(pc + 1) & 1]);
-            tr4_wait<4>(xv[pc & 1]);
-          } else {
-            tr4_wait<0>(xv[pc & 1]);
-          }
-#pragma unroll
-          for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int s = 0; s < QS; ++s) {
-              const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[kt][hh][s][0], pk[kt][hh][s][1],
-                                                                  pk[kt][hh][s][2], pk[kt][hh][s][3]});
-              oacc[2 * hf + k][s] = mfma32(tr4_operand(xv[pc & 1], k), pb, oacc[2 * hf + k][s]);
-            }
-        });
       };
       // One pipelined iteration: step j's softmax (scores in sa) and PV,
       // beside step j + 1's S products (into sb).
