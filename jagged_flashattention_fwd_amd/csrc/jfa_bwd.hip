@@ -473,6 +473,8 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
   struct Sq {
     int64_t s0, row;
     int L, n_kv, n_bulk, r;
+    const uint16_t* kb;  // K / V rows s0 of head h
+    const uint16_t* vb;
   };
   auto seq_at = [&](int r) {
     Sq q;
@@ -480,6 +482,8 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     const int b = a.seq_order[r];
     q.L = (int)seq_range(a.offsets, b, a.total_len, &q.s0);
     q.row = ((int64_t)b * H + h) * Lq;
+    q.kb = a.k + (q.s0 * H + h) * (int64_t)D;
+    q.vb = a.v + (q.s0 * H + h) * (int64_t)D;
     int kv_end = q.L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     q.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
@@ -512,14 +516,15 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     const bool cur = iss_cur < cp.n_kv;
     j_on = cur || iss_nxt < nn;
     if (!j_on) return;
-    const int64_t s0_ = cur ? cp.s0 : np.s0;
     const int L_ = cur ? cp.L : np.L;
     const int j = cur ? iss_cur : iss_nxt;
     const int base_row = min(j * BN + wave * RPW, L_ - 1);
-    j_k = a.k + ((s0_ + base_row) * H + h) * (int64_t)D;
-    j_v = a.v + ((s0_ + base_row) * H + h) * (int64_t)D;
+    // byte offset of the row within the sequence (a 32 x 32-bit product)
+    const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(ld * 2);
+    j_k = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + roff);
+    j_v = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.vb : np.vb) + roff);
     j_last = L_ - 1 - base_row;
-    const int buf = g_iss % NBUF;
+    const int buf = (int)((uint32_t)g_iss % NBUF);
     j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
     j_vd = lds_addr(smem[buf][1]) + wave * RPW * RB;
     if (cur) ++iss_cur;
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     }
     auto kv_step = [&](int j, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      const int buf = g_cmp % NBUF;
+      const int buf = (int)((uint32_t)g_cmp % NBUF);
       const int k0 = j * BN;
       // Wait for this wave's copies of the step: the copies issued after it
       // may stay in flight.  (Copies issued before this sequence's operand

@@ -320,8 +320,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     const int j = cur ? cp.m_first + iss_cur : np.m_first + iss_nxt;
     if constexpr (C::DMA) {
       const int base_row = min(j * QB + wave * C::RPW, nq_ - 1);
-      j_q = (cur ? cp.qb : np.qb) + (int64_t)base_row * qs;
-      j_d = (cur ? cp.db : np.db) + (int64_t)base_row * qs;
+      // byte offset of the row (a 32 x 32-bit product)
+      const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(qs * 2);
+      j_q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.qb : np.qb) + roff);
+      j_d = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.db : np.db) + roff);
       j_v = (cur ? cp.vb : np.vb) + (int64_t)min(j * QB + l, nq_ - 1) * sld;
       j_lds = lds_addr(smem[ring_iss]);
       j_ldw = j_lds + wave * C::RPW * RB;

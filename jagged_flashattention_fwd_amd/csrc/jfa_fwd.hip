@@ -61,6 +61,7 @@ struct Fwd {
   static constexpr int IPS = 2 * CPT;
   static constexpr int DEP = DMA ? ((2 * IPS <= 63) ? 3 : 2) : 1;
   static constexpr int NBUF = DEP + 1;
+  static_assert((NBUF & (NBUF - 1)) == 0, "ring index by mask");
   static constexpr int BUF_BYTES = TILE_BYTES + PadRowCopy::GAP;
   static_assert(!DMA || (TileGeom<D>::ROW_BYTES == 19 * 16 && RPW >= 3), "copy geometry");
 };
@@ -397,11 +398,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     const int L_ = cur ? cp.L : np.L;
     const int j = cur ? iss_cur : iss_nxt;
     const int base_row = min(j * BN + wave * RPW, L_ - 1);
-    const int64_t roff = (int64_t)base_row * ld;
-    j_k = (cur ? cp.kb : np.kb) + roff;
-    j_v = (cur ? cp.vb : np.vb) + roff;
+    // byte offset of the row within the sequence (a 32 x 32-bit product)
+    const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(ld * 2);
+    j_k = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + roff);
+    j_v = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.vb : np.vb) + roff);
     j_last = L_ - 1 - base_row;
-    const int buf = g_iss % NBUF;
+    const int buf = (int)((uint32_t)g_iss % NBUF);
     j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
     j_vd = lds_addr(smem[buf][1]) + wave * RPW * RB;
     if (cur) ++iss_cur;
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // ks + 1 is read before the products of k-step ks, and hook(ks) runs
     // after them.
     auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook) {
-      const char* Ks = smem[gi % NBUF][0];
+      const char* Ks = smem[(uint32_t)gi % NBUF][0];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // are issued before the products of the piece before.
     const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
     auto pv_phase = [&](int gi, const uint32_t (&pk)[2][2][QS][4]) {
-      const char* Vs = smem[gi % NBUF][1];
+      const char* Vs = smem[(uint32_t)gi % NBUF][1];
       uint32_t va[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
@@ -616,7 +618,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     };
     auto kv_step = [&](int j, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      const int buf = g_cmp % NBUF;
+      const int buf = (int)((uint32_t)g_cmp % NBUF);
       const int k0 = j * BN;
       // Wait for this wave's copies of step j (steps issued after it may
       // still be in flight), then for every wave's; the ring buffer of the
