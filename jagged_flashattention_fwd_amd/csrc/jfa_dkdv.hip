@@ -356,15 +356,48 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   // K[key][d]).  Lanes past the sequence end read its last key (finite
   // values; those keys are masked and never stored).
   u32x4 kraw[KS], vraw[KS];
-  auto load_kv = [&](const Tp& p) {
+  auto load_rows = [&](const Tp& p, const uint16_t* base, u32x4 (&x)[KS]) {
     const int kc = min(p.k0 + wave * 32 + lc, p.L - 1);
-    const uint16_t* kr = a.k + ((p.s0 + kc) * H + p.h) * (int64_t)D + g * 8;
-    const uint16_t* vr = a.v + ((p.s0 + kc) * H + p.h) * (int64_t)D + g * 8;
+    const uint16_t* r = base + ((p.s0 + kc) * H + p.h) * (int64_t)D + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kraw[ks] = *reinterpret_cast<const u32x4*>(kr + ks * 16);
-      vraw[ks] = *reinterpret_cast<const u32x4*>(vr + ks * 16);
+    for (int ks = 0; ks < KS; ++ks) x[ks] = *reinterpret_cast<const u32x4*>(r + ks * 16);
+  };
+  auto load_kv = [&](const Tp& p) {
+    load_rows(p, a.k, kraw);
+    load_rows(p, a.v, vraw);
+  };
+
+  // Per-wave LDS area (8 KB): the next tile's V rows, copied during the
+  // tile's last query block, and then the staging of the dK / dV stores.
+  // Row r holds key k0 + 32 wave + r; its 16-byte chunk c sits at slot
+  // c ^ (r & 15), so that the operand reads (one row per lane, one chunk
+  // column per read) are free of bank conflicts.
+  __shared__ __attribute__((aligned(16))) char wstage[C::NW][32 * 256];
+  constexpr int VDMA = D == 128 ? 8 : 0;  // copies per wave (4 rows each)
+  auto issue_v_next = [&](const Tp& p) {
+    if constexpr (VDMA > 0) {
+      const uint16_t* vb = a.v + ((p.s0 + p.k0) * H + p.h) * (int64_t)D;
+      const uint32_t lds0 = lds_addr(wstage[wave]);
+      // The lane index through an opaque copy: the offsets below are then
+      // computed here, once per tile, rather than hoisted out of the block
+      // loop and kept live through every block.
+      int lo = l;
+      asm volatile("" : "+v"(lo));
+      const int rl = lo >> 4, slot = lo & 15;
+#pragma unroll
+      for (int i = 0; i < VDMA; ++i) {
+        const int r = 4 * i + rl;
+        const int kr = min(wave * 32 + r, p.L - 1 - p.k0);
+        const uint32_t voff = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)(((slot ^ (r & 15))) * 16);
+        dma_copy16(vb, voff, lds0 + i * 1024);
+      }
     }
+  };
+  auto read_v_staged = [&]() {
+    const char* base = wstage[wave];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      vraw[ks] = *reinterpret_cast<const u32x4*>(base + lc * 256 + (((2 * ks + g) ^ (lc & 15)) * 16));
   };
 
   // dK = scale * dS^T Q and dV = P^T dO of this lane's keys.  The C layout
@@ -376,13 +409,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   // whatever its keys, and stores past the bound are dropped, so the K / V
   // wait at the next tile start has a fixed count.
   constexpr int SRS = 36;  // staging row stride in floats
-  __shared__ __attribute__((aligned(16))) float stage[C::NW][32 * SRS];
+  static_assert(32 * SRS * 4 <= 32 * 256, "staging fits the per-wave area");
   auto store_dkdv = [&](const Tp& p, int nvalid, const f32x16 (&dk)[DT], const f32x16 (&dv)[DT]) {
     const int64_t row0 = (p.s0 + p.k0) * H + p.h;
     const int nrec = nvalid * H * D * 4;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.dk + row0 * D, nrec);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.dv + row0 * D, nrec);
-    float* st = stage[wave];
+    float* st = reinterpret_cast<float*>(wstage[wave]);
     const int rk8 = l >> 3, rc = (l & 7) * 4;  // read side: key 8r + rk8, columns rc .. rc+3
     auto chunk = [&](const f32x16& acc, float mul, const __amdgpu_buffer_rsrc_t& rs, int dt) {
 #pragma unroll
@@ -420,6 +453,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     const int64_t tn = zigzag_tile(pass + 1, slot, a.P);
     const bool has_nxt = tn < T;
     const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
+    bool v_staged = false;  // the next tile's V rows are on their way to LDS
+    int vm_last = 0;        // copies of the block in progress, issued after them
     const int64_t s0 = cp.s0;
     const int L = cp.L;
     const int h = cp.h;
@@ -679,7 +714,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
       // Tile start.  Normally the first two blocks were issued during the
       // previous tile, before its K / V loads for this tile, and only the
       // previous tile's 8 * DT stores may be outstanding after those.
-      int vm_last;
       {
         const int need = min(nb, 2);
         if (iss_cur < need) {
@@ -706,6 +740,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
           }
           prep_next(cp, np, has_nxt);
           vm_last = j_n;
+          // The tile's last block copies the next tile's V rows first (the
+          // tile end waits for them with this block's own copies in flight).
+          if constexpr (VDMA > 0) {
+            if (m == m_end - 1 && has_nxt) {
+              issue_v_next(np);
+              v_staged = true;
+            }
+          }
           block(masked_tag, m, smem[ring_cmp]);
           ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
         }
@@ -723,7 +765,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     }
 
     // Tile end: the next tile's K / V loads, then this tile's stores.
-    if (has_nxt) load_kv(np);
+    if (has_nxt) {
+      if (v_staged) {
+        wait_n(vm_last);
+        read_v_staged();
+      } else {
+        load_rows(np, a.v, vraw);
+      }
+      load_rows(np, a.k, kraw);
+    }
     store_dkdv(cp, min(L - k0, BN), dk, dv);
     if (!has_nxt) break;
     cp = np;
