@@ -768,6 +768,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     if (has_nxt) {
       if (v_staged) {
         wait_n(vm_last);
+        asm volatile("" ::: "memory");  // the reads below stay after the wait
         read_v_staged();
       } else {
         load_rows(np, a.v, vraw);
