@@ -914,7 +914,7 @@ hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
                     : launch_fwd_t<D, FWD_BM_BCAST / 32, 32, false, true>(a, stream);
   }
   return a.causal ? launch_fwd_t<D, FWD_BM_SELF / 32, 32, true, false>(a, stream)
-                  : launch_fwd_t<D, FWD_BM_SELF / 32, 32, false, false>(a, stream);
+                  : launch_fwd_t<D, FWD_BM_BCAST / 32, 32, false, false>(a, stream);
 }
 
 }  // namespace

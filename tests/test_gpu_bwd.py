@@ -64,6 +64,14 @@ def test_bwd_short_sequences_many_queries(jfa, std):
     _check_case(jfa, [2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 1, 7], 2, 128, 512, True, False, seed=31, std=std)
 
 
+@pytest.mark.parametrize("lengths", [[512] * 5, [1000] * 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_dense_equal_lengths(jfa, lengths, causal):
+    """The dense LLM regime at reduced batch: equal lengths in self mode
+    (a whole number of tiles, and a ragged tail)."""
+    _check_case(jfa, lengths, 4, 128, 0, False, causal, seed=len(lengths) + 40)
+
+
 @pytest.mark.parametrize("idx", [0, 1])
 def test_bwd_workloads_full(jfa, idx):
     w = wl.workload(idx)

@@ -117,3 +117,11 @@ def test_full_skew_bcast(jfa):
     seqs = sorted(set(_sample_sequences(L, 3, seed=404)) | {int(long_ids[0])})
     _check_sequences(w, t, out, lse, dq, dk, dv, seqs, [0, 5])
     _check_broadcast_dq_rows(w, t, dq, [(1, 0), (1, 511), (6, 300)])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("idx", [5, 6])
+def test_full_dense_llm(jfa, idx):
+    w, t, out, lse, dq, dk, dv = _run_full(jfa, idx)
+    seqs = _sample_sequences(t["lengths"], 3, seed=500 + idx)
+    _check_sequences(w, t, out, lse, dq, dk, dv, seqs, range(w.H))

@@ -14,7 +14,10 @@ pytestmark = pytest.mark.gpu
 
 # Tile geometry this test expects of the library (checked against the
 # library's own report before use).
-FWD_BM = {True: 256, False: 128}
+def fwd_bm(bq, causal):
+    """Query rows of a forward tile: 256 for broadcast Q and non-causal
+    self-attention, 128 for causal self-attention."""
+    return 256 if (bq or not causal) else 128
 BWD_BN = 128
 
 
@@ -60,6 +63,14 @@ def test_fwd_negative_and_zero_scale(jfa):
     _run_case(jfa, [3, 77, 130], 2, 128, 0, False, True, seed=6, scale=0.0)
 
 
+@pytest.mark.parametrize("lengths", [[512] * 5, [1000] * 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_dense_equal_lengths(jfa, lengths, causal):
+    """The dense LLM regime at reduced batch: equal lengths in self mode
+    (a whole number of tiles, and a ragged tail)."""
+    _run_case(jfa, lengths, 4, 128, 0, False, causal, seed=len(lengths) + 40)
+
+
 @pytest.mark.parametrize("idx", [0, 1])
 def test_fwd_workloads_full(jfa, idx):
     w = wl.workload(idx)
@@ -91,13 +102,13 @@ def test_fwd_deterministic(jfa):
 
 
 @pytest.mark.parametrize("pass_", [0, 1])
-@pytest.mark.parametrize("bq", [True, False])
-def test_schedule_bit_exact(jfa, pass_, bq):
+@pytest.mark.parametrize("bq,causal", [(True, 0), (False, 0), (False, 1)])
+def test_schedule_bit_exact(jfa, pass_, bq, causal):
     lengths = wl.draw_lengths(("mix", 0.1, (0, 40), (300, 3000)), 777, 21)
     H, Lq = 3, 300
-    block, P = jfa.jfa_schedule_params(pass_, 0, int(bq), 128)
+    block, P = jfa.jfa_schedule_params(pass_, causal, int(bq), 128)
     props = torch.cuda.get_device_properties(0)
-    expect_block = FWD_BM[bq] if pass_ == 0 else BWD_BN
+    expect_block = fwd_bm(bq, causal) if pass_ == 0 else BWD_BN
     assert (block, P) == (expect_block, props.multi_processor_count)
     off = torch.from_numpy(wl.offsets_from_lengths(lengths)).cuda()
     T = int(off[-1])
@@ -107,7 +118,7 @@ def test_schedule_bit_exact(jfa, pass_, bq):
     cap = len(ref) + 5
     tiles = torch.full((cap, 4), -7, dtype=torch.int32, device="cuda")
     n = torch.zeros(1, dtype=torch.int64, device="cuda")
-    jfa.jfa_debug_schedule(off, len(lengths), H, Lq if bq else 0, 0, bq, pass_, T, tiles, n, ws)
+    jfa.jfa_debug_schedule(off, len(lengths), H, Lq if bq else 0, causal, bq, pass_, T, tiles, n, ws)
     torch.cuda.synchronize()
     assert int(n.item()) == len(ref)
     got = tiles.cpu().numpy()

@@ -165,6 +165,30 @@ def test_equal_lengths_broadcast_is_dense_attention(causal):
                                rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_lengths_self_mode_is_batched_dense_attention(causal):
+    """The dense LLM regime: B sequences of one length in self mode are a
+    batched dense attention [B, H, L, d] (causal: SDPA's is_causal)."""
+    B, H, L, d = 3, 2, 7, 6
+    scale = 1 / math.sqrt(d)
+    off = _offsets([L] * B)
+    q, k, v, dout = (_rand(B * L, H, d) for _ in range(4))
+    out, lse = jo.jagged_forward(q, k, v, off, scale, causal, False)
+    dq, dk, dv = jo.jagged_backward(q, k, v, off, scale, causal, False, dout)
+    dense = lambda x: x.reshape(B, L, H, d).transpose(0, 2, 1, 3).copy()  # noqa: E731
+    packed = lambda x: x.transpose(0, 2, 1, 3).reshape(B * L, H, d)  # noqa: E731
+    o_ref, (tq, tk, tv) = _sdpa(dense(q), dense(k), dense(v), scale, causal=causal)
+    np.testing.assert_allclose(out, packed(o_ref.detach().numpy()), rtol=1e-12, atol=1e-12)
+    o_ref.backward(torch.tensor(dense(dout)))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, packed(t.grad.numpy()), rtol=1e-10, atol=1e-12)
+    s = scale * torch.tensor(dense(q)) @ torch.tensor(dense(k)).transpose(-1, -2)
+    if causal:
+        s = s.masked_fill(~torch.tril(torch.ones(L, L, dtype=torch.bool)), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy().transpose(0, 2, 1).reshape(B * L, H),
+                               rtol=1e-12, atol=1e-12)
+
+
 def test_single_sequence_causal_is_sdpa_is_causal():
     T, H, d = 11, 3, 4
     q, k, v, dout = _rand(T, H, d), _rand(T, H, d), _rand(T, H, d), _rand(T, H, d)

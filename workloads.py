@@ -16,6 +16,12 @@ its sizes and length distribution:
   skew_bcast      broadcast Q, B=4096, H=8,  d=128, Lq=512,
                   90% L ~ U[1,32], 10% L ~ U[4096,16384], values N(0, 0.5)
 
+and two of the dense LLM regime (equal-length Q/K/V, B=768, H=4, d=128),
+at sequence length 1024, self-attention without and with the causal mask:
+
+  dense_llm_1k         self-attn,         B=768, H=4, d=128, L = 1024
+  dense_llm_1k_causal  self-attn, causal, B=768, H=4, d=128, L = 1024
+
 Lengths are drawn with numpy's PCG64 from the seed; integer draws are
 inclusive.  Log-uniform lengths are round(exp(U(ln lo, ln hi))) clipped to
 [lo, hi].  In skew_bcast exactly round(0.1*B) sequences, at seeded random
@@ -62,6 +68,9 @@ WORKLOADS = [
     Workload("long_causal_8k", False, True, 64, 16, 128, 0, ("loguniform", 128, 8192)),
     Workload("skew_bcast", True, False, 4096, 8, 128, 512,
              ("mix", 0.1, (1, 32), (4096, 16384)), std=0.5),
+    # The pages' second regime: dense LLM attention, equal-length Q/K/V.
+    Workload("dense_llm_1k", False, False, 768, 4, 128, 0, ("uniform", 1024, 1024)),
+    Workload("dense_llm_1k_causal", False, True, 768, 4, 128, 0, ("uniform", 1024, 1024)),
 ]
 
 
