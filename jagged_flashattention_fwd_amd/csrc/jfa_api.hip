@@ -246,7 +246,8 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   Schedule sq{};
   if (!broadcast_q) {
     sq = schedule_at(ws, lay.sched_b, lay.cap_b);
-    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, DQ_BM};  // self-attention dQ query tiles
+    // self-attention dQ query tiles: the forward's tile height
+    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, causal ? DQ_BM : DQ_BM_BCAST};
     if (launch_schedule(sb, sq, st) != hipSuccess) return JFA_ERR_HIP;
   }
   BwdArgs ba;
