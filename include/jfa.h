@@ -88,10 +88,9 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
             size_t workspace_bytes, void* stream);
 
 /* Tile geometry the library uses on the current device for a pass:
- * *block_rows = query rows per forward tile (pass 0: 256 for broadcast Q
- * and non-causal self-attention, 128 for causal self-attention) or key
- * rows per backward tile (pass 1); *workers = persistent workgroups that
- * share the tile list.  Host-only. */
+ * *block_rows = query rows per forward tile (pass 0) or key rows per
+ * backward tile (pass 1); *workers = persistent workgroups that share the
+ * tile list.  Host-only. */
 int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block_rows, int* workers);
 
 /* Test hook: builds the tile list of a pass exactly as jfa_fwd / jfa_bwd do

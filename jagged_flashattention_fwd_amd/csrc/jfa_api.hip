@@ -33,17 +33,14 @@ int cu_count(int* out) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Query rows of a forward tile: 256 (8 waves, two per SIMD) for broadcast
-// Q and non-causal self-attention; 128 for causal self-attention, whose
-// tiles along the diagonal are cut finer.
-int fwd_block_rows(int broadcast_q, int causal) { return (broadcast_q || !causal) ? FWD_BM_BCAST : FWD_BM_SELF; }
+// Query rows of a forward tile (8 waves, two per SIMD, in every mode).
+int fwd_block_rows() { return FWD_BM; }
 
 // Upper bound on a pass's tile count that needs only host-known sizes:
 // sum_b cdiv(L_b, blk) <= cdiv(total_len, blk) + B.
 int64_t max_tiles(int pass, int64_t total_len, int B, int H, int Lq, int broadcast_q) {
   if (pass == 0) {
-    // an upper bound for either tile height
-    const int bm = broadcast_q ? FWD_BM_BCAST : FWD_BM_SELF;
+    const int bm = fwd_block_rows();
     if (broadcast_q) return (int64_t)B * H * cdiv(Lq, bm);
     return (int64_t)H * (cdiv(total_len, bm) + B);
   }
@@ -160,7 +157,9 @@ const char* jfa_status_string(int status) {
 int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block_rows, int* workers_out) {
   if (!block_rows || !workers_out || (pass != 0 && pass != 1)) return JFA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return JFA_ERR_UNSUPPORTED;
-  *block_rows = pass == 0 ? fwd_block_rows(broadcast_q, causal) : BWD_BN;
+  (void)causal;
+  (void)broadcast_q;
+  *block_rows = pass == 0 ? fwd_block_rows() : BWD_BN;
   return workers(pass, workers_out);
 }
 
@@ -197,7 +196,7 @@ int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   char* ws = static_cast<char*>(workspace);
   const Schedule s = schedule_at(ws, lay.sched_a, lay.cap_a);
 
-  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows(broadcast_q, causal)};
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows()};
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
 
   FwdArgs fa;
@@ -246,8 +245,7 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   Schedule sq{};
   if (!broadcast_q) {
     sq = schedule_at(ws, lay.sched_b, lay.cap_b);
-    // self-attention dQ query tiles: the forward's tile height
-    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, causal ? DQ_BM : DQ_BM_BCAST};
+    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, DQ_BM};  // self-attention dQ query tiles
     if (launch_schedule(sb, sq, st) != hipSuccess) return JFA_ERR_HIP;
   }
   BwdArgs ba;
@@ -300,7 +298,7 @@ int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const Schedule s = schedule_at(static_cast<char*>(workspace), lay.sched_a, lay.cap_a);
   SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, pass,
-               pass == 0 ? fwd_block_rows(broadcast_q, causal) : BWD_BN};
+               pass == 0 ? fwd_block_rows() : BWD_BN};
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
   if (launch_schedule_dump(s, P, tiles, cap, n_tiles, st) != hipSuccess) return JFA_ERR_HIP;
   return JFA_OK;

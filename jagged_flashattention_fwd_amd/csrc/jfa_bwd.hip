@@ -748,13 +748,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
                      a.dq, a.H, a.Lq, D, DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale);
     return hipGetLastError();
   }
-  // Causal tiles of 128 rows (4 waves); non-causal tiles of 256 rows (8
-  // waves, two per SIMD), as in the forward.
+  // Tiles of 256 rows: 8 waves, two per SIMD, as in the forward.
   if (a.causal)
     JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM / 32, true, false>), dim3(a.P_dq), dim3(DQ_BM * 2), 0, st, a);
   else
-    JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, false, false>), dim3(a.P_dq), dim3(DQ_BM_BCAST * 2), 0, st,
-                     a);
+    JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM / 32, false, false>), dim3(a.P_dq), dim3(DQ_BM * 2), 0, st, a);
   return hipGetLastError();
 }
 

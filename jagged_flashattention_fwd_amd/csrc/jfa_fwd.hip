@@ -907,14 +907,14 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  // 32 query rows per wave; broadcast tiles of 256 rows use 8 waves (two
-  // per SIMD, so one wave's matrix ops overlap the other's softmax).
+  // 32 query rows per wave; tiles of 256 rows use 8 waves (two per SIMD,
+  // so one wave's matrix ops overlap the other's softmax).
   if (a.broadcast_q) {
-    return a.causal ? launch_fwd_t<D, FWD_BM_BCAST / 32, 32, true, true>(a, stream)
-                    : launch_fwd_t<D, FWD_BM_BCAST / 32, 32, false, true>(a, stream);
+    return a.causal ? launch_fwd_t<D, FWD_BM / 32, 32, true, true>(a, stream)
+                    : launch_fwd_t<D, FWD_BM / 32, 32, false, true>(a, stream);
   }
-  return a.causal ? launch_fwd_t<D, FWD_BM_SELF / 32, 32, true, false>(a, stream)
-                  : launch_fwd_t<D, FWD_BM_BCAST / 32, 32, false, false>(a, stream);
+  return a.causal ? launch_fwd_t<D, FWD_BM / 32, 32, true, false>(a, stream)
+                  : launch_fwd_t<D, FWD_BM / 32, 32, false, false>(a, stream);
 }
 
 }  // namespace

@@ -20,11 +20,10 @@ static_assert(sizeof(TileRec) == 32, "tile record layout");
 // streamed against K/V in steps of KV_STEP keys.  Backward: a tile is BN key
 // rows of one (sequence, head), streamed against query blocks of QB rows.
 constexpr int FWD_KV_STEP = 64;
-constexpr int FWD_BM_BCAST = 256;  // 8 waves x 32 query rows (also non-causal self-attention)
-constexpr int FWD_BM_SELF = 128;   // 4 waves x 32 query rows (causal self-attention)
+constexpr int FWD_BM = 256;        // forward tile: 8 waves x 32 query rows
 constexpr int BWD_BN = 128;        // 4 waves x 32 key rows
 constexpr int BWD_QB = 64;         // query rows per step of the dK/dV kernel
-constexpr int DQ_BM = 128;         // self-attention dQ kernel: 4 waves x 32 query rows
+constexpr int DQ_BM = 256;         // self-attention dQ kernel: 8 waves x 32 query rows
 constexpr int DQ_BM_BCAST = 256;   // broadcast dQ kernel: 8 waves x 32 query rows
 constexpr int DQ_KV_STEP = 64;
 constexpr int MAX_B = 8192;        // single-workgroup sequence sort

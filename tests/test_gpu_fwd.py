@@ -15,9 +15,8 @@ pytestmark = pytest.mark.gpu
 # Tile geometry this test expects of the library (checked against the
 # library's own report before use).
 def fwd_bm(bq, causal):
-    """Query rows of a forward tile: 256 for broadcast Q and non-causal
-    self-attention, 128 for causal self-attention."""
-    return 256 if (bq or not causal) else 128
+    """Query rows of a forward tile (every mode)."""
+    return 256
 BWD_BN = 128
 
 
