@@ -73,11 +73,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
 // --------------------------------------------------------- dQ reduce ----
 // dq[h][q][:] = scale * sum over the NC partials of (h, q-block), summed as a
 // perfect binary tree over MAXP leaves (leaves c >= NC are zero), left
-// operand first.  Partials: [H][n_qb][NC][BM][d].
+// operand first.  Partials: [H][n_qb][NC][BM][d].  Adding a zero leaf or a
+// zero subtree is exact, so the walk stops at NP = the least power of two
+// >= NC, which gives the same sums as all MAXP leaves.
 constexpr int MAXP = 256;
 
+template <int NP>
 __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part, float* __restrict__ dq,
                                                  int H, int Lq, int d, int BM, int n_qb, int NC, float scale) {
+  static_assert(NP >= 1 && NP <= MAXP && (NP & (NP - 1)) == 0, "power-of-two leaf count");
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)H * Lq * d;
   if (e >= n) return;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part,
   const float* p0 = part + (((int64_t)h * n_qb + qb) * NC) * stride + (int64_t)r * d + col;
   float s[9];
 #pragma unroll
-  for (int w = 0; w < MAXP; ++w) {
+  for (int w = 0; w < NP; ++w) {
     float x = w < NC ? p0[(int64_t)w * stride] : 0.f;
     // Leaf w closes one subtree per trailing one bit of w: merge them.
     int lvl = 0;
@@ -102,7 +106,10 @@ __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part,
     }
     s[lvl] = x;
   }
-  dq[e] = s[8] * scale;
+  // the root of the NP-leaf tree sits at level log2(NP)
+  constexpr int ROOT = NP >= 256 ? 8 : NP >= 128 ? 7 : NP >= 64 ? 6 : NP >= 32 ? 5 : NP >= 16 ? 4 : NP >= 8 ? 3
+                       : NP >= 4 ? 2 : NP >= 2 ? 1 : 0;
+  dq[e] = s[ROOT] * scale;
 }
 
 // ------------------------------------------------------------------ dQ ----
@@ -744,8 +751,27 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = (int64_t)a.H * a.Lq * D;
-    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dq_part,
-                     a.dq, a.H, a.Lq, D, DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale);
+    int np2 = 1;
+    while (np2 < a.dq_chunks) np2 <<= 1;
+    const dim3 grid((unsigned)((n + 255) / 256));
+#define JFA_DQ_REDUCE(NPV)                                                                                   \
+  case NPV:                                                                                                  \
+    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce<NPV>, grid, dim3(256), 0, st, a.dq_part, a.dq, a.H, a.Lq, D, \
+                     DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale);                                       \
+    break;
+    switch (np2) {
+      JFA_DQ_REDUCE(1)
+      JFA_DQ_REDUCE(2)
+      JFA_DQ_REDUCE(4)
+      JFA_DQ_REDUCE(8)
+      JFA_DQ_REDUCE(16)
+      JFA_DQ_REDUCE(32)
+      JFA_DQ_REDUCE(64)
+      JFA_DQ_REDUCE(128)
+      JFA_DQ_REDUCE(256)
+      default: return hipErrorInvalidValue;
+    }
+#undef JFA_DQ_REDUCE
     return hipGetLastError();
   }
   // Tiles of 256 rows: 8 waves, two per SIMD, as in the forward.
