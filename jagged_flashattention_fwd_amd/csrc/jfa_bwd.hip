@@ -78,6 +78,31 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
 // >= NC, which gives the same sums as all MAXP leaves.
 constexpr int MAXP = 256;
 
+// Sum of the perfect binary tree over leaves base .. base + N - 1 of the
+// chunk partials (leaves >= NC are zero), left operand first.
+template <int N>
+__device__ __forceinline__ float dq_tree(const float* p0, int64_t stride, int NC, int base) {
+  static_assert(N >= 1 && N <= 128 && (N & (N - 1)) == 0, "power-of-two leaf count");
+  float s[8];
+#pragma unroll
+  for (int w = 0; w < N; ++w) {
+    float x = base + w < NC ? p0[(int64_t)(base + w) * stride] : 0.f;
+    // Leaf w closes one subtree per trailing one bit of w: merge them.
+    int lvl = 0;
+#pragma unroll
+    for (int z = 0; z < 7; ++z) {
+      if (((w >> z) & 1) && lvl == z) {
+        x = s[z] + x;
+        lvl = z + 1;
+      }
+    }
+    s[lvl] = x;
+  }
+  // the root of the N-leaf tree sits at level log2(N)
+  constexpr int ROOT = N >= 128 ? 7 : N >= 64 ? 6 : N >= 32 ? 5 : N >= 16 ? 4 : N >= 8 ? 3 : N >= 4 ? 2 : N >= 2 ? 1 : 0;
+  return s[ROOT];
+}
+
 template <int NP>
 __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part, float* __restrict__ dq,
                                                  int H, int Lq, int d, int BM, int n_qb, int NC, float scale) {
@@ -91,25 +116,16 @@ __global__ __launch_bounds__(256) void dq_reduce(const float* __restrict__ part,
   const int qb = q / BM, r = q - qb * BM;
   const int64_t stride = (int64_t)BM * d;  // between the partials of consecutive chunks
   const float* p0 = part + (((int64_t)h * n_qb + qb) * NC) * stride + (int64_t)r * d + col;
-  float s[9];
-#pragma unroll
-  for (int w = 0; w < NP; ++w) {
-    float x = w < NC ? p0[(int64_t)w * stride] : 0.f;
-    // Leaf w closes one subtree per trailing one bit of w: merge them.
-    int lvl = 0;
-#pragma unroll
-    for (int z = 0; z < 8; ++z) {
-      if (((w >> z) & 1) && lvl == z) {
-        x = s[z] + x;
-        lvl = z + 1;
-      }
-    }
-    s[lvl] = x;
+  float sum;
+  if constexpr (NP <= 128) {
+    sum = dq_tree<NP>(p0, stride, NC, 0);
+  } else {
+    // the root of a 256-leaf tree joins its two 128-leaf halves
+    static_assert(NP == 2 * 128, "two halves");
+    const float left = dq_tree<128>(p0, stride, NC, 0);
+    sum = left + dq_tree<128>(p0, stride, NC, 128);
   }
-  // the root of the NP-leaf tree sits at level log2(NP)
-  constexpr int ROOT = NP >= 256 ? 8 : NP >= 128 ? 7 : NP >= 64 ? 6 : NP >= 32 ? 5 : NP >= 16 ? 4 : NP >= 8 ? 3
-                       : NP >= 4 ? 2 : NP >= 2 ? 1 : 0;
-  dq[e] = s[ROOT] * scale;
+  dq[e] = sum * scale;
 }
 
 // ------------------------------------------------------------------ dQ ----

@@ -11,10 +11,13 @@
 // lse*log2(e), delta) stream through a ring of 3 LDS buffers, copied straight
 // from global memory (16 bytes per lane, 3 rows per copy) two blocks ahead of
 // use; the stream runs on across tile boundaries, and the copies are issued
-// from inside the previous block's first products.  The dK / dV stores go
-// through a per-wave LDS transpose into whole 128-byte segments, after the
-// next tile's K / V loads, and drain while that tile computes.  Each block is two 32-row
-// subtiles, ordered so that the vector-ALU work of a subtile (P and dS) sits
+// from inside the previous block's first products.  The next tile's V rows
+// are copied to a per-wave LDS area during the tile's last block; at the
+// tile end they are read from there and the next tile's K rows loaded, then
+// the dK / dV stores go through a per-wave LDS transpose (the same area)
+// into whole 128-byte segments and drain while the next tile computes.  Each
+// block is two 32-row subtiles, ordered so that the vector-ALU work of a
+// subtile (P and dS) sits
 // beside matrix-core work of the other (S and dP of subtile 1, dV and dK of
 // subtile 0) in one basic block; with one wave per SIMD that overlap is the
 // only latency hiding there is.
@@ -133,11 +136,6 @@ __device__ __forceinline__ void copy_gather(const void* src, uint32_t lds) {
 #pragma clang diagnostic pop
 
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x2;
-constexpr int SG_MFMA = 0x8;
-constexpr int SG_DS_READ = 0x100;
-#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // Operand reads of S = Q K^T and dP = dO V^T for one subtile: for each
 // k-step ks the 16-byte chunk (2ks + g) of this lane's query row, of Q and
@@ -455,9 +453,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
     bool v_staged = false;  // the next tile's V rows are on their way to LDS
     int vm_last = 0;        // copies of the block in progress, issued after them
-    const int64_t s0 = cp.s0;
     const int L = cp.L;
-    const int h = cp.h;
     const int k0 = cp.k0;                 // first key of the tile
     const int kw = k0 + wave * 32 + lc;   // this lane's key
     const bool key_ok = kw < L;

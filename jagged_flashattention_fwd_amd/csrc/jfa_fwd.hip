@@ -325,12 +325,14 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
 }
 
 // d = 128 form of the kernel.  K/V steps form one stream over this
-// workgroup's tiles: copies run DEP steps ahead across tile boundaries, and a
-// step's copies are issued from inside the S^T products of the step DEP
-// before it.  The next tile's Q rows are loaded before the current tile's O /
-// lse are stored, and the stores are bounded buffer stores of a fixed count
-// per wave, so the wait at the next tile start covers exactly the copies and
-// Q loads and lets the stores drain.
+// workgroup's tiles: copies run DEP steps ahead across tile boundaries, and
+// are issued from inside S^T products.  Non-causal tiles are
+// software-pipelined: each iteration runs the S^T products of step j + 1
+// with the softmax of step j between them, then the PV products of step j.
+// The next tile's Q rows are loaded before the current tile's O / lse are
+// stored, and the stores are bounded buffer stores of a fixed count per
+// wave, so the wait at the next tile start covers exactly the copies and Q
+// loads and lets the stores drain.
 template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const TileRec* __restrict__ tiles) {
   using C = Fwd<D, NW, QW, CAUSAL, BCAST>;
@@ -618,7 +620,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     };
     auto kv_step = [&](int j, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      const int buf = (int)((uint32_t)g_cmp % NBUF);
       const int k0 = j * BN;
       // Wait for this wave's copies of step j (steps issued after it may
       // still be in flight), then for every wave's; the ring buffer of the

@@ -34,7 +34,7 @@ const char* const kNames[K_COUNT] = {"sched_sort_scan", "sched_expand", "sched_d
                                      "delta_exact_kernel"};
 
 void release_all() {
-  for (hipEvent_t e : g_timer.events) hipEventDestroy(e);
+  for (hipEvent_t e : g_timer.events) (void)hipEventDestroy(e);
   g_timer.events.clear();
   g_timer.free_slots.clear();
   g_timer.pending.clear();
@@ -77,7 +77,7 @@ int timing_begin(hipStream_t stream, int kernel) {
 
 void timing_end(hipStream_t stream, int token) {
   if (token < 0) return;
-  hipEventRecord(g_timer.events[token + 1], stream);
+  (void)hipEventRecord(g_timer.events[token + 1], stream);
 }
 
 }  // namespace jfa

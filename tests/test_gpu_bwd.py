@@ -64,6 +64,13 @@ def test_bwd_short_sequences_many_queries(jfa, std):
     _check_case(jfa, [2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 1, 7], 2, 128, 512, True, False, seed=31, std=std)
 
 
+def test_bwd_broadcast_dq_many_chunks(jfa):
+    """One head and more sequences than compute units: the broadcast dQ runs
+    256 sequence chunks and sums their partials with a 256-leaf tree."""
+    lengths = wl.draw_lengths(("uniform", 1, 90), 300, 77)
+    _check_case(jfa, lengths, 1, 128, 64, True, False, seed=77)
+
+
 @pytest.mark.parametrize("lengths", [[512] * 5, [1000] * 3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_dense_equal_lengths(jfa, lengths, causal):
