@@ -65,7 +65,7 @@ struct Layout {
   size_t sched_a[4];  // order, cum, n_tiles, tiles
   size_t sched_b[4];
   int64_t cap_a = 0, cap_b = 0;
-  size_t delta = 0, lse2 = 0, dq_part = 0;
+  size_t delta = 0, lse2 = 0, term_l = 0, term_d = 0, dq_part = 0;
   size_t total = 0;
 };
 
@@ -92,6 +92,8 @@ Layout layout(int pass, int64_t total_len, int B, int H, int Lq, int d, int broa
     const size_t rows = broadcast_q ? (size_t)B * H * Lq : (size_t)total_len * H;
     L.delta = at; at = align256(at + sizeof(float) * rows);
     L.lse2 = at; at = align256(at + sizeof(float) * rows);
+    L.term_l = at; at = align256(at + 16 * rows);
+    L.term_d = at; at = align256(at + 16 * rows);
     if (broadcast_q) {
       int n_qb, nc;
       dq_split(B, H, Lq, P, &n_qb, &nc);
@@ -259,6 +261,8 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   ba.dq = dq; ba.dk = dk; ba.dv = dv;
   ba.delta = reinterpret_cast<float*>(ws + lay.delta);
   ba.lse2 = reinterpret_cast<float*>(ws + lay.lse2);
+  ba.term_l = reinterpret_cast<uint16_t*>(ws + lay.term_l);
+  ba.term_d = reinterpret_cast<uint16_t*>(ws + lay.term_d);
   ba.dq_part = broadcast_q ? reinterpret_cast<float*>(ws + lay.dq_part) : nullptr;
   ba.seq_order = sk.order;
   ba.dq_qblocks = 0;

@@ -8,7 +8,8 @@
 //
 // Kernels, in launch order:
 //   delta_kernel        streaming pre-pass: delta = rowsum(dO o O) (O as
-//                       stored) and lse * log2(e), per query row.
+//                       stored), lse * log2(e), and the bf16 row terms of
+//                       -lse / scale and -delta, per query row.
 //   delta_exact_kernel  delta again, exactly, for sequences of at most 128
 //                       keys (jfa_dkdv.hip).
 //   dkdv_kernel         dK and dV (jfa_dkdv.hip).
@@ -40,13 +41,16 @@ constexpr float SPLIT_DS = 0.25f;
 
 // ------------------------------------------------------------- delta ----
 // Rows of d elements; D/8 threads per row, 16 bytes each.  Also writes the
-// row's lse in base-2 units (lse * log2(e)), the form the dK/dV kernel reads.
+// row's lse in base-2 units (lse * log2(e)), the form the dQ kernels read, and
+// the row terms (row_terms) of -lse / scale and -delta that the dK/dV kernel
+// folds into its score products.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
                                                     const float* __restrict__ lse,
                                                     float* __restrict__ delta, float* __restrict__ lse2,
-                                                    int64_t rows) {
+                                                    u32x4* __restrict__ term_l, u32x4* __restrict__ term_d,
+                                                    float inv_scale, int64_t rows) {
   constexpr int TPR = D / 8;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -66,6 +70,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
     if (c == 0) {
       delta[row] = acc;
       lse2[row] = lse[row] * LOG2E;
+      term_l[row] = row_terms(-lse[row] * inv_scale);
+      term_d[row] = row_terms(-acc);
     }
   }
 }
@@ -746,7 +752,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const int64_t want = (work + 255) / 256;
     const int blocks = (int)(want < 4096 ? want : 4096);
     JFA_TIMED_LAUNCH(K_DELTA, st, (delta_kernel<D>), dim3(blocks), dim3(256), 0, st, a.out, a.dout, a.lse, a.delta,
-                     a.lse2, rows);
+                     a.lse2, reinterpret_cast<u32x4*>(a.term_l), reinterpret_cast<u32x4*>(a.term_d),
+                     1.0f / a.scale, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -70,6 +70,19 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t* hi, uin
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// x as three bf16 values whose sum is exactly x (the first two truncate the
+// value and its remainder to 8 significant bits; the last remainder has at
+// most 8 left), then five zeros: eight bf16 MFMA operand slots.  Multiplied by
+// ones in the matching slots of the other operand, one extra k-step adds x to
+// every product of the row in the fp32 accumulator.
+__device__ __forceinline__ u32x4 row_terms(float x) {
+  const uint32_t u0 = __float_as_uint(x) & 0xffff0000u;
+  const float r1 = x - __uint_as_float(u0);
+  const uint32_t u1 = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(u1);
+  return u32x4{(u0 >> 16) | u1, __float_as_uint(r2) >> 16, 0u, 0u};
+}
+
 // Full-row reductions for the transposed score layout, where lanes l and
 // l+32 hold the two halves of one row: after the swap every lane sees both.
 __device__ __forceinline__ float max_across_halves(float x) {

@@ -7,8 +7,9 @@
 //
 // dkdv_kernel is persistent.  A tile is 128 keys of one (sequence, head); each
 // of the 4 waves keeps its 32 keys' K and V rows in registers as MFMA
-// operands and accumulates their dK^T / dV^T.  Query blocks of 64 rows (Q, dO,
-// lse*log2(e), delta) stream through a ring of 3 LDS buffers, copied straight
+// operands and accumulates their dK^T / dV^T.  Query blocks of 64 rows (Q, dO
+// and each row's terms of -lse / scale and -delta) stream through a ring of 3
+// LDS buffers, copied straight
 // from global memory (16 bytes per lane, 3 rows per copy) two blocks ahead of
 // use; the stream runs on across tile boundaries, and the copies are issued
 // from inside the previous block's first products.  The next tile's V rows
@@ -21,6 +22,11 @@
 // beside matrix-core work of the other (S and dP of subtile 1, dV and dK of
 // subtile 0) in one basic block; with one wave per SIMD that overlap is the
 // only latency hiding there is.
+//
+// The row terms enter as one extra k-step of the S and dP products (three
+// bf16 terms times ones, row_terms), so the accumulators hold S - lse / scale
+// and dP - delta: P = exp2(c S'), dS = P o dP', with no per-row values held
+// in registers or read per element.
 //
 // Masks are compile-time variants chosen per block: blocks that cross the
 // causal diagonal, the key tile at a sequence end and the last (partial)
@@ -54,15 +60,15 @@ struct Dkdv {
   // padded rows per copy (PadRowCopy); a wave's 16 rows of a tile take 6.
   static constexpr bool DMA = D == 128;
   static constexpr int NBUF = 3;
-  // One ring buffer: Q tile, dO tile, then four 64-float rows: lse*log2(e),
-  // delta and two spares (waves 2 and 3 copy a duplicate row there, which
-  // keeps the number of copies equal across waves).  Each tile is followed by
-  // the gap that absorbs the overhang of its last row copy.
+  // One ring buffer: Q tile, dO tile, then the 64 rows' terms of -lse / scale
+  // and of -delta (16 bytes per row; waves 2 and 3 copy the same rows as waves
+  // 0 and 1, which keeps the number of copies equal across waves).  Each tile
+  // is followed by the gap that absorbs the overhang of its last row copy.
   static constexpr int GAP = PadRowCopy::GAP;
   static constexpr int OFF_DO = TILE + GAP;
-  static constexpr int OFF_LSE = OFF_DO + TILE + GAP;
-  static constexpr int OFF_DEL = OFF_LSE + QB * 4;
-  static constexpr int BUF = OFF_LSE + 4 * QB * 4;
+  static constexpr int OFF_TL = OFF_DO + TILE + GAP;
+  static constexpr int OFF_TD = OFF_TL + QB * 16;
+  static constexpr int BUF = OFF_TD + QB * 16;
   static constexpr int RPW = QB / NW;                  // rows per wave per tile
   static constexpr int CPT = PadRowCopy::copies(RPW);  // copies per wave per tile
   static_assert(!DMA || (RB == 19 * 16 && RPW >= 3), "copy geometry");
@@ -128,9 +134,9 @@ __device__ __forceinline__ bf16x8 tr_operand(const i16x4 (&x)[8], int dt) {
 // kernels uses M0, and each statement sets it before its copy.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// One dword per lane from a per-lane address.
-__device__ __forceinline__ void copy_gather(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+// 16 bytes per lane from a per-lane address.
+__device__ __forceinline__ void copy_gather16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
 }
 #pragma clang diagnostic pop
@@ -162,28 +168,15 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait2(u32x4& a, u32x4& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
 }
-// lse*log2(e) and delta of rows OFF/4 + 8 i4 + 4g + 0..3 (i4 = 0..3), issued
-// as l0 d0 l1 d1 l2 d2 l3 d3 (`addr` holds this lane's 16 * g).
+// The row terms of this lane's query row, of -lse / scale (at OFFL) and of
+// -delta (at OFFD), as A operands of the extra k-step (`addr` holds the row's
+// 16 * row; both lane halves read the row's 16 bytes, which meet the zero
+// half of the ones operand in the upper k-slots).
 template <int OFFL, int OFFD>
-__device__ __forceinline__ void ld_issue(uint32_t addr, f32x4 (&l)[4], f32x4 (&d)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:%9\n\t"
-      "ds_read_b128 %1, %8 offset:%10\n\t"
-      "ds_read_b128 %2, %8 offset:%11\n\t"
-      "ds_read_b128 %3, %8 offset:%12\n\t"
-      "ds_read_b128 %4, %8 offset:%13\n\t"
-      "ds_read_b128 %5, %8 offset:%14\n\t"
-      "ds_read_b128 %6, %8 offset:%15\n\t"
-      "ds_read_b128 %7, %8 offset:%16"
-      : "=&v"(l[0]), "=&v"(d[0]), "=&v"(l[1]), "=&v"(d[1]), "=&v"(l[2]), "=&v"(d[2]), "=&v"(l[3]), "=&v"(d[3])
-      : "v"(addr), "i"(OFFL), "i"(OFFD), "i"(OFFL + 32), "i"(OFFD + 32), "i"(OFFL + 64), "i"(OFFD + 64),
-        "i"(OFFL + 96), "i"(OFFD + 96));
-}
-template <int N>
-__device__ __forceinline__ void ld_wait(f32x4 (&l)[4], f32x4 (&d)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(l[0]), "+v"(d[0]), "+v"(l[1]), "+v"(d[1]), "+v"(l[2]), "+v"(d[2]), "+v"(l[3]), "+v"(d[3])
-               : "i"(N));
+__device__ __forceinline__ void tm_issue(uint32_t addr, u32x4& tl, u32x4& td) {
+  asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4"
+               : "=&v"(tl), "=&v"(td)
+               : "v"(addr), "i"(OFFL), "i"(OFFD));
 }
 
 // Residual of a packed bf16 pair: bf16(a - hi.a), bf16(b - hi.b).
@@ -222,15 +215,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   if (t0 >= T) return;
 
   const int64_t qs = BCAST ? (int64_t)D : ld;          // row stride of Q / dO
-  const int64_t sld = BCAST ? 1 : H;                    // row stride of lse / delta
+  const int64_t sld = BCAST ? 1 : H;                    // row stride of the per-row arrays
   // Per-tile values, with the tile's row-0 addresses of Q, dO and this
-  // wave's lse*log2(e) (even waves) or delta (odd waves) rows.
+  // wave's row terms of -lse / scale (even waves) or -delta (odd waves).
   struct Tp {
     int64_t s0;
     int L, h, b, k0, m_first, m_end, nq;
     const uint16_t* qb;
     const uint16_t* db;
-    const float* vb;
+    const u32x4* vb;
   };
   auto tparams = [&](const TileRec& r) {
     Tp p;
@@ -244,7 +237,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     p.m_end = max((p.nq + QB - 1) / QB, p.m_first);     // exclusive
     p.qb = BCAST ? a.q + (int64_t)r.h * Lq * D : a.q + (r.s0 * H + r.h) * (int64_t)D;
     p.db = BCAST ? a.dout + ((int64_t)r.b * H + r.h) * Lq * D : a.dout + (r.s0 * H + r.h) * (int64_t)D;
-    p.vb = ((wave & 1) ? a.delta : a.lse2) + (BCAST ? ((int64_t)r.b * H + r.h) * Lq : r.s0 * H + r.h);
+    p.vb = reinterpret_cast<const u32x4*>((wave & 1) ? a.term_d : a.term_l) +
+           (BCAST ? ((int64_t)r.b * H + r.h) * Lq : r.s0 * H + r.h);
     return p;
   };
 
@@ -254,12 +248,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   // where their scalar address work overlaps the products.  Rows past the
   // last query repeat it: finite values the masked body discards.
   // The prepared job: this wave's first Q / dO source rows of the block, this
-  // lane's lse*log2(e) (even waves) or delta (odd waves) source, the ring
+  // lane's row terms of -lse / scale (even waves) or -delta (odd waves), the ring
   // buffer's LDS address, rows i > j_last repeat row j_last, and the number
   // of vector-memory operations the job issues (0: none).
   const uint16_t* j_q = a.q;
   const uint16_t* j_d = a.q;
-  const float* j_v = a.lse2;
+  const u32x4* j_v = reinterpret_cast<const u32x4*>(a.term_l);
   uint32_t j_lds = 0;  // ring buffer
   uint32_t j_ldw = 0;  // this wave's first row in it
   int j_last = 0, j_n = 0;
@@ -281,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   auto issue_vec = [&]() {
     if constexpr (C::DMA) {
       if (j_n == 0) return;
-      copy_gather(j_v, j_lds + C::OFF_LSE + wave * QB * 4);
+      copy_gather16(j_v, j_lds + C::OFF_TL + (wave & 1) * QB * 16);
     }
   };
   // d = 64: the block is staged through registers right away (the job then
@@ -292,15 +286,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     const int nr = min(QB, nq - r0);
     ql.load(qbase + (int64_t)r0 * qs, qs, nr, tid);
     dol.load(dobase + (int64_t)r0 * qs, qs, nr, tid);
-    float v = 0.f;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
     if (tid < 2 * QB) {
       const int r = tid & (QB - 1);
       const int64_t ri = rbase + (int64_t)min(r0 + r, nq - 1) * sld;
-      v = tid < QB ? a.lse2[ri] : a.delta[ri];
+      v = reinterpret_cast<const u32x4*>(tid < QB ? a.term_l : a.term_d)[ri];
     }
     ql.store(buf, tid);
     dol.store(buf + C::OFF_DO, tid);
-    if (tid < 2 * QB) reinterpret_cast<float*>(buf + C::OFF_LSE)[tid] = v;
+    if (tid < 2 * QB) reinterpret_cast<u32x4*>(buf + C::OFF_TL)[tid] = v;
   };
 
   // Issue state of the block stream.
@@ -472,7 +466,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
 
     // Lane bases of the LDS reads (the buffer address is added per block).
     const uint32_t qd_lane = (uint32_t)(lc * RB + g * 16);
-    const uint32_t ld_lane = (uint32_t)(g * 16);
+    const uint32_t tm_lane = (uint32_t)(lc * 16);
+    // B operand of the row-term k-step: ones in k-slots 0..2, zeros elsewhere.
+    const bf16x8 ones3 = __builtin_bit_cast(bf16x8, g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
 
     // S = Q K^T and dP = dO V^T of subtile S_ from the operand reads q / d
     // (issued by qd_issue; W0 = reads issued after the last pair, so pair ks
@@ -497,22 +493,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
       qd_issue4<S_ * 32 * RB, S_ * 32 * RB + C::OFF_DO>(base, q, d);
       if constexpr (KS == 8) qd_issue4<S_ * 32 * RB + 128, S_ * 32 * RB + C::OFF_DO + 128>(base, q + 4, d + 4);
     };
-    auto ldv_issue = [&](auto s_tag, uint32_t base, f32x4 (&l)[4], f32x4 (&d)[4]) {
+    auto tm_read = [&](auto s_tag, uint32_t base, u32x4& tl, u32x4& td) {
       constexpr int S_ = decltype(s_tag)::value;
-      ld_issue<C::OFF_LSE + S_ * 128, C::OFF_DEL + S_ * 128>(base, l, d);
+      tm_issue<C::OFF_TL + S_ * 32 * 16, C::OFF_TD + S_ * 32 * 16>(base, tl, td);
     };
 
     // P and dS of registers 4*i4 .. 4*i4+3 (query rows s*32 + 8*i4 + 4g + e)
-    // of subtile s of block m, from its S / dP and the rows' lse*log2(e) /
-    // delta.
-    auto pds = [&](auto masked_tag, int m, int s, const f32x16& sc, const f32x16& dc, int i4, const f32x4& ls,
-                   const f32x4& dl, float (&p4)[4], float (&d4)[4]) {
+    // of subtile s of block m, from its S - lse / scale and dP - delta.
+    auto pds = [&](auto masked_tag, int m, int s, const f32x16& sc, const f32x16& dc, int i4, float (&p4)[4],
+                   float (&d4)[4]) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       const int r = s * 32 + i4 * 8 + g * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = i4 * 4 + e;
-        float pv = fast_exp2(sc[i] * c2 - ls[e]);
+        float pv = fast_exp2(sc[i] * c2);
         if constexpr (MASKED) {
           const int row = m * QB + r + e;
           bool ok = key_ok && row < nq;
@@ -520,19 +515,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
           pv = ok ? pv : 0.f;
         }
         p4[e] = pv;
-        d4[e] = pv * (dc[i] - dl[e]);
+        d4[e] = pv * dc[i];
       }
     };
 
     // P and dS of subtile s as packed bf16 MFMA B operands pp / dsp (pair
     // hh: query rows s*32 + hh*16 + 4g + {0..3, 8..11}); pmax / dsmax
     // collect max |value|.
-    auto probs = [&](auto masked_tag, int m, int s, const f32x16& sc, const f32x16& dc, const f32x4 (&l)[4],
-                     const f32x4 (&dl)[4], uint32_t (&pp)[2][4], uint32_t (&dsp)[2][4], float& pmax, float& dsmax,
-                     int i4) {
+    auto probs = [&](auto masked_tag, int m, int s, const f32x16& sc, const f32x16& dc, uint32_t (&pp)[2][4],
+                     uint32_t (&dsp)[2][4], float& pmax, float& dsmax, int i4) {
       {
         float p4[4], d4[4];
-        pds(masked_tag, m, s, sc, dc, i4, l[i4], dl[i4], p4, d4);
+        pds(masked_tag, m, s, sc, dc, i4, p4, d4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           pmax = fmaxf(pmax, p4[e]);
@@ -602,11 +596,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int i4 = 2 * hh + k;
-          const int r = s * 32 + i4 * 8 + g * 4;
-          const f32x4 ls = *reinterpret_cast<const f32x4*>(buf + C::OFF_LSE + r * 4);
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(buf + C::OFF_DEL + r * 4);
           float p4[4], d4[4];
-          pds(masked_tag, m, s, sc2, dc2, i4, ls, dl, p4, d4);
+          pds(masked_tag, m, s, sc2, dc2, i4, p4, d4);
           plo[2 * k] = bf16x2_residual(p4[0], p4[1], pp[hh][2 * k]);
           plo[2 * k + 1] = bf16x2_residual(p4[2], p4[3], pp[hh][2 * k + 1]);
           dlo[2 * k] = bf16x2_residual(d4[0], d4[1], dsp[hh][2 * k]);
@@ -633,29 +624,29 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
 
     // One query block, every LDS read issued explicitly so that its latency
     // overlaps other work:
-    //   1. lse/delta(0), Q/dO(0) reads; S0, dP0.
-    //   2. Q/dO(1) reads; P0, dS0 (vector ALU) beside S1, dP1; lse/delta(1)
-    //      reads once half of Q/dO(1) is consumed (the wait counter counts at
-    //      most 15 later reads).
+    //   1. Row terms(0), Q/dO(0) reads; S0, dP0 from the row-term k-step.
+    //   2. Row terms(1), Q/dO(1) reads; P0, dS0 (vector ALU) beside S1, dP1.
     //   3. dV/dK of subtile 0 beside P1, dS1.
     //   4. dV/dK of subtile 1.
     auto block = [&](auto masked_tag, int m, const char* buf) {
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
       using W0 = std::integral_constant<int, 0>;
-      using W8 = std::integral_constant<int, 8>;
       using K0 = std::integral_constant<int, 0>;
-      using KH = std::integral_constant<int, KS / 2>;
       using KE = std::integral_constant<int, KS>;
       const uint32_t lb = lds_addr(buf);
-      const uint32_t qb = lb + qd_lane, lsb = lb + ld_lane, tb = lb + tr_lane;
-      f32x16 sa = f32x16{}, da = f32x16{}, sb = f32x16{}, db = f32x16{};
+      const uint32_t qb = lb + qd_lane, tmb = lb + tm_lane, tb = lb + tr_lane;
       uint32_t pa[2][4], dsa[2][4], pb[2][4], dsb[2][4];
-      f32x4 l0[4], e0[4], l1[4], e1[4];
-      u32x4 q[KS], d[KS];
+      u32x4 q[KS], d[KS], tl, td;
       auto none = [](auto) {};
-      ldv_issue(S0{}, lsb, l0, e0);
+      // S / dP accumulators start from the row-term k-step (its reads issued
+      // first and waited for with up to 15 operand reads after them in flight;
+      // the counter holds no more).
+      tm_read(S0{}, tmb, tl, td);
       qd_issue(S0{}, qb, q, d);
+      lgkm_wait2<(2 * KS > 15 ? 15 : 2 * KS)>(tl, td);
+      f32x16 sa = mfma32(__builtin_bit_cast(bf16x8, tl), ones3, f32x16{});
+      f32x16 da = mfma32(__builtin_bit_cast(bf16x8, td), ones3, f32x16{});
       // The next block's copies, spread over the k-steps.
       auto copy_hook = [&](auto ks_tag) {
         constexpr int ks = decltype(ks_tag)::value;
@@ -666,22 +657,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
       mma_scores(W0{}, K0{}, KE{}, q, d, sa, da, copy_hook);
 
       // P0 / dS0 in four row groups, one after every KS/4 k-steps of S1 / dP1.
+      tm_read(S1{}, tmb, tl, td);
       qd_issue(S1{}, qb, q, d);
-      ld_wait<15>(l0, e0);
+      lgkm_wait2<(2 * KS > 15 ? 15 : 2 * KS)>(tl, td);
+      f32x16 sb = mfma32(__builtin_bit_cast(bf16x8, tl), ones3, f32x16{});
+      f32x16 db = mfma32(__builtin_bit_cast(bf16x8, td), ones3, f32x16{});
       float pmax = 0.f, dsmax = 0.f;
       auto p0_hook = [&](auto ks_tag) {
         constexpr int ks = decltype(ks_tag)::value;
-        if constexpr (ks % (KS / 4) == KS / 4 - 1) probs(masked_tag, m, 0, sa, da, l0, e0, pa, dsa, pmax, dsmax, ks / (KS / 4));
+        if constexpr (ks % (KS / 4) == KS / 4 - 1) probs(masked_tag, m, 0, sa, da, pa, dsa, pmax, dsmax, ks / (KS / 4));
       };
-      mma_scores(W0{}, K0{}, KH{}, q, d, sb, db, p0_hook);
-      ldv_issue(S1{}, lsb, l1, e1);
-      mma_scores(W8{}, KH{}, KE{}, q, d, sb, db, p0_hook);
+      mma_scores(W0{}, K0{}, KE{}, q, d, sb, db, p0_hook);
 
       // P1 / dS1 beside dV / dK of subtile 0.
-      ld_wait<0>(l1, e1);
       float pmax1 = 0.f, dsmax1 = 0.f;
       auto p1_hook = [&](auto g_tag) {
-        probs(masked_tag, m, 1, sb, db, l1, e1, pb, dsb, pmax1, dsmax1, decltype(g_tag)::value);
+        probs(masked_tag, m, 1, sb, db, pb, dsb, pmax1, dsmax1, decltype(g_tag)::value);
       };
       dvdk(S0{}, tb, pa, dsa, p1_hook);
       dvdk(S1{}, tb, pb, dsb, none);
@@ -690,10 +681,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
       if (__builtin_expect(__any(f0p || f0d || f1p || f1d), 0)) {
         fixup(masked_tag, S0{}, m, buf, sa, da, pa, dsa, __any(f0p), __any(f0d));
         fixup(masked_tag, S1{}, m, buf, sb, db, pb, dsb, __any(f1p), __any(f1d));
-        // The fixup's lse / delta reads are consumed only where a product
-        // needed them; waiting for the rest here (a wait the compiler sees)
-        // keeps it from assuming them outstanding in every later block.
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       }
     };
 
@@ -835,7 +822,10 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
     }
   }
   acc = sum_across_halves(acc);
-  if (g == 0 && q < nq) a.delta[ri] = acc;
+  if (g == 0 && q < nq) {
+    a.delta[ri] = acc;
+    reinterpret_cast<u32x4*>(a.term_d)[ri] = row_terms(-acc);
+  }
 }
 
 template <int D>

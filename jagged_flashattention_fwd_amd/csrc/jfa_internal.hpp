@@ -76,6 +76,12 @@ struct BwdArgs {
   float* dv;
   float* delta;           // [rows] scratch: delta per query row
   float* lse2;            // [rows] scratch: lse * log2(e) per query row
+  // [rows][8] bf16 scratch: -lse / scale (term_l) and -delta (term_d) of each
+  // query row as three bf16 terms (t0 + t1 + t2 within 2^-24 of it), then
+  // five zeros: the extra k-step that folds the row terms into the score
+  // products of the dK / dV kernel.
+  uint16_t* term_l;
+  uint16_t* term_d;
   float* dq_part;         // [H][n_qb][NC][DQ_BM_BCAST][d] broadcast-mode partials
   const int* seq_order;   // sequences sorted by length (broadcast dQ chunks)
   int dq_qblocks;         // n_qb = cdiv(Lq, DQ_BM_BCAST)
