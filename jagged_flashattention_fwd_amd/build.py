@@ -24,6 +24,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # Packed fp32 VALU ops stay disabled for every kernel.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Atomics stay as written: the forward's one-lane tile hand-out leaves its
+    # result unread until the next tile start, where the optimizer's rewrite
+    # would read it back at once (a full vector-memory wait).
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-result",
 ]

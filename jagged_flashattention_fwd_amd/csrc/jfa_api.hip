@@ -72,7 +72,7 @@ struct Layout {
 void place_schedule(size_t* at, size_t off[4], int B, int64_t cap) {
   off[0] = *at; *at = align256(*at + sizeof(int) * (size_t)B);
   off[1] = *at; *at = align256(*at + sizeof(int64_t) * ((size_t)B + 1));
-  off[2] = *at; *at = align256(*at + sizeof(int64_t));
+  off[2] = *at; *at = align256(*at + 2 * sizeof(int64_t));
   off[3] = *at; *at = align256(*at + sizeof(TileRec) * (size_t)cap);
 }
 
@@ -210,6 +210,7 @@ int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   fa.lse = lse;
   fa.tiles = s.tiles;
   fa.n_tiles = s.n_tiles;
+  fa.tile_ctr = reinterpret_cast<unsigned int*>(s.n_tiles + 1);
   fa.total_len = total_len;
   fa.B = B; fa.H = H; fa.Lq = Lq; fa.d = d;
   fa.scale_log2 = scale * 1.4426950408889634f;

@@ -39,6 +39,9 @@ namespace jfa {
 namespace {
 
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
+// d = 128: tiles past each workgroup's first two come from a global hand-out
+// counter (runtime balance) rather than the static zigzag order.
+constexpr bool DYN_FWD = true;
 
 template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
 struct Fwd {
@@ -504,10 +507,16 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     store_out(cp, 0);
   }
 
+  // Tile hand-out: each workgroup takes its first two tiles by the zigzag
+  // order (passes 0 and 1) and every later one from a global counter over
+  // the rest of the longest-first list, one tile ahead: the index for pass
+  // p + 2 is fetched at the start of pass p (one lane of wave 0, a vector
+  // atomic) and shared through LDS at the start of pass p + 1.  Its latency
+  // hides behind a whole tile; the compiler's wait for it falls at the tile
+  // start, where everything but the previous tile's stores has landed.
+  __shared__ int s_next;
+  unsigned int fetched = 0;
   for (int64_t pass = 0;; ++pass) {
-    const int64_t tn = zigzag_tile(pass + 1, slot, a.P);
-    const bool has_nxt = tn < T;
-    const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
     const int64_t s0 = cp.s0;
     const int L = cp.L, h = cp.h, q0 = cp.q0, n_kv = cp.n_kv;
     const int nq = BCAST ? Lq : L;
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       const int need = min(DEP, n_kv);
       if (iss_cur < need) {
         while (iss_cur < need) {
-          prep_next(cp, np, has_nxt);
+          prep_next(cp, cp, false);  // this tile's steps only
           issue_copies(0, 2 * C::CPT);
         }
         wait_vmcnt<0>();
@@ -537,6 +546,14 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
         wait_vmcnt<NST>();
       }
     }
+    if (DYN_FWD && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
+    if (DYN_FWD) barrier_lds();
+    const int64_t tn = !DYN_FWD ? zigzag_tile(pass + 1, slot, a.P)
+                       : pass == 0 ? zigzag_tile(1, slot, a.P)
+                                   : 2 * (int64_t)a.P + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
+    const bool has_nxt = tn < T;
+    if (DYN_FWD && has_nxt && wave == 0 && l == 0) fetched = atomicAdd(a.tile_ctr, 1u);
+    const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
 #pragma unroll
     for (int s = 0; s < QS; ++s)
 #pragma unroll

@@ -32,7 +32,7 @@ struct Schedule {
   int* order;         // [B]
   int64_t* cum;       // [B+1]
   TileRec* tiles;     // [max_tiles]
-  int64_t* n_tiles;   // [1]
+  int64_t* n_tiles;   // [2]: tile count, then the forward's hand-out counter (reset by the sort)
   int64_t max_tiles;  // capacity of `tiles`
 };
 
@@ -55,6 +55,7 @@ struct FwdArgs {
   float* lse;
   const TileRec* tiles;
   const int64_t* n_tiles;
+  unsigned int* tile_ctr;  // tiles handed out past the first two per workgroup (starts at 0)
   int64_t total_len;
   int B, H, Lq, d;
   float scale_log2;  // softmax scale times log2(e)

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Sch
   if (tid == SORT_THREADS - 1) {
     const int64_t T = part[tid] < s.max_tiles ? part[tid] : s.max_tiles;
     s.cum[B] = T;
-    *s.n_tiles = T;
+    s.n_tiles[0] = T;
+    s.n_tiles[1] = 0;  // the forward's dynamic hand-out counter
   }
 }
 

@@ -100,6 +100,34 @@ def test_fwd_deterministic(jfa):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("bq,causal", [(True, False), (False, True)])
+def test_fwd_dynamic_handout_reused_workspace(jfa, bq, causal):
+    """More tiles than two per workgroup, so most come from the hand-out
+    counter; three calls on one workspace into NaN-filled outputs must each
+    cover every tile once (the counter restarts per call) and agree bitwise."""
+    rng = np.random.default_rng(21)
+    lengths = [int(x) for x in rng.integers(1, 300, size=700 if bq else 900)]
+    H, d, Lq = 2, 128, (300 if bq else 0)
+    t = wl.make_tensors(lengths, H, d, Lq, bq, seed=21, device="cuda", with_dout=False)
+    B, T = len(lengths), int(sum(lengths))
+    n_tiles = B * H * -(-Lq // fwd_bm(bq, causal)) if bq else H * sum(-(-L // fwd_bm(bq, causal)) for L in lengths)
+    assert n_tiles > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    ws = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, "cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.full((B, H, Lq, d) if bq else (T, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, H, Lq) if bq else (T, H), float("nan"), dtype=torch.float32, device="cuda")
+        jfa.jfa_fwd(t["q"], t["k"], t["v"], t["offsets"], B, H, Lq, d, 0.09, causal, bq, out, lse, T, ws)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    ref_o, ref_lse = jo.jagged_forward(to64(t["q"]), to64(t["k"]), to64(t["v"]), t["offsets"].cpu().numpy(),
+                                       0.09, causal, bq)
+    compare("O", to64(outs[0][0]), ref_o)
+    compare_lse("lse", to64(outs[0][1]), ref_lse)
+
+
 @pytest.mark.parametrize("pass_", [0, 1])
 @pytest.mark.parametrize("bq,causal", [(True, 0), (False, 0), (False, 1)])
 def test_schedule_bit_exact(jfa, pass_, bq, causal):
