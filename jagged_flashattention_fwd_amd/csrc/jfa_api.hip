@@ -271,8 +271,10 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   if (broadcast_q) dq_split(B, H, Lq, P, &ba.dq_qblocks, &ba.dq_chunks);
   ba.ktiles = sk.tiles;
   ba.n_ktiles = sk.n_tiles;
+  ba.ktile_ctr = reinterpret_cast<unsigned int*>(sk.n_tiles + 1);
   ba.qtiles = broadcast_q ? nullptr : sq.tiles;
   ba.n_qtiles = broadcast_q ? nullptr : sq.n_tiles;
+  ba.qtile_ctr = broadcast_q ? nullptr : reinterpret_cast<unsigned int*>(sq.n_tiles + 1);
   ba.B = B; ba.H = H; ba.Lq = Lq; ba.d = d;
   ba.total_len = total_len;
   ba.scale = scale;

@@ -11,7 +11,8 @@
 //                       stored), lse * log2(e), and the bf16 row terms of
 //                       -lse / scale and -delta, per query row.
 //   delta_exact_kernel  delta again, exactly, for sequences of at most 128
-//                       keys (jfa_dkdv.hip).
+//                       keys and, under the causal mask, the first 128 query
+//                       rows of every sequence (jfa_dkdv.hip).
 //   dkdv_kernel         dK and dV (jfa_dkdv.hip).
 //   dq_kernel           dQ.  Self-attention: persistent, a tile is 128 query
 //                       rows, looping over K/V steps recomputing S^T, dP^T,
@@ -381,9 +382,17 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
   if constexpr (!BCAST) {
     const int slot = logical_slot(blockIdx.x, a.P_dq);
     const int64_t T = *a.n_qtiles;
+    // Tile hand-out: the first tile by slot, every later one from a global
+    // counter over the rest of the list, fetched one tile ahead (one lane of
+    // wave 0, a vector atomic) and shared through LDS at the next tile start.
+    __shared__ int s_next;
+    unsigned int fetched = 0;
     for (int64_t pass = 0;; ++pass) {
-      const int64_t t = zigzag_tile(pass, slot, a.P_dq);
+      if (pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
+      __syncthreads();
+      const int64_t t = pass == 0 ? (int64_t)slot : a.P_dq + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
       if (t >= T) break;
+      if (wave == 0 && l == 0) fetched = atomicAdd(a.qtile_ctr, 1u);
       const TileRec tile = a.qtiles[t];
       int64_t s0;
       const int L = (int)seq_range(a.offsets, tile.b, a.total_len, &s0);

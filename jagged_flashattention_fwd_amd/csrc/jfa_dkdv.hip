@@ -441,10 +441,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     store_dkdv(cp, 0, z, z);
   }
 
+  // Tile hand-out.  Causal or self-attention tiles differ in cost: each
+  // workgroup takes its first two tiles by the zigzag order and every later
+  // one from a global counter over the rest of the list (every dK / dV
+  // element is written once by one lane, so the results do not depend on the
+  // assignment).  The index for pass p + 2 is fetched at the start of pass p
+  // (one lane of wave 0, a vector atomic) and shared through LDS at the
+  // tile-start barrier of pass p + 1, where the compiler's wait for it falls
+  // behind the wait for everything but the stores.  Non-causal broadcast
+  // tiles all cost the same: the static zigzag order alone.
+  constexpr bool DYN = CAUSAL || !BCAST;
+  __shared__ int s_next;
+  unsigned int fetched = 0;
   for (int64_t pass = 0;; ++pass) {
-    const int64_t tn = zigzag_tile(pass + 1, slot, a.P);
-    const bool has_nxt = tn < T;
-    const Tp np = has_nxt ? tparams(tiles[tn]) : cp;
+    // The next tile: known here in the static order, at the tile start
+    // (handoff) otherwise.
+    const int64_t tn0 = zigzag_tile(pass + 1, slot, a.P);
+    bool has_nxt = !DYN && tn0 < T;
+    Tp np = has_nxt ? tparams(tiles[tn0]) : cp;
+    auto handoff = [&]() {
+      if constexpr (DYN) {
+        const int64_t tn = pass == 0 ? tn0 : 2 * (int64_t)a.P + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
+        has_nxt = tn < T;
+        if (has_nxt && wave == 0 && l == 0) fetched = atomicAdd(a.ktile_ctr, 1u);
+        if (has_nxt) np = tparams(tiles[tn]);
+      }
+    };
     bool v_staged = false;  // the next tile's V rows are on their way to LDS
     int vm_last = 0;        // copies of the block in progress, issued after them
     const int L = cp.L;
@@ -701,7 +723,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
         const int need = min(nb, 2);
         if (iss_cur < need) {
           while (iss_cur < need) {
-            prep_next(cp, np, has_nxt);
+            prep_next(cp, cp, false);  // this tile's blocks only
             issue_now();
           }
           wait_vmcnt<0>();
@@ -709,7 +731,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
           static_assert(8 * DT <= 63, "store count");
           wait_vmcnt<8 * DT>();
         }
+        if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
         barrier_lds();  // the block's copies landed for every wave; the previous block's readers are done
+        handoff();
       }
       // Blocks [m0, m1) with one body (a loop per mask variant, rather than
       // a branch per block, keeps register allocation to one body at a time).
@@ -745,6 +769,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
         run(std::false_type{}, u0, u1);
         run(std::true_type{}, u1, m_end);
       }
+    } else {
+      // A tile with no query block (causal broadcast keys past the queries).
+      if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
+      if (DYN) barrier_lds();
+      handoff();
     }
 
     // Tile end: the next tile's K / V loads, then this tile's stores.
@@ -770,7 +799,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
 // For a sequence with at most BWD_BN keys, delta_i = sum_k P_ik dP_ik from
 // fp32 P and dP (the same quantity as rowsum(dO o O), without the bf16
 // rounding of the stored O, which dominates the dK and dQ error when P is
-// large).  One workgroup: 128 query rows of one (sequence, head); wave w takes
+// large).  With the causal mask the same holds for the first BWD_BN query
+// rows of any sequence: they see only keys below BWD_BN, and few of them, so
+// their P is large too (in broadcast mode their dQ then sums such rows over
+// every sequence).  One workgroup: 128 query rows of one (sequence, head); wave w takes
 // rows 32w .. 32w+31 with the transposed score layout S^T = K Q^T (lane ->
 // query, registers -> keys), so each lane sums its registers and the two
 // halves of the wave are added.
@@ -780,7 +812,9 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
   const int b = blockIdx.x, h = blockIdx.y;
   int64_t s0;
   const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
-  if (L == 0 || L > BWD_BN) return;
+  if (L == 0 || (L > BWD_BN && !(CAUSAL && blockIdx.z == 0))) return;
+  static_assert(BWD_BN == 128, "the causal rows of block 0 see keys below 128 only");
+  const int Lk = min(L, BWD_BN);  // keys any row of this workgroup sees
   const int H = a.H, Lq = a.Lq;
   const int nq = BCAST ? Lq : L;
   const int wave = threadIdx.x / WAVE, l = threadIdx.x % WAVE, g = l / 32, lc = l % 32;
@@ -800,8 +834,8 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
   const float ls2 = a.lse2[ri];
   const float c2 = a.scale_log2;
   float acc = 0.f;
-  for (int kt = 0; kt * 32 < L; ++kt) {
-    const int key = min(kt * 32 + lc, L - 1);
+  for (int kt = 0; kt * 32 < Lk; ++kt) {
+    const int key = min(kt * 32 + lc, Lk - 1);
     const uint16_t* kr = a.k + ((s0 + key) * H + h) * (int64_t)D;
     const uint16_t* vr = a.v + ((s0 + key) * H + h) * (int64_t)D;
     f32x16 st = f32x16{}, dpt = f32x16{};
@@ -815,7 +849,7 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk = kt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-      bool ok = kk < L;
+      bool ok = kk < Lk;
       if (CAUSAL) ok = ok && kk <= q;
       const float p = ok ? fast_exp2(st[i] * c2 - ls2) : 0.f;
       acc += p * dpt[i];

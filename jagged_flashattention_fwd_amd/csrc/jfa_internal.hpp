@@ -89,8 +89,10 @@ struct BwdArgs {
   int dq_chunks;          // NC
   const TileRec* ktiles;  // key-block tiles (dK/dV kernel)
   const int64_t* n_ktiles;
+  unsigned int* ktile_ctr;  // key tiles handed out past the zigzag ones (starts at 0)
   const TileRec* qtiles;  // query-block tiles (self-attention dQ kernel)
   const int64_t* n_qtiles;
+  unsigned int* qtile_ctr;  // query tiles handed out past the first one per workgroup
   int B, H, Lq, d;
   int64_t total_len;
   float scale;

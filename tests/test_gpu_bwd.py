@@ -95,6 +95,39 @@ def test_bwd_bitwise_deterministic(jfa, bq, causal):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("bq,causal", [(True, True), (False, True), (False, False)])
+def test_bwd_dynamic_handout_reused_workspace(jfa, bq, causal):
+    """Causal or self-attention tiles come from hand-out counters past each
+    workgroup's first zigzag tiles: with more tiles than that, three calls on
+    one workspace into NaN-filled outputs must each cover every tile once and
+    agree bitwise, and match the oracle."""
+    rng = np.random.default_rng(33)
+    lengths = [int(x) for x in rng.integers(1, 300 if not bq else 400, size=500)]
+    H, d, Lq = 2, 128, (200 if bq else 0)
+    t = wl.make_tensors(lengths, H, d, Lq, bq, seed=33, device="cuda")
+    B, T = len(lengths), int(sum(lengths))
+    assert H * sum(-(-L // 128) for L in lengths) > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    scale = 0.09
+    out, lse = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], scale, causal, bq)
+    ws = jfa.workspace(T, B, H, Lq, d, causal, bq, 1, "cuda")
+    res = []
+    for _ in range(3):
+        dq = torch.full(tuple(t["q"].shape), float("nan"), dtype=torch.float32, device="cuda")
+        dk = torch.full((T, H, d), float("nan"), dtype=torch.float32, device="cuda")
+        dv = torch.full((T, H, d), float("nan"), dtype=torch.float32, device="cuda")
+        jfa.jfa_bwd(t["q"], t["k"], t["v"], t["offsets"], B, H, Lq, d, scale, causal, bq, out, lse, t["dout"],
+                    dq, dk, dv, T, ws)
+        torch.cuda.synchronize()
+        res.append((dq, dk, dv))
+    for r in res[1:]:
+        for x, y in zip(res[0], r):
+            assert torch.equal(x, y)
+    rq, rk, rv = jo.jagged_backward(to64(t["q"]), to64(t["k"]), to64(t["v"]), t["offsets"].cpu().numpy(), scale,
+                                    causal, bq, to64(t["dout"]))
+    for name, got, ref in (("dQ", res[0][0], rq), ("dK", res[0][1], rk), ("dV", res[0][2], rv)):
+        compare(name, to64(got), ref)
+
+
 def test_bwd_single_key_dv_is_column_sum_of_dout(jfa):
     # One key: P = 1 for every query, so dV = sum of dO over the query rows
     # and dK = 0 (dS = P (dP - delta) = 0 when delta = dP).
