@@ -73,11 +73,11 @@ def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q
     if kernel == "fwd_kernel":
         return 2 * kv + q_bytes + row_bf16 + rows * 4
     if kernel == "delta_kernel":
-        # O, dO, lse in; delta, lse*log2(e) out
-        return 2 * row_bf16 + 3 * rows * 4
+        # O, dO, lse in; delta, lse*log2(e) and the two 16-byte row terms out
+        return 2 * row_bf16 + 3 * rows * 4 + 2 * rows * 16
     if kernel == "dkdv_kernel":
-        # K, V, Q, dO, lse*log2(e), delta in; dK, dV (fp32) out
-        return 2 * kv + q_bytes + row_bf16 + 2 * rows * 4 + 2 * T * H * d * 4
+        # K, V, Q, dO, the two 16-byte row terms in; dK, dV (fp32) out
+        return 2 * kv + q_bytes + row_bf16 + 2 * rows * 16 + 2 * T * H * d * 4
     if kernel == "dq_kernel":
         # K, V, Q, dO, lse, delta in; dQ (self) or the fp32 partials (broadcast) out
         b = 2 * kv + q_bytes + row_bf16 + 2 * rows * 4

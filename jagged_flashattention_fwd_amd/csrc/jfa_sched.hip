@@ -30,41 +30,75 @@ __device__ __forceinline__ int64_t tiles_of(int64_t L, int H, int Lq, int broadc
   return (int64_t)H * cdiv64(L, blk);
 }
 
-// Single workgroup: bitonic sort of N = 2^k keys in LDS, then a chunked
-// exclusive scan of the per-sequence tile counts.
+// Single workgroup: bitonic sort of N = 2^k keys, then a chunked exclusive
+// scan of the per-sequence tile counts.  Thread t holds keys c * 1024 + t;
+// compare-exchange stages between lanes of one wave go through register
+// shuffles, the others through LDS (two barriers each), so a sort of N keys
+// takes 2 log2(N / 64) (log2(N / 64) + 1) / 2 barriers instead of one per
+// stage.
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int m) {
+  const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)x, m);
+  const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(x >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// New value of element i after the stage (k, j) compare-exchange with its
+// partner i ^ j holding y: the lower index of an ascending (i & k == 0) pair
+// keeps the minimum.
+__device__ __forceinline__ unsigned long long bitonic_pick(int i, int k, int j, unsigned long long x,
+                                                           unsigned long long y) {
+  const bool up = (i & k) == 0, lower = (i & j) == 0;
+  const unsigned long long mn = x < y ? x : y, mx = x < y ? y : x;
+  return lower == up ? mn : mx;
+}
+
 __global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Schedule s, int N) {
   extern __shared__ __attribute__((aligned(16))) unsigned long long keys[];
-  __shared__ int64_t part[SORT_THREADS];
+  __shared__ int64_t wsum[SORT_THREADS / WAVE];
+  constexpr int EMAX = MAX_B / SORT_THREADS;
   const int tid = threadIdx.x;
   const int B = a.B;
-  for (int i = tid; i < N; i += SORT_THREADS) {
+  const int E = (N + SORT_THREADS - 1) / SORT_THREADS;  // keys per thread
+  unsigned long long v[EMAX];
+#pragma unroll
+  for (int c = 0; c < EMAX; ++c) {
+    const int i = c * SORT_THREADS + tid;
     unsigned long long k = ~0ull;
-    if (i < B) {
+    if (c < E && i < B) {
       int64_t s0;
       const int64_t L = seq_range(a.offsets, i, a.total_len, &s0);
       unsigned long long Lc = L > 0xffffffffll ? 0xffffffffull : (unsigned long long)L;
       k = ((0xffffffffull - Lc) << 32) | (unsigned long long)i;
     }
-    keys[i] = k;
+    v[c] = k;
   }
-  __syncthreads();
   for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += SORT_THREADS) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = keys[i], y = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
+    int j = k >> 1;
+    for (; j >= WAVE; j >>= 1) {
+#pragma unroll
+      for (int c = 0; c < EMAX; ++c)
+        if (c < E && c * SORT_THREADS + tid < N) keys[c * SORT_THREADS + tid] = v[c];
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < EMAX; ++c) {
+        const int i = c * SORT_THREADS + tid;
+        if (c < E && i < N) v[c] = bitonic_pick(i, k, j, v[c], keys[i ^ j]);
       }
       __syncthreads();
     }
+    for (; j > 0; j >>= 1) {
+#pragma unroll
+      for (int c = 0; c < EMAX; ++c) {
+        const int i = c * SORT_THREADS + tid;
+        if (c < E) v[c] = bitonic_pick(i, k, j, v[c], shfl_xor_u64(v[c], j));
+      }
+    }
   }
-  // Chunked exclusive scan over ranks 0..B-1.
+#pragma unroll
+  for (int c = 0; c < EMAX; ++c)
+    if (c < E && c * SORT_THREADS + tid < N) keys[c * SORT_THREADS + tid] = v[c];
+  __syncthreads();
+  // Chunked exclusive scan over ranks 0..B-1: a shuffle scan inside each
+  // wave, then the totals of the waves before.
   const int per = (B + SORT_THREADS - 1) / SORT_THREADS;
   const int r0 = tid * per, r1 = min(B, r0 + per);
   int64_t local = 0;
@@ -74,17 +108,22 @@ __global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Sch
     int64_t s0;
     local += tiles_of(seq_range(a.offsets, b, a.total_len, &s0), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
   }
-  part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < SORT_THREADS; off <<= 1) {
-    const int64_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  const int lane = tid % WAVE, wv = tid / WAVE;
+  int64_t incl = local;
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const int64_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
+  if (lane == WAVE - 1) wsum[wv] = incl;
+  __syncthreads();
+  int64_t before = 0;
+  for (int w = 0; w < wv; ++w) before += wsum[w];
+  int64_t total = 0;
+  for (int w = 0; w < SORT_THREADS / WAVE; ++w) total += wsum[w];
   // Positions are clamped to the list's capacity, which well-formed offsets
   // never reach.
-  int64_t run = part[tid] - local;  // exclusive prefix of this chunk
+  int64_t run = before + incl - local;  // exclusive prefix of this chunk
   for (int r = r0; r < r1; ++r) {
     s.cum[r] = run < s.max_tiles ? run : s.max_tiles;
     const int b = (int)(keys[r] & 0xffffffffull);
@@ -92,7 +131,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Sch
     run += tiles_of(seq_range(a.offsets, b, a.total_len, &s0), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
   }
   if (tid == SORT_THREADS - 1) {
-    const int64_t T = part[tid] < s.max_tiles ? part[tid] : s.max_tiles;
+    const int64_t T = total < s.max_tiles ? total : s.max_tiles;
     s.cum[B] = T;
     s.n_tiles[0] = T;
     s.n_tiles[1] = 0;  // the forward's dynamic hand-out counter
@@ -142,7 +181,7 @@ __global__ __launch_bounds__(256) void sched_dump(Schedule s, int P, int32_t* ou
 }  // namespace
 
 hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t stream) {
-  int N = 1;
+  int N = WAVE;  // at least one wave of keys: the shuffle stages span whole waves
   while (N < a.B) N <<= 1;
   static bool attr_set = false;
   if (!attr_set) {
