@@ -28,13 +28,19 @@ Readings where the pages are silent (each also listed in the design notes):
   * The backward is the exact derivative of the forward: dP = dO V^T,
     delta_i = sum_d dO_id O_id, dS = P o (dP - delta), dQ = scale dS K,
     dK = scale dS^T Q, dV = P^T dO.  The pages do not print it.
+  * Grouped-query attention ([JFA] "3. Attention Variants: the flexibility
+    of TLX", block-sparse part, and "Conclusion" name GQA support without
+    defining it): with H query heads and H_kv = H / G key/value heads, query
+    head h attends with key/value head h // G (consecutive query heads share
+    one), so that head's dK and dV are the sums over its G query heads.
 
 Layouts (numpy arrays, any float dtype; converted to float64 on entry):
-  k, v         [T, H, d], T = offsets[-1]
+  k, v         [T, H_kv, d], T = offsets[-1]; H_kv divides H (H_kv = H: plain
+               multi-head attention)
   broadcast:   q [H, Lq, d]; out, dout [B, H, Lq, d]; lse [B, H, Lq];
                dq [H, Lq, d] (sum over sequences)
   self:        q, out, dout, dq [T, H, d]; lse [T, H]
-  dk, dv       [T, H, d]
+  dk, dv       [T, H_kv, d]
 """
 from __future__ import annotations
 
@@ -99,6 +105,13 @@ def sequence_backward(qb, kb, vb, dob, scale: float, causal: bool):
     return scale * (ds @ kb), scale * (ds.T @ qb), p.T @ dob
 
 
+def _group(H: int, H_kv: int) -> int:
+    """Query heads per key/value head."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"{H} query heads do not split into groups over {H_kv} key/value heads")
+    return H // H_kv
+
+
 def _seq_bounds(offsets):
     off = np.asarray(offsets, dtype=np.int64)
     return [(int(off[b]), int(off[b + 1])) for b in range(off.size - 1)]
@@ -112,7 +125,8 @@ def jagged_forward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bo
     q, k, v = _f64(q), _f64(k), _f64(v)
     bounds = _seq_bounds(offsets)
     B = len(bounds)
-    H, d = k.shape[1], k.shape[2]
+    H = q.shape[0] if broadcast_q else q.shape[1]
+    G = _group(H, k.shape[1])
     if broadcast_q:
         Lq = q.shape[1]
         out = np.zeros((B, H, Lq, v.shape[2]))
@@ -123,7 +137,7 @@ def jagged_forward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bo
     for b, (s0, s1) in enumerate(bounds):
         for h in range(H):
             qb = q[h] if broadcast_q else q[s0:s1, h]
-            o, ls, _ = sequence_forward(qb, k[s0:s1, h], v[s0:s1, h], scale, causal)
+            o, ls, _ = sequence_forward(qb, k[s0:s1, h // G], v[s0:s1, h // G], scale, causal)
             if broadcast_q:
                 out[b, h], lse[b, h] = o, ls
             else:
@@ -136,21 +150,22 @@ def jagged_backward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: b
     per-sequence dQ over the whole batch ([JFA] "1. The Challenge")."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     bounds = _seq_bounds(offsets)
-    H = k.shape[1]
+    H = q.shape[0] if broadcast_q else q.shape[1]
+    G = _group(H, k.shape[1])
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for b, (s0, s1) in enumerate(bounds):
         for h in range(H):
+            kb, vb = k[s0:s1, h // G], v[s0:s1, h // G]
             if broadcast_q:
-                g = sequence_backward(q[h], k[s0:s1, h], v[s0:s1, h], dout[b, h], scale, causal)
+                g = sequence_backward(q[h], kb, vb, dout[b, h], scale, causal)
                 dq[h] += g[0]
             else:
-                g = sequence_backward(q[s0:s1, h], k[s0:s1, h], v[s0:s1, h], dout[s0:s1, h],
-                                      scale, causal)
+                g = sequence_backward(q[s0:s1, h], kb, vb, dout[s0:s1, h], scale, causal)
                 dq[s0:s1, h] = g[0]
-            dk[s0:s1, h] = g[1]
-            dv[s0:s1, h] = g[2]
+            dk[s0:s1, h // G] += g[1]
+            dv[s0:s1, h // G] += g[2]
     return dq, dk, dv
 
 
@@ -161,13 +176,14 @@ def broadcast_dq_rows(q, k, v, offsets, scale: float, causal: bool, dout, rows):
     ds = p o (dO_b[i] V_b^T - delta), dQ[h,i] = scale * sum_b ds K_b."""
     out = []
     bounds = _seq_bounds(offsets)
+    G = _group(q.shape[0], k.shape[1])
     for (h, i) in rows:
         qi = _f64(q[h, i:i + 1])
         acc = np.zeros(q.shape[2])
         for b, (s0, s1) in enumerate(bounds):
             if s1 == s0:
                 continue
-            kb, vb = _f64(k[s0:s1, h]), _f64(v[s0:s1, h])
+            kb, vb = _f64(k[s0:s1, h // G]), _f64(v[s0:s1, h // G])
             s = scale * (qi @ kb.T)[0]
             if causal:
                 s = np.where(np.arange(s1 - s0) <= i, s, -np.inf)

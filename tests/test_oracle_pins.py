@@ -128,13 +128,68 @@ def test_online_recurrence_matches_materialised(n, L, BM, BN, causal):
 
 
 # ---------------------------------------------------------------- P5 ------
-def _sdpa(q, k, v, scale, mask=None, causal=False):
-    """fp64 CPU SDPA with autograd; q [..., n, d], k/v [..., L, d]."""
+def _sdpa(q, k, v, scale, mask=None, causal=False, gqa=False):
+    """fp64 CPU SDPA with autograd; q [..., n, d], k/v [..., L, d] (gqa: k/v
+    with fewer heads, torch's own grouped-query mapping)."""
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
     o = torch.nn.functional.scaled_dot_product_attention(
         tq, tk, tv, attn_mask=None if mask is None else torch.tensor(mask),
-        is_causal=causal, scale=scale)
+        is_causal=causal, scale=scale, enable_gqa=gqa)
     return o, (tq, tk, tv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (6, 1), (3, 3)])
+def test_gqa_self_mode_is_sdpa_grouped_query(causal, H, H_kv):
+    """Grouped-query attention: B equal-length sequences in self mode against
+    torch's SDPA with enable_gqa (its own head mapping and its autograd sums
+    dK / dV over each group)."""
+    B, L, d = 2, 7, 5
+    scale = 0.4
+    off = _offsets([L] * B)
+    q, dout = _rand(B * L, H, d), _rand(B * L, H, d)
+    k, v = _rand(B * L, H_kv, d), _rand(B * L, H_kv, d)
+    out, lse = jo.jagged_forward(q, k, v, off, scale, causal, False)
+    dq, dk, dv = jo.jagged_backward(q, k, v, off, scale, causal, False, dout)
+    dense = lambda x: x.reshape(B, L, x.shape[1], d).transpose(0, 2, 1, 3).copy()  # noqa: E731
+    packed = lambda x: x.transpose(0, 2, 1, 3).reshape(B * L, x.shape[1], d)  # noqa: E731
+    o_ref, (tq, tk, tv) = _sdpa(dense(q), dense(k), dense(v), scale, causal=causal, gqa=True)
+    np.testing.assert_allclose(out, packed(o_ref.detach().numpy()), rtol=1e-12, atol=1e-12)
+    o_ref.backward(torch.tensor(dense(dout)))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, packed(t.grad.numpy()), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_broadcast_is_sdpa_grouped_query(causal):
+    """Broadcast mode with grouped-query heads: equal lengths against SDPA
+    with the dense Q repeated over the batch and enable_gqa."""
+    B, H, H_kv, Lq, L, d = 3, 4, 2, 5, 8, 6
+    scale = 1 / math.sqrt(d)
+    off = _offsets([L] * B)
+    k, v = _rand(B * L, H_kv, d), _rand(B * L, H_kv, d)
+    q = _rand(H, Lq, d)
+    dout = _rand(B, H, Lq, d)
+    out, _ = jo.jagged_forward(q, k, v, off, scale, causal, True)
+    dq, dk, dv = jo.jagged_backward(q, k, v, off, scale, causal, True, dout)
+    kd = k.reshape(B, L, H_kv, d).transpose(0, 2, 1, 3)
+    vd = v.reshape(B, L, H_kv, d).transpose(0, 2, 1, 3)
+    qd = np.broadcast_to(q, (B, H, Lq, d)).copy()
+    mask = np.tril(np.ones((Lq, L), dtype=bool)) if causal else None
+    o_ref, (tq, tk, tv) = _sdpa(qd, kd, vd, scale, mask=mask, gqa=True)
+    np.testing.assert_allclose(out, o_ref.detach().numpy(), rtol=1e-12, atol=1e-12)
+    o_ref.backward(torch.tensor(dout))
+    np.testing.assert_allclose(dq, tq.grad.sum(0).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy().transpose(0, 2, 1, 3).reshape(B * L, H_kv, d),
+                               rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy().transpose(0, 2, 1, 3).reshape(B * L, H_kv, d),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_gqa_rejects_heads_that_do_not_split():
+    off = _offsets([3])
+    with pytest.raises(ValueError):
+        jo.jagged_forward(_rand(3, 4, 2), _rand(3, 3, 2), _rand(3, 3, 2), off, 1.0, False, False)
 
 
 @pytest.mark.parametrize("causal", [False, True])
