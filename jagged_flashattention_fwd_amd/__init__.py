@@ -31,6 +31,15 @@ _SIGS = {
                            _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
                            _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                            _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_workspace_size_gqa": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                          _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
+    "jfa_fwd_gqa": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                               _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
+                               _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_bwd_gqa": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                               _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
+                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                               _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "jfa_schedule_params": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_int),
                                        _c.POINTER(_c.c_int)]),
     "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -90,6 +99,29 @@ def jfa_workspace_size(total_len, B, H, Lq, d, causal, broadcast_q, pass_) -> in
     _check(lib().jfa_workspace_size(int(total_len), B, H, Lq, d, int(causal), int(broadcast_q), pass_,
                                     ctypes.byref(out)), "jfa_workspace_size")
     return out.value
+
+
+def jfa_workspace_size_gqa(total_len, B, H, H_kv, Lq, d, causal, broadcast_q, pass_) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jfa_workspace_size_gqa(int(total_len), B, H, H_kv, Lq, d, int(causal), int(broadcast_q),
+                                        pass_, ctypes.byref(out)), "jfa_workspace_size_gqa")
+    return out.value
+
+
+def jfa_fwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, total_len,
+                workspace, stream=None):
+    _check(lib().jfa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
+                             int(causal), int(broadcast_q), _ptr(out), _ptr(lse), int(total_len),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream)), "jfa_fwd_gqa")
+
+
+def jfa_bwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
+                total_len, workspace, stream=None):
+    _check(lib().jfa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
+                             int(causal), int(broadcast_q), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                             _ptr(dk), _ptr(dv), int(total_len), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_bwd_gqa")
 
 
 def jfa_schedule_params(pass_, causal, broadcast_q, d):
@@ -156,22 +188,25 @@ def kernel_times():
 
 # --------------------------------------------- allocating helpers --------
 def _shape_args(q, k, offsets, broadcast_q):
-    T, H, d = k.shape
+    """(B, H, H_kv, Lq, d, T): query heads from q, key / value heads from k."""
+    T, H_kv, d = k.shape
     B = offsets.numel() - 1
+    H = q.shape[0] if broadcast_q else q.shape[1]
     Lq = q.shape[1] if broadcast_q else 0
-    return B, H, Lq, d, T
+    return B, H, H_kv, Lq, d, T
 
 
-def workspace(total_len, B, H, Lq, d, causal, broadcast_q, pass_, device):
+def workspace(total_len, B, H, Lq, d, causal, broadcast_q, pass_, device, H_kv=None):
     import torch
-    n = jfa_workspace_size(total_len, B, H, Lq, d, causal, broadcast_q, pass_)
+    n = jfa_workspace_size_gqa(total_len, B, H, H if H_kv is None else H_kv, Lq, d, causal, broadcast_q, pass_)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def attention_fwd(q, k, v, offsets, scale, causal=False, broadcast_q=True, ws=None):
-    """(out bf16, lse fp32) of jagged attention; see include/jfa.h for layouts."""
+    """(out bf16, lse fp32) of jagged attention; see include/jfa.h for layouts
+    (k / v with fewer heads than q: grouped-query attention)."""
     import torch
-    B, H, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
+    B, H, H_kv, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
     if broadcast_q:
         out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=k.device)
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=k.device)
@@ -179,20 +214,21 @@ def attention_fwd(q, k, v, offsets, scale, causal=False, broadcast_q=True, ws=No
         out = torch.empty((T, H, d), dtype=torch.bfloat16, device=k.device)
         lse = torch.empty((T, H), dtype=torch.float32, device=k.device)
     if ws is None:
-        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 0, k.device)
-    jfa_fwd(q, k, v, offsets, B, H, Lq, d, scale, causal, broadcast_q, out, lse, T, ws)
+        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 0, k.device, H_kv)
+    jfa_fwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, T, ws)
     return out, lse
 
 
 def attention_bwd(q, k, v, offsets, scale, causal, broadcast_q, out, lse, dout, ws=None):
-    """(dq, dk, dv) fp32 of jagged attention; see include/jfa.h for layouts."""
+    """(dq, dk, dv) fp32 of jagged attention; see include/jfa.h for layouts
+    (dk / dv with k's head count)."""
     import torch
-    B, H, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
+    B, H, H_kv, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
     dq = torch.empty(q.shape, dtype=torch.float32, device=k.device)
-    dk = torch.empty((T, H, d), dtype=torch.float32, device=k.device)
-    dv = torch.empty((T, H, d), dtype=torch.float32, device=k.device)
+    dk = torch.empty((T, H_kv, d), dtype=torch.float32, device=k.device)
+    dv = torch.empty((T, H_kv, d), dtype=torch.float32, device=k.device)
     if ws is None:
-        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 1, k.device)
-    jfa_bwd(q, k, v, offsets, B, H, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv, T,
-            ws)
+        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 1, k.device, H_kv)
+    jfa_bwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
+                T, ws)
     return dq, dk, dv

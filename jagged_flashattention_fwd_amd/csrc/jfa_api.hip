@@ -66,6 +66,7 @@ struct Layout {
   size_t sched_b[4];
   int64_t cap_a = 0, cap_b = 0;
   size_t delta = 0, lse2 = 0, term_l = 0, term_d = 0, dq_part = 0;
+  size_t dk_heads = 0, dv_heads = 0;  // grouped heads: dK / dV per query head before the group sum
   size_t total = 0;
 };
 
@@ -76,7 +77,7 @@ void place_schedule(size_t* at, size_t off[4], int B, int64_t cap) {
   off[3] = *at; *at = align256(*at + sizeof(TileRec) * (size_t)cap);
 }
 
-Layout layout(int pass, int64_t total_len, int B, int H, int Lq, int d, int broadcast_q, int P) {
+Layout layout(int pass, int64_t total_len, int B, int H, int Hkv, int Lq, int d, int broadcast_q, int P) {
   Layout L;
   size_t at = 0;
   if (pass == 0) {
@@ -99,6 +100,10 @@ Layout layout(int pass, int64_t total_len, int B, int H, int Lq, int d, int broa
       dq_split(B, H, Lq, P, &n_qb, &nc);
       L.dq_part = at;
       at = align256(at + sizeof(float) * (size_t)H * n_qb * nc * DQ_BM_BCAST * d);
+    }
+    if (Hkv < H) {
+      L.dk_heads = at; at = align256(at + sizeof(float) * (size_t)total_len * H * d);
+      L.dv_heads = at; at = align256(at + sizeof(float) * (size_t)total_len * H * d);
     }
   }
   L.total = at;
@@ -126,6 +131,12 @@ int check_sizes(int64_t total_len, int B, int H, int Lq, int d, int broadcast_q)
   if (total_len > (int64_t)INT32_MAX || (broadcast_q && (int64_t)Lq * H > (int64_t)INT32_MAX))
     return JFA_ERR_UNSUPPORTED;
   if (H > 65535) return JFA_ERR_UNSUPPORTED;
+  return JFA_OK;
+}
+
+// Grouped heads: H_kv key / value heads, each shared by H / H_kv query heads.
+int check_heads(int H, int Hkv) {
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return JFA_ERR_INVALID_ARG;
   return JFA_OK;
 }
 
@@ -165,22 +176,29 @@ int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block
   return workers(pass, workers_out);
 }
 
-int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q,
-                       int pass, size_t* bytes) {
+int jfa_workspace_size_gqa(int64_t total_len, int B, int H, int H_kv, int Lq, int d, int causal,
+                           int broadcast_q, int pass, size_t* bytes) {
   (void)causal;
   if (!bytes || (pass != 0 && pass != 1)) return JFA_ERR_INVALID_ARG;
   int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
   if (rc != JFA_OK) return rc;
+  rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
   int P = 0;
   rc = workers(pass, &P);
   if (rc != JFA_OK) return rc;
-  *bytes = layout(pass, total_len, B, H, Lq, d, broadcast_q, P).total;
+  *bytes = layout(pass, total_len, B, H, H_kv, broadcast_q ? Lq : 0, d, broadcast_q, P).total;
   return JFA_OK;
 }
 
-int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
-            int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
-            void* workspace, size_t workspace_bytes, void* stream) {
+int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q,
+                       int pass, size_t* bytes) {
+  return jfa_workspace_size_gqa(total_len, B, H, H, Lq, d, causal, broadcast_q, pass, bytes);
+}
+
+int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+                int Lq, int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !offsets || !out || !lse || !workspace) return JFA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 7))
@@ -188,11 +206,13 @@ int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
   int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
   if (rc != JFA_OK) return rc;
+  rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
   if (!broadcast_q) Lq = 0;
   int P = 0;
   rc = workers(0, &P);
   if (rc != JFA_OK) return rc;
-  const Layout lay = layout(0, total_len, B, H, Lq, d, broadcast_q, P);
+  const Layout lay = layout(0, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
   if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -213,6 +233,7 @@ int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   fa.tile_ctr = reinterpret_cast<unsigned int*>(s.n_tiles + 1);
   fa.total_len = total_len;
   fa.B = B; fa.H = H; fa.Lq = Lq; fa.d = d;
+  fa.Hkv = H_kv; fa.G = H / H_kv;
   fa.scale_log2 = scale * 1.4426950408889634f;
   fa.causal = causal ? 1 : 0;
   fa.broadcast_q = broadcast_q ? 1 : 0;
@@ -221,10 +242,17 @@ int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   return JFA_OK;
 }
 
-int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
-            int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
-            const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
-            size_t workspace_bytes, void* stream) {
+int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
+            int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  return jfa_fwd_gqa(q, k, v, offsets, B, H, H, Lq, d, scale, causal, broadcast_q, out, lse, total_len,
+                     workspace, workspace_bytes, stream);
+}
+
+int jfa_bwd_gqa(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+                int Lq, int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
     return JFA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
@@ -234,11 +262,13 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
   int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
   if (rc != JFA_OK) return rc;
+  rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
   if (!broadcast_q) Lq = 0;
   int P = 0;
   rc = workers(1, &P);
   if (rc != JFA_OK) return rc;
-  const Layout lay = layout(1, total_len, B, H, Lq, d, broadcast_q, P);
+  const Layout lay = layout(1, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
   if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -259,7 +289,12 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   ba.out = static_cast<const uint16_t*>(out);
   ba.lse = lse;
   ba.dout = static_cast<const uint16_t*>(dout);
-  ba.dq = dq; ba.dk = dk; ba.dv = dv;
+  // Grouped heads: the dK / dV kernel writes one slice per query head, summed
+  // over each group afterwards.
+  const bool grouped = H_kv < H;
+  ba.dq = dq;
+  ba.dk = grouped ? reinterpret_cast<float*>(ws + lay.dk_heads) : dk;
+  ba.dv = grouped ? reinterpret_cast<float*>(ws + lay.dv_heads) : dv;
   ba.delta = reinterpret_cast<float*>(ws + lay.delta);
   ba.lse2 = reinterpret_cast<float*>(ws + lay.lse2);
   ba.term_l = reinterpret_cast<uint16_t*>(ws + lay.term_l);
@@ -276,6 +311,7 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   ba.n_qtiles = broadcast_q ? nullptr : sq.n_tiles;
   ba.qtile_ctr = broadcast_q ? nullptr : reinterpret_cast<unsigned int*>(sq.n_tiles + 1);
   ba.B = B; ba.H = H; ba.Lq = Lq; ba.d = d;
+  ba.Hkv = H_kv; ba.G = H / H_kv;
   ba.total_len = total_len;
   ba.scale = scale;
   ba.scale_log2 = scale * 1.4426950408889634f;
@@ -284,7 +320,19 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
   ba.P = P;
   ba.P_dq = P;
   if (launch_bwd(ba, st) != hipSuccess) return JFA_ERR_HIP;
+  if (grouped) {
+    if (launch_group_sum(ba.dk, dk, total_len, H, H_kv, d, st) != hipSuccess) return JFA_ERR_HIP;
+    if (launch_group_sum(ba.dv, dv, total_len, H, H_kv, d, st) != hipSuccess) return JFA_ERR_HIP;
+  }
   return JFA_OK;
+}
+
+int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
+            int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
+            const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  return jfa_bwd_gqa(q, k, v, offsets, B, H, H, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
+                     total_len, workspace, workspace_bytes, stream);
 }
 
 int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q, int pass,
@@ -300,7 +348,7 @@ int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal,
   int P = 0;
   rc = workers(pass, &P);
   if (rc != JFA_OK) return rc;
-  const Layout lay = layout(pass, total_len, B, H, Lq, 64, broadcast_q, P);
+  const Layout lay = layout(pass, total_len, B, H, H, Lq, 64, broadcast_q, P);
   if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const Schedule s = schedule_at(static_cast<char*>(workspace), lay.sched_a, lay.cap_a);

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
   const int wave = tid / WAVE, l = tid % WAVE, g = l / 32, lc = l % 32;
   const PadRowCopy pc;
   const int H = a.H;
-  const int64_t ld = (int64_t)H * D;
+  const int64_t ld = (int64_t)a.Hkv * D;  // K / V row stride
   const float c2 = a.scale_log2;
 
   bf16x8 qreg[KS], doreg[KS];
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     const int n_bulk = CAUSAL ? min(q0 / BN, L / BN) : L / BN;
-    const uint16_t* kbase = a.k + (s0 * H + h) * (int64_t)D;
-    const uint16_t* vbase = a.v + (s0 * H + h) * (int64_t)D;
+    const uint16_t* kbase = a.k + (s0 * a.Hkv + h / a.G) * (int64_t)D;
+    const uint16_t* vbase = a.v + (s0 * a.Hkv + h / a.G) * (int64_t)D;
     auto issue = [&](int j) {
       constexpr int RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
       const int base_row = min(j * BN + wave * RPW, L - 1);
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
   const int l = tid % WAVE, g = l / 32, lc = l % 32;
   const PadRowCopy pc;
   const int H = a.H, Lq = a.Lq, B = a.B;
-  const int64_t ld = (int64_t)H * D;
+  const int64_t ld = (int64_t)a.Hkv * D;  // K / V row stride
   const float c2 = a.scale_log2;
 
   const int NC = a.dq_chunks, n_qb = a.dq_qblocks;
@@ -520,8 +520,8 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     const int b = a.seq_order[r];
     q.L = (int)seq_range(a.offsets, b, a.total_len, &q.s0);
     q.row = ((int64_t)b * H + h) * Lq;
-    q.kb = a.k + (q.s0 * H + h) * (int64_t)D;
-    q.vb = a.v + (q.s0 * H + h) * (int64_t)D;
+    q.kb = a.k + (q.s0 * a.Hkv + h / a.G) * (int64_t)D;
+    q.vb = a.v + (q.s0 * a.Hkv + h / a.G) * (int64_t)D;
     int kv_end = q.L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     q.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
@@ -753,6 +753,25 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     }
 }
 
+// ------------------------------------------------------- group sum ----
+// Grouped-query heads: the dK / dV of a key / value head is the sum over the
+// query heads that share it, taken here in ascending head order from the
+// per-query-head slices the dK / dV kernel wrote.  One thread per 16 bytes of
+// the output.
+__global__ __launch_bounds__(256) void group_sum_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst,
+                                                        int64_t n, int Hkv, int G, int D4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const int64_t t = e / ((int64_t)Hkv * D4);
+    const int rem = (int)(e - t * Hkv * D4);
+    const int hk = rem / D4, c = rem - hk * D4;
+    const f32x4* s = src + (t * Hkv * G + (int64_t)hk * G) * D4 + c;
+    f32x4 acc = s[0];
+    for (int i = 1; i < G; ++i) acc += s[(int64_t)i * D4];
+    dst[e] = acc;
+  }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   const int64_t rows = a.broadcast_q ? (int64_t)a.B * a.H * a.Lq : a.total_len * a.H;
@@ -815,6 +834,17 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_group_sum(const float* src, float* dst, int64_t total_len, int H, int Hkv, int d,
+                            hipStream_t stream) {
+  const int64_t n = total_len * Hkv * (d / 4);
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 4096 ? want : 4096);
+  JFA_TIMED_LAUNCH(K_GROUP_SUM, stream, group_sum_kernel, dim3(blocks), dim3(256), 0, stream,
+                   reinterpret_cast<const f32x4*>(src), reinterpret_cast<f32x4*>(dst), n, Hkv, H / Hkv, d / 4);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.broadcast_q && a.dq_chunks > MAXP) return hipErrorInvalidValue;

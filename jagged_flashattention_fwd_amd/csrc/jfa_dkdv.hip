@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   // wave's row terms of -lse / scale (even waves) or -delta (odd waves).
   struct Tp {
     int64_t s0;
-    int L, h, b, k0, m_first, m_end, nq;
+    int L, h, hk, b, k0, m_first, m_end, nq;  // hk: the key / value head of query head h
     const uint16_t* qb;
     const uint16_t* db;
     const u32x4* vb;
@@ -230,6 +230,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     p.s0 = r.s0;
     p.L = r.L;
     p.h = r.h;
+    p.hk = r.h / a.G;
     p.b = r.b;
     p.k0 = r.blk * BN;
     p.nq = BCAST ? Lq : r.L;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   u32x4 kraw[KS], vraw[KS];
   auto load_rows = [&](const Tp& p, const uint16_t* base, u32x4 (&x)[KS]) {
     const int kc = min(p.k0 + wave * 32 + lc, p.L - 1);
-    const uint16_t* r = base + ((p.s0 + kc) * H + p.h) * (int64_t)D + g * 8;
+    const uint16_t* r = base + ((p.s0 + kc) * a.Hkv + p.hk) * (int64_t)D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) x[ks] = *reinterpret_cast<const u32x4*>(r + ks * 16);
   };
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   constexpr int VDMA = D == 128 ? 8 : 0;  // copies per wave (4 rows each)
   auto issue_v_next = [&](const Tp& p) {
     if constexpr (VDMA > 0) {
-      const uint16_t* vb = a.v + ((p.s0 + p.k0) * H + p.h) * (int64_t)D;
+      const uint16_t* vb = a.v + ((p.s0 + p.k0) * a.Hkv + p.hk) * (int64_t)D;
       const uint32_t lds0 = lds_addr(wstage[wave]);
       // The lane index through an opaque copy: the offsets below are then
       // computed here, once per tile, rather than hoisted out of the block
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
       for (int i = 0; i < VDMA; ++i) {
         const int r = 4 * i + rl;
         const int kr = min(wave * 32 + r, p.L - 1 - p.k0);
-        const uint32_t voff = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)(((slot ^ (r & 15))) * 16);
+        const uint32_t voff = (uint32_t)kr * (uint32_t)(a.Hkv * D * 2) + (uint32_t)(((slot ^ (r & 15))) * 16);
         dma_copy16(vb, voff, lds0 + i * 1024);
       }
     }
@@ -836,8 +837,8 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
   float acc = 0.f;
   for (int kt = 0; kt * 32 < Lk; ++kt) {
     const int key = min(kt * 32 + lc, Lk - 1);
-    const uint16_t* kr = a.k + ((s0 + key) * H + h) * (int64_t)D;
-    const uint16_t* vr = a.v + ((s0 + key) * H + h) * (int64_t)D;
+    const uint16_t* kr = a.k + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
+    const uint16_t* vr = a.v + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
     f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {

@@ -58,6 +58,7 @@ struct FwdArgs {
   unsigned int* tile_ctr;  // tiles handed out past the first two per workgroup (starts at 0)
   int64_t total_len;
   int B, H, Lq, d;
+  int Hkv, G;        // key / value heads; G = H / Hkv query heads share one
   float scale_log2;  // softmax scale times log2(e)
   int causal, broadcast_q;
   int P;             // persistent workgroups
@@ -94,6 +95,7 @@ struct BwdArgs {
   const int64_t* n_qtiles;
   unsigned int* qtile_ctr;  // query tiles handed out past the first one per workgroup
   int B, H, Lq, d;
+  int Hkv, G;             // key / value heads; G = H / Hkv query heads share one
   int64_t total_len;
   float scale;
   float scale_log2;
@@ -102,6 +104,10 @@ struct BwdArgs {
   int P_dq;    // persistent workgroups of the self-attention dQ kernel
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// Grouped heads: dst[t][g][:] = sum over i < H / Hkv, ascending, of
+// src[t][g * (H / Hkv) + i][:] (fp32 rows of d elements).
+hipError_t launch_group_sum(const float* src, float* dst, int64_t total_len, int H, int Hkv, int d,
+                            hipStream_t stream);
 // Exact delta for short sequences, then dK / dV (delta and lse2 must hold the
 // pre-pass values).
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream);

@@ -14,6 +14,7 @@ enum KernelId {
   K_DQ_REDUCE,
   K_DQ,
   K_DELTA_EXACT,
+  K_GROUP_SUM,
   K_COUNT
 };
 
