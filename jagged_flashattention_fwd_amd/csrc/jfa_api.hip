@@ -218,7 +218,7 @@ int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
   char* ws = static_cast<char*>(workspace);
   const Schedule s = schedule_at(ws, lay.sched_a, lay.cap_a);
 
-  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows()};
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows(), H / H_kv};
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
 
   FwdArgs fa;
@@ -273,12 +273,12 @@ int jfa_bwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const Schedule sk = schedule_at(ws, lay.sched_a, lay.cap_a);
-  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 1, BWD_BN};
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 1, BWD_BN, H / H_kv};
   if (launch_schedule(sa, sk, st) != hipSuccess) return JFA_ERR_HIP;
   Schedule sq{};
   if (!broadcast_q) {
     sq = schedule_at(ws, lay.sched_b, lay.cap_b);
-    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, DQ_BM};  // self-attention dQ query tiles
+    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, DQ_BM, H / H_kv};  // self-attention dQ query tiles
     if (launch_schedule(sb, sq, st) != hipSuccess) return JFA_ERR_HIP;
   }
   BwdArgs ba;
@@ -353,7 +353,7 @@ int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const Schedule s = schedule_at(static_cast<char*>(workspace), lay.sched_a, lay.cap_a);
   SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, pass,
-               pass == 0 ? fwd_block_rows() : BWD_BN};
+               pass == 0 ? fwd_block_rows() : BWD_BN, 1};
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
   if (launch_schedule_dump(s, P, tiles, cap, n_tiles, st) != hipSuccess) return JFA_ERR_HIP;
   return JFA_OK;

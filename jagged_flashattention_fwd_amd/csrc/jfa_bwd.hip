@@ -11,8 +11,8 @@
 //                       stored), lse * log2(e), and the bf16 row terms of
 //                       -lse / scale and -delta, per query row.
 //   delta_exact_kernel  delta again, exactly, for sequences of at most 128
-//                       keys and, under the causal mask, the first 128 query
-//                       rows of every sequence (jfa_dkdv.hip).
+//                       keys and, in causal broadcast mode, the first 128
+//                       query rows of every sequence (jfa_dkdv.hip).
 //   dkdv_kernel         dK and dV (jfa_dkdv.hip).
 //   dq_kernel           dQ.  Self-attention: persistent, a tile is 128 query
 //                       rows, looping over K/V steps recomputing S^T, dP^T,
@@ -306,13 +306,13 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
   // All K/V steps of one sequence (rows s0.. of head h), with the same ring
   // discipline as the forward.  `after_prologue` runs once the first copies
   // are in flight (loads of per-sequence rows go there).
-  auto sequence = [&](int64_t s0, int L, int h, int q0, int wq0, int qi, auto after_prologue) {
+  auto sequence = [&](int64_t s0, int L, int hk, int q0, int wq0, int qi, auto after_prologue) {
     int kv_end = L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     const int n_bulk = CAUSAL ? min(q0 / BN, L / BN) : L / BN;
-    const uint16_t* kbase = a.k + (s0 * a.Hkv + h / a.G) * (int64_t)D;
-    const uint16_t* vbase = a.v + (s0 * a.Hkv + h / a.G) * (int64_t)D;
+    const uint16_t* kbase = a.k + (s0 * a.Hkv + hk) * (int64_t)D;
+    const uint16_t* vbase = a.v + (s0 * a.Hkv + hk) * (int64_t)D;
     auto issue = [&](int j) {
       constexpr int RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
       const int base_row = min(j * BN + wave * RPW, L - 1);
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
       del = q_ok ? a.delta[(s0 + qi) * H + h] : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
-      sequence(s0, L, h, q0, wq0, qi, [] {});
+      sequence(s0, L, tile.hk, q0, wq0, qi, [] {});
       if (q_ok) {
         float* dst = a.dq + ((s0 + qi) * H + h) * (int64_t)D;
 #pragma unroll
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
       const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
       if (L <= 0) continue;
       const int64_t row = ((int64_t)b * H + h) * Lq + qi;
-      sequence(s0, L, h, q0, wq0, qi, [&] {
+      sequence(s0, L, h / a.G, q0, wq0, qi, [&] {
         load_rows(a.dout + row * D, q_ok, doreg);
         lse2 = q_ok ? a.lse[row] * LOG2E : INFINITY;
         del = q_ok ? a.delta[row] : 0.f;
@@ -484,6 +484,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
   const int NC = a.dq_chunks, n_qb = a.dq_qblocks;
   const int item = blockIdx.x;
   const int h = item / (n_qb * NC);
+  const int hk = h / a.G;  // key / value head
   const int rem = item - h * n_qb * NC;
   const int qb = rem / NC, c = rem - qb * NC;
   const int q0 = qb * BM;
@@ -520,8 +521,8 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     const int b = a.seq_order[r];
     q.L = (int)seq_range(a.offsets, b, a.total_len, &q.s0);
     q.row = ((int64_t)b * H + h) * Lq;
-    q.kb = a.k + (q.s0 * a.Hkv + h / a.G) * (int64_t)D;
-    q.vb = a.v + (q.s0 * a.Hkv + h / a.G) * (int64_t)D;
+    q.kb = a.k + (q.s0 * a.Hkv + hk) * (int64_t)D;
+    q.vb = a.v + (q.s0 * a.Hkv + hk) * (int64_t)D;
     int kv_end = q.L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     q.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     p.s0 = r.s0;
     p.L = r.L;
     p.h = r.h;
-    p.hk = r.h / a.G;
+    p.hk = r.hk;
     p.b = r.b;
     p.k0 = r.blk * BN;
     p.nq = BCAST ? Lq : r.L;
@@ -800,10 +800,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
 // For a sequence with at most BWD_BN keys, delta_i = sum_k P_ik dP_ik from
 // fp32 P and dP (the same quantity as rowsum(dO o O), without the bf16
 // rounding of the stored O, which dominates the dK and dQ error when P is
-// large).  With the causal mask the same holds for the first BWD_BN query
-// rows of any sequence: they see only keys below BWD_BN, and few of them, so
-// their P is large too (in broadcast mode their dQ then sums such rows over
-// every sequence).  One workgroup: 128 query rows of one (sequence, head); wave w takes
+// large).  In causal broadcast mode the same holds for the first BWD_BN
+// query rows of any sequence: they see only keys below BWD_BN, and few of
+// them, so their P is large too, and dQ sums such rows over every sequence.
+// (Self-attention rows are not summed across sequences; their error stays
+// within the bar, and the pass would cost a workgroup per (sequence, head).)
+// One workgroup: 128 query rows of one (sequence, head); wave w takes
 // rows 32w .. 32w+31 with the transposed score layout S^T = K Q^T (lane ->
 // query, registers -> keys), so each lane sums its registers and the two
 // halves of the wave are added.
@@ -813,7 +815,7 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
   const int b = blockIdx.x, h = blockIdx.y;
   int64_t s0;
   const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
-  if (L == 0 || (L > BWD_BN && !(CAUSAL && blockIdx.z == 0))) return;
+  if (L == 0 || (L > BWD_BN && !(CAUSAL && BCAST && blockIdx.z == 0))) return;
   static_assert(BWD_BN == 128, "the causal rows of block 0 see keys below 128 only");
   const int Lk = min(L, BWD_BN);  // keys any row of this workgroup sees
   const int H = a.H, Lq = a.Lq;

@@ -126,8 +126,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     const int n_bulk = CAUSAL ? min(q0 / BN, L / BN) : L / BN;
 
-    const uint16_t* kbase = a.k + (s0 * a.Hkv + h / a.G) * (int64_t)D;
-    const uint16_t* vbase = a.v + (s0 * a.Hkv + h / a.G) * (int64_t)D;
+    const uint16_t* kbase = a.k + (s0 * a.Hkv + tile.hk) * (int64_t)D;
+    const uint16_t* vbase = a.v + (s0 * a.Hkv + tile.hk) * (int64_t)D;
     TileLoader<BN, D, NT> kl, vl;
     // Copies K/V step j into ring buffer j % NBUF (d = 128 path).  Rows past
     // the sequence end repeat its last row: finite values that the mask
@@ -373,8 +373,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     p.L = r.L;
     p.h = r.h;
     p.b = r.b;
-    p.kb = a.k + (r.s0 * a.Hkv + r.h / a.G) * (int64_t)D;
-    p.vb = a.v + (r.s0 * a.Hkv + r.h / a.G) * (int64_t)D;
+    p.kb = a.k + (r.s0 * a.Hkv + r.hk) * (int64_t)D;
+    p.vb = a.v + (r.s0 * a.Hkv + r.hk) * (int64_t)D;
     p.q0 = r.blk * BM;
     const int nq = BCAST ? Lq : r.L;
     int kv_end = r.L;

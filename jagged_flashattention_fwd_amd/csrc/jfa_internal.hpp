@@ -12,7 +12,8 @@ namespace jfa {
 struct TileRec {
   int b, h, blk, L;
   int64_t s0;
-  int64_t pad;
+  int hk;   // key / value head of query head h (h / G; h with plain heads)
+  int pad;
 };
 static_assert(sizeof(TileRec) == 32, "tile record layout");
 
@@ -40,6 +41,7 @@ struct SchedArgs {
   const int64_t* offsets;
   int64_t total_len;
   int B, H, Lq, broadcast_q, pass, blk;
+  int G;  // query heads per key / value head (the tile records' hk = h / G)
 };
 
 hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t stream);
