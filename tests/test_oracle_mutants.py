@@ -103,6 +103,47 @@ def _mut_jagged_dq_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout)
     return dq, dk, dv
 
 
+def _mut_gqa_interleaved_heads(q, k, v, offsets, scale, causal, broadcast_q):
+    """Grouped heads mapped round-robin (h % H_kv) instead of by group."""
+    q, k, v = jo._f64(q), jo._f64(k), jo._f64(v)
+    bounds = jo._seq_bounds(offsets)
+    H = q.shape[0] if broadcast_q else q.shape[1]
+    Hkv = k.shape[1]
+    B, Lq = len(bounds), (q.shape[1] if broadcast_q else 0)
+    out = np.zeros((B, H, Lq, v.shape[2])) if broadcast_q else np.zeros((q.shape[0], H, v.shape[2]))
+    lse = np.zeros((B, H, Lq)) if broadcast_q else np.zeros((q.shape[0], H))
+    for b, (s0, s1) in enumerate(bounds):
+        for h in range(H):
+            qb = q[h] if broadcast_q else q[s0:s1, h]
+            o, ls, _ = jo.sequence_forward(qb, k[s0:s1, h % Hkv], v[s0:s1, h % Hkv], scale, causal)
+            if broadcast_q:
+                out[b, h], lse[b, h] = o, ls
+            else:
+                out[s0:s1, h], lse[s0:s1, h] = o, ls
+    return out, lse
+
+
+def _mut_gqa_dkv_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout):
+    """dK / dV of a shared head keep only the last query head of the group."""
+    q, k, v, dout = jo._f64(q), jo._f64(k), jo._f64(v), jo._f64(dout)
+    bounds = jo._seq_bounds(offsets)
+    H = q.shape[0] if broadcast_q else q.shape[1]
+    G = H // k.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b, (s0, s1) in enumerate(bounds):
+        for h in range(H):
+            kb, vb = k[s0:s1, h // G], v[s0:s1, h // G]
+            if broadcast_q:
+                g = jo.sequence_backward(q[h], kb, vb, dout[b, h], scale, causal)
+                dq[h] += g[0]
+            else:
+                g = jo.sequence_backward(q[s0:s1, h], kb, vb, dout[s0:s1, h], scale, causal)
+                dq[s0:s1, h] = g[0]
+            dk[s0:s1, h // G] = g[1]
+            dv[s0:s1, h // G] = g[2]
+    return dq, dk, dv
+
+
 def _pin_suite():
     """Every pin, as (name, callable) pairs; a mutant must fail at least one."""
     return [
@@ -114,6 +155,8 @@ def _pin_suite():
         ("block_diag", lambda: [pins.test_self_mode_is_block_diagonal_dense_attention(c) for c in (False, True)]),
         ("dq_sum", pins.test_broadcast_dq_is_sum_of_per_sequence_dq),
         ("fd", lambda: [pins.test_finite_differences(b, c) for b in (True, False) for c in (False, True)]),
+        ("gqa_self", lambda: [pins.test_gqa_self_mode_is_sdpa_grouped_query(c, 4, 2) for c in (False, True)]),
+        ("gqa_bcast", lambda: [pins.test_gqa_broadcast_is_sdpa_grouped_query(c) for c in (False, True)]),
     ]
 
 
@@ -129,6 +172,8 @@ MUTANTS = {
     "lse_base2": ("sequence_forward", _mut_lse_log2),
     "lse_shifted": ("sequence_forward", _mut_softmax_no_max_shift),
     "bcast_dq_overwrite": ("jagged_backward", _mut_jagged_dq_overwrite),
+    "gqa_interleaved_heads": ("jagged_forward", _mut_gqa_interleaved_heads),
+    "gqa_dkv_overwrite": ("jagged_backward", _mut_gqa_dkv_overwrite),
 }
 
 
