@@ -756,8 +756,9 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       // after the barrier of iteration j go to the buffer of step j - 1 (the
       // stream's next step is j + 3); the tile's last step issues one more
       // after a barrier of its own, and the stream stays DEP steps ahead.
-      auto wait_step = [&](int gi) {  // this wave's copies of stream step gi landed
-        const int after = g_iss - 1 - gi;
+      // This wave's copies of stream step gi landed, with iss steps' copies out.
+      auto wait_step = [&](int gi, int iss) {
+        const int after = iss - 1 - gi;
         if constexpr (DEP >= 3) {
           if (after >= 2) wait_vmcnt<2 * IPS>();
           else if (after == 1) wait_vmcnt<IPS>();
@@ -846,9 +847,13 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       uint32_t pk[2][2][QS][4];
       auto iter = [&](int j, f32x16 (&sa)[2][QS], f32x16 (&sb)[2][QS]) {
         const int gj = g_first + j;
-        wait_step(gj + 1);
-        barrier_lds();
+        // The next step's copy preparation (addresses only) runs before the
+        // wait and the barrier, beside the other waves' arrival; the wait
+        // counts the steps whose copies are out, which excludes it.
+        const int iss0 = g_iss;
         prep_next(cp, np, has_nxt);
+        wait_step(gj + 1, iss0);
+        barrier_lds();
         using F = std::false_type;
         s_phase(gj + 1, sb, [&](auto ks_tag) {
           constexpr int ks = decltype(ks_tag)::value;
