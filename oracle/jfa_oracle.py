@@ -28,6 +28,12 @@ Readings where the pages are silent (each also listed in the design notes):
   * The backward is the exact derivative of the forward: dP = dO V^T,
     delta_i = sum_d dO_id O_id, dS = P o (dP - delta), dQ = scale dS K,
     dK = scale dS^T Q, dV = P^T dO.  The pages do not print it.
+  * Sliding window ([JFA] "3. Attention Variants: the flexibility of TLX",
+    block-sparse part, and "Conclusion" name windowing support without a
+    rule): with the causal mask and a window of W keys, query i sees keys j
+    with i - W < j <= i (W <= 0: no window).  A query row that sees no key
+    (possible in broadcast mode when i - W >= L) gives O = 0, lse = -inf and
+    no gradient, like a sequence with no keys.
   * Grouped-query attention ([JFA] "3. Attention Variants: the flexibility
     of TLX", block-sparse part, and "Conclusion" name GQA support without
     defining it): with H query heads and H_kv = H / G key/value heads, query
@@ -51,24 +57,29 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def causal_visible(n_q: int, n_k: int) -> np.ndarray:
+def causal_visible(n_q: int, n_k: int, window: int = 0) -> np.ndarray:
     """Boolean [n_q, n_k]: True where query i may see key j, i.e. j <= i
-    ([FMHA] "cuTile Implementation": keep a score where offs_m >= offs_n)."""
+    ([FMHA] "cuTile Implementation": keep a score where offs_m >= offs_n),
+    and, with a window of W > 0 keys, j > i - W."""
     i = np.arange(n_q)[:, None]
     j = np.arange(n_k)[None, :]
-    return j <= i
+    vis = j <= i
+    if window > 0:
+        vis = vis & (j > i - window)
+    return vis
 
 
-def sequence_scores(qb, kb, scale: float, causal: bool) -> np.ndarray:
-    """S = scale * Q K^T, future scores set to -inf when causal
-    ([FMHA] "Attention Basics")."""
+def sequence_scores(qb, kb, scale: float, causal: bool, window: int = 0) -> np.ndarray:
+    """S = scale * Q K^T, future scores (and, with a window, scores of keys
+    W or more positions back) set to -inf when causal ([FMHA] "Attention
+    Basics")."""
     s = scale * (_f64(qb) @ _f64(kb).T)
     if causal:
-        s = np.where(causal_visible(s.shape[0], s.shape[1]), s, -np.inf)
+        s = np.where(causal_visible(s.shape[0], s.shape[1], window), s, -np.inf)
     return s
 
 
-def sequence_forward(qb, kb, vb, scale: float, causal: bool):
+def sequence_forward(qb, kb, vb, scale: float, causal: bool, window: int = 0):
     """One (sequence, head): returns (O [n,d], lse [n], P [n,L]).
 
     P = softmax(S) row-wise with the row maximum subtracted first; O = P V;
@@ -79,15 +90,17 @@ def sequence_forward(qb, kb, vb, scale: float, causal: bool):
     L = kb.shape[0]
     if L == 0:
         return np.zeros((n, vb.shape[1])), np.full(n, -np.inf), np.zeros((n, 0))
-    s = sequence_scores(qb, kb, scale, causal)
+    s = sequence_scores(qb, kb, scale, causal, window)
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
+    seen = np.isfinite(m)  # rows that see at least one key
+    e = np.exp(s - np.where(seen, m, 0.0)[:, None])
     l = e.sum(axis=1)
-    p = e / l[:, None]
-    return p @ vb, m + np.log(l), p
+    p = e / np.where(seen, l, 1.0)[:, None]
+    lse = np.where(seen, np.where(seen, m, 0.0) + np.log(np.where(seen, l, 1.0)), -np.inf)
+    return p @ vb, lse, p
 
 
-def sequence_backward(qb, kb, vb, dob, scale: float, causal: bool):
+def sequence_backward(qb, kb, vb, dob, scale: float, causal: bool, window: int = 0):
     """One (sequence, head): returns (dQ [n,d], dK [L,d], dV [L,d]).
 
     The derivative of O = softmax(scale Q K^T) V: with P and O recomputed by
@@ -98,7 +111,7 @@ def sequence_backward(qb, kb, vb, dob, scale: float, causal: bool):
     L = kb.shape[0]
     if L == 0:
         return np.zeros_like(qb), np.zeros((0, qb.shape[1])), np.zeros((0, vb.shape[1]))
-    o, _, p = sequence_forward(qb, kb, vb, scale, causal)
+    o, _, p = sequence_forward(qb, kb, vb, scale, causal, window)
     delta = (dob * o).sum(axis=1)
     dp = dob @ vb.T
     ds = p * (dp - delta[:, None])
@@ -117,7 +130,7 @@ def _seq_bounds(offsets):
     return [(int(off[b]), int(off[b + 1])) for b in range(off.size - 1)]
 
 
-def jagged_forward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bool):
+def jagged_forward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bool, window: int = 0):
     """Forward over a packed batch ([JFA] "Introduction": sequence b owns the
     packed rows offsets[b]..offsets[b+1]-1 of K and V; in self mode also of
     Q; [JFA] "1. The Challenge": in broadcast mode every sequence attends
@@ -137,7 +150,7 @@ def jagged_forward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bo
     for b, (s0, s1) in enumerate(bounds):
         for h in range(H):
             qb = q[h] if broadcast_q else q[s0:s1, h]
-            o, ls, _ = sequence_forward(qb, k[s0:s1, h // G], v[s0:s1, h // G], scale, causal)
+            o, ls, _ = sequence_forward(qb, k[s0:s1, h // G], v[s0:s1, h // G], scale, causal, window)
             if broadcast_q:
                 out[b, h], lse[b, h] = o, ls
             else:
@@ -145,7 +158,7 @@ def jagged_forward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bo
     return out, lse
 
 
-def jagged_backward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bool, dout):
+def jagged_backward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: bool, dout, window: int = 0):
     """Backward over a packed batch.  In broadcast mode dQ is the sum of the
     per-sequence dQ over the whole batch ([JFA] "1. The Challenge")."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -159,10 +172,10 @@ def jagged_backward(q, k, v, offsets, scale: float, causal: bool, broadcast_q: b
         for h in range(H):
             kb, vb = k[s0:s1, h // G], v[s0:s1, h // G]
             if broadcast_q:
-                g = sequence_backward(q[h], kb, vb, dout[b, h], scale, causal)
+                g = sequence_backward(q[h], kb, vb, dout[b, h], scale, causal, window)
                 dq[h] += g[0]
             else:
-                g = sequence_backward(q[s0:s1, h], kb, vb, dout[s0:s1, h], scale, causal)
+                g = sequence_backward(q[s0:s1, h], kb, vb, dout[s0:s1, h], scale, causal, window)
                 dq[s0:s1, h] = g[0]
             dk[s0:s1, h // G] += g[1]
             dv[s0:s1, h // G] += g[2]

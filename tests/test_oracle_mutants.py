@@ -17,14 +17,14 @@ def _fails(fn, *args):
     return False
 
 
-def _mut_scores_no_scale(qb, kb, scale, causal):
+def _mut_scores_no_scale(qb, kb, scale, causal, window=0):
     s = jo._f64(qb) @ jo._f64(kb).T
     if causal:
         s = np.where(jo.causal_visible(*s.shape), s, -np.inf)
     return s
 
 
-def _mut_scores_wrong_causal(qb, kb, scale, causal):
+def _mut_scores_wrong_causal(qb, kb, scale, causal, window=0):
     s = scale * (jo._f64(qb) @ jo._f64(kb).T)
     if causal:
         i = np.arange(s.shape[0])[:, None]
@@ -33,7 +33,7 @@ def _mut_scores_wrong_causal(qb, kb, scale, causal):
     return s
 
 
-def _mut_scores_off_by_one(qb, kb, scale, causal):
+def _mut_scores_off_by_one(qb, kb, scale, causal, window=0):
     s = scale * (jo._f64(qb) @ jo._f64(kb).T)
     if causal:
         i = np.arange(s.shape[0])[:, None]
@@ -42,10 +42,22 @@ def _mut_scores_off_by_one(qb, kb, scale, causal):
     return s
 
 
+def _mut_scores_window_off_by_one(qb, kb, scale, causal, window=0):
+    s = scale * (jo._f64(qb) @ jo._f64(kb).T)
+    if causal:
+        i = np.arange(s.shape[0])[:, None]
+        j = np.arange(s.shape[1])[None, :]
+        vis = j <= i
+        if window > 0:
+            vis = vis & (j >= i - window)
+        s = np.where(vis, s, -np.inf)
+    return s
+
+
 def _make_bwd_mutant(kind):
     orig = jo.sequence_backward
 
-    def bwd(qb, kb, vb, dob, scale, causal):
+    def bwd(qb, kb, vb, dob, scale, causal, window=0):
         qb, kb, vb, dob = (jo._f64(x) for x in (qb, kb, vb, dob))
         if kb.shape[0] == 0:
             return orig(qb, kb, vb, dob, scale, causal)
@@ -71,7 +83,7 @@ def _make_bwd_mutant(kind):
     return bwd
 
 
-def _mut_lse_log2(qb, kb, vb, scale, causal):
+def _mut_lse_log2(qb, kb, vb, scale, causal, window=0):
     o, lse, p = ORIG_FWD(qb, kb, vb, scale, causal)
     return o, lse / np.log(2.0), p
 
@@ -79,12 +91,12 @@ def _mut_lse_log2(qb, kb, vb, scale, causal):
 ORIG_FWD = jo.sequence_forward
 
 
-def _mut_softmax_no_max_shift(qb, kb, vb, scale, causal):
+def _mut_softmax_no_max_shift(qb, kb, vb, scale, causal, window=0):
     o, lse, p = ORIG_FWD(qb, kb, vb, scale, causal)
     return o, lse - 0.5, p
 
 
-def _mut_jagged_dq_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout):
+def _mut_jagged_dq_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout, window=0):
     q64, k64, v64, d64 = (jo._f64(x) for x in (q, k, v, dout))
     dq = np.zeros_like(q64)
     dk = np.zeros_like(k64)
@@ -103,7 +115,7 @@ def _mut_jagged_dq_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout)
     return dq, dk, dv
 
 
-def _mut_gqa_interleaved_heads(q, k, v, offsets, scale, causal, broadcast_q):
+def _mut_gqa_interleaved_heads(q, k, v, offsets, scale, causal, broadcast_q, window=0):
     """Grouped heads mapped round-robin (h % H_kv) instead of by group."""
     q, k, v = jo._f64(q), jo._f64(k), jo._f64(v)
     bounds = jo._seq_bounds(offsets)
@@ -123,7 +135,7 @@ def _mut_gqa_interleaved_heads(q, k, v, offsets, scale, causal, broadcast_q):
     return out, lse
 
 
-def _mut_gqa_dkv_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout):
+def _mut_gqa_dkv_overwrite(q, k, v, offsets, scale, causal, broadcast_q, dout, window=0):
     """dK / dV of a shared head keep only the last query head of the group."""
     q, k, v, dout = jo._f64(q), jo._f64(k), jo._f64(v), jo._f64(dout)
     bounds = jo._seq_bounds(offsets)
@@ -157,6 +169,8 @@ def _pin_suite():
         ("fd", lambda: [pins.test_finite_differences(b, c) for b in (True, False) for c in (False, True)]),
         ("gqa_self", lambda: [pins.test_gqa_self_mode_is_sdpa_grouped_query(c, 4, 2) for c in (False, True)]),
         ("gqa_bcast", lambda: [pins.test_gqa_broadcast_is_sdpa_grouped_query(c) for c in (False, True)]),
+        ("window_self", lambda: [pins.test_window_self_mode_is_sdpa_with_a_band_mask(w) for w in (1, 3)]),
+        ("window_bcast", pins.test_window_broadcast_rows_that_see_no_key),
     ]
 
 
@@ -172,6 +186,7 @@ MUTANTS = {
     "lse_base2": ("sequence_forward", _mut_lse_log2),
     "lse_shifted": ("sequence_forward", _mut_softmax_no_max_shift),
     "bcast_dq_overwrite": ("jagged_backward", _mut_jagged_dq_overwrite),
+    "window_off_by_one": ("sequence_scores", _mut_scores_window_off_by_one),
     "gqa_interleaved_heads": ("jagged_forward", _mut_gqa_interleaved_heads),
     "gqa_dkv_overwrite": ("jagged_backward", _mut_gqa_dkv_overwrite),
 }

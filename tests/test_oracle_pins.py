@@ -186,6 +186,78 @@ def test_gqa_broadcast_is_sdpa_grouped_query(causal):
                                rtol=1e-10, atol=1e-12)
 
 
+def _band(n_q, n_k, window):
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return (j <= i) & (j > i - window)
+
+
+@pytest.mark.parametrize("window", [1, 3, 6, 100])
+def test_window_self_mode_is_sdpa_with_a_band_mask(window):
+    """Causal sliding window: equal lengths in self mode against SDPA with the
+    explicit band mask i - W < j <= i, forward and autograd gradients."""
+    B, H, L, d = 2, 2, 9, 4
+    scale = 0.6
+    off = _offsets([L] * B)
+    q, k, v, dout = (_rand(B * L, H, d) for _ in range(4))
+    out, lse = jo.jagged_forward(q, k, v, off, scale, True, False, window=window)
+    dq, dk, dv = jo.jagged_backward(q, k, v, off, scale, True, False, dout, window=window)
+    dense = lambda x: x.reshape(B, L, H, d).transpose(0, 2, 1, 3).copy()  # noqa: E731
+    packed = lambda x: x.transpose(0, 2, 1, 3).reshape(B * L, H, d)  # noqa: E731
+    mask = _band(L, L, window)
+    o_ref, (tq, tk, tv) = _sdpa(dense(q), dense(k), dense(v), scale, mask=mask)
+    np.testing.assert_allclose(out, packed(o_ref.detach().numpy()), rtol=1e-12, atol=1e-12)
+    o_ref.backward(torch.tensor(dense(dout)))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, packed(t.grad.numpy()), rtol=1e-10, atol=1e-12)
+    s = scale * torch.tensor(dense(q)) @ torch.tensor(dense(k)).transpose(-1, -2)
+    s = s.masked_fill(~torch.tensor(mask), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy().transpose(0, 2, 1).reshape(B * L, H),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_window_broadcast_rows_that_see_no_key():
+    """Broadcast mode, window W: query rows i >= L + W - 1 see no key of a
+    length-L sequence: O = 0, lse = -inf, and they add nothing to dQ, dK, dV
+    (the other rows match SDPA with the band mask)."""
+    H, Lq, d, W = 2, 10, 3, 2
+    lengths = [4, 1, 7]
+    off = _offsets(lengths)
+    T = sum(lengths)
+    q, k, v = _rand(H, Lq, d), _rand(T, H, d), _rand(T, H, d)
+    dout = _rand(len(lengths), H, Lq, d)
+    out, lse = jo.jagged_forward(q, k, v, off, 0.5, True, True, window=W)
+    dq, dk, dv = jo.jagged_backward(q, k, v, off, 0.5, True, True, dout, window=W)
+    dq_ref = np.zeros_like(dq)
+    for b, L in enumerate(lengths):
+        s0 = int(off[b])
+        seen = np.arange(Lq) < L + W - 1
+        assert np.all(out[b][:, ~seen] == 0) and np.all(np.isneginf(lse[b][:, ~seen]))
+        mask = _band(int(seen.sum()), L, W)
+        kd, vd = k[s0:s0 + L].transpose(1, 0, 2), v[s0:s0 + L].transpose(1, 0, 2)
+        o_ref, (tq, tk, tv) = _sdpa(q[:, seen], kd.copy(), vd.copy(), 0.5, mask=mask)
+        np.testing.assert_allclose(out[b][:, seen], o_ref.detach().numpy(), rtol=1e-12, atol=1e-12)
+        o_ref.backward(torch.tensor(dout[b][:, seen].copy()))
+        dq_ref[:, seen] += tq.grad.numpy()
+        np.testing.assert_allclose(dk[s0:s0 + L], tk.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv[s0:s0 + L], tv.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dq, dq_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_window_wider_than_every_sequence_is_plain_causal():
+    lengths = [5, 2, 8]
+    off = _offsets(lengths)
+    q, k, v, dout = (_rand(sum(lengths), 2, 3) for _ in range(4))
+    a = jo.jagged_forward(q, k, v, off, 0.7, True, False, window=8)
+    b = jo.jagged_forward(q, k, v, off, 0.7, True, False)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    ga = jo.jagged_backward(q, k, v, off, 0.7, True, False, dout, window=8)
+    gb = jo.jagged_backward(q, k, v, off, 0.7, True, False, dout)
+    for x, y in zip(ga, gb):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_gqa_rejects_heads_that_do_not_split():
     off = _offsets([3])
     with pytest.raises(ValueError):
