@@ -87,27 +87,37 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
             const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
             size_t workspace_bytes, void* stream);
 
-/* Grouped-query attention ("Optimizing Jagged Flash Attention with TLX",
- * "3. Attention Variants: the flexibility of TLX" and "Conclusion" name GQA
- * support; the grouping is the usual one): k and v hold H_kv heads,
- * [total_len, H_kv, d], and query head h attends with key/value head
- * h / (H / H_kv), so consecutive query heads share one; dk and dv are
- * [total_len, H_kv, d], each the sum over the H / H_kv query heads of the
- * group.  H_kv must divide H (JFA_ERR_INVALID_ARG otherwise); H_kv = H is
- * plain multi-head attention and the calls above are exactly these with
- * H_kv = H.  Every other argument, layout and rule is as above.  With
- * H_kv < H the backward's workspace also holds per-query-head dK / dV
+/* Grouped-query attention and the sliding window ("Optimizing Jagged Flash
+ * Attention with TLX", "3. Attention Variants: the flexibility of TLX" and
+ * "Conclusion" name both without giving a rule; these are the usual ones).
+ *
+ * Grouped-query heads: k and v hold H_kv heads, [total_len, H_kv, d], and
+ * query head h attends with key/value head h / (H / H_kv), so consecutive
+ * query heads share one; dk and dv are [total_len, H_kv, d], each the sum
+ * over the H / H_kv query heads of the group.  H_kv must divide H
+ * (JFA_ERR_INVALID_ARG otherwise); H_kv = H is plain multi-head attention.
+ * With H_kv < H the backward's workspace also holds per-query-head dK / dV
  * (2 * total_len * H * d fp32), summed per group in ascending head order,
- * so results stay bitwise reproducible. */
+ * so results stay bitwise reproducible.
+ *
+ * Sliding window: window = W > 0 (with causal = 1 only; JFA_ERR_UNSUPPORTED
+ * otherwise, JFA_ERR_INVALID_ARG for W < 0) lets query i see keys j with
+ * i - W < j <= i; window = 0 is no window.  A query row that sees no key
+ * (broadcast mode, i - W >= L_b) gives O = 0, lse = -inf and no gradient.
+ * Out-of-window keys are masked inside the causal key range (every step
+ * takes the masked path); they are not skipped.
+ *
+ * jfa_fwd and jfa_bwd above are these with H_kv = H and window = 0.  Every
+ * other argument, layout and rule is as above. */
 int jfa_workspace_size_gqa(int64_t total_len, int B, int H, int H_kv, int Lq, int d, int causal,
                            int broadcast_q, int pass, size_t* bytes);
-int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
-                int Lq, int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
-                void* workspace, size_t workspace_bytes, void* stream);
-int jfa_bwd_gqa(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
-                int Lq, int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
-                const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
-                size_t workspace_bytes, void* stream);
+int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+               int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
+               int64_t total_len, void* workspace, size_t workspace_bytes, void* stream);
+int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+               int Lq, int d, float scale, int causal, int window, int broadcast_q, const void* out,
+               const float* lse, const void* dout, float* dq, float* dk, float* dv, int64_t total_len,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Tile geometry the library uses on the current device for a pass:
  * *block_rows = query rows per forward tile (pass 0) or key rows per

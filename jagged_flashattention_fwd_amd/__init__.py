@@ -33,13 +33,13 @@ _SIGS = {
                            _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "jfa_workspace_size_gqa": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                           _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
-    "jfa_fwd_gqa": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
-                               _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
-                               _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
-    "jfa_bwd_gqa": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
-                               _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
-                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
-                               _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_fwd_ex": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                              _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_int,
+                              _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_bwd_ex": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                              _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_int,
+                              _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                              _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "jfa_schedule_params": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_int),
                                        _c.POINTER(_c.c_int)]),
     "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -108,20 +108,20 @@ def jfa_workspace_size_gqa(total_len, B, H, H_kv, Lq, d, causal, broadcast_q, pa
     return out.value
 
 
-def jfa_fwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, total_len,
-                workspace, stream=None):
-    _check(lib().jfa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
-                             int(causal), int(broadcast_q), _ptr(out), _ptr(lse), int(total_len),
-                             _ptr(workspace), workspace.numel() * workspace.element_size(),
-                             _stream(stream)), "jfa_fwd_gqa")
+def jfa_fwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, total_len,
+               workspace, stream=None):
+    _check(lib().jfa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
+                            int(causal), int(window), int(broadcast_q), _ptr(out), _ptr(lse), int(total_len),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream)), "jfa_fwd_ex")
 
 
-def jfa_bwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
-                total_len, workspace, stream=None):
-    _check(lib().jfa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
-                             int(causal), int(broadcast_q), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
-                             _ptr(dk), _ptr(dv), int(total_len), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_bwd_gqa")
+def jfa_bwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, dout, dq,
+               dk, dv, total_len, workspace, stream=None):
+    _check(lib().jfa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
+                            int(causal), int(window), int(broadcast_q), _ptr(out), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dk), _ptr(dv), int(total_len), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_bwd_ex")
 
 
 def jfa_schedule_params(pass_, causal, broadcast_q, d):
@@ -202,9 +202,10 @@ def workspace(total_len, B, H, Lq, d, causal, broadcast_q, pass_, device, H_kv=N
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def attention_fwd(q, k, v, offsets, scale, causal=False, broadcast_q=True, ws=None):
+def attention_fwd(q, k, v, offsets, scale, causal=False, broadcast_q=True, ws=None, window=0):
     """(out bf16, lse fp32) of jagged attention; see include/jfa.h for layouts
-    (k / v with fewer heads than q: grouped-query attention)."""
+    (k / v with fewer heads than q: grouped-query attention; window > 0 with
+    causal: sliding window)."""
     import torch
     B, H, H_kv, Lq, d, T = _shape_args(q, k, offsets, broadcast_q)
     if broadcast_q:
@@ -215,11 +216,11 @@ def attention_fwd(q, k, v, offsets, scale, causal=False, broadcast_q=True, ws=No
         lse = torch.empty((T, H), dtype=torch.float32, device=k.device)
     if ws is None:
         ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 0, k.device, H_kv)
-    jfa_fwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, T, ws)
+    jfa_fwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, T, ws)
     return out, lse
 
 
-def attention_bwd(q, k, v, offsets, scale, causal, broadcast_q, out, lse, dout, ws=None):
+def attention_bwd(q, k, v, offsets, scale, causal, broadcast_q, out, lse, dout, ws=None, window=0):
     """(dq, dk, dv) fp32 of jagged attention; see include/jfa.h for layouts
     (dk / dv with k's head count)."""
     import torch
@@ -229,6 +230,6 @@ def attention_bwd(q, k, v, offsets, scale, causal, broadcast_q, out, lse, dout, 
     dv = torch.empty((T, H_kv, d), dtype=torch.float32, device=k.device)
     if ws is None:
         ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 1, k.device, H_kv)
-    jfa_bwd_gqa(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
-                T, ws)
+    jfa_bwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, dout, dq, dk,
+               dv, T, ws)
     return dq, dk, dv

@@ -140,6 +140,13 @@ int check_heads(int H, int Hkv) {
   return JFA_OK;
 }
 
+// Sliding window: W >= 0 keys (0: none), only with the causal mask.
+int check_window(int causal, int window) {
+  if (window < 0) return JFA_ERR_INVALID_ARG;
+  if (window > 0 && !causal) return JFA_ERR_UNSUPPORTED;
+  return JFA_OK;
+}
+
 int workers(int pass, int* P) {
   int cus = 0;
   const int rc = cu_count(&cus);
@@ -196,9 +203,9 @@ int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causa
   return jfa_workspace_size_gqa(total_len, B, H, H, Lq, d, causal, broadcast_q, pass, bytes);
 }
 
-int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
-                int Lq, int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
-                void* workspace, size_t workspace_bytes, void* stream) {
+int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+               int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
+               int64_t total_len, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !offsets || !out || !lse || !workspace) return JFA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 7))
@@ -207,6 +214,8 @@ int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
   int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
   if (rc != JFA_OK) return rc;
   rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
+  rc = check_window(causal, window);
   if (rc != JFA_OK) return rc;
   if (!broadcast_q) Lq = 0;
   int P = 0;
@@ -234,6 +243,7 @@ int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
   fa.total_len = total_len;
   fa.B = B; fa.H = H; fa.Lq = Lq; fa.d = d;
   fa.Hkv = H_kv; fa.G = H / H_kv;
+  fa.window = window;
   fa.scale_log2 = scale * 1.4426950408889634f;
   fa.causal = causal ? 1 : 0;
   fa.broadcast_q = broadcast_q ? 1 : 0;
@@ -245,14 +255,14 @@ int jfa_fwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
 int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
             int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
             void* workspace, size_t workspace_bytes, void* stream) {
-  return jfa_fwd_gqa(q, k, v, offsets, B, H, H, Lq, d, scale, causal, broadcast_q, out, lse, total_len,
-                     workspace, workspace_bytes, stream);
+  return jfa_fwd_ex(q, k, v, offsets, B, H, H, Lq, d, scale, causal, 0, broadcast_q, out, lse, total_len,
+                    workspace, workspace_bytes, stream);
 }
 
-int jfa_bwd_gqa(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
-                int Lq, int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
-                const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
-                size_t workspace_bytes, void* stream) {
+int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+               int Lq, int d, float scale, int causal, int window, int broadcast_q, const void* out,
+               const float* lse, const void* dout, float* dq, float* dk, float* dv, int64_t total_len,
+               void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
     return JFA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
@@ -263,6 +273,8 @@ int jfa_bwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
   int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
   if (rc != JFA_OK) return rc;
   rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
+  rc = check_window(causal, window);
   if (rc != JFA_OK) return rc;
   if (!broadcast_q) Lq = 0;
   int P = 0;
@@ -312,6 +324,7 @@ int jfa_bwd_gqa(const void* q, const void* k, const void* v, const int64_t* offs
   ba.qtile_ctr = broadcast_q ? nullptr : reinterpret_cast<unsigned int*>(sq.n_tiles + 1);
   ba.B = B; ba.H = H; ba.Lq = Lq; ba.d = d;
   ba.Hkv = H_kv; ba.G = H / H_kv;
+  ba.window = window;
   ba.total_len = total_len;
   ba.scale = scale;
   ba.scale_log2 = scale * 1.4426950408889634f;
@@ -331,8 +344,8 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
             int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
             const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
             size_t workspace_bytes, void* stream) {
-  return jfa_bwd_gqa(q, k, v, offsets, B, H, H, Lq, d, scale, causal, broadcast_q, out, lse, dout, dq, dk, dv,
-                     total_len, workspace, workspace_bytes, stream);
+  return jfa_bwd_ex(q, k, v, offsets, B, H, H, Lq, d, scale, causal, 0, broadcast_q, out, lse, dout, dq, dk,
+                    dv, total_len, workspace, workspace_bytes, stream);
 }
 
 int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q, int pass,

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
         float pv = fast_exp2(sacc[i] * c2 - lse2);
         if (MASKED) {
           const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          const bool ok = key < L && (!CAUSAL || key <= qi);
+          const bool ok = key < L && (!CAUSAL || (key <= qi && (a.window <= 0 || key > qi - a.window)));
           pv = ok ? pv : 0.f;
         }
         dsf[i] = pv * (dpacc[i] - del);
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
     int kv_end = L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-    const int n_bulk = CAUSAL ? min(q0 / BN, L / BN) : L / BN;
+    const int n_bulk = a.window > 0 ? 0 : CAUSAL ? min(q0 / BN, L / BN) : L / BN;  // window: all masked
     const uint16_t* kbase = a.k + (s0 * a.Hkv + hk) * (int64_t)D;
     const uint16_t* vbase = a.v + (s0 * a.Hkv + hk) * (int64_t)D;
     auto issue = [&](int j) {
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     int kv_end = q.L;
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     q.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-    q.n_bulk = min(CAUSAL ? min(q0 / BN, q.L / BN) : q.L / BN, q.n_kv);
+    q.n_bulk = a.window > 0 ? 0 : min(CAUSAL ? min(q0 / BN, q.L / BN) : q.L / BN, q.n_kv);  // window: all masked
     return q;
   };
   // The first sequence of the chunk at or after position r with keys to
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
             float pv = fast_exp2(sacc[i] * c2 - lse2);
             if (MASKED) {
               const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-              const bool ok = key < L && (!CAUSAL || key <= qi);
+              const bool ok = key < L && (!CAUSAL || (key <= qi && (a.window <= 0 || key > qi - a.window)));
               pv = ok ? pv : 0.f;
             }
             dsf[i] = pv * (dpacc[i] - del);

@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     const int nb = m_end - m_first;
     // Blocks m < m_diag hold a row before the tile's last key.
     const int m_diag = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
-    const bool tile_partial = k0 + BN > L;
+    const bool tile_partial = k0 + BN > L || a.window > 0;  // a window cuts blocks anywhere
     const int m_full = nq / QB;  // blocks m < m_full have all QB rows
 
     bf16x8 kreg[KS], vreg[KS];
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
         if constexpr (MASKED) {
           const int row = m * QB + r + e;
           bool ok = key_ok && row < nq;
-          if constexpr (CAUSAL) ok = ok && kw <= row;
+          if constexpr (CAUSAL) ok = ok && kw <= row && (a.window <= 0 || kw > row - a.window);
           pv = ok ? pv : 0.f;
         }
         p4[e] = pv;
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) {
       const int kk = kt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
       bool ok = kk < Lk;
-      if (CAUSAL) ok = ok && kk <= q;
+      if (CAUSAL) ok = ok && kk <= q && (a.window <= 0 || kk > q - a.window);
       const float p = ok ? fast_exp2(st[i] * c2 - ls2) : 0.f;
       acc += p * dpt[i];
     }

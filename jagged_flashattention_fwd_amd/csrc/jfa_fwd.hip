@@ -124,7 +124,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
     int kv_end = L;
     if (CAUSAL) kv_end = min(kv_end, min(q0 + BM, nq));
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-    const int n_bulk = CAUSAL ? min(q0 / BN, L / BN) : L / BN;
+    // A window cuts steps anywhere: every step takes the masked body then.
+    const int n_bulk = a.window > 0 ? 0 : CAUSAL ? min(q0 / BN, L / BN) : L / BN;
 
     const uint16_t* kbase = a.k + (s0 * a.Hkv + tile.hk) * (int64_t)D;
     const uint16_t* vbase = a.v + (s0 * a.Hkv + tile.hk) * (int64_t)D;
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
               float x = sacc[kt][s][i] * c2;
               if (MASKED) {
                 const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-                const bool ok = key < L && (!CAUSAL || key <= qi);
+                const bool ok = key < L && (!CAUSAL || (key <= qi && (a.window <= 0 || key > qi - a.window)));
                 x = ok ? x : -INFINITY;
               }
               sacc[kt][s][i] = x;
@@ -380,7 +381,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     int kv_end = r.L;
     if (CAUSAL) kv_end = min(kv_end, min(p.q0 + BM, nq));
     p.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-    p.n_bulk = min(CAUSAL ? min(p.q0 / BN, r.L / BN) : r.L / BN, p.n_kv);
+    // A window cuts steps anywhere: every step takes the masked body then.
+    p.n_bulk = a.window > 0 ? 0 : min(CAUSAL ? min(p.q0 / BN, r.L / BN) : r.L / BN, p.n_kv);
     return p;
   };
 
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
               for (int i = 0; i < 16; ++i) {
                 float x = sacc[kt][s][i] * c2;
                 const int key = k0 + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-                const bool ok = key < L && (!CAUSAL || key <= qi);
+                const bool ok = key < L && (!CAUSAL || (key <= qi && (a.window <= 0 || key > qi - a.window)));
                 x = ok ? x : -INFINITY;
                 sacc[kt][s][i] = x;
                 mt = fmaxf(mt, x);

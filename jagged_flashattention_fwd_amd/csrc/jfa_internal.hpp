@@ -61,6 +61,7 @@ struct FwdArgs {
   int64_t total_len;
   int B, H, Lq, d;
   int Hkv, G;        // key / value heads; G = H / Hkv query heads share one
+  int window;        // causal sliding window in keys (query i sees i - window < j <= i); 0: none
   float scale_log2;  // softmax scale times log2(e)
   int causal, broadcast_q;
   int P;             // persistent workgroups
@@ -98,6 +99,7 @@ struct BwdArgs {
   unsigned int* qtile_ctr;  // query tiles handed out past the first one per workgroup
   int B, H, Lq, d;
   int Hkv, G;             // key / value heads; G = H / Hkv query heads share one
+  int window;             // causal sliding window in keys; 0: none
   int64_t total_len;
   float scale;
   float scale_log2;

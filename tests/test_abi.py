@@ -31,7 +31,7 @@ def test_header_declares_expected_calls():
     assert _declared_functions() == sorted([
         "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_kernel_name", "jfa_schedule_params",
         "jfa_status_string", "jfa_timing_enable", "jfa_timing_read", "jfa_timing_reset",
-        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_gqa", "jfa_bwd_gqa"])
+        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -91,18 +91,28 @@ def test_gqa_calls_reject_heads_that_do_not_split(lib, H, H_kv):
     vp = ctypes.c_void_p
     out = ctypes.c_size_t(0)
     assert lib.jfa_workspace_size_gqa(10, 2, H, H_kv, 8, 128, 0, 1, 1, ctypes.byref(out)) == 1
-    assert lib.jfa_fwd_gqa(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, H, H_kv, 8, 128, 0.1, 0, 1, vp(FAKE),
-                           vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
-    assert lib.jfa_bwd_gqa(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, H, H_kv, 8, 128, 0.1, 0, 1, vp(FAKE),
-                           vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
+    assert lib.jfa_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, H, H_kv, 8, 128, 0.1, 0, 0, 1, vp(FAKE),
+                          vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
+    assert lib.jfa_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, H, H_kv, 8, 128, 0.1, 0, 0, 1, vp(FAKE),
+                          vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
 
 
 def test_gqa_calls_check_sizes_like_the_plain_ones(lib):
     vp = ctypes.c_void_p
-    assert lib.jfa_fwd_gqa(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 4, 2, 8, 96, 0.1, 0, 1, vp(FAKE),
-                           vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 2
-    assert lib.jfa_fwd_gqa(vp(FAKE), vp(0), vp(FAKE), vp(FAKE), 2, 4, 2, 8, 128, 0.1, 0, 1, vp(FAKE),
-                           vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
+    assert lib.jfa_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 4, 2, 8, 96, 0.1, 0, 0, 1, vp(FAKE),
+                          vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 2
+    assert lib.jfa_fwd_ex(vp(FAKE), vp(0), vp(FAKE), vp(FAKE), 2, 4, 2, 8, 128, 0.1, 0, 0, 1, vp(FAKE),
+                          vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
+
+
+@pytest.mark.parametrize("causal,window,code", [(0, 5, 2), (1, -1, 1), (0, -3, 1)])
+def test_window_argument_checks(lib, causal, window, code):
+    vp = ctypes.c_void_p
+    assert lib.jfa_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 2, 2, 8, 128, 0.1, causal, window, 1,
+                          vp(FAKE), vp(FAKE), 10, vp(FAKE), 1 << 30, None) == code
+    assert lib.jfa_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 2, 2, 8, 128, 0.1, causal, window, 1,
+                          vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 10, vp(FAKE), 1 << 30,
+                          None) == code
 
 
 def test_kernel_names(lib):
