@@ -34,9 +34,18 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 # ------------------------------------------------------------ counting ----
-def visible_pairs(lengths, Lq: int, causal: bool, broadcast_q: bool) -> int:
-    """Number of (query, key) pairs the mask leaves visible, per head."""
+def visible_pairs(lengths, Lq: int, causal: bool, broadcast_q: bool, window: int = 0) -> int:
+    """Number of (query, key) pairs the mask leaves visible, per head
+    (window W > 0 with causal: query i sees keys i - W < j <= i)."""
     L = np.asarray(lengths, dtype=np.int64)
+    if causal and window > 0:
+        if broadcast_q:
+            i = np.arange(Lq, dtype=np.int64)[:, None]
+            hi = np.minimum(i, L[None, :] - 1)
+            lo = np.maximum(i - window + 1, 0)
+            return int(np.maximum(hi - lo + 1, 0).sum())
+        short = np.minimum(L, window)
+        return int((short * (short + 1) // 2 + (L - short) * window).sum())
     if broadcast_q:
         if not causal:
             return int(Lq * L.sum())
@@ -48,8 +57,8 @@ def visible_pairs(lengths, Lq: int, causal: bool, broadcast_q: bool) -> int:
     return int((L * L).sum())
 
 
-def useful_flops(lengths, H: int, d: int, Lq: int, causal: bool, broadcast_q: bool):
-    n = visible_pairs(lengths, Lq, causal, broadcast_q)
+def useful_flops(lengths, H: int, d: int, Lq: int, causal: bool, broadcast_q: bool, window: int = 0):
+    n = visible_pairs(lengths, Lq, causal, broadcast_q, window)
     return 4 * d * H * n, 10 * d * H * n
 
 
@@ -61,12 +70,16 @@ def dq_split(B: int, H: int, Lq: int, P: int):
     return n_qb, nc
 
 
-def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q: bool, P: int) -> int:
+def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q: bool, P: int,
+                      H_kv: int = 0) -> int:
     """Bytes a kernel must move between HBM and the chip for one launch:
-    every input element read once and every output element written once."""
+    every input element read once and every output element written once.
+    With H_kv < H key / value heads the dK/dV kernel writes one fp32 slice
+    per query head, which group_sum_kernel adds per group."""
     T = int(np.asarray(lengths).sum())
     B = len(lengths)
-    kv = T * H * d * 2                    # one bf16 [T, H, d] tensor
+    H_kv = H_kv or H
+    kv = T * H_kv * d * 2                 # one bf16 [T, H_kv, d] tensor
     rows = B * H * Lq if broadcast_q else T * H
     row_bf16 = rows * d * 2               # out / dout, bf16
     q_bytes = H * Lq * d * 2 if broadcast_q else T * H * d * 2
@@ -85,6 +98,8 @@ def algorithmic_bytes(kernel: str, lengths, H: int, d: int, Lq: int, broadcast_q
             n_qb, nc = dq_split(B, H, Lq, P)
             return b + H * n_qb * nc * 256 * d * 4
         return b + T * H * d * 4
+    if kernel == "group_sum_kernel":
+        return 2 * T * H * d * 4 + 2 * T * H_kv * d * 4
     if kernel == "dq_reduce":
         n_qb, nc = dq_split(B, H, Lq, P)
         return H * n_qb * nc * 256 * d * 4 + H * Lq * d * 4
@@ -209,9 +224,9 @@ def cpu_baseline(t, w, scale, seconds: float):
             qb = t["q"][s0:s1].float().cpu().numpy().astype(np.float64)
             dob = t["dout"][s0:s1].float().cpu().numpy().astype(np.float64)
         o1 = np.array([0, s1 - s0], dtype=np.int64)
-        jo.jagged_forward(qb, k, v, o1, scale, w.causal, w.broadcast_q)
-        jo.jagged_backward(qb, k, v, o1, scale, w.causal, w.broadcast_q, dob)
-        f, b = useful_flops([s1 - s0], w.H, w.d, w.Lq, w.causal, w.broadcast_q)
+        jo.jagged_forward(qb, k, v, o1, scale, w.causal, w.broadcast_q, window=w.window)
+        jo.jagged_backward(qb, k, v, o1, scale, w.causal, w.broadcast_q, dob, window=w.window)
+        f, b = useful_flops([s1 - s0], w.H, w.d, w.Lq, w.causal, w.broadcast_q, w.window)
         flops += f + b
         done += 1
     el = time.perf_counter() - t0
@@ -264,6 +279,7 @@ def main(argv=None):
     T = t["total_len"]
     scale = w.scale
     H, d, Lq, B = w.H, w.d, w.Lq, w.B
+    H_kv, window = w.kv_heads, w.window
     bq, causal = w.broadcast_q, w.causal
     q, k, v, off, dout = t["q"], t["k"], t["v"], t["offsets"], t["dout"]
 
@@ -274,15 +290,22 @@ def main(argv=None):
         out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dk = torch.empty((T, H, d), dtype=torch.float32, device=dev)
-    dv = torch.empty((T, H, d), dtype=torch.float32, device=dev)
-    ws_f = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, dev)
-    ws_b = jfa.workspace(T, B, H, Lq, d, causal, bq, 1, dev)
+    dk = torch.empty((T, H_kv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((T, H_kv, d), dtype=torch.float32, device=dev)
+    ws_f = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, dev, H_kv=H_kv)
+    ws_b = jfa.workspace(T, B, H, Lq, d, causal, bq, 1, dev, H_kv=H_kv)
     _, P = jfa.jfa_schedule_params(1, causal, bq, d)
 
+    def fwd():
+        jfa.jfa_fwd_ex(q, k, v, off, B, H, H_kv, Lq, d, scale, causal, window, bq, out, lse, T, ws_f)
+
+    def bwd():
+        jfa.jfa_bwd_ex(q, k, v, off, B, H, H_kv, Lq, d, scale, causal, window, bq, out, lse, dout, dq, dk, dv,
+                       T, ws_b)
+
     def step():
-        jfa.jfa_fwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, T, ws_f)
-        jfa.jfa_bwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, dout, dq, dk, dv, T, ws_b)
+        fwd()
+        bwd()
 
     for _ in range(args.warmup):
         step()
@@ -298,9 +321,9 @@ def main(argv=None):
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        jfa.jfa_fwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, T, ws_f)
+        fwd()
         ev[i][1].record(stream)
-        jfa.jfa_bwd(q, k, v, off, B, H, Lq, d, scale, causal, bq, out, lse, dout, dq, dk, dv, T, ws_b)
+        bwd()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -310,7 +333,7 @@ def main(argv=None):
     ms_step = (t1 - t0) * 1e3 / args.steps
     fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
     bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
-    fwd_fl, bwd_fl = useful_flops(lengths, H, d, Lq, causal, bq)
+    fwd_fl, bwd_fl = useful_flops(lengths, H, d, Lq, causal, bq, window)
     value = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
     fwd_tf = fwd_fl / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_fl / (bwd_ms * 1e-3) / 1e12
@@ -323,7 +346,7 @@ def main(argv=None):
                                 "ms_per_step": ms / args.steps}
     dom = max(per_kernel, key=lambda n: per_kernel[n]["ms_per_step"])
     avg_s = per_kernel[dom]["avg_ms"] * 1e-3
-    nbytes = algorithmic_bytes(dom, lengths, H, d, Lq, bq, P)
+    nbytes = algorithmic_bytes(dom, lengths, H, d, Lq, bq, P, H_kv)
     kfl = kernel_flops(dom, fwd_fl, bwd_fl, bq)
     gbs = nbytes / avg_s / 1e9
     tfl = kfl / avg_s / 1e12 if kfl else 0.0
@@ -340,7 +363,7 @@ def main(argv=None):
                  "algorithmic_bytes": nbytes, "kernel_useful_flops": kfl,
                  "kernel_tflops": round(tfl, 1), "kernel_gbs": round(gbs, 1)})
     for name, rec in per_kernel.items():
-        b = algorithmic_bytes(name, lengths, H, d, Lq, bq, P)
+        b = algorithmic_bytes(name, lengths, H, d, Lq, bq, P, H_kv)
         rec["avg_ms"] = round(rec["avg_ms"], 4)
         rec["ms_per_step"] = round(rec["ms_per_step"], 4)
         if b:
@@ -351,7 +374,7 @@ def main(argv=None):
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "d": d, "Lq": Lq,
+        "config": {"workload": w.name, "B": B, "H": H, "H_kv": H_kv, "window": window, "d": d, "Lq": Lq,
                    "lengths": list(w.lengths), "causal": causal, "broadcast_q": bq,
                    "total_len": T, "seed": seed, "accumulate": "fp32", "grad_dtype": "fp32"},
         "pct_of_peak": round(value / peak_tflops, 4),

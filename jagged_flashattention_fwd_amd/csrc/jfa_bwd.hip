@@ -311,6 +311,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     const int n_bulk = a.window > 0 ? 0 : CAUSAL ? min(q0 / BN, L / BN) : L / BN;  // window: all masked
+    // First step with a key inside some row's window; earlier steps are skipped.
+    const int j0 = CAUSAL && a.window > 0 ? min(max(0, q0 - a.window + 1) / BN, n_kv) : 0;
     const uint16_t* kbase = a.k + (s0 * a.Hkv + hk) * (int64_t)D;
     const uint16_t* vbase = a.v + (s0 * a.Hkv + hk) * (int64_t)D;
     auto issue = [&](int j) {
@@ -332,15 +334,16 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
     __syncthreads();  // earlier readers of the ring are done
     if constexpr (C::DMA) {
       wait_vmcnt<0>();
-      for (int jj = 0; jj < DEP && jj < n_kv; ++jj) issue(jj);
+      for (int jj = j0; jj < j0 + DEP && jj < n_kv; ++jj) issue(jj);
       after_prologue();
     } else {
       after_prologue();
-      if (n_kv > 0) {
-        kl.load(kbase, ld, min(BN, L), tid);
-        vl.load(vbase, ld, min(BN, L), tid);
-        kl.store(smem[0][0], tid);
-        vl.store(smem[0][1], tid);
+      if (n_kv > j0) {
+        const int r0 = j0 * BN;
+        kl.load(kbase + (int64_t)r0 * ld, ld, min(BN, L - r0), tid);
+        vl.load(vbase + (int64_t)r0 * ld, ld, min(BN, L - r0), tid);
+        kl.store(smem[j0 % NBUF][0], tid);
+        vl.store(smem[j0 % NBUF][1], tid);
       }
       __syncthreads();
     }
@@ -375,8 +378,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
       }
     };
     const int n_plain = min(n_bulk, n_kv);
-    for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
-    for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+    for (int j = j0; j < n_plain; ++j) kv_step(j, std::false_type{});
+    for (int j = max(n_plain, j0); j < n_kv; ++j) kv_step(j, std::true_type{});
   };
 
   if constexpr (!BCAST) {
@@ -512,6 +515,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
   struct Sq {
     int64_t s0, row;
     int L, n_kv, n_bulk, r;
+    int j0;              // first step: the steps before it lie wholly outside every row's window
     const uint16_t* kb;  // K / V rows s0 of head h
     const uint16_t* vb;
   };
@@ -527,6 +531,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     if (CAUSAL) kv_end = min(kv_end, q0 + BM);
     q.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     q.n_bulk = a.window > 0 ? 0 : min(CAUSAL ? min(q0 / BN, q.L / BN) : q.L / BN, q.n_kv);  // window: all masked
+    q.j0 = CAUSAL && a.window > 0 ? min(max(0, q0 - a.window + 1) / BN, q.n_kv) : 0;
     return q;
   };
   // The first sequence of the chunk at or after position r with keys to
@@ -535,9 +540,10 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     Sq q;
     q.r = B;
     q.n_kv = 0;
+    q.j0 = 0;
     for (; r < B; r += NC) {
       q = seq_at(r);
-      if (q.n_kv > 0) break;
+      if (q.n_kv > q.j0) break;
       q.r = B;
     }
     return q;
@@ -551,12 +557,12 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
   int j_last = 0;
   bool j_on = false;
   auto prep_next = [&](const Sq& cp, const Sq& np, bool has_nxt) {
-    const int nn = has_nxt ? np.n_kv : 0;
-    const bool cur = iss_cur < cp.n_kv;
+    const int nn = has_nxt ? np.n_kv - np.j0 : 0;
+    const bool cur = iss_cur < cp.n_kv - cp.j0;
     j_on = cur || iss_nxt < nn;
     if (!j_on) return;
     const int L_ = cur ? cp.L : np.L;
-    const int j = cur ? iss_cur : iss_nxt;
+    const int j = cur ? cp.j0 + iss_cur : np.j0 + iss_nxt;
     const int base_row = min(j * BN + wave * RPW, L_ - 1);
     // byte offset of the row within the sequence (a 32 x 32-bit product)
     const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(ld * 2);
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     if (has_nxt) load_seq(np);
     const int L = cp.L, n_kv = cp.n_kv;
     {
-      const int need = min(DEP, n_kv);
+      const int need = min(DEP, n_kv - cp.j0);
       if (iss_cur < need) {
         while (iss_cur < need) {
           prep_next(cp, np, has_nxt);
@@ -735,8 +741,8 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
       }
       ++g_cmp;
     };
-    for (int j = 0; j < cp.n_bulk; ++j) kv_step(j, std::false_type{});
-    for (int j = cp.n_bulk; j < n_kv; ++j) kv_step(j, std::true_type{});
+    for (int j = cp.j0; j < cp.n_bulk; ++j) kv_step(j, std::false_type{});
+    for (int j = max(cp.n_bulk, cp.j0); j < n_kv; ++j) kv_step(j, std::true_type{});
     cp = np;
     iss_cur = iss_nxt;
     iss_nxt = 0;

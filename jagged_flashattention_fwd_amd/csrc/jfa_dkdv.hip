@@ -236,6 +236,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
     p.nq = BCAST ? Lq : r.L;
     p.m_first = CAUSAL ? p.k0 / QB : 0;                 // query blocks that can see a key of the tile
     p.m_end = max((p.nq + QB - 1) / QB, p.m_first);     // exclusive
+    // Window: rows past k0 + BN - 2 + window see no key of the tile.
+    if (CAUSAL && a.window > 0) p.m_end = max(min(p.m_end, (p.k0 + BN - 2 + a.window) / QB + 1), p.m_first);
     p.qb = BCAST ? a.q + (int64_t)r.h * Lq * D : a.q + (r.s0 * H + r.h) * (int64_t)D;
     p.db = BCAST ? a.dout + ((int64_t)r.b * H + r.h) * Lq * D : a.dout + (r.s0 * H + r.h) * (int64_t)D;
     p.vb = reinterpret_cast<const u32x4*>((wave & 1) ? a.term_d : a.term_l) +

@@ -126,6 +126,9 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     // A window cuts steps anywhere: every step takes the masked body then.
     const int n_bulk = a.window > 0 ? 0 : CAUSAL ? min(q0 / BN, L / BN) : L / BN;
+    // First step with a key inside some row's window (the tile's first row
+    // sees keys from q0 - window + 1 on); the steps before it are skipped.
+    const int j0 = CAUSAL && a.window > 0 ? min(max(0, q0 - a.window + 1) / BN, n_kv) : 0;
 
     const uint16_t* kbase = a.k + (s0 * a.Hkv + tile.hk) * (int64_t)D;
     const uint16_t* vbase = a.v + (s0 * a.Hkv + tile.hk) * (int64_t)D;
@@ -154,13 +157,14 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
     __syncthreads();  // the previous tile's readers are done with LDS
     if constexpr (C::DMA) {
       wait_vmcnt<0>();  // Q rows (and the last tile's stores) are not counted below
-      for (int jj = 0; jj < DEP && jj < n_kv; ++jj) issue(jj);
+      for (int jj = j0; jj < j0 + DEP && jj < n_kv; ++jj) issue(jj);
     } else {
-      if (n_kv > 0) {
-        kl.load(kbase, ld, min(BN, L), tid);
-        vl.load(vbase, ld, min(BN, L), tid);
-        kl.store(smem[0][0], tid);
-        vl.store(smem[0][1], tid);
+      if (n_kv > j0) {
+        const int r0 = j0 * BN;
+        kl.load(kbase + (int64_t)r0 * ld, ld, min(BN, L - r0), tid);
+        vl.load(vbase + (int64_t)r0 * ld, ld, min(BN, L - r0), tid);
+        kl.store(smem[j0 % NBUF][0], tid);
+        vl.store(smem[j0 % NBUF][1], tid);
       }
       __syncthreads();
     }
@@ -294,8 +298,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel(FwdArgs a) {
       }
     };
     const int n_plain = min(n_bulk, n_kv);
-    for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
-    for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+    for (int j = j0; j < n_plain; ++j) kv_step(j, std::false_type{});
+    for (int j = max(n_plain, j0); j < n_kv; ++j) kv_step(j, std::true_type{});
 
     // ---- epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2.
 #pragma unroll
@@ -365,6 +369,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   struct Tp {
     int64_t s0;
     int L, h, b, q0, n_kv, n_bulk;
+    int j0;  // first step: the steps before it lie wholly outside every row's window
     const uint16_t* kb;
     const uint16_t* vb;
   };
@@ -383,6 +388,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     p.n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     // A window cuts steps anywhere: every step takes the masked body then.
     p.n_bulk = a.window > 0 ? 0 : min(CAUSAL ? min(p.q0 / BN, r.L / BN) : r.L / BN, p.n_kv);
+    p.j0 = CAUSAL && a.window > 0 ? min(max(0, p.q0 - a.window + 1) / BN, p.n_kv) : 0;
     return p;
   };
 
@@ -398,12 +404,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   int j_last = 0;
   bool j_on = false;
   auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
-    const int nn = has_nxt ? np.n_kv : 0;
-    const bool cur = iss_cur < cp.n_kv;
+    const int nn = has_nxt ? np.n_kv - np.j0 : 0;
+    const bool cur = iss_cur < cp.n_kv - cp.j0;
     j_on = cur || iss_nxt < nn;
     if (!j_on) return;
     const int L_ = cur ? cp.L : np.L;
-    const int j = cur ? iss_cur : iss_nxt;
+    const int j = cur ? cp.j0 + iss_cur : np.j0 + iss_nxt;
     const int base_row = min(j * BN + wave * RPW, L_ - 1);
     // byte offset of the row within the sequence (a 32 x 32-bit product)
     const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(ld * 2);
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // the previous tile, before its Q loads for this tile, and only the
     // previous tile's NST stores may be outstanding after those.
     {
-      const int need = min(DEP, n_kv);
+      const int need = min(DEP, n_kv - cp.j0);
       if (iss_cur < need) {
         while (iss_cur < need) {
           prep_next(cp, cp, false);  // this tile's steps only
@@ -747,8 +753,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     };
     if constexpr (CAUSAL) {
       const int n_plain = cp.n_bulk;
-      for (int j = 0; j < n_plain; ++j) kv_step(j, std::false_type{});
-      for (int j = n_plain; j < n_kv; ++j) kv_step(j, std::true_type{});
+      for (int j = cp.j0; j < n_plain; ++j) kv_step(j, std::false_type{});
+      for (int j = max(n_plain, cp.j0); j < n_kv; ++j) kv_step(j, std::true_type{});
     } else if (n_kv > 0) {
       // Software-pipelined steps: the S products of step j + 1 run beside
       // the softmax of step j (split into pieces between their k-steps), then

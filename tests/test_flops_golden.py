@@ -49,3 +49,21 @@ def test_visible_pairs_closed_forms():
 
 def test_bench_refuses_more_than_one_gpu():
     assert bench.main(["--gpus", "2"]) == 2
+
+
+@pytest.mark.parametrize("bq", [False, True])
+def test_visible_pairs_with_a_window_by_brute_force(bq):
+    """Query i sees key j when j <= i, i - W < j and j < L: counted pair by
+    pair on small cases, against the closed forms bench.py uses."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        L = [int(x) for x in rng.integers(0, 40, size=5)]
+        W = int(rng.integers(1, 50))
+        Lq = int(rng.integers(1, 60)) if bq else 0
+        n = 0
+        for Lb in L:
+            for i in range(Lq if bq else Lb):
+                n += sum(1 for j in range(Lb) if j <= i and j > i - W)
+        assert bench.visible_pairs(L, Lq, True, bq, W) == n
+    # a window at least as long as every sequence is the plain causal count
+    assert bench.visible_pairs([5, 9], 12, True, bq, 64) == bench.visible_pairs([5, 9], 12, True, bq)

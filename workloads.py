@@ -22,6 +22,12 @@ at sequence length 1024, self-attention without and with the causal mask:
   dense_llm_1k         self-attn,         B=768, H=4, d=128, L = 1024
   dense_llm_1k_causal  self-attn, causal, B=768, H=4, d=128, L = 1024
 
+and two of the attention variants the pages name (grouped-query heads and a
+sliding window), on the shapes above:
+
+  prod_bcast_gqa         prod_bcast with one key/value head for the 4 query heads
+  long_causal_8k_window  long_causal_8k with a causal window of 1024 keys
+
 Lengths are drawn with numpy's PCG64 from the seed; integer draws are
 inclusive.  Log-uniform lengths are round(exp(U(ln lo, ln hi))) clipped to
 [lo, hi].  In skew_bcast exactly round(0.1*B) sequences, at seeded random
@@ -55,6 +61,12 @@ class Workload:
     lengths: tuple  # ("uniform", lo, hi) | ("loguniform", lo, hi) | ("mix", frac_long, (lo,hi), (lo,hi))
     std: float = 1.0
     tags: tuple = field(default_factory=tuple)
+    H_kv: int = 0  # key / value heads (grouped-query attention); 0: H
+    window: int = 0  # causal sliding window in keys; 0: none
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def scale(self) -> float:
@@ -71,6 +83,9 @@ WORKLOADS = [
     # The pages' second regime: dense LLM attention, equal-length Q/K/V.
     Workload("dense_llm_1k", False, False, 768, 4, 128, 0, ("uniform", 1024, 1024)),
     Workload("dense_llm_1k_causal", False, True, 768, 4, 128, 0, ("uniform", 1024, 1024)),
+    # Attention variants on the shapes above.
+    Workload("prod_bcast_gqa", True, False, 1024, 4, 128, 256, ("uniform", 64, 2048), H_kv=1),
+    Workload("long_causal_8k_window", False, True, 64, 16, 128, 0, ("loguniform", 128, 8192), window=1024),
 ]
 
 
@@ -169,5 +184,8 @@ def make_workload(w, seed: int | None = None, device="cpu", with_dout: bool = Tr
         seed = WORKLOADS.index(w)
     lengths = draw_lengths(w.lengths, w.B, seed)
     t = make_tensors(lengths, w.H, w.d, w.Lq, w.broadcast_q, w.std, seed, device, with_dout)
+    if w.kv_heads < w.H:  # the first H_kv heads of the draw
+        t["k"] = t["k"][:, :w.kv_heads].contiguous()
+        t["v"] = t["v"][:, :w.kv_heads].contiguous()
     t["workload"] = w
     return t
