@@ -45,6 +45,11 @@
  *   - Every call returns a jfa_status.  Argument errors are detected on the
  *     host before anything is enqueued; JFA_ERR_HIP reports a failed HIP
  *     runtime call or kernel launch.
+ *   - Offsets are device data, so their values are not checked by default
+ *     (see the clamping above).  With JFA_DEBUG=1 in the environment,
+ *     jfa_fwd / jfa_bwd (and the _ex forms) first copy the offsets to the
+ *     host, synchronising `stream`, and return JFA_ERR_INVALID_ARG unless
+ *     offsets[0] = 0, offsets[b] <= offsets[b+1] and offsets[B] = total_len.
  */
 #ifndef JFA_H
 #define JFA_H
@@ -65,11 +70,11 @@ typedef enum {
 } jfa_status;
 
 /* Workspace bytes needed by jfa_fwd (pass = 0) or jfa_bwd (pass = 1) for
- * these sizes, written to *bytes.  The size depends on the current device's
- * compute-unit count (the backward keeps one fp32 dQ partial [H, Lq, d] per
- * persistent workgroup in broadcast mode).  No work is enqueued. */
-int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q,
-                       int pass, size_t* bytes);
+ * these sizes (tile lists, per-row scratch of the backward, the broadcast
+ * dQ partials; the size depends on the current device's compute-unit
+ * count).  Returns 0 for arguments the calls would reject (a valid size is
+ * never 0).  No work is enqueued. */
+size_t jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q, int pass);
 
 /* Forward.  Writes out (bf16) and lse (fp32) in the layouts above.
  * Scheduling (sequence sort by length, tile list) runs on the device. */
@@ -77,11 +82,18 @@ int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets,
             int d, float scale, int causal, int broadcast_q, void* out, float* lse, int64_t total_len,
             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward.  `out` and `lse` must come from jfa_fwd with identical
- * arguments; `dout` is dL/dO.  Writes dq, dk, dv (fp32) in the layouts
- * above.  The result is bitwise reproducible for a given device: every
- * reduction runs in a fixed order (broadcast-mode dQ is summed from
- * per-workgroup partials by a fixed pairwise tree, never by atomics). */
+/* Backward: the exact derivative of the forward, dP = dO V^T,
+ * delta = rowsum(dO o O), dS = P o (dP - delta), dQ = scale dS K,
+ * dK = scale dS^T Q, dV = P^T dO (five products per K/V block,
+ * "Optimizing Jagged Flash Attention with TLX", "2-CTA collaborative MMA";
+ * broadcast dQ summed over the batch, "1. The Challenge").  `out` and `lse`
+ * must come from jfa_fwd with identical arguments; `dout` is dL/dO.  Writes
+ * dq, dk, dv (fp32) in the layouts above.  The result is bitwise
+ * reproducible for a given device: every reduction runs in a fixed order
+ * (broadcast-mode dQ is summed from per-workgroup partials by a fixed
+ * pairwise tree, never by atomics).  |scale| must be at least 2^-100
+ * (JFA_ERR_INVALID_ARG otherwise, scale = 0 included): the dK / dV kernel
+ * folds -lse / scale into its score products. */
 int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,
             int d, float scale, int causal, int broadcast_q, const void* out, const float* lse,
             const void* dout, float* dq, float* dk, float* dv, int64_t total_len, void* workspace,
@@ -104,13 +116,13 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
  * otherwise, JFA_ERR_INVALID_ARG for W < 0) lets query i see keys j with
  * i - W < j <= i; window = 0 is no window.  A query row that sees no key
  * (broadcast mode, i - W >= L_b) gives O = 0, lse = -inf and no gradient.
- * Out-of-window keys are masked inside the causal key range (every step
- * takes the masked path); they are not skipped.
+ * Key steps and query blocks wholly outside every row's window are skipped;
+ * the steps and blocks that remain take the masked path.
  *
  * jfa_fwd and jfa_bwd above are these with H_kv = H and window = 0.  Every
  * other argument, layout and rule is as above. */
-int jfa_workspace_size_gqa(int64_t total_len, int B, int H, int H_kv, int Lq, int d, int causal,
-                           int broadcast_q, int pass, size_t* bytes);
+size_t jfa_workspace_size_gqa(int64_t total_len, int B, int H, int H_kv, int Lq, int d, int causal,
+                              int broadcast_q, int pass);
 int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
                int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
                int64_t total_len, void* workspace, size_t workspace_bytes, void* stream);
@@ -125,13 +137,27 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
  * tile list.  Host-only. */
 int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block_rows, int* workers);
 
-/* Test hook: builds the tile list of a pass exactly as jfa_fwd / jfa_bwd do
- * and copies it to `tiles` (device int32 [cap][4]: b, h, block, worker slot),
- * in list order; *n_tiles (device int64) receives the full tile count.  At
- * most `cap` tiles are written.  Uses the workspace of that pass. */
+/* Test hooks for the tile schedule ("Optimizing Jagged Flash Attention with
+ * TLX", "Scheduling jagged tiles across SMs": sequences sorted by K/V
+ * workload, longest first, and tiles handed to the persistent workers in a
+ * zigzag).  Each builds a tile list exactly as jfa_fwd / jfa_bwd do and
+ * copies it to `tiles` (device int32), in list order; *n_tiles (device
+ * int64) receives the full tile count; at most `cap` tiles are written.
+ * total_len is offsets[B], passed so that the workspace is sized on the
+ * host without reading the offsets.
+ *   jfa_debug_schedule: pass 0 = forward query tiles, 1 = backward key
+ *     tiles; [cap][4] = b, h, block, worker slot; workspace of that pass.
+ *   jfa_debug_schedule_ex: list 0 = forward query tiles, 1 = backward key
+ *     tiles, 2 = the self-attention backward's dQ query tiles
+ *     (broadcast_q = 0 only); H_kv key / value heads as in jfa_fwd_ex;
+ *     [cap][5] = b, h, block, key / value head, worker slot; workspace of
+ *     the forward (list 0) or backward (lists 1, 2). */
 int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q,
                        int pass, int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles,
                        void* workspace, size_t workspace_bytes, void* stream);
+int jfa_debug_schedule_ex(const int64_t* offsets, int B, int H, int H_kv, int Lq, int causal, int broadcast_q,
+                          int list, int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing for measurement tools (not thread-safe; host-only
  * bookkeeping).  jfa_timing_enable(capacity) creates 2*capacity hipEvents and

@@ -22,8 +22,8 @@ STATUS_NAMES = {0: "JFA_OK", 1: "JFA_ERR_INVALID_ARG", 2: "JFA_ERR_UNSUPPORTED",
 # Symbols declared in include/jfa.h, with their ctypes signatures.
 _c = ctypes
 _SIGS = {
-    "jfa_workspace_size": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
-                                      _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
+    "jfa_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                         _c.c_int, _c.c_int]),
     "jfa_fwd": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
                            _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
                            _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -31,8 +31,8 @@ _SIGS = {
                            _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p,
                            _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                            _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
-    "jfa_workspace_size_gqa": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
-                                          _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
+    "jfa_workspace_size_gqa": (_c.c_size_t, [_c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                             _c.c_int, _c.c_int, _c.c_int]),
     "jfa_fwd_ex": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
                               _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_int,
                               _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -45,6 +45,9 @@ _SIGS = {
     "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                       _c.c_int, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                       _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_debug_schedule_ex": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                         _c.c_int, _c.c_int, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                         _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "jfa_status_string": (_c.c_char_p, [_c.c_int]),
     "jfa_timing_enable": (_c.c_int, [_c.c_int]),
     "jfa_timing_reset": (_c.c_int, []),
@@ -95,17 +98,17 @@ def _stream(stream):
 
 # ------------------------------------------------------- C names ---------
 def jfa_workspace_size(total_len, B, H, Lq, d, causal, broadcast_q, pass_) -> int:
-    out = ctypes.c_size_t(0)
-    _check(lib().jfa_workspace_size(int(total_len), B, H, Lq, d, int(causal), int(broadcast_q), pass_,
-                                    ctypes.byref(out)), "jfa_workspace_size")
-    return out.value
+    n = lib().jfa_workspace_size(int(total_len), B, H, Lq, d, int(causal), int(broadcast_q), pass_)
+    if n == 0:
+        raise RuntimeError("jfa_workspace_size: arguments rejected")
+    return n
 
 
 def jfa_workspace_size_gqa(total_len, B, H, H_kv, Lq, d, causal, broadcast_q, pass_) -> int:
-    out = ctypes.c_size_t(0)
-    _check(lib().jfa_workspace_size_gqa(int(total_len), B, H, H_kv, Lq, d, int(causal), int(broadcast_q),
-                                        pass_, ctypes.byref(out)), "jfa_workspace_size_gqa")
-    return out.value
+    n = lib().jfa_workspace_size_gqa(int(total_len), B, H, H_kv, Lq, d, int(causal), int(broadcast_q), pass_)
+    if n == 0:
+        raise RuntimeError("jfa_workspace_size_gqa: arguments rejected")
+    return n
 
 
 def jfa_fwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, total_len,
@@ -153,6 +156,14 @@ def jfa_debug_schedule(offsets, B, H, Lq, causal, broadcast_q, pass_, total_len,
                                     int(total_len), _ptr(tiles), tiles.shape[0], _ptr(n_tiles),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "jfa_debug_schedule")
+
+
+def jfa_debug_schedule_ex(offsets, B, H, H_kv, Lq, causal, broadcast_q, list_, total_len, tiles, n_tiles,
+                          workspace, stream=None):
+    _check(lib().jfa_debug_schedule_ex(_ptr(offsets), B, H, H_kv, Lq, int(causal), int(broadcast_q), list_,
+                                       int(total_len), _ptr(tiles), tiles.shape[0], _ptr(n_tiles),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "jfa_debug_schedule_ex")
 
 
 def jfa_timing_enable(capacity: int):

@@ -1,11 +1,14 @@
 // Host side of the C-ABI (include/jfa.h): argument checks, workspace
 // carving, template dispatch and launches on the caller's stream.  Nothing
-// here allocates, frees or synchronises.
+// here allocates or frees device memory, and nothing synchronises unless
+// JFA_DEBUG=1 asks for the offsets check.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "jfa.h"
 #include "jfa_internal.hpp"
@@ -14,20 +17,61 @@ namespace jfa {
 namespace {
 
 constexpr int MAX_DEVICES = 64;
-int g_cu_count[MAX_DEVICES];
-std::once_flag g_cu_once[MAX_DEVICES];
 
-// Compute units of the current device (cached per device).
-int cu_count(int* out) {
+// Per-device set-up, done once per device with that device current: the
+// compute-unit count and the kernel attributes the launches rely on.
+struct DeviceState {
+  int cus = 0;
+  int rc = JFA_ERR_HIP;
+};
+DeviceState g_dev[MAX_DEVICES];
+std::once_flag g_dev_once[MAX_DEVICES];
+
+int device_state(DeviceState** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return JFA_ERR_HIP;
-  std::call_once(g_cu_once[dev], [dev] {
+  std::call_once(g_dev_once[dev], [dev] {
+    DeviceState& st = g_dev[dev];
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    g_cu_count[dev] = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return;
+    if (init_schedule_kernels() != hipSuccess) return;
+    st.cus = n;
+    st.rc = JFA_OK;
   });
-  if (g_cu_count[dev] <= 0) return JFA_ERR_HIP;
-  *out = g_cu_count[dev];
+  *out = &g_dev[dev];
+  return g_dev[dev].rc;
+}
+
+// Compute units of the current device.
+int cu_count(int* out) {
+  DeviceState* st = nullptr;
+  const int rc = device_state(&st);
+  if (rc != JFA_OK) return rc;
+  *out = st->cus;
+  return JFA_OK;
+}
+
+// JFA_DEBUG=1 in the environment: check the offsets tensor on the host
+// before launching (one synchronous copy of B + 1 values).
+bool debug_checks() {
+  static const bool on = [] {
+    const char* e = getenv("JFA_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+// offsets[0] = 0, non-decreasing, offsets[B] = total_len ("Optimizing Jagged
+// Flash Attention with TLX", "Introduction": sequence b owns the packed rows
+// offsets[b] .. offsets[b+1]-1).
+int check_offsets_sync(const int64_t* offsets, int B, int64_t total_len, hipStream_t st) {
+  std::vector<int64_t> h((size_t)B + 1);
+  if (hipMemcpyAsync(h.data(), offsets, sizeof(int64_t) * h.size(), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return JFA_ERR_HIP;
+  if (h[0] != 0 || h[B] != total_len) return JFA_ERR_INVALID_ARG;
+  for (int b = 0; b < B; ++b)
+    if (h[b + 1] < h[b]) return JFA_ERR_INVALID_ARG;
   return JFA_OK;
 }
 
@@ -152,7 +196,7 @@ int workers(int pass, int* P) {
   const int rc = cu_count(&cus);
   if (rc != JFA_OK) return rc;
   (void)pass;
-  *P = cus;  // one persistent workgroup (4 waves) per compute unit
+  *P = cus;  // one persistent workgroup per compute unit
   return JFA_OK;
 }
 
@@ -183,24 +227,18 @@ int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block
   return workers(pass, workers_out);
 }
 
-int jfa_workspace_size_gqa(int64_t total_len, int B, int H, int H_kv, int Lq, int d, int causal,
-                           int broadcast_q, int pass, size_t* bytes) {
+size_t jfa_workspace_size_gqa(int64_t total_len, int B, int H, int H_kv, int Lq, int d, int causal,
+                              int broadcast_q, int pass) {
   (void)causal;
-  if (!bytes || (pass != 0 && pass != 1)) return JFA_ERR_INVALID_ARG;
-  int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
-  if (rc != JFA_OK) return rc;
-  rc = check_heads(H, H_kv);
-  if (rc != JFA_OK) return rc;
+  if (pass != 0 && pass != 1) return 0;
+  if (check_sizes(total_len, B, H, Lq, d, broadcast_q) != JFA_OK || check_heads(H, H_kv) != JFA_OK) return 0;
   int P = 0;
-  rc = workers(pass, &P);
-  if (rc != JFA_OK) return rc;
-  *bytes = layout(pass, total_len, B, H, H_kv, broadcast_q ? Lq : 0, d, broadcast_q, P).total;
-  return JFA_OK;
+  if (workers(pass, &P) != JFA_OK) return 0;
+  return layout(pass, total_len, B, H, H_kv, broadcast_q ? Lq : 0, d, broadcast_q, P).total;
 }
 
-int jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q,
-                       int pass, size_t* bytes) {
-  return jfa_workspace_size_gqa(total_len, B, H, H, Lq, d, causal, broadcast_q, pass, bytes);
+size_t jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int causal, int broadcast_q, int pass) {
+  return jfa_workspace_size_gqa(total_len, B, H, H, Lq, d, causal, broadcast_q, pass);
 }
 
 int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
@@ -224,6 +262,10 @@ int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   const Layout lay = layout(0, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
   if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    rc = check_offsets_sync(offsets, B, total_len, st);
+    if (rc != JFA_OK) return rc;
+  }
   char* ws = static_cast<char*>(workspace);
   const Schedule s = schedule_at(ws, lay.sched_a, lay.cap_a);
 
@@ -269,7 +311,9 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 7))
     return JFA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
+  // The dK / dV kernel folds -lse / scale into its score products, which
+  // needs |scale| >= 2^-100 (then |lse / scale| stays finite in fp32).
+  if (!isfinite(scale) || !(fabsf(scale) >= MIN_BWD_SCALE)) return JFA_ERR_INVALID_ARG;
   int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
   if (rc != JFA_OK) return rc;
   rc = check_heads(H, H_kv);
@@ -283,6 +327,10 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   const Layout lay = layout(1, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
   if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    rc = check_offsets_sync(offsets, B, total_len, st);
+    if (rc != JFA_OK) return rc;
+  }
   char* ws = static_cast<char*>(workspace);
   const Schedule sk = schedule_at(ws, lay.sched_a, lay.cap_a);
   SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 1, BWD_BN, H / H_kv};
@@ -348,13 +396,43 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
                     dv, total_len, workspace, workspace_bytes, stream);
 }
 
+int jfa_debug_schedule_ex(const int64_t* offsets, int B, int H, int H_kv, int Lq, int causal, int broadcast_q,
+                          int list, int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  (void)causal;
+  if (!offsets || !tiles || !n_tiles || !workspace || cap < 0 || list < 0 || list > 2)
+    return JFA_ERR_INVALID_ARG;
+  if (list == 2 && broadcast_q) return JFA_ERR_INVALID_ARG;  // the query-tile list is self-attention only
+  // The schedule does not depend on d; the size checks need a supported one.
+  int rc = check_sizes(total_len, B, H, Lq, 128, broadcast_q);
+  if (rc != JFA_OK) return rc;
+  rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
+  if (!broadcast_q) Lq = 0;
+  const int pass = list == 0 ? 0 : 1;
+  int P = 0;
+  rc = workers(pass, &P);
+  if (rc != JFA_OK) return rc;
+  // The backward's own workspace layout, so that the same workspace serves.
+  const Layout lay = layout(pass, total_len, B, H, H_kv, Lq, 64, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const Schedule s = list == 2 ? schedule_at(ws, lay.sched_b, lay.cap_b) : schedule_at(ws, lay.sched_a, lay.cap_a);
+  const int blk = list == 0 ? fwd_block_rows() : list == 1 ? BWD_BN : DQ_BM;
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, pass, blk, H / H_kv};
+  if (list == 2) sa.pass = 0;  // query tiles: the forward's per-sequence rule
+  if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
+  if (launch_schedule_dump(s, P, tiles, cap, n_tiles, 5, st) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
+}
+
 int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q, int pass,
                        int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles, void* workspace,
                        size_t workspace_bytes, void* stream) {
   (void)causal;
   if (!offsets || !tiles || !n_tiles || !workspace || cap < 0 || (pass != 0 && pass != 1))
     return JFA_ERR_INVALID_ARG;
-  // The fwd check_sizes needs some d; the schedule does not depend on it.
   int rc = check_sizes(total_len, B, H, Lq, 128, broadcast_q);
   if (rc != JFA_OK) return rc;
   if (!broadcast_q) Lq = 0;
@@ -368,7 +446,7 @@ int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal,
   SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, pass,
                pass == 0 ? fwd_block_rows() : BWD_BN, 1};
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
-  if (launch_schedule_dump(s, P, tiles, cap, n_tiles, st) != hipSuccess) return JFA_ERR_HIP;
+  if (launch_schedule_dump(s, P, tiles, cap, n_tiles, 4, st) != hipSuccess) return JFA_ERR_HIP;
   return JFA_OK;
 }
 

@@ -28,6 +28,7 @@ constexpr int DQ_BM = 256;         // self-attention dQ kernel: 8 waves x 32 que
 constexpr int DQ_BM_BCAST = 256;   // broadcast dQ kernel: 8 waves x 32 query rows
 constexpr int DQ_KV_STEP = 64;
 constexpr int MAX_B = 8192;        // single-workgroup sequence sort
+constexpr float MIN_BWD_SCALE = 0x1p-100f;  // smallest |scale| the backward accepts
 
 struct Schedule {
   int* order;         // [B]
@@ -44,8 +45,10 @@ struct SchedArgs {
   int G;  // query heads per key / value head (the tile records' hk = h / G)
 };
 
+// Once per device, with it current: kernel attributes of the scheduler.
+hipError_t init_schedule_kernels();
 hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t stream);
-hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out,
+hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out, int ncol,
                                 hipStream_t stream);
 
 struct FwdArgs {

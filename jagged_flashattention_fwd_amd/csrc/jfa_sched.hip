@@ -150,10 +150,10 @@ __global__ __launch_bounds__(256) void sched_expand(SchedArgs a, Schedule s) {
   const int64_t nblk = a.pass == 0 ? cdiv64(a.broadcast_q ? a.Lq : L, a.blk) : cdiv64(L, a.blk);
   if (nblk <= 0) return;
   // Broadcast-Q backward: the list is head-major (all tiles of head 0, then
-  // head 1, ...), so at any time the persistent workgroups work on one head
-  // and their dQ partials for that head stay cache-resident.  Every
-  // sequence has the same tile count in every head, so head h's part of the
-  // list starts at h * (T / H) and this sequence's tiles at cum[r] / H.
+  // head 1, ...), so at any time the persistent workgroups read one head's
+  // 64-128 KB of Q, which stays resident in L2 beside the K / V streams.
+  // Every sequence has the same tile count in every head, so head h's part
+  // of the list starts at h * (T / H) and this sequence's tiles at cum[r] / H.
   const bool head_major = a.pass == 1 && a.broadcast_q;
   const int64_t T = s.cum[a.B];
   for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
@@ -165,32 +165,35 @@ __global__ __launch_bounds__(256) void sched_expand(SchedArgs a, Schedule s) {
   }
 }
 
-__global__ __launch_bounds__(256) void sched_dump(Schedule s, int P, int32_t* out, int64_t cap, int64_t* n_out) {
+// Tile list in list order, `ncol` int32 per tile: b, h, block, worker slot
+// (ncol = 4) or b, h, block, key / value head, worker slot (ncol = 5).
+__global__ __launch_bounds__(256) void sched_dump(Schedule s, int P, int32_t* out, int64_t cap, int64_t* n_out,
+                                                  int ncol) {
   const int64_t T = *s.n_tiles;
   const int64_t n = T < cap ? T : cap;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
     const TileRec r = s.tiles[t];
-    out[4 * t + 0] = r.b;
-    out[4 * t + 1] = r.h;
-    out[4 * t + 2] = r.blk;
-    out[4 * t + 3] = zigzag_slot(t, P);
+    int32_t* o = out + ncol * t;
+    o[0] = r.b;
+    o[1] = r.h;
+    o[2] = r.blk;
+    if (ncol == 5) o[3] = r.hk;
+    o[ncol - 1] = zigzag_slot(t, P);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_out = T;
 }
 
 }  // namespace
 
+hipError_t init_schedule_kernels() {
+  // Sorting MAX_B keys needs 64 KiB of dynamic LDS.
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(sched_sort_scan),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, MAX_B * 8);
+}
+
 hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t stream) {
   int N = WAVE;  // at least one wave of keys: the shuffle stages span whole waves
   while (N < a.B) N <<= 1;
-  static bool attr_set = false;
-  if (!attr_set) {
-    // Sorting MAX_B keys needs 64 KiB of dynamic LDS.
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sched_sort_scan),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, MAX_B * 8);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   JFA_TIMED_LAUNCH(K_SCHED_SORT, stream, sched_sort_scan, dim3(1), dim3(SORT_THREADS), (size_t)N * 8, stream, a, s, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -198,9 +201,9 @@ hipError_t launch_schedule(const SchedArgs& a, const Schedule& s, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out,
+hipError_t launch_schedule_dump(const Schedule& s, int P, int32_t* out, int64_t cap, int64_t* n_out, int ncol,
                                 hipStream_t stream) {
-  JFA_TIMED_LAUNCH(K_SCHED_DUMP, stream, sched_dump, dim3(256), dim3(256), 0, stream, s, P, out, cap, n_out);
+  JFA_TIMED_LAUNCH(K_SCHED_DUMP, stream, sched_dump, dim3(256), dim3(256), 0, stream, s, P, out, cap, n_out, ncol);
   return hipGetLastError();
 }
 

@@ -30,6 +30,11 @@ count P are parameters; tie-breaks are this library's reading):
      then head 1's, and so on.
   5. Tile t goes to worker slot: pass p = t // P, s = t % P,
      slot = s if p is even else P - 1 - s.
+  6. With grouped-query heads (G query heads per key/value head), a tile
+     of query head h reads key/value head h // G.
+
+The self-attention backward's dQ pass walks query tiles by the forward's
+rules (pass 0) with its own block size.
 """
 from __future__ import annotations
 
@@ -58,12 +63,17 @@ def zigzag_slot(t: int, P: int) -> int:
     return s if p % 2 == 0 else P - 1 - s
 
 
-def schedule(lengths, H: int, Lq: int, broadcast_q: bool, pass_: int, BM: int, BN: int, P: int):
-    """Full tile list: [(b, h, block, slot), ...] in tile order t = 0, 1, ..."""
+def schedule(lengths, H: int, Lq: int, broadcast_q: bool, pass_: int, BM: int, BN: int, P: int,
+             G: int = 0):
+    """Full tile list in tile order t = 0, 1, ...: [(b, h, block, slot), ...],
+    or with G > 0 query heads per key/value head [(b, h, block, h // G,
+    slot), ...]."""
     triples = []
     for b in sequence_order(lengths):
         for (h, blk) in tiles_of_sequence(int(lengths[b]), H, Lq, broadcast_q, pass_, BM, BN):
             triples.append((b, h, blk))
     if pass_ == 1 and broadcast_q:
         triples = [x for h in range(H) for x in triples if x[1] == h]
+    if G:
+        return [(b, h, blk, h // G, zigzag_slot(t, P)) for t, (b, h, blk) in enumerate(triples)]
     return [(b, h, blk, zigzag_slot(t, P)) for t, (b, h, blk) in enumerate(triples)]

@@ -31,7 +31,7 @@ def test_header_declares_expected_calls():
     assert _declared_functions() == sorted([
         "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_kernel_name", "jfa_schedule_params",
         "jfa_status_string", "jfa_timing_enable", "jfa_timing_read", "jfa_timing_reset",
-        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex"])
+        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex", "jfa_debug_schedule_ex"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -79,18 +79,55 @@ def test_bwd_rejects_null_gradient(lib):
 
 
 def test_workspace_size_argument_checks(lib):
-    out = ctypes.c_size_t(0)
-    assert lib.jfa_workspace_size(10, 2, 2, 8, 96, 0, 1, 0, ctypes.byref(out)) == 2
-    assert lib.jfa_workspace_size(10, 0, 2, 8, 128, 0, 1, 0, ctypes.byref(out)) == 1
-    assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 7, ctypes.byref(out)) == 1
-    assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 0, None) == 1
+    # rejected sizes give 0 bytes (a valid workspace is never empty)
+    assert lib.jfa_workspace_size(10, 2, 2, 8, 96, 0, 1, 0) == 0
+    assert lib.jfa_workspace_size(10, 0, 2, 8, 128, 0, 1, 0) == 0
+    assert lib.jfa_workspace_size(10, 2, 2, 8, 128, 0, 1, 7) == 0
+    assert lib.jfa_workspace_size(-1, 2, 2, 8, 128, 0, 1, 0) == 0
+    assert lib.jfa_workspace_size_gqa(10, 2, 4, 3, 8, 128, 0, 1, 1) == 0
+
+
+def _bwd(lib, scale, **kw):
+    vp = ctypes.c_void_p
+    args = dict(B=2, H=2, Lq=8, d=128, causal=0, bq=1, T=10)
+    args.update(kw)
+    return lib.jfa_bwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), args["B"], args["H"], args["Lq"], args["d"],
+                       scale, args["causal"], args["bq"], vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                       vp(FAKE), args["T"], vp(FAKE), 1 << 30, None)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, 1e-31, -1e-35, 2.0 ** -101, math.inf, math.nan])
+def test_bwd_rejects_zero_and_tiny_scale(lib, scale):
+    """The backward folds -lse / scale into its score products: |scale| below
+    2^-100 (scale = 0 included) is an argument error, found on the host."""
+    assert _bwd(lib, scale) == 1
+    vp = ctypes.c_void_p
+    assert lib.jfa_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 2, 1, 8, 128, scale, 0, 0, 1, vp(FAKE),
+                          vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -100, -(2.0 ** -100), -0.3, 1e30])
+def test_bwd_accepts_scales_from_the_minimum(lib, scale):
+    # past the scale check the next failure is the missing device (HIP error),
+    # or success where a GPU is present -- never an argument error
+    assert _bwd(lib, scale, d=96) == 2  # unsupported head dim is still reported
+    assert _bwd(lib, scale, B=0) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(list_=3), dict(list_=-1), dict(list_=2, bq=1), dict(H_kv=3),
+                                dict(cap=-1), dict(tiles=0)])
+def test_debug_schedule_ex_argument_checks(lib, kw):
+    vp = ctypes.c_void_p
+    a = dict(H=4, H_kv=2, bq=0, list_=1, cap=16, tiles=FAKE)
+    a.update(kw)
+    assert lib.jfa_debug_schedule_ex(vp(FAKE), 2, a["H"], a["H_kv"], 8, 0, a["bq"], a["list_"], 10,
+                                     vp(a["tiles"]), a["cap"], vp(FAKE), vp(FAKE), 1 << 30, None) == 1
 
 
 @pytest.mark.parametrize("H,H_kv", [(4, 3), (4, 0), (2, 4), (6, -1)])
 def test_gqa_calls_reject_heads_that_do_not_split(lib, H, H_kv):
     vp = ctypes.c_void_p
-    out = ctypes.c_size_t(0)
-    assert lib.jfa_workspace_size_gqa(10, 2, H, H_kv, 8, 128, 0, 1, 1, ctypes.byref(out)) == 1
+    assert lib.jfa_workspace_size_gqa(10, 2, H, H_kv, 8, 128, 0, 1, 1) == 0
     assert lib.jfa_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, H, H_kv, 8, 128, 0.1, 0, 0, 1, vp(FAKE),
                           vp(FAKE), 10, vp(FAKE), 1 << 30, None) == 1
     assert lib.jfa_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, H, H_kv, 8, 128, 0.1, 0, 0, 1, vp(FAKE),

@@ -140,3 +140,48 @@ def test_bwd_single_key_dv_is_column_sum_of_dout(jfa):
         ref = to64(t["dout"][b]).sum(axis=1)  # [H, d]
         np.testing.assert_allclose(to64(dv[off[b]]), ref, rtol=1e-5, atol=1e-4)
         assert float(dk[off[b]].abs().max()) < 1e-3
+
+
+@pytest.mark.parametrize("bq,causal", [(True, False), (True, True), (False, False), (False, True)])
+def test_bwd_negative_scale_d128(jfa, bq, causal):
+    """Negative scale on the d = 128 kernels (the row terms -lse / scale
+    change sign, and the forward keeps the minimum raw score)."""
+    _check_case(jfa, [3, 77, 130, 300, 1], 2, 128, 70 if bq else 0, bq, causal, seed=7, scale=-0.3)
+
+
+@pytest.mark.parametrize("bq,causal", [(True, False), (False, True)])
+def test_bwd_single_sequence(jfa, bq, causal):
+    """B = 1: one sequence, several key tiles."""
+    _check_case(jfa, [777], 3, 128, 300 if bq else 0, bq, causal, seed=8)
+
+
+def test_bwd_rejects_zero_scale(jfa):
+    t = wl.make_tensors([5, 9], 2, 128, 16, True, seed=3, device="cuda")
+    out, lse = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], 0.0, False, True)
+    with pytest.raises(RuntimeError, match="INVALID_ARG"):
+        jfa.attention_bwd(t["q"], t["k"], t["v"], t["offsets"], 0.0, False, True, out, lse, t["dout"])
+
+
+@pytest.mark.parametrize("bq,causal", [(True, False), (False, True)])
+def test_bwd_sequence_permutation(jfa, bq, causal):
+    """Permuting the order of the sequences permutes dK, dV (and self-mode
+    dQ) the same way, bitwise; the broadcast dQ, a sum over sequences taken
+    in length order (all lengths distinct here), is unchanged bitwise."""
+    lengths = [300, 1, 64, 129, 0, 700, 33, 256]
+    H, d, Lq = 2, 128, 100
+    t = wl.make_tensors(lengths, H, d, Lq if bq else 0, bq, seed=12, device="cuda")
+    perm = [5, 2, 7, 0, 4, 1, 6, 3]
+    off = t["offsets"].cpu().numpy()
+    plen = [lengths[p] for p in perm]
+    pt = {"offsets": torch.from_numpy(wl.offsets_from_lengths(plen)).cuda()}
+    rows = torch.cat([torch.arange(int(off[p]), int(off[p + 1])) for p in perm]).cuda()
+    pt["k"], pt["v"] = t["k"][rows].contiguous(), t["v"][rows].contiguous()
+    pt["q"] = t["q"] if bq else t["q"][rows].contiguous()
+    pt["dout"] = t["dout"][perm].contiguous() if bq else t["dout"][rows].contiguous()
+    a = _run(jfa, t, bq, causal, 0.09)
+    b = _run(jfa, pt, bq, causal, 0.09)
+    if bq:
+        assert torch.equal(b[0], a[0])
+    else:
+        assert torch.equal(b[0], a[0][rows])
+    assert torch.equal(b[1], a[1][rows]) and torch.equal(b[2], a[2][rows])

@@ -1,18 +1,22 @@
 """Parity at the full sizes of the larger workloads, through the C-ABI, in
 the launch configuration bench.py times.
 
-The oracle cannot redo a whole workload in seconds, so the outputs are
-sampled: every head of a few sequences (the longest, the shortest and
-seeded random ones) for O, lse, dK, dV (and self-attention dQ), and a few
-whole rows of the broadcast-Q dQ, each computed one by one by the oracle.
+prod_bcast and long_causal_8k are compared over their whole O, lse, dQ, dK
+and dV tensors; skew_bcast over every sequence of two heads (the whole dQ
+of those heads, summed over all 4096 sequences, and O, lse, dK, dV of every
+sequence in them).  The oracle's per-(sequence, head) functions run in a
+process pool (tests/_oracle_pool.py).  The variant workloads are sampled:
+every head of a few sequences, and a few whole broadcast dQ rows.
 """
 import math
+import time
 
 import numpy as np
 import pytest
 
 import workloads as wl
 from oracle import jfa_oracle as jo
+from tests._oracle_pool import WholeLse, WholeTensor, run_items
 from tests._parity import compare, compare_lse
 
 torch = pytest.importorskip("torch")
@@ -105,29 +109,87 @@ def _check_broadcast_dq_rows(w, t, dq, rows):
         compare(f"dQ {w.name} head {h} rows {[i for _, i in mine]}", got, ref)
 
 
+def _check_whole(w, t, out, lse, dq, dk, dv, heads):
+    """Every (sequence, head) of the listed heads (plain heads, H_kv = H):
+    O, lse, dK, dV (and self-attention dQ) item by item, broadcast dQ of
+    those heads summed over every sequence in fp64; each statistic over the
+    whole tensor."""
+    assert w.kv_heads == w.H
+    off = t["offsets"].cpu().numpy()
+    B, bq, scale = w.B, w.broadcast_q, w.scale
+    t0 = time.perf_counter()
+    host = {}
+    for h in heads:
+        host[h] = {
+            "k": t["k"][:, h].float().cpu().numpy(),
+            "v": t["v"][:, h].float().cpu().numpy(),
+            "q": (t["q"][h] if bq else t["q"][:, h]).float().cpu().numpy(),
+            "do": (t["dout"][:, h] if bq else t["dout"][:, h]).float().cpu().numpy(),
+            "o": (out[:, h] if bq else out[:, h]).float().cpu().numpy(),
+            "lse": (lse[:, h] if bq else lse[:, h]).cpu().numpy(),
+            "dq": (dq[h] if bq else dq[:, h]).cpu().numpy(),
+            "dk": dk[:, h].cpu().numpy(),
+            "dv": dv[:, h].cpu().numpy(),
+        }
+    print(f"  host copies of heads {list(heads)}: {time.perf_counter() - t0:.1f} s", flush=True)
+    items, cost, where = [], [], []
+    for h in heads:
+        x = host[h]
+        for b in range(B):
+            s0, s1 = int(off[b]), int(off[b + 1])
+            qb = x["q"] if bq else x["q"][s0:s1]
+            dob = x["do"][b] if bq else x["do"][s0:s1]
+            items.append((qb, x["k"][s0:s1], x["v"][s0:s1], dob, scale, w.causal, w.window))
+            cost.append(qb.shape[0] * max(s1 - s0, 1))
+            where.append((h, b, s0, s1))
+    chk = {n: WholeTensor(f"{n} {w.name}") for n in ("O", "dQ", "dK", "dV")}
+    chk_lse = WholeLse(f"lse {w.name}")
+    ref_dq = {h: np.zeros_like(host[h]["dq"], dtype=np.float64) for h in heads} if bq else None
+    done = 0
+    for i, (o_r, l_r, q_r, k_r, v_r) in run_items(items, cost):
+        h, b, s0, s1 = where[i]
+        x = host[h]
+        if bq:
+            chk["O"].add(x["o"][b], o_r)
+            chk_lse.add(x["lse"][b], l_r)
+            ref_dq[h] += q_r
+        else:
+            chk["O"].add(x["o"][s0:s1], o_r)
+            chk_lse.add(x["lse"][s0:s1], l_r)
+            chk["dQ"].add(x["dq"][s0:s1], q_r)
+        chk["dK"].add(x["dk"][s0:s1], k_r)
+        chk["dV"].add(x["dv"][s0:s1], v_r)
+        done += 1
+        if done % max(1, len(items) // 8) == 0:
+            print(f"  oracle {done}/{len(items)} items, {time.perf_counter() - t0:.1f} s", flush=True)
+    if bq:
+        for h in heads:
+            chk["dQ"].add(host[h]["dq"], ref_dq[h])
+    for c in chk.values():
+        c.check()
+    chk_lse.check()
+
+
 @pytest.mark.timeout(900)
 def test_full_prod_bcast(jfa):
+    """The whole of every output, all 1024 sequences and 4 heads."""
     w, t, out, lse, dq, dk, dv = _run_full(jfa, 2)
-    seqs = _sample_sequences(t["lengths"], 4, seed=202)
-    _check_sequences(w, t, out, lse, dq, dk, dv, seqs, range(w.H))
-    _check_broadcast_dq_rows(w, t, dq, [(0, 0), (0, 255), (3, 130), (2, 77)])
+    _check_whole(w, t, out, lse, dq, dk, dv, range(w.H))
 
 
 @pytest.mark.timeout(900)
 def test_full_long_causal(jfa):
+    """The whole of every output, all 64 sequences and 16 heads."""
     w, t, out, lse, dq, dk, dv = _run_full(jfa, 3)
-    seqs = _sample_sequences(t["lengths"], 2, seed=303)
-    _check_sequences(w, t, out, lse, dq, dk, dv, seqs, [0, 7, 15])
+    _check_whole(w, t, out, lse, dq, dk, dv, range(w.H))
 
 
 @pytest.mark.timeout(900)
 def test_full_skew_bcast(jfa):
+    """Two of the 8 heads whole: dQ summed over all 4096 sequences, and O,
+    lse, dK, dV of every sequence (the 410 long ones included)."""
     w, t, out, lse, dq, dk, dv = _run_full(jfa, 4)
-    L = np.asarray(t["lengths"])
-    long_ids = np.nonzero(L >= 4096)[0]
-    seqs = sorted(set(_sample_sequences(L, 3, seed=404)) | {int(long_ids[0])})
-    _check_sequences(w, t, out, lse, dq, dk, dv, seqs, [0, 5])
-    _check_broadcast_dq_rows(w, t, dq, [(1, 0), (1, 511), (6, 300)])
+    _check_whole(w, t, out, lse, dq, dk, dv, [1, 6])
 
 
 @pytest.mark.timeout(900)

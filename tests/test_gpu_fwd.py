@@ -62,6 +62,42 @@ def test_fwd_negative_and_zero_scale(jfa):
     _run_case(jfa, [3, 77, 130], 2, 128, 0, False, True, seed=6, scale=0.0)
 
 
+@pytest.mark.parametrize("bq,causal", [(True, False), (True, True), (False, False), (False, True)])
+def test_fwd_negative_scale_d128(jfa, bq, causal):
+    """A negative scale turns the running maximum into the minimum of the
+    raw scores: the d = 128 kernel's branch for it, in every mode."""
+    _run_case(jfa, [3, 77, 130, 300, 1], 2, 128, 70 if bq else 0, bq, causal, seed=7, scale=-0.3)
+
+
+@pytest.mark.parametrize("bq,causal", [(True, False), (False, True)])
+def test_fwd_single_sequence(jfa, bq, causal):
+    """B = 1: one sequence (several tiles of it in self mode)."""
+    _run_case(jfa, [777], 3, 128, 300 if bq else 0, bq, causal, seed=8)
+
+
+@pytest.mark.parametrize("bq,causal", [(True, False), (False, True)])
+def test_fwd_sequence_permutation(jfa, bq, causal):
+    """Permuting the order of the sequences permutes O and lse the same way,
+    bitwise (each output row is computed from its own sequence only)."""
+    lengths = [300, 1, 64, 129, 0, 700, 33, 256]
+    H, d, Lq = 2, 128, 100
+    t = wl.make_tensors(lengths, H, d, Lq if bq else 0, bq, seed=12, device="cuda", with_dout=False)
+    perm = [5, 2, 7, 0, 4, 1, 6, 3]
+    off = t["offsets"].cpu().numpy()
+    plen = [lengths[p] for p in perm]
+    poff = torch.from_numpy(wl.offsets_from_lengths(plen)).cuda()
+    rows = torch.cat([torch.arange(int(off[p]), int(off[p + 1])) for p in perm]).cuda()
+    k, v = t["k"][rows].contiguous(), t["v"][rows].contiguous()
+    q = t["q"] if bq else t["q"][rows].contiguous()
+    o1, l1 = jfa.attention_fwd(t["q"], t["k"], t["v"], t["offsets"], 0.09, causal, bq)
+    o2, l2 = jfa.attention_fwd(q, k, v, poff, 0.09, causal, bq)
+    torch.cuda.synchronize()
+    if bq:
+        assert torch.equal(o2, o1[perm]) and torch.equal(l2, l1[perm])
+    else:
+        assert torch.equal(o2, o1[rows]) and torch.equal(l2, l1[rows])
+
+
 @pytest.mark.parametrize("lengths", [[512] * 5, [1000] * 3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_dense_equal_lengths(jfa, lengths, causal):
@@ -147,6 +183,40 @@ def test_schedule_bit_exact(jfa, pass_, bq, causal):
     n = torch.zeros(1, dtype=torch.int64, device="cuda")
     jfa.jfa_debug_schedule(off, len(lengths), H, Lq if bq else 0, causal, bq, pass_, T, tiles, n, ws)
     torch.cuda.synchronize()
+    assert int(n.item()) == len(ref)
+    got = tiles.cpu().numpy()
+    assert np.array_equal(got[:len(ref)], np.array(ref, dtype=np.int32))
+    assert np.all(got[len(ref):] == -7)
+
+
+DQ_BM = 256  # query rows of the self-attention backward's dQ tiles
+
+
+@pytest.mark.parametrize("list_", [0, 1, 2])
+@pytest.mark.parametrize("name", ["tiny_bcast", "self_causal_1k", "prod_bcast", "long_causal_8k", "skew_bcast",
+                                  "prod_bcast_gqa", "dense_llm_1k"])
+def test_schedule_bit_exact_on_workload_offsets(jfa, name, list_):
+    """Every tile list the library builds (forward query tiles, backward key
+    tiles, self-attention dQ query tiles), on each workload's own seeded
+    offsets, equals the integer reference, key / value head included."""
+    w = wl.workload(name)
+    if list_ == 2 and w.broadcast_q:
+        pytest.skip("the dQ query-tile list exists in self-attention mode only")
+    lengths = wl.draw_lengths(w.lengths, w.B, wl.WORKLOADS.index(w))
+    B, H, Hkv, Lq, bq = w.B, w.H, w.kv_heads, w.Lq, w.broadcast_q
+    block, P = jfa.jfa_schedule_params(1 if list_ == 1 else 0, w.causal, int(bq), w.d)
+    assert block == (BWD_BN if list_ == 1 else fwd_bm(bq, w.causal))
+    blk = {0: fwd_bm(bq, w.causal), 1: BWD_BN, 2: DQ_BM}[list_]
+    off = torch.from_numpy(wl.offsets_from_lengths(lengths)).cuda()
+    T = int(off[-1])
+    ws = jfa.workspace(T, B, H, Lq, w.d, w.causal, bq, 0 if list_ == 0 else 1, "cuda", H_kv=Hkv)
+    ref = sr.schedule(lengths, H, Lq, bq, 1 if list_ == 1 else 0, blk, blk, P, G=H // Hkv)
+    cap = len(ref) + 3
+    tiles = torch.full((cap, 5), -7, dtype=torch.int32, device="cuda")
+    n = torch.zeros(1, dtype=torch.int64, device="cuda")
+    jfa.jfa_debug_schedule_ex(off, B, H, Hkv, Lq, w.causal, bq, list_, T, tiles, n, ws)
+    torch.cuda.synchronize()
+    print(f"schedule {name} list {list_}: {len(ref)} tiles", flush=True)
     assert int(n.item()) == len(ref)
     got = tiles.cpu().numpy()
     assert np.array_equal(got[:len(ref)], np.array(ref, dtype=np.int32))
