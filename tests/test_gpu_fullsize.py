@@ -1,10 +1,8 @@
 """Parity at the full sizes of the larger workloads, through the C-ABI, in
 the launch configuration bench.py times.
 
-prod_bcast and long_causal_8k are compared over their whole O, lse, dQ, dK
-and dV tensors; skew_bcast over every sequence of two heads (the whole dQ
-of those heads, summed over all 4096 sequences, and O, lse, dK, dV of every
-sequence in them).  The oracle's per-(sequence, head) functions run in a
+prod_bcast, long_causal_8k and skew_bcast are compared over their whole O,
+lse, dQ, dK and dV tensors.  The oracle's per-(sequence, head) functions run in a
 process pool (tests/_oracle_pool.py).  The variant workloads are sampled:
 every head of a few sequences, and a few whole broadcast dQ rows.
 """
@@ -109,11 +107,12 @@ def _check_broadcast_dq_rows(w, t, dq, rows):
         compare(f"dQ {w.name} head {h} rows {[i for _, i in mine]}", got, ref)
 
 
-def _check_whole(w, t, out, lse, dq, dk, dv, heads):
+def _check_whole(w, t, out, lse, dq, dk, dv, heads, acc=None):
     """Every (sequence, head) of the listed heads (plain heads, H_kv = H):
     O, lse, dK, dV (and self-attention dQ) item by item, broadcast dQ of
     those heads summed over every sequence in fp64; each statistic over the
-    whole tensor."""
+    whole tensor.  With `acc` (accumulators of an earlier call over other
+    heads) the statistics continue and are checked by the caller."""
     assert w.kv_heads == w.H
     off = t["offsets"].cpu().numpy()
     B, bq, scale = w.B, w.broadcast_q, w.scale
@@ -142,8 +141,11 @@ def _check_whole(w, t, out, lse, dq, dk, dv, heads):
             items.append((qb, x["k"][s0:s1], x["v"][s0:s1], dob, scale, w.causal, w.window))
             cost.append(qb.shape[0] * max(s1 - s0, 1))
             where.append((h, b, s0, s1))
-    chk = {n: WholeTensor(f"{n} {w.name}") for n in ("O", "dQ", "dK", "dV")}
-    chk_lse = WholeLse(f"lse {w.name}")
+    if acc is None:
+        chk = {n: WholeTensor(f"{n} {w.name}") for n in ("O", "dQ", "dK", "dV")}
+        chk_lse = WholeLse(f"lse {w.name}")
+    else:
+        chk, chk_lse = acc
     ref_dq = {h: np.zeros_like(host[h]["dq"], dtype=np.float64) for h in heads} if bq else None
     done = 0
     for i, (o_r, l_r, q_r, k_r, v_r) in run_items(items, cost):
@@ -165,6 +167,8 @@ def _check_whole(w, t, out, lse, dq, dk, dv, heads):
     if bq:
         for h in heads:
             chk["dQ"].add(host[h]["dq"], ref_dq[h])
+    if acc is not None:
+        return
     for c in chk.values():
         c.check()
     chk_lse.check()
@@ -186,10 +190,16 @@ def test_full_long_causal(jfa):
 
 @pytest.mark.timeout(900)
 def test_full_skew_bcast(jfa):
-    """Two of the 8 heads whole: dQ summed over all 4096 sequences, and O,
-    lse, dK, dV of every sequence (the 410 long ones included)."""
+    """The whole of every output: dQ summed over all 4096 sequences, and O,
+    lse, dK, dV of every sequence (the 410 long ones included), all 8 heads
+    (two at a time, to bound the host copies)."""
     w, t, out, lse, dq, dk, dv = _run_full(jfa, 4)
-    _check_whole(w, t, out, lse, dq, dk, dv, [1, 6])
+    acc = ({n: WholeTensor(f"{n} {w.name}") for n in ("O", "dQ", "dK", "dV")}, WholeLse(f"lse {w.name}"))
+    for h0 in range(0, w.H, 2):
+        _check_whole(w, t, out, lse, dq, dk, dv, [h0, h0 + 1], acc=acc)
+    for c in acc[0].values():
+        c.check()
+    acc[1].check()
 
 
 @pytest.mark.timeout(900)
