@@ -131,6 +131,25 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
                const float* lse, const void* dout, float* dq, float* dk, float* dv, int64_t total_len,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): jfa_fwd_ex without the workspace
+ * arguments.  Its scratch (the tile schedule: sort keys, prefix sums, tile
+ * list, hand-out counter) is a static device array inside the library, one
+ * copy per GPU, JFA_NOALLOC_MAX_WORKSPACE bytes, held until the process
+ * ends.  Calls whose forward workspace (jfa_workspace_size_gqa, pass 0)
+ * would exceed it return JFA_ERR_WORKSPACE before anything is enqueued.
+ * Nothing is allocated or freed and nothing synchronises (JFA_DEBUG's
+ * offsets check does not apply here).  Every call on a GPU uses that GPU's
+ * one array, and each call rewrites all of the scratch it reads, so calls
+ * in sequence on any streams that are ordered are fine; calls that can run
+ * concurrently on one GPU (different unsynchronised streams or host
+ * threads) race and give wrong results. */
+#define JFA_NOALLOC_MAX_WORKSPACE (16u << 20)
+int jfa_fwd_noalloc(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+                    int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
+                    int64_t total_len, void* stream);
+
 /* Tile geometry the library uses on the current device for a pass:
  * *block_rows = query rows per forward tile (pass 0) or key rows per
  * backward tile (pass 1); *workers = persistent workgroups that share the

@@ -40,6 +40,9 @@ _SIGS = {
                               _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_int,
                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                               _c.c_int64, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "jfa_fwd_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                                   _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_int,
+                                   _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "jfa_schedule_params": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_int),
                                        _c.POINTER(_c.c_int)]),
     "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -125,6 +128,13 @@ def jfa_bwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broad
                             int(causal), int(window), int(broadcast_q), _ptr(out), _ptr(lse), _ptr(dout),
                             _ptr(dq), _ptr(dk), _ptr(dv), int(total_len), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_bwd_ex")
+
+
+def jfa_fwd_noalloc(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, total_len,
+                    stream=None):
+    _check(lib().jfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
+                                 int(causal), int(window), int(broadcast_q), _ptr(out), _ptr(lse),
+                                 int(total_len), _stream(stream)), "jfa_fwd_noalloc")
 
 
 def jfa_schedule_params(pass_, causal, broadcast_q, d):

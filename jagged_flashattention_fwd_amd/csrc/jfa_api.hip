@@ -18,11 +18,21 @@ namespace {
 
 constexpr int MAX_DEVICES = 64;
 
+// Scratch of jfa_fwd_noalloc: the forward's workspace (sort keys, prefix
+// sums, tile list, hand-out counter) in a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never uses this name as
+// an address: each device's copy is reached through the pointer that
+// hipGetSymbolAddress returns at that device's set-up.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)JFA_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
 // Per-device set-up, done once per device with that device current: the
-// compute-unit count and the kernel attributes the launches rely on.
+// compute-unit count, the kernel attributes the launches rely on, and the
+// device address of this device's scratch array.
 struct DeviceState {
   int cus = 0;
   int rc = JFA_ERR_HIP;
+  char* scratch = nullptr;  // this device's copy of `scratch` (null if the lookup failed)
 };
 DeviceState g_dev[MAX_DEVICES];
 std::once_flag g_dev_once[MAX_DEVICES];
@@ -35,6 +45,11 @@ int device_state(DeviceState** out) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return;
     if (init_schedule_kernels() != hipSuccess) return;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr != nullptr)
+      st.scratch = static_cast<char*>(ptr);
+    else
+      (void)hipGetLastError();  // only jfa_fwd_noalloc needs it; it reports the failure
     st.cus = n;
     st.rc = JFA_OK;
   });
@@ -241,11 +256,18 @@ size_t jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int ca
   return jfa_workspace_size_gqa(total_len, B, H, H, Lq, d, causal, broadcast_q, pass);
 }
 
-int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
-               int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
-               int64_t total_len, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !offsets || !out || !lse || !workspace) return JFA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+}  // extern "C"
+
+namespace jfa {
+namespace {
+
+// Argument checks shared by the forward entry points (everything but the
+// workspace).
+int check_fwd_args(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+                   int Lq, int d, float scale, int causal, int window, int broadcast_q, const void* out,
+                   const float* lse, int64_t total_len) {
+  if (!q || !k || !v || !offsets || !out || !lse) return JFA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 7))
     return JFA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
@@ -253,22 +275,15 @@ int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   if (rc != JFA_OK) return rc;
   rc = check_heads(H, H_kv);
   if (rc != JFA_OK) return rc;
-  rc = check_window(causal, window);
-  if (rc != JFA_OK) return rc;
-  if (!broadcast_q) Lq = 0;
-  int P = 0;
-  rc = workers(0, &P);
-  if (rc != JFA_OK) return rc;
-  const Layout lay = layout(0, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
-  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (debug_checks()) {
-    rc = check_offsets_sync(offsets, B, total_len, st);
-    if (rc != JFA_OK) return rc;
-  }
-  char* ws = static_cast<char*>(workspace);
-  const Schedule s = schedule_at(ws, lay.sched_a, lay.cap_a);
+  return check_window(causal, window);
+}
 
+// The forward's launches on a checked workspace `ws` laid out by `lay`
+// (Lq already 0 in self mode).
+int fwd_launch(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv, int Lq,
+               int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
+               int64_t total_len, char* ws, const Layout& lay, int P, hipStream_t st) {
+  const Schedule s = schedule_at(ws, lay.sched_a, lay.cap_a);
   SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows(), H / H_kv};
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
 
@@ -292,6 +307,52 @@ int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   fa.P = P;
   if (launch_fwd(fa, st) != hipSuccess) return JFA_ERR_HIP;
   return JFA_OK;
+}
+
+}  // namespace
+}  // namespace jfa
+
+extern "C" {
+
+int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+               int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
+               int64_t total_len, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_fwd_args(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse,
+                          total_len);
+  if (rc != JFA_OK) return rc;
+  if (!workspace || !aligned16(workspace)) return JFA_ERR_INVALID_ARG;
+  if (!broadcast_q) Lq = 0;
+  int P = 0;
+  rc = workers(0, &P);
+  if (rc != JFA_OK) return rc;
+  const Layout lay = layout(0, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    rc = check_offsets_sync(offsets, B, total_len, st);
+    if (rc != JFA_OK) return rc;
+  }
+  return fwd_launch(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, total_len,
+                    static_cast<char*>(workspace), lay, P, st);
+}
+
+int jfa_fwd_noalloc(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
+                    int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
+                    int64_t total_len, void* stream) {
+  int rc = check_fwd_args(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse,
+                          total_len);
+  if (rc != JFA_OK) return rc;
+  if (!broadcast_q) Lq = 0;
+  // The forward's layout does not depend on the worker count: its size is
+  // checked against the scratch before any device call.
+  const Layout lay = layout(0, total_len, B, H, H_kv, Lq, d, broadcast_q, 1);
+  if (lay.total > NOALLOC_SCRATCH_BYTES) return JFA_ERR_WORKSPACE;
+  DeviceState* dst = nullptr;
+  rc = device_state(&dst);
+  if (rc != JFA_OK) return rc;
+  if (!dst->scratch) return JFA_ERR_HIP;
+  return fwd_launch(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, total_len,
+                    dst->scratch, lay, dst->cus, reinterpret_cast<hipStream_t>(stream));
 }
 
 int jfa_fwd(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int Lq,

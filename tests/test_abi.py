@@ -31,7 +31,7 @@ def test_header_declares_expected_calls():
     assert _declared_functions() == sorted([
         "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_kernel_name", "jfa_schedule_params",
         "jfa_status_string", "jfa_timing_enable", "jfa_timing_read", "jfa_timing_reset",
-        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex", "jfa_debug_schedule_ex"])
+        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex", "jfa_debug_schedule_ex", "jfa_fwd_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -160,3 +160,19 @@ def test_kernel_names(lib):
         k += 1
     assert "fwd_kernel" in names and "dkdv_kernel" in names and len(names) == len(set(names))
     assert lib.jfa_timing_read(-1, None, None) == 1
+
+
+def test_noalloc_forward_host_checks(lib):
+    """jfa_fwd_noalloc checks its arguments, and its size against the static
+    scratch, before any HIP call."""
+    vp = ctypes.c_void_p
+
+    def call(B=2, H=2, H_kv=2, Lq=8, d=128, scale=0.1, q=FAKE, T=10):
+        return lib.jfa_fwd_noalloc(vp(q), vp(FAKE), vp(FAKE), vp(FAKE), B, H, H_kv, Lq, d, scale, 0, 0, 0,
+                                   vp(FAKE), vp(FAKE), T, None)
+    assert call(q=0) == 1
+    assert call(d=96) == 2
+    assert call(scale=math.nan) == 1
+    assert call(H_kv=3) == 1
+    # 1000 heads x (8192 sequences + 2^30 / 256 rows) tiles: far beyond the 16 MiB scratch
+    assert call(B=8192, H=1000, H_kv=1000, T=1 << 30) == 3
