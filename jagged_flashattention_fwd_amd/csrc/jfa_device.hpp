@@ -67,6 +67,14 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t* hi, uin
   f32x2 r = {a - __uint_as_float(ua), b - __uint_as_float(ub)};
   *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
+// fp32 pair -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -798,6 +798,514 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
   }
 }
 
+// ============================================== dK / dV, d = 128, 8 waves --
+// The same tiles, block stream and results as dkdv_kernel, with the work of
+// each 32-key group split between two waves so that two waves share every
+// SIMD and one's vector work runs beside the other's matrix products:
+//   score wave (waves 0-3):    K rows of its keys; S = Q K^T (+ the -lse /
+//                              scale row terms), P = exp2(c S'), masked;
+//                              P to LDS; dV^T += dO^T P.
+//   gradient wave (waves 4-7): V rows of the same keys; dP = dO V^T (+ the
+//                              -delta row terms); after P arrives,
+//                              dS = P o dP', dK^T += Q^T dS.
+// P passes lane to lane (both waves own the same key per lane and the same
+// query rows per register), through a 32 KB area that also stages the tile's
+// dK / dV stores.  Each wave holds one operand set (K or V) and one fp32
+// accumulator (dV or dK), half of dkdv_kernel's, so that it fits in the 256
+// registers of a wave sharing its SIMD.  Per block: the ring barrier, the
+// scores and products of both subtiles, the hand-over barrier, then dV or dK.
+struct Pair {
+  static constexpr int NW = 8, NG = 4;  // waves; key groups of 32 keys (one score + one gradient wave each)
+  static constexpr int QB = BWD_QB, BN = BWD_BN, D = 128, KS = 8, DT = 4;
+  static constexpr int RB = TileGeom<128>::ROW_BYTES;
+  static constexpr int TILE = QB * RB;
+  static constexpr int NBUF = 3;
+  static constexpr int GAP = PadRowCopy::GAP;
+  static constexpr int OFF_DO = TILE + GAP;
+  static constexpr int OFF_TL = OFF_DO + TILE + GAP;
+  static constexpr int OFF_TD = OFF_TL + QB * 16;
+  static constexpr int BUF = OFF_TD + QB * 16;
+  static constexpr int RPW = QB / NW;                  // rows per wave per tile
+  static constexpr int CPT = PadRowCopy::copies(RPW);  // copies per wave per tile
+  static constexpr int IPS = 2 * CPT + 1;              // copies per wave per block
+  // P hand-over as fp16, two areas (consecutive iterations): [area]
+  // [subtile][key group][register group][lane] x 8 bytes.
+  static constexpr int XBYTES = 2 * 2 * NG * 4 * WAVE * 8;
+  static_assert(RB == 19 * 16 && RPW >= 3, "copy geometry");
+  static_assert(NBUF * BUF + XBYTES + 64 <= 160 * 1024, "LDS");
+  static_assert(NW * 32 * 32 * 4 <= XBYTES, "the store staging fits the hand-over area");
+};
+
+// Eight 16-byte LDS reads at OFF + 32 ks (k-step ks of a 128-wide row, the
+// lane's chunk already in `addr`), not waited for.
+template <int OFF>
+__device__ __forceinline__ void rows_issue8(uint32_t addr, u32x4 (&x)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(addr), "i"(OFF), "i"(OFF + 32), "i"(OFF + 64), "i"(OFF + 96), "i"(OFF + 128), "i"(OFF + 160),
+        "i"(OFF + 192), "i"(OFF + 224));
+}
+// One 16-byte LDS read at byte offset OFF from `addr`, not waited for.
+template <int OFF>
+__device__ __forceinline__ void lds_read16_issue(uint32_t addr, u32x4& x) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(x) : "v"(addr), "i"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait1(u32x4& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
+template <bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const TileRec* __restrict__ tiles) {
+  using C = Pair;
+  constexpr int QB = C::QB, BN = C::BN, KS = C::KS, DT = C::DT, NBUF = C::NBUF, RB = C::RB, D = C::D;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF][C::BUF];
+  __shared__ __attribute__((aligned(16))) char xchg[C::XBYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int kgrp = wave & (C::NG - 1);  // key group: keys 32 kgrp .. 32 kgrp + 31 of the tile
+  const bool grad = wave >= C::NG;      // gradient wave (V, dP, dS, dK); else score wave (K, S, P, dV)
+  const int l = tid % WAVE, g = l / 32, lc = l % 32;
+  const int slot = logical_slot(blockIdx.x, a.P);
+  const int64_t T = *a.n_ktiles;
+  const int H = a.H, Lq = a.Lq;
+  const int64_t ld = (int64_t)H * D;
+  const float c2 = a.scale_log2;
+
+  // This lane's part of a transposed read (see lds_operand_tr).
+  const int trs = l & 15;
+  const uint32_t tr_lane = (uint32_t)((g * 4 + (trs >> 2)) * RB + (((((l >> 4) & 1) << 4) + ((trs & 3) << 2)) << 1));
+
+  const int64_t t0 = zigzag_tile(0, slot, a.P);
+  if (t0 >= T) return;
+
+  const int64_t qs = BCAST ? (int64_t)D : ld;  // row stride of Q / dO
+  const int64_t sld = BCAST ? 1 : H;           // row stride of the per-row arrays
+  struct Tp {
+    int64_t s0;
+    int L, h, hk, b, k0, m_first, m_end, nq;
+    const uint16_t* qb;
+    const uint16_t* db;
+    const u32x4* vb;
+  };
+  auto tparams = [&](const TileRec& r) {
+    Tp p;
+    p.s0 = r.s0;
+    p.L = r.L;
+    p.h = r.h;
+    p.hk = r.hk;
+    p.b = r.b;
+    p.k0 = r.blk * BN;
+    p.nq = BCAST ? Lq : r.L;
+    p.m_first = CAUSAL ? p.k0 / QB : 0;
+    p.m_end = max((p.nq + QB - 1) / QB, p.m_first);
+    if (CAUSAL && a.window > 0) p.m_end = max(min(p.m_end, (p.k0 + BN - 2 + a.window) / QB + 1), p.m_first);
+    p.qb = BCAST ? a.q + (int64_t)r.h * Lq * D : a.q + (r.s0 * H + r.h) * (int64_t)D;
+    p.db = BCAST ? a.dout + ((int64_t)r.b * H + r.h) * Lq * D : a.dout + (r.s0 * H + r.h) * (int64_t)D;
+    p.vb = reinterpret_cast<const u32x4*>((wave & 1) ? a.term_d : a.term_l) +
+           (BCAST ? ((int64_t)r.b * H + r.h) * Lq : r.s0 * H + r.h);
+    return p;
+  };
+
+  // The block stream, as in dkdv_kernel: each wave copies its 8 rows of Q
+  // and of dO (three padded rows per copy) and one row-term array (even
+  // waves -lse / scale, odd waves -delta) of the block two ahead.
+  const uint16_t* j_q = a.q;
+  const uint16_t* j_d = a.q;
+  const u32x4* j_v = reinterpret_cast<const u32x4*>(a.term_l);
+  uint32_t j_lds = 0, j_ldw = 0;
+  int j_last = 0, j_n = 0;
+  const PadRowCopy pc;
+  auto issue_rows = [&](int k0, int k1) {
+    if (j_n == 0) return;
+#pragma unroll
+    for (int k = k0; k < k1; ++k) {
+      const int R = PadRowCopy::start(k % C::CPT, C::RPW);
+      const uint32_t voff = pc.voff(R, j_last, (uint32_t)(qs * 2));
+      if (k < C::CPT) dma_copy16(j_q, voff, j_ldw + R * RB);
+      else dma_copy16(j_d, voff, j_ldw + C::OFF_DO + R * RB);
+    }
+  };
+  auto issue_vec = [&]() {
+    if (j_n == 0) return;
+    copy_gather16(j_v, j_lds + C::OFF_TL + (wave & 1) * QB * 16);
+  };
+  int ring_iss = 0, ring_cmp = 0;
+  int iss_cur = 0, iss_nxt = 0;
+  auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
+    j_n = 0;
+    const int nbc = cp.m_end - cp.m_first;
+    const int nbn = has_nxt ? np.m_end - np.m_first : 0;
+    const bool cur = iss_cur < nbc;
+    if (!cur && iss_nxt >= nbn) return;
+    const int nq_ = cur ? cp.nq : np.nq;
+    const int j = cur ? cp.m_first + iss_cur : np.m_first + iss_nxt;
+    const int base_row = min(j * QB + wave * C::RPW, nq_ - 1);
+    const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(qs * 2);
+    j_q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.qb : np.qb) + roff);
+    j_d = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.db : np.db) + roff);
+    j_v = (cur ? cp.vb : np.vb) + (int64_t)min(j * QB + l, nq_ - 1) * sld;
+    j_lds = lds_addr(smem[ring_iss]);
+    j_ldw = j_lds + wave * C::RPW * RB;
+    j_last = nq_ - 1 - base_row;
+    j_n = C::IPS;
+    if (cur) ++iss_cur;
+    else ++iss_nxt;
+    ring_iss = ring_iss == NBUF - 1 ? 0 : ring_iss + 1;
+  };
+  auto issue_now = [&]() {
+    issue_rows(0, 2 * C::CPT);
+    issue_vec();
+  };
+  auto wait_n = [&](int n) {
+    if (n >= C::IPS) wait_vmcnt<C::IPS>();
+    else wait_vmcnt<0>();
+  };
+
+  // This wave's operand rows (K for a score wave, V for a gradient wave) of
+  // its key, as B operands; lanes past the sequence end read its last key.
+  u32x4 kvraw[KS];
+  auto load_rows = [&](const Tp& p) {
+    const int kc = min(p.k0 + kgrp * 32 + lc, p.L - 1);
+    const uint16_t* r = (grad ? a.v : a.k) + ((p.s0 + kc) * a.Hkv + p.hk) * (int64_t)D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kvraw[ks] = *reinterpret_cast<const u32x4*>(r + ks * 16);
+  };
+
+  // dV (score wave) or scale * dK (gradient wave) of this wave's keys:
+  // each 32 x 32 chunk is transposed through the wave's 4 KB of the
+  // hand-over area (16-byte chunks XOR-swizzled by key) and leaves as whole
+  // 128-byte segments of 8 keys; bounded buffer stores, 4 * DT per wave.
+  auto store_acc = [&](const Tp& p, int nvalid, const f32x16 (&acc)[DT]) {
+    const int64_t row0 = (p.s0 + p.k0) * H + p.h;
+    const int nrec = nvalid * H * D * 4;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((grad ? a.dk : a.dv) + row0 * D, nrec);
+    const float mul = grad ? a.scale : 1.0f;
+    float* st = reinterpret_cast<float*>(xchg + wave * 4096);
+    const int rk8 = l >> 3, rc = l & 7;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[dt][i4 * 4 + e] * mul;
+        *reinterpret_cast<f32x4*>(st + lc * 32 + (((2 * i4 + g) ^ (lc & 7)) << 2)) = v;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = r * 8 + rk8;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + kr * 32 + ((rc ^ (kr & 7)) << 2));
+        const int off = ((kgrp * 32 + kr) * H * D + dt * 32 + rc * 4) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
+      }
+    }
+  };
+
+  Tp cp = tparams(tiles[t0]);
+  load_rows(cp);
+  {
+    f32x16 z[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
+    store_acc(cp, 0, z);  // stores that write nothing: the first tile start waits like every later one
+  }
+
+  constexpr bool DYN = CAUSAL || !BCAST;
+  __shared__ int s_next;
+  unsigned int fetched = 0;
+  for (int64_t pass = 0;; ++pass) {
+    const int64_t tn0 = zigzag_tile(pass + 1, slot, a.P);
+    bool has_nxt = !DYN && tn0 < T;
+    Tp np = has_nxt ? tparams(tiles[tn0]) : cp;
+    auto handoff = [&]() {
+      if constexpr (DYN) {
+        const int64_t tn = pass == 0 ? tn0 : 2 * (int64_t)a.P + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
+        has_nxt = tn < T;
+        if (has_nxt && wave == 0 && l == 0) fetched = atomicAdd(a.ktile_ctr, 1u);
+        if (has_nxt) np = tparams(tiles[tn]);
+      }
+    };
+    int vm_last = 0;
+    const int L = cp.L;
+    const int k0 = cp.k0;
+    const int kw = k0 + kgrp * 32 + lc;  // this lane's key
+    const bool key_ok = kw < L;
+    const int nq = BCAST ? Lq : L;
+    const int m_first = cp.m_first, m_end = cp.m_end;
+    const int nb = m_end - m_first;
+    const int m_diag = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
+    const bool tile_partial = k0 + BN > L || a.window > 0;
+    const int m_full = nq / QB;
+
+    bf16x8 kv[KS];
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+    // B operand of the row-term k-step: ones in k-slots 0..2.
+    const bf16x8 ones3 = __builtin_bit_cast(bf16x8, g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+    // Lane bases: this lane's query row and chunk g of the role's row tile,
+    // its row term, and its 16-byte slots of the hand-over area.
+    const uint32_t row_lane = (uint32_t)(lc * RB + g * 16) + (grad ? (uint32_t)C::OFF_DO : 0u);
+    const uint32_t tm_lane = (uint32_t)(lc * 16) + (grad ? (uint32_t)C::OFF_TD : (uint32_t)C::OFF_TL);
+    u32x2* const xw = reinterpret_cast<u32x2*>(xchg) + (kgrp * 4) * WAVE + l;  // + ((xs * 2 + s) * NG * 4 + i4) * WAVE
+
+    // Carried from one iteration to the next, in one register array for
+    // both roles: the score wave's P of the block just scored as packed
+    // bf16 B operands (carry[8 s + 4 hh + k], subtile s, pair hh) and their
+    // rounded remainders (carry[16 + ...]), plus the largest value per
+    // subtile; the gradient wave's dP' of that block (carry[16 s + i] as
+    // fp32 bits).
+    uint32_t carry[32];
+    float pmaxc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) carry[i] = 0u;
+
+    // Front of an iteration: S (score wave) or dP (gradient wave) of block
+    // m, each subtile from its row-term k-step and KS k-steps of LDS rows
+    // (three reads ahead) against the registers.  The score wave turns S
+    // into P, writes it to hand-over area xs for the gradient wave and keeps
+    // it packed; the gradient wave keeps dP'.
+    auto front = [&](auto masked_tag, int m, const char* buf, int xs) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const uint32_t lb = lds_addr(buf);
+      f32x16 sc[2];
+      // score wave: P of register group I4 of subtile S_ (rows S_ * 32 + 8 I4 + 4 g + e)
+      auto p_rows = [&](auto s_tag, auto i4_tag) __attribute__((always_inline)) {
+        constexpr int S_ = decltype(s_tag)::value, I4 = decltype(i4_tag)::value;
+        const int r = S_ * 32 + I4 * 8 + g * 4;
+        float p4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = fast_exp2(sc[S_][I4 * 4 + e] * c2);
+          if constexpr (MASKED) {
+            const int row = m * QB + r + e;
+            bool ok = key_ok && row < nq;
+            if constexpr (CAUSAL) ok = ok && kw <= row && (a.window <= 0 || kw > row - a.window);
+            pv = ok ? pv : 0.f;
+          }
+          p4[e] = pv;
+          pmaxc[S_] = fmaxf(pmaxc[S_], pv);
+        }
+        xw[((xs * 2 + S_) * C::NG * 4 + I4) * WAVE] = u32x2{pack_f16x2(p4[0], p4[1]), pack_f16x2(p4[2], p4[3])};
+        const uint32_t h0 = pack_bf16x2(p4[0], p4[1]), h1 = pack_bf16x2(p4[2], p4[3]);
+        constexpr int c = 8 * S_ + 4 * (I4 >> 1) + (I4 & 1) * 2;
+        carry[c] = h0;
+        carry[c + 1] = h1;
+        carry[16 + c] = bf16x2_residual(p4[0], p4[1], h0);
+        carry[16 + c + 1] = bf16x2_residual(p4[2], p4[3], h1);
+      };
+      using Z = std::integral_constant<int, 0>;
+      using O = std::integral_constant<int, 1>;
+      if (!grad) pmaxc[0] = pmaxc[1] = 0.f;
+      static_for<0, 2>([&](auto s_tag) {
+        constexpr int s = decltype(s_tag)::value;
+        constexpr int LA = 3;  // row reads in flight ahead of the products
+        u32x4 rw[KS], tmv;
+        const uint32_t rb = lb + row_lane;
+        lds_read16_issue<s * 32 * 16>(lb + tm_lane, tmv);
+        static_for<0, LA>([&](auto k_tag) {
+          constexpr int k = decltype(k_tag)::value;
+          lds_read16_issue<s * 32 * RB + 32 * k>(rb, rw[k]);
+        });
+        lgkm_wait1<LA>(tmv);
+        sc[s] = mfma32(__builtin_bit_cast(bf16x8, tmv), ones3, f32x16{});
+        static_for<0, KS>([&](auto ks_tag) {
+          constexpr int ks = decltype(ks_tag)::value;
+          // reads issued after this k-step's: ks + 1 .. ks + LA - 1 (and any
+          // hand-over writes, which only make the wait conservative)
+          lgkm_wait1<(KS - 1 - ks < LA - 1 ? KS - 1 - ks : LA - 1)>(rw[ks]);
+          if constexpr (ks + LA < KS) lds_read16_issue<s * 32 * RB + 32 * (ks + LA)>(rb, rw[ks + LA]);
+          sc[s] = mfma32(__builtin_bit_cast(bf16x8, rw[ks]), kv[ks], sc[s]);
+          if constexpr (s == 1 && (ks & 1)) {
+            // score wave: P of subtile 0 beside subtile 1's products
+            if (!grad) p_rows(Z{}, std::integral_constant<int, (ks >> 1)>{});
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+      if (!grad) {
+        static_for<0, 4>([&](auto i4_tag) { p_rows(O{}, i4_tag); });
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          carry[i] = __float_as_uint(sc[0][i]);
+          carry[16 + i] = __float_as_uint(sc[1][i]);
+        }
+      }
+    };
+
+    // Back of an iteration: dV^T += dO^T P (score wave) or dK^T += Q^T dS
+    // (gradient wave, dS = P o dP' with P from hand-over area xs) of the
+    // block before, one instruction stream for both: the A operands are
+    // transposed reads of the dO or Q tile at the query rows of the packed
+    // operand's k-slots (pair hh: rows s * 32 + 16 hh + 4 g + {0..3,
+    // 8..11}).  Where a subtile holds a value above its threshold the
+    // rounded remainders are multiplied in as well.
+    auto back = [&](const char* buf, int xs) __attribute__((always_inline)) {
+      const uint32_t tbr = lds_addr(buf) + tr_lane + (grad ? 0u : (uint32_t)C::OFF_DO);
+      static_for<0, 2>([&](auto s_tag) {
+        constexpr int s = decltype(s_tag)::value;
+        constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
+        const u32x2* xr = reinterpret_cast<const u32x2*>(xchg) + (((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l;
+        i16x4 x0[8], x1[8];
+        tr_issue<D, OF0, RB>(tbr, x0);
+        tr_issue<D, OF1, RB>(tbr, x1);
+        // gradient wave: dS of register group i4 = P (fp16, from the score
+        // wave's lanes) times dP'
+        auto ds4 = [&](int i4, float (&d4)[4]) __attribute__((always_inline)) {
+          const u32x2 pv = xr[i4 * WAVE];
+          const float pf[4] = {f16_lo(pv[0]), f16_hi(pv[0]), f16_lo(pv[1]), f16_hi(pv[1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d4[e] = pf[e] * __uint_as_float(carry[16 * s + i4 * 4 + e]);
+        };
+        uint32_t op[2][4];
+        bool big;
+        if (grad) {
+          float dsmax = 0.f;
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            float d4[4];
+            ds4(i4, d4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dsmax = fmaxf(dsmax, fabsf(d4[e]));
+            op[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(d4[0], d4[1]);
+            op[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(d4[2], d4[3]);
+          }
+          big = dsmax > SPLIT_DS;
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) op[hh][k] = carry[8 * s + 4 * hh + k];
+          big = pmaxc[s] > SPLIT_P;
+        }
+        const bf16x8 o0 = __builtin_bit_cast(bf16x8, u32x4{op[0][0], op[0][1], op[0][2], op[0][3]});
+        const bf16x8 o1 = __builtin_bit_cast(bf16x8, u32x4{op[1][0], op[1][1], op[1][2], op[1][3]});
+        tr_wait<2 * DT>(x0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_operand(x0, dt), o0, acc[dt]);
+        tr_wait<0>(x1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_operand(x1, dt), o1, acc[dt]);
+        if (__builtin_expect(__any(big), 0)) {
+          u32x4 lo[2];
+          if (grad) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              float d4[4];
+              ds4(i4, d4);
+              lo[i4 >> 1][(i4 & 1) * 2] = bf16x2_residual(d4[0], d4[1], op[i4 >> 1][(i4 & 1) * 2]);
+              lo[i4 >> 1][(i4 & 1) * 2 + 1] = bf16x2_residual(d4[2], d4[3], op[i4 >> 1][(i4 & 1) * 2 + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) lo[hh][k] = carry[16 + 8 * s + 4 * hh + k];
+          }
+          // reads and their wait in one statement: on this rare path the
+          // compiler may move registers freely
+          bf16x8 y[4];
+          lds_operand_tr_x4(tbr + OF0 + 0 * RB, tbr + OF0 + 8 * RB, y);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(y[dt], __builtin_bit_cast(bf16x8, lo[0]), acc[dt]);
+          lds_operand_tr_x4(tbr + OF1 + 0 * RB, tbr + OF1 + 8 * RB, y);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(y[dt], __builtin_bit_cast(bf16x8, lo[1]), acc[dt]);
+        }
+      });
+    };
+
+    // The operand registers are taken here, outside the loops, so that the
+    // compiler's wait for their loads happens once per tile.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      asm volatile("" : "+v"(kvraw[ks]));
+      kv[ks] = __builtin_bit_cast(bf16x8, kvraw[ks]);
+    }
+    if (nb > 0) {
+      // Iteration i (0 <= i <= nb): the back of block i - 1, then the front
+      // of block i.  Blocks stream one ahead: block i + 1 is copied during
+      // iteration i into the ring buffer that block i - 2 left, so the ring
+      // holds the back's block, the front's block and the copies in flight.
+      {
+        if (iss_cur < 1) {
+          prep_next(cp, cp, false);  // this tile's first block
+          issue_now();
+          wait_vmcnt<0>();
+        } else {
+          static_assert(4 * DT <= 63, "store count");
+          wait_vmcnt<4 * DT>();
+        }
+        if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
+        barrier_lds();
+        handoff();
+        prep_next(cp, np, has_nxt);
+        issue_now();
+      }
+      int ring_back = 0;
+      auto iter = [&](auto masked_tag, int i) __attribute__((always_inline)) {
+        if (i > 0) {
+          wait_vmcnt<0>();  // this wave's copies of block i
+          barrier_lds();    // every wave's copies landed; block i - 2's buffer and hand-over area free
+          // Block i + 1 (the next tile's first block at i = nb - 1); the
+          // last iteration copies nothing, so that the stream never runs
+          // more than one block ahead of the fronts.
+          if (i < nb) {
+            prep_next(cp, np, has_nxt);
+            issue_now();
+          }
+          back(smem[ring_back], (i - 1) & 1);
+        }
+        if (i < nb) {
+          front(masked_tag, m_first + i, smem[ring_cmp], i & 1);
+          ring_back = ring_cmp;  // the next iteration's back reads this block
+          ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
+        }
+      };
+      // iterations [i0, i1) whose fronts take one mask variant (a loop per
+      // variant keeps register allocation to one body at a time)
+      auto run = [&](auto masked_tag, int i0, int i1) __attribute__((always_inline)) {
+        for (int i = i0; i < i1; ++i) iter(masked_tag, i);
+      };
+      if (tile_partial) {
+        run(std::true_type{}, 0, nb);
+      } else {
+        const int u0 = CAUSAL ? min(max(m_diag, m_first), m_end) - m_first : 0;
+        const int u1 = max(u0, min(m_full, m_end) - m_first);
+        run(std::true_type{}, 0, u0);
+        run(std::false_type{}, u0, u1);
+        run(std::true_type{}, u1, nb);
+      }
+      iter(std::false_type{}, nb);  // the last back
+    } else {
+      if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
+      if (DYN) barrier_lds();
+      handoff();
+    }
+
+    // Tile end: the next tile's operand rows, then (once every wave has
+    // read its P) this tile's stores through the hand-over area.
+    if (has_nxt) load_rows(np);
+    barrier_lds();
+    store_acc(cp, min(L - k0, BN), acc);
+    if (!has_nxt) break;
+    cp = np;
+    iss_cur = iss_nxt;
+    iss_nxt = 0;
+  }
+}
+
 // ----------------------------------------------------------- exact delta --
 // For a sequence with at most BWD_BN keys, delta_i = sum_k P_ik dP_ik from
 // fp32 P and dP (the same quantity as rowsum(dO o O), without the bf16
@@ -880,12 +1388,22 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.broadcast_q) {
-    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
-    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+  if constexpr (D == 128) {
+    if (a.broadcast_q) {
+      if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_pair_kernel<true, true>), dim3(a.P), dim3(512), 0, st, a, a.ktiles);
+      else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_pair_kernel<false, true>), dim3(a.P), dim3(512), 0, st, a, a.ktiles);
+    } else {
+      if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_pair_kernel<true, false>), dim3(a.P), dim3(512), 0, st, a, a.ktiles);
+      else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_pair_kernel<false, false>), dim3(a.P), dim3(512), 0, st, a, a.ktiles);
+    }
   } else {
-    if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
-    else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+    if (a.broadcast_q) {
+      if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, true>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+      else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, true>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+    } else {
+      if (a.causal) JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, true, false>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+      else JFA_TIMED_LAUNCH(K_DKDV, st, (dkdv_kernel<D, false, false>), dim3(a.P), dim3(256), 0, st, a, a.ktiles);
+    }
   }
   return hipGetLastError();
 }
@@ -898,3 +1416,4 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace jfa
+
