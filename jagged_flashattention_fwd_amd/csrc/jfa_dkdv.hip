@@ -858,6 +858,22 @@ template <int OFF>
 __device__ __forceinline__ void lds_read16_issue(uint32_t addr, u32x4& x) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(x) : "v"(addr), "i"(OFF));
 }
+// The four 8-byte hand-over values of one lane and subtile (register groups
+// 0..3 at a stride of 512 bytes), not waited for; hand_wait<N> makes them
+// available once at most N later LDS reads of this wave are outstanding.
+__device__ __forceinline__ void hand_issue(uint32_t addr, u32x2 (&x)[4]) {
+  asm volatile(
+      "ds_read_b64 %0, %4\n\t"
+      "ds_read_b64 %1, %4 offset:512\n\t"
+      "ds_read_b64 %2, %4 offset:1024\n\t"
+      "ds_read_b64 %3, %4 offset:1536"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(addr));
+}
+template <int N>
+__device__ __forceinline__ void hand_wait(u32x2 (&x)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(N));
+}
 template <int N>
 __device__ __forceinline__ void lgkm_wait1(u32x4& a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
@@ -982,15 +998,20 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
   };
 
   // dV (score wave) or scale * dK (gradient wave) of this wave's keys:
-  // each 32 x 32 chunk is transposed through the wave's 4 KB of the
-  // hand-over area (16-byte chunks XOR-swizzled by key) and leaves as whole
-  // 128-byte segments of 8 keys; bounded buffer stores, 4 * DT per wave.
-  auto store_acc = [&](const Tp& p, int nvalid, const f32x16 (&acc)[DT]) {
+  // each 32 x 32 chunk is transposed through LDS (16-byte chunks
+  // XOR-swizzled by key) and leaves as whole 128-byte segments of 8 keys;
+  // bounded buffer stores, 4 * DT per wave.  The staging is this wave's two
+  // 2 KB slots of hand-over area xs (keys 0..15, then 16..31), which no other
+  // wave touches at the tile end: the gradient wave's own, just read, and for
+  // the score wave the other area, whose P the gradient waves have consumed.
+  auto store_acc = [&](const Tp& p, int nvalid, const f32x16 (&acc)[DT], int xs) {
     const int64_t row0 = (p.s0 + p.k0) * H + p.h;
     const int nrec = nvalid * H * D * 4;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc((grad ? a.dk : a.dv) + row0 * D, nrec);
     const float mul = grad ? a.scale : 1.0f;
-    float* st = reinterpret_cast<float*>(xchg + wave * 4096);
+    char* slot0 = xchg + ((xs * 2 + 0) * C::NG + kgrp) * 2048;
+    char* slot1 = xchg + ((xs * 2 + 1) * C::NG + kgrp) * 2048;
+    auto row_at = [&](int kr) { return reinterpret_cast<float*>((kr < 16 ? slot0 : slot1) + (kr & 15) * 128); };
     const int rk8 = l >> 3, rc = l & 7;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -999,12 +1020,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[dt][i4 * 4 + e] * mul;
-        *reinterpret_cast<f32x4*>(st + lc * 32 + (((2 * i4 + g) ^ (lc & 7)) << 2)) = v;
+        *reinterpret_cast<f32x4*>(row_at(lc) + (((2 * i4 + g) ^ (lc & 7)) << 2)) = v;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kr = r * 8 + rk8;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(st + kr * 32 + ((rc ^ (kr & 7)) << 2));
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row_at(kr) + ((rc ^ (kr & 7)) << 2));
         const int off = ((kgrp * 32 + kr) * H * D + dt * 32 + rc * 4) * 4;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
       }
@@ -1017,7 +1038,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     f32x16 z[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
-    store_acc(cp, 0, z);  // stores that write nothing: the first tile start waits like every later one
+    store_acc(cp, 0, z, grad ? 1 : 0);  // stores that write nothing: the first tile start waits like every later one
   }
 
   constexpr bool DYN = CAUSAL || !BCAST;
@@ -1156,18 +1177,21 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
       static_for<0, 2>([&](auto s_tag) {
         constexpr int s = decltype(s_tag)::value;
         constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
-        const u32x2* xr = reinterpret_cast<const u32x2*>(xchg) + (((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l;
+        // gradient wave: its P values (fp16, from the score wave's lanes),
+        // read before the transposed reads so that dS is formed while those
+        // land
+        u32x2 pv[4];
+        if (grad) hand_issue(lds_addr(xchg) + (uint32_t)(((((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l) * 8), pv);
         i16x4 x0[8], x1[8];
         tr_issue<D, OF0, RB>(tbr, x0);
         tr_issue<D, OF1, RB>(tbr, x1);
-        // gradient wave: dS of register group i4 = P (fp16, from the score
-        // wave's lanes) times dP'
+        // dS of register group i4 = P times dP'
         auto ds4 = [&](int i4, float (&d4)[4]) __attribute__((always_inline)) {
-          const u32x2 pv = xr[i4 * WAVE];
-          const float pf[4] = {f16_lo(pv[0]), f16_hi(pv[0]), f16_lo(pv[1]), f16_hi(pv[1])};
+          const float pf[4] = {f16_lo(pv[i4][0]), f16_hi(pv[i4][0]), f16_lo(pv[i4][1]), f16_hi(pv[i4][1])};
 #pragma unroll
           for (int e = 0; e < 4; ++e) d4[e] = pf[e] * __uint_as_float(carry[16 * s + i4 * 4 + e]);
         };
+        if (grad) hand_wait<4 * DT>(pv);
         uint32_t op[2][4];
         bool big;
         if (grad) {
@@ -1294,11 +1318,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
       handoff();
     }
 
-    // Tile end: the next tile's operand rows, then (once every wave has
-    // read its P) this tile's stores through the hand-over area.
+    // Tile end: the next tile's operand rows, then this tile's stores
+    // through the wave's staging slots (the gradient waves last read area
+    // (nb - 1) & 1, which the score waves left in iteration nb - 1).
     if (has_nxt) load_rows(np);
-    barrier_lds();
-    store_acc(cp, min(L - k0, BN), acc);
+    store_acc(cp, min(L - k0, BN), acc, grad ? ((nb + 1) & 1) : (nb & 1));
     if (!has_nxt) break;
     cp = np;
     iss_cur = iss_nxt;
