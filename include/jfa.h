@@ -108,9 +108,11 @@ int jfa_bwd(const void* q, const void* k, const void* v, const int64_t* offsets,
  * query heads share one; dk and dv are [total_len, H_kv, d], each the sum
  * over the H / H_kv query heads of the group.  H_kv must divide H
  * (JFA_ERR_INVALID_ARG otherwise); H_kv = H is plain multi-head attention.
- * With H_kv < H the backward's workspace also holds per-query-head dK / dV
- * (2 * total_len * H * d fp32), summed per group in ascending head order,
- * so results stay bitwise reproducible.
+ * With H_kv < H the backward sums each group in a fixed order, so results
+ * stay bitwise reproducible: for d = 128 inside the dK / dV kernel (one tile
+ * per key / value head walks the group's query heads in ascending order);
+ * for d = 64 from per-query-head dK / dV in the workspace
+ * (2 * total_len * H * d fp32), summed per group in ascending head order.
  *
  * Sliding window: window = W > 0 (with causal = 1 only; JFA_ERR_UNSUPPORTED
  * otherwise, JFA_ERR_INVALID_ARG for W < 0) lets query i see keys j with
@@ -167,10 +169,11 @@ int jfa_schedule_params(int pass, int causal, int broadcast_q, int d, int* block
  *   jfa_debug_schedule: pass 0 = forward query tiles, 1 = backward key
  *     tiles; [cap][4] = b, h, block, worker slot; workspace of that pass.
  *   jfa_debug_schedule_ex: list 0 = forward query tiles, 1 = backward key
- *     tiles, 2 = the self-attention backward's dQ query tiles
- *     (broadcast_q = 0 only); H_kv key / value heads as in jfa_fwd_ex;
- *     [cap][5] = b, h, block, key / value head, worker slot; workspace of
- *     the forward (list 0) or backward (lists 1, 2). */
+ *     tiles as the d = 128 backward builds them (one per key / value head,
+ *     h = the group's first query head), 2 = the self-attention backward's
+ *     dQ query tiles (broadcast_q = 0 only); H_kv key / value heads as in
+ *     jfa_fwd_ex; [cap][5] = b, h, block, key / value head, worker slot;
+ *     workspace of the forward (list 0) or backward (lists 1, 2). */
 int jfa_debug_schedule(const int64_t* offsets, int B, int H, int Lq, int causal, int broadcast_q,
                        int pass, int64_t total_len, int32_t* tiles, int64_t cap, int64_t* n_tiles,
                        void* workspace, size_t workspace_bytes, void* stream);

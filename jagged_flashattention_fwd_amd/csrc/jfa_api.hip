@@ -126,6 +126,7 @@ struct Layout {
   int64_t cap_a = 0, cap_b = 0;
   size_t delta = 0, lse2 = 0, term_l = 0, term_d = 0, dq_part = 0;
   size_t dk_heads = 0, dv_heads = 0;  // grouped heads: dK / dV per query head before the group sum
+  size_t sched_end = 0;               // end of the tile lists (the layout's first part)
   size_t total = 0;
 };
 
@@ -142,6 +143,7 @@ Layout layout(int pass, int64_t total_len, int B, int H, int Hkv, int Lq, int d,
   if (pass == 0) {
     L.cap_a = max_tiles(0, total_len, B, H, Lq, broadcast_q);
     place_schedule(&at, L.sched_a, B, L.cap_a);
+    L.sched_end = at;
   } else {
     L.cap_a = max_tiles(1, total_len, B, H, Lq, broadcast_q);
     place_schedule(&at, L.sched_a, B, L.cap_a);
@@ -149,6 +151,7 @@ Layout layout(int pass, int64_t total_len, int B, int H, int Hkv, int Lq, int d,
       L.cap_b = max_tiles(0, total_len, B, H, Lq, broadcast_q);
       place_schedule(&at, L.sched_b, B, L.cap_b);
     }
+    L.sched_end = at;
     const size_t rows = broadcast_q ? (size_t)B * H * Lq : (size_t)total_len * H;
     L.delta = at; at = align256(at + sizeof(float) * rows);
     L.lse2 = at; at = align256(at + sizeof(float) * rows);
@@ -160,7 +163,7 @@ Layout layout(int pass, int64_t total_len, int B, int H, int Hkv, int Lq, int d,
       L.dq_part = at;
       at = align256(at + sizeof(float) * (size_t)H * n_qb * nc * DQ_BM_BCAST * d);
     }
-    if (Hkv < H) {
+    if (Hkv < H && d == 64) {  // d = 128 sums each group inside the dK / dV kernel
       L.dk_heads = at; at = align256(at + sizeof(float) * (size_t)total_len * H * d);
       L.dv_heads = at; at = align256(at + sizeof(float) * (size_t)total_len * H * d);
     }
@@ -394,7 +397,11 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   }
   char* ws = static_cast<char*>(workspace);
   const Schedule sk = schedule_at(ws, lay.sched_a, lay.cap_a);
-  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 1, BWD_BN, H / H_kv};
+  // Key tiles: d = 128, one per key / value head (its G query heads summed
+  // in the dK / dV kernel); d = 64, one per query head.
+  const bool kv_tiles = d == 128;
+  SchedArgs sa{offsets, total_len, B, kv_tiles ? H_kv : H, Lq, broadcast_q ? 1 : 0, 1, BWD_BN, H / H_kv};
+  sa.kv_tiles = kv_tiles ? 1 : 0;
   if (launch_schedule(sa, sk, st) != hipSuccess) return JFA_ERR_HIP;
   Schedule sq{};
   if (!broadcast_q) {
@@ -410,9 +417,9 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   ba.out = static_cast<const uint16_t*>(out);
   ba.lse = lse;
   ba.dout = static_cast<const uint16_t*>(dout);
-  // Grouped heads: the dK / dV kernel writes one slice per query head, summed
-  // over each group afterwards.
-  const bool grouped = H_kv < H;
+  // Grouped heads at d = 64: the dK / dV kernel writes one slice per query
+  // head, summed over each group afterwards.
+  const bool grouped = H_kv < H && !kv_tiles;
   ba.dq = dq;
   ba.dk = grouped ? reinterpret_cast<float*>(ws + lay.dk_heads) : dk;
   ba.dv = grouped ? reinterpret_cast<float*>(ws + lay.dv_heads) : dv;
@@ -475,13 +482,16 @@ int jfa_debug_schedule_ex(const int64_t* offsets, int B, int H, int H_kv, int Lq
   rc = workers(pass, &P);
   if (rc != JFA_OK) return rc;
   // The backward's own workspace layout, so that the same workspace serves.
-  const Layout lay = layout(pass, total_len, B, H, H_kv, Lq, 64, broadcast_q, P);
-  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  // Only the tile lists, at the front of the pass's layout, are used here.
+  const Layout lay = layout(pass, total_len, B, H, H_kv, Lq, 128, broadcast_q, P);
+  if (workspace_bytes < lay.sched_end) return JFA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const Schedule s = list == 2 ? schedule_at(ws, lay.sched_b, lay.cap_b) : schedule_at(ws, lay.sched_a, lay.cap_a);
   const int blk = list == 0 ? fwd_block_rows() : list == 1 ? BWD_BN : DQ_BM;
-  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, pass, blk, H / H_kv};
+  // the d = 128 lists: key tiles per key / value head
+  SchedArgs sa{offsets, total_len, B, list == 1 ? H_kv : H, Lq, broadcast_q ? 1 : 0, pass, blk, H / H_kv};
+  sa.kv_tiles = list == 1 ? 1 : 0;
   if (list == 2) sa.pass = 0;  // query tiles: the forward's per-sequence rule
   if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
   if (launch_schedule_dump(s, P, tiles, cap, n_tiles, 5, st) != hipSuccess) return JFA_ERR_HIP;

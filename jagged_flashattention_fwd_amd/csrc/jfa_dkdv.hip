@@ -858,22 +858,6 @@ template <int OFF>
 __device__ __forceinline__ void lds_read16_issue(uint32_t addr, u32x4& x) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(x) : "v"(addr), "i"(OFF));
 }
-// The four 8-byte hand-over values of one lane and subtile (register groups
-// 0..3 at a stride of 512 bytes), not waited for; hand_wait<N> makes them
-// available once at most N later LDS reads of this wave are outstanding.
-__device__ __forceinline__ void hand_issue(uint32_t addr, u32x2 (&x)[4]) {
-  asm volatile(
-      "ds_read_b64 %0, %4\n\t"
-      "ds_read_b64 %1, %4 offset:512\n\t"
-      "ds_read_b64 %2, %4 offset:1024\n\t"
-      "ds_read_b64 %3, %4 offset:1536"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
-      : "v"(addr));
-}
-template <int N>
-__device__ __forceinline__ void hand_wait(u32x2 (&x)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(N));
-}
 template <int N>
 __device__ __forceinline__ void lgkm_wait1(u32x4& a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
@@ -906,13 +890,20 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
 
   const int64_t qs = BCAST ? (int64_t)D : ld;  // row stride of Q / dO
   const int64_t sld = BCAST ? 1 : H;           // row stride of the per-row arrays
+  // A tile: 128 keys of one sequence and key / value head hk, against the
+  // query blocks m_first .. m_end - 1 of each of its ng query heads h ..
+  // h + ng - 1 (ng = G with grouped heads, one dK / dV accumulator for the
+  // group); its block stream is head-major, nb = ng * nbh blocks.
   struct Tp {
     int64_t s0;
-    int L, h, hk, b, k0, m_first, m_end, nq;
-    const uint16_t* qb;
+    int L, h, hk, b, k0, m_first, m_end, nq, nbh, nb;
+    const uint16_t* qb;  // Q, dO, row terms of the first query head
     const uint16_t* db;
     const u32x4* vb;
   };
+  const int ng = a.G;
+  const int64_t hs_qd = BCAST ? (int64_t)Lq * D : (int64_t)D;  // Q / dO: next query head
+  const int64_t hs_row = BCAST ? (int64_t)Lq : 1;              // row terms: next query head
   auto tparams = [&](const TileRec& r) {
     Tp p;
     p.s0 = r.s0;
@@ -925,6 +916,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     p.m_first = CAUSAL ? p.k0 / QB : 0;
     p.m_end = max((p.nq + QB - 1) / QB, p.m_first);
     if (CAUSAL && a.window > 0) p.m_end = max(min(p.m_end, (p.k0 + BN - 2 + a.window) / QB + 1), p.m_first);
+    p.nbh = p.m_end - p.m_first;
+    p.nb = ng * p.nbh;
     p.qb = BCAST ? a.q + (int64_t)r.h * Lq * D : a.q + (r.s0 * H + r.h) * (int64_t)D;
     p.db = BCAST ? a.dout + ((int64_t)r.b * H + r.h) * Lq * D : a.dout + (r.s0 * H + r.h) * (int64_t)D;
     p.vb = reinterpret_cast<const u32x4*>((wave & 1) ? a.term_d : a.term_l) +
@@ -957,25 +950,40 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
   };
   int ring_iss = 0, ring_cmp = 0;
   int iss_cur = 0, iss_nxt = 0;
+  // position of the current tile's next block to issue: query head gi
+  // (0 .. ng-1), block j - m_first (0 .. nbh-1).  The stream runs at most
+  // one block ahead, so of the next tile only its first block (head 0,
+  // block m_first) is ever issued early.
+  int cur_gi = 0, cur_jb = 0;
   auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
     j_n = 0;
-    const int nbc = cp.m_end - cp.m_first;
-    const int nbn = has_nxt ? np.m_end - np.m_first : 0;
-    const bool cur = iss_cur < nbc;
-    if (!cur && iss_nxt >= nbn) return;
+    const int nbn = has_nxt ? np.nb : 0;
+    const bool cur = iss_cur < cp.nb;
+    if (!cur && iss_nxt >= min(nbn, 1)) return;
+    // the block: query head gi, block j of the current tile, or the next
+    // tile's first block
+    const int gi = cur ? cur_gi : 0;
+    const int j = cur ? cp.m_first + cur_jb : np.m_first;
     const int nq_ = cur ? cp.nq : np.nq;
-    const int j = cur ? cp.m_first + iss_cur : np.m_first + iss_nxt;
     const int base_row = min(j * QB + wave * C::RPW, nq_ - 1);
     const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(qs * 2);
-    j_q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.qb : np.qb) + roff);
-    j_d = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.db : np.db) + roff);
-    j_v = (cur ? cp.vb : np.vb) + (int64_t)min(j * QB + l, nq_ - 1) * sld;
+    j_q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>((cur ? cp.qb : np.qb) + gi * hs_qd) + roff);
+    j_d = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>((cur ? cp.db : np.db) + gi * hs_qd) + roff);
+    j_v = (cur ? cp.vb : np.vb) + gi * hs_row + (int64_t)min(j * QB + l, nq_ - 1) * sld;
     j_lds = lds_addr(smem[ring_iss]);
     j_ldw = j_lds + wave * C::RPW * RB;
     j_last = nq_ - 1 - base_row;
     j_n = C::IPS;
-    if (cur) ++iss_cur;
-    else ++iss_nxt;
+    // (value selects, not a branch over which counter to bump: the latter
+    // becomes an increment through a selected address, which puts the
+    // counters in scratch memory)
+    const int c1 = cur ? 1 : 0;
+    const int jb1 = cur_jb + c1;
+    const bool wrap = jb1 == cp.nbh;
+    iss_cur += c1;
+    iss_nxt += 1 - c1;
+    cur_jb = wrap ? 0 : jb1;
+    cur_gi += wrap ? 1 : 0;
     ring_iss = ring_iss == NBUF - 1 ? 0 : ring_iss + 1;
   };
   auto issue_now = [&]() {
@@ -998,20 +1006,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
   };
 
   // dV (score wave) or scale * dK (gradient wave) of this wave's keys:
-  // each 32 x 32 chunk is transposed through LDS (16-byte chunks
-  // XOR-swizzled by key) and leaves as whole 128-byte segments of 8 keys;
-  // bounded buffer stores, 4 * DT per wave.  The staging is this wave's two
-  // 2 KB slots of hand-over area xs (keys 0..15, then 16..31), which no other
-  // wave touches at the tile end: the gradient wave's own, just read, and for
-  // the score wave the other area, whose P the gradient waves have consumed.
-  auto store_acc = [&](const Tp& p, int nvalid, const f32x16 (&acc)[DT], int xs) {
-    const int64_t row0 = (p.s0 + p.k0) * H + p.h;
-    const int nrec = nvalid * H * D * 4;
+  // each 32 x 32 chunk is transposed through the wave's 4 KB of the
+  // hand-over area (16-byte chunks XOR-swizzled by key; every wave has read
+  // its P when this runs) and leaves as whole 128-byte segments of 8 keys;
+  // bounded buffer stores, 4 * DT per wave.
+  auto store_acc = [&](const Tp& p, int nvalid, const f32x16 (&acc)[DT]) {
+    const int64_t row0 = (p.s0 + p.k0) * a.Hkv + p.hk;  // dK / dV are [total_len, H_kv, d]
+    const int nrec = nvalid * a.Hkv * D * 4;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc((grad ? a.dk : a.dv) + row0 * D, nrec);
     const float mul = grad ? a.scale : 1.0f;
-    char* slot0 = xchg + ((xs * 2 + 0) * C::NG + kgrp) * 2048;
-    char* slot1 = xchg + ((xs * 2 + 1) * C::NG + kgrp) * 2048;
-    auto row_at = [&](int kr) { return reinterpret_cast<float*>((kr < 16 ? slot0 : slot1) + (kr & 15) * 128); };
+    char* const st = xchg + wave * 4096;
+    auto row_at = [&](int kr) { return reinterpret_cast<float*>(st + kr * 128); };
     const int rk8 = l >> 3, rc = l & 7;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -1026,7 +1031,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
       for (int r = 0; r < 4; ++r) {
         const int kr = r * 8 + rk8;
         const f32x4 v = *reinterpret_cast<const f32x4*>(row_at(kr) + ((rc ^ (kr & 7)) << 2));
-        const int off = ((kgrp * 32 + kr) * H * D + dt * 32 + rc * 4) * 4;
+        const int off = ((kgrp * 32 + kr) * a.Hkv * D + dt * 32 + rc * 4) * 4;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
       }
     }
@@ -1038,7 +1043,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     f32x16 z[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
-    store_acc(cp, 0, z, grad ? 1 : 0);  // stores that write nothing: the first tile start waits like every later one
+    store_acc(cp, 0, z);  // stores that write nothing: the first tile start waits like every later one
   }
 
   constexpr bool DYN = CAUSAL || !BCAST;
@@ -1063,7 +1068,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     const bool key_ok = kw < L;
     const int nq = BCAST ? Lq : L;
     const int m_first = cp.m_first, m_end = cp.m_end;
-    const int nb = m_end - m_first;
+    const int nbh = cp.nbh, nb = cp.nb;  // blocks per query head; of the whole stream
     const int m_diag = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
     const bool tile_partial = k0 + BN > L || a.window > 0;
     const int m_full = nq / QB;
@@ -1177,21 +1182,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
       static_for<0, 2>([&](auto s_tag) {
         constexpr int s = decltype(s_tag)::value;
         constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
-        // gradient wave: its P values (fp16, from the score wave's lanes),
-        // read before the transposed reads so that dS is formed while those
-        // land
-        u32x2 pv[4];
-        if (grad) hand_issue(lds_addr(xchg) + (uint32_t)(((((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l) * 8), pv);
+        const u32x2* xr = reinterpret_cast<const u32x2*>(xchg) + (((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l;
         i16x4 x0[8], x1[8];
         tr_issue<D, OF0, RB>(tbr, x0);
         tr_issue<D, OF1, RB>(tbr, x1);
-        // dS of register group i4 = P times dP'
+        // gradient wave: dS of register group i4 = P (fp16, from the score
+        // wave's lanes) times dP'
         auto ds4 = [&](int i4, float (&d4)[4]) __attribute__((always_inline)) {
-          const float pf[4] = {f16_lo(pv[i4][0]), f16_hi(pv[i4][0]), f16_lo(pv[i4][1]), f16_hi(pv[i4][1])};
+          const u32x2 pv = xr[i4 * WAVE];
+          const float pf[4] = {f16_lo(pv[0]), f16_hi(pv[0]), f16_lo(pv[1]), f16_hi(pv[1])};
 #pragma unroll
           for (int e = 0; e < 4; ++e) d4[e] = pf[e] * __uint_as_float(carry[16 * s + i4 * 4 + e]);
         };
-        if (grad) hand_wait<4 * DT>(pv);
         uint32_t op[2][4];
         bool big;
         if (grad) {
@@ -1278,7 +1280,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
         issue_now();
       }
       int ring_back = 0;
-      auto iter = [&](auto masked_tag, int i) __attribute__((always_inline)) {
+      // iteration i; its front is block m (of the stream's current query head)
+      auto iter = [&](auto masked_tag, int i, int m) __attribute__((always_inline)) {
         if (i > 0) {
           wait_vmcnt<0>();  // this wave's copies of block i
           barrier_lds();    // every wave's copies landed; block i - 2's buffer and hand-over area free
@@ -1292,38 +1295,41 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
           back(smem[ring_back], (i - 1) & 1);
         }
         if (i < nb) {
-          front(masked_tag, m_first + i, smem[ring_cmp], i & 1);
+          front(masked_tag, m, smem[ring_cmp], i & 1);
           ring_back = ring_cmp;  // the next iteration's back reads this block
           ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
         }
       };
       // iterations [i0, i1) whose fronts take one mask variant (a loop per
       // variant keeps register allocation to one body at a time)
-      auto run = [&](auto masked_tag, int i0, int i1) __attribute__((always_inline)) {
-        for (int i = i0; i < i1; ++i) iter(masked_tag, i);
+      // iterations [i0, i1) of the head whose blocks start at iteration hb
+      auto run = [&](auto masked_tag, int i0, int i1, int hb) __attribute__((always_inline)) {
+        for (int i = i0; i < i1; ++i) iter(masked_tag, i, m_first + (i - hb));
       };
-      if (tile_partial) {
-        run(std::true_type{}, 0, nb);
-      } else {
-        const int u0 = CAUSAL ? min(max(m_diag, m_first), m_end) - m_first : 0;
-        const int u1 = max(u0, min(m_full, m_end) - m_first);
-        run(std::true_type{}, 0, u0);
-        run(std::false_type{}, u0, u1);
-        run(std::true_type{}, u1, nb);
+      // per query head: blocks [0, u0) and [u1, nbh) take the masked front
+      const int u0 = tile_partial ? nbh : CAUSAL ? min(max(m_diag, m_first), m_end) - m_first : 0;
+      const int u1 = tile_partial ? nbh : max(u0, min(m_full, m_end) - m_first);
+      for (int i0 = 0; i0 < nb; i0 += nbh) {
+        run(std::true_type{}, i0, i0 + u0, i0);
+        run(std::false_type{}, i0 + u0, i0 + u1, i0);
+        run(std::true_type{}, i0 + u1, i0 + nbh, i0);
       }
-      iter(std::false_type{}, nb);  // the last back
+      iter(std::false_type{}, nb, 0);  // the last back
     } else {
       if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
       if (DYN) barrier_lds();
       handoff();
     }
 
-    // Tile end: the next tile's operand rows, then this tile's stores
-    // through the wave's staging slots (the gradient waves last read area
-    // (nb - 1) & 1, which the score waves left in iteration nb - 1).
+    // Tile end: the next tile's operand rows, then (once every wave has
+    // read its P) this tile's stores through the hand-over area.
     if (has_nxt) load_rows(np);
-    store_acc(cp, min(L - k0, BN), acc, grad ? ((nb + 1) & 1) : (nb & 1));
+    barrier_lds();
+    store_acc(cp, min(L - k0, BN), acc);
     if (!has_nxt) break;
+    // the next tile's first block may already be issued
+    cur_gi = iss_nxt > 0 && np.nbh == 1 ? 1 : 0;
+    cur_jb = iss_nxt > 0 && np.nbh > 1 ? 1 : 0;
     cp = np;
     iss_cur = iss_nxt;
     iss_nxt = 0;

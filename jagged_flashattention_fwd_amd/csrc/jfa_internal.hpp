@@ -43,6 +43,10 @@ struct SchedArgs {
   int64_t total_len;
   int B, H, Lq, broadcast_q, pass, blk;
   int G;  // query heads per key / value head (the tile records' hk = h / G)
+  // 1: the tiles are per key / value head (H above is H_kv): each covers the
+  // G query heads of its group, its record carries the group's first query
+  // head h = hk * G and hk.  0: per query head.
+  int kv_tiles = 0;
 };
 
 // Once per device, with it current: kernel attributes of the scheduler.

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(256) void sched_expand(SchedArgs a, Schedule s) {
     const int64_t i = j - (int64_t)h * nblk;
     const int blk = (int)(a.pass == 0 ? nblk - 1 - i : i);
     const int64_t pos = head_major ? h * (T / a.H) + start / a.H + i : start + j;
-    if (pos < s.max_tiles) s.tiles[pos] = TileRec{b, h, blk, (int)L, s0, h / a.G, 0};
+    const TileRec rec = a.kv_tiles ? TileRec{b, h * a.G, blk, (int)L, s0, h, 0} : TileRec{b, h, blk, (int)L, s0, h / a.G, 0};
+    if (pos < s.max_tiles) s.tiles[pos] = rec;
   }
 }
 

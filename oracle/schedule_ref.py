@@ -31,7 +31,10 @@ count P are parameters; tie-breaks are this library's reading):
   5. Tile t goes to worker slot: pass p = t // P, s = t % P,
      slot = s if p is even else P - 1 - s.
   6. With grouped-query heads (G query heads per key/value head), a tile
-     of query head h reads key/value head h // G.
+     of query head h reads key/value head h // G.  The backward's key tiles
+     are per key/value head instead (one tile covers the G query heads of
+     its group): rules 3-5 with H // G heads, each tile recorded with the
+     group's first query head hk * G and hk.
 
 The self-attention backward's dQ pass walks query tiles by the forward's
 rules (pass 0) with its own block size.
@@ -67,13 +70,17 @@ def schedule(lengths, H: int, Lq: int, broadcast_q: bool, pass_: int, BM: int, B
              G: int = 0):
     """Full tile list in tile order t = 0, 1, ...: [(b, h, block, slot), ...],
     or with G > 0 query heads per key/value head [(b, h, block, h // G,
-    slot), ...]."""
+    slot), ...]; for the backward's key tiles (pass 1) with G > 0, H counts
+    key/value heads and the records are (b, hk * G, block, hk, slot)."""
     triples = []
     for b in sequence_order(lengths):
         for (h, blk) in tiles_of_sequence(int(lengths[b]), H, Lq, broadcast_q, pass_, BM, BN):
             triples.append((b, h, blk))
     if pass_ == 1 and broadcast_q:
         triples = [x for h in range(H) for x in triples if x[1] == h]
+    if G and pass_ == 1:
+        # key tiles per key/value head: H here counts key/value heads
+        return [(b, hk * G, blk, hk, zigzag_slot(t, P)) for t, (b, hk, blk) in enumerate(triples)]
     if G:
         return [(b, h, blk, h // G, zigzag_slot(t, P)) for t, (b, h, blk) in enumerate(triples)]
     return [(b, h, blk, zigzag_slot(t, P)) for t, (b, h, blk) in enumerate(triples)]

@@ -210,7 +210,7 @@ def test_schedule_bit_exact_on_workload_offsets(jfa, name, list_):
     off = torch.from_numpy(wl.offsets_from_lengths(lengths)).cuda()
     T = int(off[-1])
     ws = jfa.workspace(T, B, H, Lq, w.d, w.causal, bq, 0 if list_ == 0 else 1, "cuda", H_kv=Hkv)
-    ref = sr.schedule(lengths, H, Lq, bq, 1 if list_ == 1 else 0, blk, blk, P, G=H // Hkv)
+    ref = sr.schedule(lengths, Hkv if list_ == 1 else H, Lq, bq, 1 if list_ == 1 else 0, blk, blk, P, G=H // Hkv)
     cap = len(ref) + 3
     tiles = torch.full((cap, 5), -7, dtype=torch.int32, device="cuda")
     n = torch.zeros(1, dtype=torch.int64, device="cuda")
