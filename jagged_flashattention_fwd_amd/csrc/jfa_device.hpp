@@ -6,10 +6,14 @@
 //   A:  lane l holds A[l % 32][8*(l/32) + 0..7]
 //   B:  lane l holds B[8*(l/32) + 0..7][l % 32]
 //   C:  lane l, register i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
-// LDS tiles are row-major bf16 with padded rows (TileGeom) so that both
-// access patterns the kernels use are free of bank conflicts within 16
-// lanes: 16-byte reads of 16 rows at one chunk, and the transposing read
-// ds_read_b64_tr_b16 (4 rows x 32 bytes per 16 lanes).
+// LDS tiles are row-major bf16 with padded rows (TileGeom).  The LDS serves
+// 256 bytes per cycle: a 16-byte read takes 16 lanes per cycle, the
+// transposing read ds_read_b64_tr_b16 32 lanes (4 rows x 64 bytes).  Rows of
+// 304 bytes keep 16-byte reads of 16 consecutive rows free of bank
+// conflicts; under the transposing read, neighbouring rows overlap by 16
+// bytes (a two-way conflict, seen in the SQ_LDS_BANK_CONFLICT counter).
+// Tiles read only by the transposing read use 320-byte rows, which are free
+// of conflicts there (no conflict cycles counted).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -108,10 +112,8 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 
 // ------------------------------------------------------------- LDS tiles --
 // Row-major bf16 tile with D columns, rows padded to ROW_BYTES.  The padding
-// is chosen so that (a) 16-byte reads of 16 consecutive rows at one column
-// hit 16 distinct 16-byte bank groups (ROW_BYTES / 16 is odd), and (b) the
-// transpose read, which takes 32 bytes from each of 4 consecutive rows per
-// 16 lanes, touches 4 disjoint 32-byte ranges modulo 256 bytes.  Because the
+// is chosen so that 16-byte reads of 16 consecutive rows at one column hit
+// 16 distinct 16-byte bank groups (ROW_BYTES / 16 is odd).  Because the
 // layout is affine in (row, column), every operand address is one per-lane
 // base plus a compile-time constant, which the LDS instructions take as an
 // immediate offset.
@@ -120,9 +122,6 @@ struct TileGeom {
   static_assert(D == 64 || D == 128, "tile width");
   static constexpr int ROW_BYTES = D == 128 ? 304 : 208;
 };
-// Row bytes of a 64-column tile that is only ever read with the transpose
-// read (condition (b) alone).
-constexpr int TR_ONLY_ROW_BYTES_64 = 160;
 // Byte offset of (row, 16-byte chunk).
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {
@@ -287,6 +286,16 @@ __device__ __forceinline__ void dma_copy16(const void* base, uint32_t voff, uint
                "s"((const void*)(uintptr_t)ru), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
 }
+// The same copy through a buffer resource: 16 bytes per lane from byte
+// soff + voff of the resource into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds).  The range check covers soff + voff: a
+// lane at or past the resource's size reads nothing and writes zeros to its
+// 16 bytes of LDS (checked on the device).  soff is wave-uniform.
+__device__ __forceinline__ void dma_copy16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rs),
+               "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "m0");
+}
 #pragma clang diagnostic pop
 
 // Buffer resource over [base, base + nbytes): buffer stores at byte offsets
@@ -301,22 +310,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
-// Rows of 256 data bytes padded to 304 in LDS (19 chunks of 16 bytes), copied
-// with dma_copy16: one copy fills 3 whole rows and the first 7 chunks of a
-// fourth.  Lane l moves chunk l % 19 of row l / 19; chunks 16..18 are padding
-// (those lanes re-read chunk 0 into it).  A run of n >= 3 rows takes
-// ceil(n / 3) copies starting at rows min(3 k, n - 3); the overhang into the
-// row after the run writes the values that row's own copy writes, or lands
-// in a gap of at least 112 bytes after the tile.
-struct PadRowCopy {
+// Rows of 256 data bytes padded to NCH 16-byte chunks in LDS (NCH = 19:
+// 304-byte rows; 20: 320-byte rows), copied with dma_copy16: one copy fills
+// 3 whole rows and the first 64 - 3 NCH chunks of a fourth.  Lane l moves
+// chunk l % NCH of row l / NCH; chunks 16 .. NCH - 1 are padding (those
+// lanes re-read chunk 0 into it).  A run of n >= 3 rows takes ceil(n / 3)
+// copies starting at rows min(3 k, n - 3); the overhang into the row after
+// the run writes the values that row's own copy writes, or lands in the
+// GAP bytes kept after the tile.
+template <int NCH>
+struct PadRowCopyN {
   static constexpr int GAP = 128;
+  static_assert(NCH >= 16 && 64 / NCH == 3 && (64 - 3 * NCH) * 16 <= GAP, "three rows and part of a fourth");
+  static constexpr int ROW_BYTES = NCH * 16;
   uint32_t row;   // row of this lane within a copy (0..3)
   uint32_t byte;  // byte offset of its chunk within the row
-  __device__ __forceinline__ PadRowCopy() {
-    const int l = lane_id();
-    row = (uint32_t)(l / 19);
-    byte = (l % 19) < 16 ? (uint32_t)(l % 19) * 16u : 0u;
-  }
+  __device__ __forceinline__ PadRowCopyN() : row(lane_row(lane_id())), byte(lane_byte(lane_id())) {}
+  __device__ static constexpr uint32_t lane_row(int l) { return (uint32_t)(l / NCH); }
+  __device__ static constexpr uint32_t lane_byte(int l) { return (l % NCH) < 16 ? (uint32_t)(l % NCH) * 16u : 0u; }
   static constexpr int copies(int n) { return (n + 2) / 3; }
   static constexpr int start(int k, int n) { return 3 * k < n - 3 ? 3 * k : n - 3; }
   // Per-lane source offset of copy k of a run whose rows past `last` repeat
@@ -325,6 +336,7 @@ struct PadRowCopy {
     return (uint32_t)min(R + (int)row, last) * stride + byte;
   }
 };
+using PadRowCopy = PadRowCopyN<19>;
 
 // s_waitcnt with only the vector-memory counter constrained (at most n
 // operations of this wave still outstanding; n <= 63).

@@ -53,20 +53,28 @@ struct Fwd {
   static constexpr int DT = D / 32;    // 32-wide head-dim tiles of O^T
   static constexpr int TILE_BYTES = tile_bytes<BN, D>();
   // d = 128: K/V rows go straight from global memory to LDS (three padded
-  // rows per copy), DEP steps ahead of the one being computed, in a ring of
-  // DEP + 1 buffers.  Each wave copies RPW rows of K and of V per step, IPS
+  // rows per copy), DEP = 2 steps ahead of the one being computed, in a ring
+  // of 4 buffers.  Each wave copies RPW rows of K and of V per step, IPS
   // copies; the vector-memory counter can hold at most 63 outstanding
-  // operations, which bounds DEP.
+  // operations.
   // d = 64: rows are staged through registers one step ahead.
   static constexpr bool DMA = D == 128;
   static constexpr int RPW = BN / NW;
   static constexpr int CPT = PadRowCopy::copies(RPW);
   static constexpr int IPS = 2 * CPT;
-  static constexpr int DEP = DMA ? ((2 * IPS <= 63) ? 3 : 2) : 1;
-  static constexpr int NBUF = DEP + 1;
+  static constexpr int DEP = DMA ? 2 : 1;
+  static constexpr int NBUF = DMA ? 4 : 2;
   static_assert((NBUF & (NBUF - 1)) == 0, "ring index by mask");
   static constexpr int BUF_BYTES = TILE_BYTES + PadRowCopy::GAP;
-  static_assert(!DMA || (TileGeom<D>::ROW_BYTES == 19 * 16 && RPW >= 3), "copy geometry");
+  static_assert(!DMA || (TileGeom<D>::ROW_BYTES == PadRowCopy::ROW_BYTES && RPW >= 3), "copy geometry");
+  // V tiles of the direct-copy form are only read with the transposing read
+  // (32 lanes take 64 bytes from each of 4 consecutive rows): 320-byte rows
+  // put those rows 64 bytes apart modulo the 256 bytes of the LDS banks, so
+  // the 32 lanes touch every bank once.  Rows of 304 bytes (K) overlap by
+  // 16 bytes between neighbours there.
+  using VCopy = PadRowCopyN<20>;
+  static constexpr int ROW_BYTES_V = DMA ? VCopy::ROW_BYTES : TileGeom<D>::ROW_BYTES;
+  static constexpr int BUF_BYTES_V = BN * ROW_BYTES_V + VCopy::GAP;
 };
 
 template <int D, int NW, int QW, bool CAUSAL, bool BCAST>
@@ -347,10 +355,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   static_assert(C::DMA, "direct-copy form");
   constexpr int BN = C::BN, QS = C::QS, BM = C::BM, KS = C::KS, DT = C::DT;
   constexpr int NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS, RPW = C::RPW, RB = TileGeom<D>::ROW_BYTES;
+  constexpr int RBV = C::ROW_BYTES_V;
   // Stores per wave at a tile end: O (DT * 2 pieces of 16 bytes) and lse, per subtile.
   constexpr int NST = QS * (2 * DT + 1);
   static_assert(DEP * IPS + NST <= 63, "vector-memory counter");
-  __shared__ __attribute__((aligned(16))) char smem[NBUF][2][C::BUF_BYTES];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char smem_k[NBUF][C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem_v[NBUF][C::BUF_BYTES_V];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -360,7 +370,11 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   const int H = a.H, Lq = a.Lq;
   const int64_t ld = (int64_t)a.Hkv * D;  // K / V row stride (elements)
   const float c2 = a.scale_log2;
-  const PadRowCopy pc;
+  // This lane's source byte offset within a K copy (304-byte rows in LDS)
+  // and a V copy (320-byte rows), relative to the copy's first row.
+  const uint32_t rstride = (uint32_t)(ld * 2);
+  const uint32_t voff_k = PadRowCopy::lane_row(l) * rstride + PadRowCopy::lane_byte(l);
+  const uint32_t voff_v = C::VCopy::lane_row(l) * rstride + C::VCopy::lane_byte(l);
 
   const int64_t t0 = zigzag_tile(0, slot, a.P);
   if (t0 >= T) return;
@@ -396,12 +410,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   // over the whole stream; iss_cur / iss_nxt: steps of the current / next
   // tile issued.
   int g_iss = 0, g_cmp = 0, iss_cur = 0, iss_nxt = 0;
-  // The prepared step: this wave's first K and V source rows, rows past
-  // j_last repeat row j_last, its ring buffer, and whether there is one.
-  const uint16_t* j_k = a.k;
-  const uint16_t* j_v = a.v;
+  // The prepared step: buffer resources over this wave's K and V source
+  // rows of it (the rows that exist, at most RPW + 1: a copy's overhang
+  // reaches one row past the run; rows past the sequence end read as
+  // zeros), its ring buffer, and whether there is one.
+  __amdgpu_buffer_rsrc_t j_rk = make_rsrc(a.k, 0), j_rv = make_rsrc(a.v, 0);
   uint32_t j_kd = 0, j_vd = 0;
-  int j_last = 0;
   bool j_on = false;
   auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
     const int nn = has_nxt ? np.n_kv - np.j0 : 0;
@@ -410,28 +424,28 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     if (!j_on) return;
     const int L_ = cur ? cp.L : np.L;
     const int j = cur ? cp.j0 + iss_cur : np.j0 + iss_nxt;
-    const int base_row = min(j * BN + wave * RPW, L_ - 1);
+    const int base_row = j * BN + wave * RPW;
+    const int rows = max(0, min(L_ - base_row, RPW + 1));
     // byte offset of the row within the sequence (a 32 x 32-bit product)
-    const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(ld * 2);
-    j_k = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + roff);
-    j_v = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.vb : np.vb) + roff);
-    j_last = L_ - 1 - base_row;
+    const uint64_t roff = (uint64_t)(uint32_t)base_row * rstride;
+    j_rk = make_rsrc(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + roff, rows * (int)rstride);
+    j_rv = make_rsrc(reinterpret_cast<const char*>(cur ? cp.vb : np.vb) + roff, rows * (int)rstride);
     const int buf = (int)((uint32_t)g_iss % NBUF);
-    j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
-    j_vd = lds_addr(smem[buf][1]) + wave * RPW * RB;
+    j_kd = lds_addr(smem_k[buf]) + wave * RPW * RB;
+    j_vd = lds_addr(smem_v[buf]) + wave * RPW * RBV;
     if (cur) ++iss_cur;
     else ++iss_nxt;
     ++g_iss;
   };
-  // Copies [k0, k1) of the prepared step (K for k < CPT, V after).
+  // Copies [k0, k1) of the prepared step (K for k < CPT, V after); the
+  // copy's first row goes into the scalar offset.
   auto issue_copies = [&](int k0, int k1) {
     if (!j_on) return;
 #pragma unroll
     for (int k = k0; k < k1; ++k) {
       const int R = PadRowCopy::start(k % C::CPT, RPW);
-      const uint32_t vo = pc.voff(R, j_last, (uint32_t)(ld * 2));
-      if (k < C::CPT) dma_copy16(j_k, vo, j_kd + R * RB);
-      else dma_copy16(j_v, vo, j_vd + R * RB);
+      if (k < C::CPT) dma_copy16_buf(j_rk, voff_k, R * rstride, j_kd + R * RB);
+      else dma_copy16_buf(j_rv, voff_v, R * rstride, j_vd + R * RBV);
     }
   };
 
@@ -579,7 +593,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // ks + 1 is read before the products of k-step ks, and hook(ks) runs
     // after them.
     auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook) {
-      const char* Ks = smem[(uint32_t)gi % NBUF][0];
+      const char* Ks = smem_k[(uint32_t)gi % NBUF];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -612,23 +626,23 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // are issued before the products of the piece before.
     const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
     auto pv_phase = [&](int gi, const uint32_t (&pk)[2][2][QS][4]) {
-      const char* Vs = smem[(uint32_t)gi % NBUF][1];
+      const char* Vs = smem_v[(uint32_t)gi % NBUF];
       uint32_t va[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int r0 = (grp >> 1) * 32 + (grp & 1) * 16 + g * 4;
-        va[grp] = lds_addr(Vs + tile_off_col4<D>(r0 + jj, cq));
+        va[grp] = lds_addr(Vs + tile_off_col4<D, RBV>(r0 + jj, cq));
       }
       i16x4 xv[2][4];
       static_assert(DT == 4, "two pieces of two head-dim tiles per key group");
-      tr4_issue<0>(va[0], va[0] + 8 * RB, xv[0]);
+      tr4_issue<0>(va[0], va[0] + 8 * RBV, xv[0]);
       static_for<0, 8>([&](auto pc_tag) {
         constexpr int pc = decltype(pc_tag)::value;
         constexpr int grp = pc >> 1, hf = pc & 1;
         constexpr int kt = grp >> 1, hh = grp & 1;
         if constexpr (pc + 1 < 8) {
           constexpr int ng = (pc + 1) >> 1, nh = (pc + 1) & 1;
-          tr4_issue<nh * 128>(va[ng], va[ng] + 8 * RB, xv[(pc + 1) & 1]);
+          tr4_issue<nh * 128>(va[ng], va[ng] + 8 * RBV, xv[(pc + 1) & 1]);
           tr4_wait<4>(xv[pc & 1]);
         } else {
           tr4_wait<0>(xv[pc & 1]);
