@@ -149,53 +149,206 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, kernel: str, copy_bytes: int) -> str:
-    """Write profiles/traffic_<kernel>_<workload>.txt from two rocprofv3 --pmc
-    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each counter is scaled
-    by bytes-moved / counter-reading of the plain device copy of copy_bytes
-    that bench.py --copy-calibration-mib runs in the same process."""
+# Kernel symbols behind each of the library's timing labels.
+LABEL_SYMBOLS = {
+    "fwd_kernel": ("fwd_kernel", "fwd_kernel_dma"),
+    "delta_kernel": ("delta_kernel",),
+    "delta_exact_kernel": ("delta_exact_kernel",),
+    "dkdv_kernel": ("dkdv_kernel", "dkdv_pair_kernel"),
+    "dq_kernel": ("dq_kernel", "dq_bcast_kernel"),
+    "dq_reduce": ("dq_reduce",),
+    "group_sum_kernel": ("group_sum_kernel",),
+}
+# Counter passes of the counters summary (rocprofv3 collects each pass in a
+# run of its own; at most 8 SQ and 2 GRBM counters per pass).
+COUNTER_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SALU "
+    "SQ_INSTS_VMEM SQ_WAVES GRBM_GUI_ACTIVE",
+)
+N_XCD = 8          # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs
+SIMD_PER_CU = 4
+MFMA_CYCLES = 32   # v_mfma_f32_32x32x16_bf16 on one SIMD
+
+
+def kernel_base(name: str) -> str:
+    """Bare function name of a rocprofv3 kernel name ("void ns::f<...>(...)" -> "f")."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("(anonymous namespace)", "")
+    depth, out = 0, []
+    for ch in n:  # drop template arguments and the parameter list
+        if ch in "<(":
+            if depth == 0 and ch == "(":
+                break
+            depth += 1
+        elif ch in ">)":
+            depth -= 1
+        elif depth == 0:
+            out.append(ch)
+    return "".join(out).split("::")[-1].strip()
+
+
+def label_of(name: str):
+    base = kernel_base(name)
+    for label, syms in LABEL_SYMBOLS.items():
+        if base in syms:
+            return label
+    return None
+
+
+def counter_rows(paths):
+    """{label: {counter: [value per dispatch]}} and the plain copy's values."""
     import csv
-
-    def per_kernel(path, counter):
-        out = {}
+    out, copy = {}, {}
+    for path in paths:
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
+            name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name:
+                copy.setdefault(ctr, []).append(val)
                 continue
-            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
-        return out
+            lab = label_of(name)
+            if lab:
+                out.setdefault(lab, {}).setdefault(ctr, []).append(val)
+    return out, copy
 
-    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
-    write = per_kernel(write_csv, "WRITE_SIZE")
 
-    def pick(d, key):
-        vals = [v for name, vs in d.items() if key in name for v in vs]
-        return sum(vals) / len(vals), len(vals), sum(vals)
-
-    _, _, copy_fetch = pick(fetch, "copyBuffer")
-    _, _, copy_write = pick(write, "copyBuffer")
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int):
+    """Write profiles/traffic_<kernel>_<workload>.txt for every timed kernel
+    from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by bytes-moved / counter-reading of the plain
+    device copy of copy_bytes that bench.py --copy-calibration-mib runs in
+    the same process."""
+    fetch, fcopy = counter_rows([fetch_csv])
+    write, wcopy = counter_rows([write_csv])
+    copy_fetch = sum(fcopy["FETCH_SIZE"]) * 1024.0
+    copy_write = sum(wcopy["WRITE_SIZE"]) * 1024.0
     f_scale = copy_bytes / copy_fetch
     w_scale = copy_bytes / copy_write
-    kf, nf, _ = pick(fetch, kernel)
-    kw, nw, _ = pick(write, kernel)
-    total = kf * f_scale + kw * w_scale
-    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.txt")
+    paths = []
+    for label in sorted(set(fetch) & set(write)):
+        fv = [v * 1024.0 for v in fetch[label].get("FETCH_SIZE", [])]
+        wv = [v * 1024.0 for v in write[label].get("WRITE_SIZE", [])]
+        if not fv or not wv:
+            continue
+        kf, kw = sum(fv) / len(fv), sum(wv) / len(wv)
+        path = os.path.join(PROFILE_DIR, f"traffic_{label}_{workload}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of {label} ({', '.join(LABEL_SYMBOLS[label])}) on {workload}, "
+                    "from rocprofv3 FETCH_SIZE and WRITE_SIZE\n")
+            f.write("# commands (MI355X; one counter per run):\n")
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                f.write(f"#   cd /tmp && rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/pmc_{ctr} "
+                        f"-o pmc -- python -u $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
+                        f"--no-cpu-baseline --copy-calibration-mib {copy_bytes >> 20}\n")
+            f.write(f"#   python bench.py --summarize-pmc <fetch csv> <write csv> --workload {workload}\n")
+            f.write(f"# calibration: plain copy of {copy_bytes} bytes read {copy_fetch:.0f} FETCH bytes and "
+                    f"{copy_write:.0f} WRITE bytes\n")
+            f.write(f"fetch_scale: {f_scale:.4f}\n")
+            f.write(f"write_scale: {w_scale:.4f}\n")
+            f.write(f"dispatches: {len(fv)} / {len(wv)}\n")
+            f.write(f"fetch_bytes_per_launch_raw: {kf:.0f}\n")
+            f.write(f"write_bytes_per_launch_raw: {kw:.0f}\n")
+            f.write(f"hbm_bytes_per_launch: {kf * f_scale + kw * w_scale:.0f}\n")
+            f.write(f"source_digest: {kernel_source_digest()}\n")
+        paths.append(path)
+    return paths
+
+
+def summarize_stats(stats_csv: str, bench_json: str, workload: str) -> str:
+    """Write profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace
+    --stats run of bench.py and the JSON line of a plain bench.py run."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    b = json.load(open(bench_json))
+    c = b["config"]
+    path = os.path.join(PROFILE_DIR, f"kernels_{workload}.md")
+    lines = [f"# rocprofv3 kernel statistics, {workload} (B={c['B']}, H={c['H']}, H_kv={c['H_kv']}, d={c['d']}, "
+             f"Lq={c['Lq']}, causal={c['causal']}, broadcast_q={c['broadcast_q']})", "",
+             "Commands (MI355X, one GPU; `$REPO` is the repository root):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             f"-d $REPO/gpurun_out/stats_{workload} -o stats -- python -u $REPO/bench.py --workload {workload} "
+             "--steps 10 --warmup 2 --no-cpu-baseline",
+             f"python bench.py --workload {workload} --no-cpu-baseline > bench.json",
+             f"python bench.py --summarize-stats <stats_kernel_stats.csv> bench.json --workload {workload}",
+             "```", "", "| kernel | calls | avg (us) | total (ms) | % |", "|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"].replace("|", "/")
+        if len(n) > 90:
+            n = n[:90] + "..."
+        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", f"HIP-event timing inside the bench run (`bench.py --steps {b['steps']} --warmup {b['warmup']}`):", ""]
+    for k, v in b["kernels"].items():
+        lines.append(f"- {k}: {v['launches']} launches, avg {v['avg_ms']} ms"
+                     + (f", {v['gbs']} GB/s algorithmic" if "gbs" in v else ""))
+    r = b["roofline"]
+    lines += ["", f"Step: {b['value']} useful TFLOP/s ({b['pct_of_peak'] * 100:.1f}% of "
+                  f"{b['device']['bf16_peak_tflops']} TFLOP/s), {b['ms_per_step']} ms; forward {b['fwd']['ms']} ms "
+                  f"({b['fwd']['tflops']} TFLOP/s), backward {b['bwd']['ms']} ms ({b['bwd']['tflops']} TFLOP/s).",
+              f"Dominant kernel {r['kernel']}: {r['achieved']} {r['unit']} of {r['peak']} "
+              f"({r['frac'] * 100:.1f}%), traffic {r['traffic']}.", ""]
     with open(path, "w") as f:
-        f.write(f"# HBM traffic of {kernel} on {workload}, from rocprofv3 FETCH_SIZE and WRITE_SIZE\n")
-        f.write("# commands (MI355X; one counter per run):\n")
-        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-            f.write(f"#   cd /tmp && rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/pmc_{ctr} "
-                    f"-o pmc -- python -u $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
-                    f"--no-cpu-baseline --copy-calibration-mib {copy_bytes >> 20}\n")
-        f.write(f"#   python bench.py --summarize-pmc <fetch csv> <write csv> --workload {workload}\n")
-        f.write(f"# calibration: plain copy of {copy_bytes} bytes read {copy_fetch:.0f} FETCH bytes and "
-                f"{copy_write:.0f} WRITE bytes\n")
-        f.write(f"fetch_scale: {f_scale:.4f}\n")
-        f.write(f"write_scale: {w_scale:.4f}\n")
-        f.write(f"dispatches: {nf} / {nw}\n")
-        f.write(f"fetch_bytes_per_launch_raw: {kf:.0f}\n")
-        f.write(f"write_bytes_per_launch_raw: {kw:.0f}\n")
-        f.write(f"hbm_bytes_per_launch: {total:.0f}\n")
-        f.write(f"source_digest: {kernel_source_digest()}\n")
+        f.write("\n".join(lines))
+    return path
+
+
+def summarize_counters(csvs, workload: str, cus: int = 256) -> str:
+    """Write profiles/counters_<workload>.md from the COUNTER_PASSES runs:
+    per kernel, the mean of each counter over its dispatches and the ratios
+    read from them."""
+    rows, _ = counter_rows(csvs)
+    path = os.path.join(PROFILE_DIR, f"counters_{workload}.md")
+    simds = cus * SIMD_PER_CU
+    lines = [f"# Hardware counters per kernel, {workload} (MI355X)", "",
+             "Commands (one rocprofv3 run per counter pass; `$REPO` is the repository root):", "", "```"]
+    for i, ps in enumerate(COUNTER_PASSES):
+        lines.append(f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {ps} --output-format csv "
+                     f"-d $REPO/gpurun_out/ctr_p{i} -o pmc -- python -u $REPO/bench.py --workload {workload} "
+                     "--steps 2 --warmup 1 --no-cpu-baseline")
+    lines += [f"python bench.py --summarize-counters <the {len(COUNTER_PASSES)} counter_collection.csv files> "
+              f"--workload {workload}", "```", "",
+              "Ratios:",
+              f"- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} x {simds} SIMDs); "
+              f"GRBM_GUI_ACTIVE counts every XCD's cycles. SQ_VALU_MFMA_BUSY_CYCLES = {MFMA_CYCLES} x "
+              "SQ_INSTS_MFMA, one 32x32x16 bf16 product per 32 cycles of a SIMD.",
+              "- LDS conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles the LDS stalls on "
+              "bank conflicts, of the cycles it is busy with indexed access).",
+              "- LDS cycles per instruction = SQ_LDS_IDX_ACTIVE / SQ_INSTS_LDS.",
+              "- VALU / MFMA co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES.",
+              "- wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave cycles spent in s_waitcnt).", ""]
+    order = [k for k in ("fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "dq_reduce",
+                         "delta_exact_kernel", "group_sum_kernel") if k in rows]
+    ratio_hdr = "| kernel | MFMA busy | LDS conflict share | LDS cycles / instr | VALU-MFMA co-issue | wait share | VALU / MFMA instr |"
+    lines += [ratio_hdr, "|" + "---|" * 7]
+
+    def mean(lab, c):
+        v = rows[lab].get(c)
+        return sum(v) / len(v) if v else None
+
+    def ratio(a, b, scale=1.0):
+        return f"{a / b * scale:.3f}" if a is not None and b else "n/a"
+
+    for lab in order:
+        gui = mean(lab, "GRBM_GUI_ACTIVE")
+        busy = mean(lab, "SQ_VALU_MFMA_BUSY_CYCLES")
+        lines.append(f"| {lab} | {ratio(busy, gui / N_XCD * simds if gui else None)} | "
+                     f"{ratio(mean(lab, 'SQ_LDS_BANK_CONFLICT'), mean(lab, 'SQ_LDS_IDX_ACTIVE'))} | "
+                     f"{ratio(mean(lab, 'SQ_LDS_IDX_ACTIVE'), mean(lab, 'SQ_INSTS_LDS'))} | "
+                     f"{ratio(mean(lab, 'SQ_VALU_MFMA_COEXEC_CYCLES'), busy)} | "
+                     f"{ratio(mean(lab, 'SQ_WAIT_INST_ANY'), mean(lab, 'SQ_WAVE_CYCLES'))} | "
+                     f"{ratio(mean(lab, 'SQ_INSTS_VALU'), mean(lab, 'SQ_INSTS_MFMA'))} |")
+    ctrs = sorted({c for lab in order for c in rows[lab]})
+    lines += ["", "Mean per dispatch:", "", "| counter | " + " | ".join(order) + " |", "|" + "---|" * (len(order) + 1)]
+    for c in ctrs:
+        vals = []
+        for lab in order:
+            m = mean(lab, c)
+            vals.append(f"{m:.4g}" if m is not None else "")
+        lines.append(f"| {c} | " + " | ".join(vals) + " |")
+    lines += ["", f"source_digest: {kernel_source_digest()}", ""]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
     return path
 
 
@@ -275,12 +428,22 @@ def main(argv=None):
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference kernel for scaling hardware byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic summary under profiles/ from two counter runs and exit")
-    ap.add_argument("--kernel", default="dkdv_kernel", help="kernel for --summarize-pmc")
+                    help="write the traffic summaries under profiles/ from two counter runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="write profiles/counters_<workload>.md from the counter-pass runs and exit")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+                    help="write profiles/kernels_<workload>.md from a --kernel-trace --stats run and exit")
     args = ap.parse_args(argv)
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.workload))
+        return 0
     if args.summarize_pmc:
-        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.kernel,
-                            (args.copy_calibration_mib or 1024) << 20))
+        for p in summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                               (args.copy_calibration_mib or 1024) << 20):
+            print(p)
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.workload))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -67,3 +67,37 @@ def test_visible_pairs_with_a_window_by_brute_force(bq):
         assert bench.visible_pairs(L, Lq, True, bq, W) == n
     # a window at least as long as every sequence is the plain causal count
     assert bench.visible_pairs([5, 9], 12, True, bq, 64) == bench.visible_pairs([5, 9], 12, True, bq)
+
+
+def test_kernel_names_map_to_timing_labels():
+    """rocprofv3 kernel names (templates, anonymous namespace) map to the
+    library's timing labels the traffic summaries are keyed by."""
+    names = {
+        "void jfa::(anonymous namespace)::fwd_kernel_dma<128, 8, 32, false, true>(jfa::FwdArgs, jfa::TileRec const*)":
+            "fwd_kernel",
+        "void jfa::(anonymous namespace)::fwd_kernel<64, 8, 32, true, false>(jfa::FwdArgs)": "fwd_kernel",
+        "void jfa::(anonymous namespace)::dkdv_pair_kernel<false, true>(jfa::BwdArgs, jfa::TileRec const*)":
+            "dkdv_kernel",
+        "void jfa::(anonymous namespace)::dq_bcast_kernel<128, false>(jfa::BwdArgs)": "dq_kernel",
+        "void jfa::(anonymous namespace)::dq_reduce<64>(float const*, float*, int, int, int, int, int)": "dq_reduce",
+        "jfa::(anonymous namespace)::sched_expand(jfa::SchedArgs, jfa::Schedule)": None,
+        "__amd_rocclr_copyBuffer": None,
+    }
+    for n, lab in names.items():
+        assert bench.label_of(n) == lab, n
+
+
+def test_committed_traffic_summaries_parse():
+    """Every committed traffic summary names a timing label and holds a byte
+    count per launch; measured_traffic reads it while the sources match."""
+    d = bench.PROFILE_DIR
+    files = [f for f in os.listdir(d) if f.startswith("traffic_") and f.endswith(".txt")]
+    assert files
+    for f in files:
+        stem = f[len("traffic_"):-len(".txt")]
+        label = next((k for k in bench.LABEL_SYMBOLS if stem.startswith(k + "_")), None)
+        assert label is not None, f
+        vals = dict(line.split(":", 1) for line in open(os.path.join(d, f)) if ":" in line and not line.startswith("#"))
+        assert float(vals["hbm_bytes_per_launch"]) > 0
+        if vals["source_digest"].strip() == bench.kernel_source_digest():
+            assert bench.measured_traffic(label, stem[len(label) + 1:]) == float(vals["hbm_bytes_per_launch"])
