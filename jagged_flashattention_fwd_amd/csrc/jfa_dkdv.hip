@@ -79,9 +79,11 @@ struct Dkdv {
 
 // Issue the transposed reads of DT head-dim operand tiles for the 8 k-slots at
 // rows (row0 .. row0+3) and (row0+8 .. row0+11), where `addr` already holds
-// this lane's row and column and OFF is the byte offset of row0.  Nothing
-// waits here: tr_wait<N> below makes the values available.
-template <int OFF, int RB>
+// this lane's row and column and OFF is the byte offset of row0; the second
+// group of rows lies R2 bytes after the first (8 rows unless the tile's rows
+// are permuted).  Nothing waits here: tr_wait<N> below makes the values
+// available.
+template <int OFF, int RB, int R2 = 8 * RB>
 __device__ __forceinline__ void tr_issue4(uint32_t addr, i16x4 (&x)[8]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
@@ -94,8 +96,8 @@ __device__ __forceinline__ void tr_issue4(uint32_t addr, i16x4 (&x)[8]) {
       "ds_read_b64_tr_b16 %7, %8 offset:%16"
       : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
         "=&v"(x[7])
-      : "v"(addr), "i"(OFF), "i"(OFF + 8 * RB), "i"(OFF + 64), "i"(OFF + 8 * RB + 64), "i"(OFF + 128),
-        "i"(OFF + 8 * RB + 128), "i"(OFF + 192), "i"(OFF + 8 * RB + 192));
+      : "v"(addr), "i"(OFF), "i"(OFF + R2), "i"(OFF + 64), "i"(OFF + R2 + 64), "i"(OFF + 128),
+        "i"(OFF + R2 + 128), "i"(OFF + 192), "i"(OFF + R2 + 192));
 }
 template <int OFF, int RB>
 __device__ __forceinline__ void tr_issue2(uint32_t addr, i16x4 (&x)[8]) {
@@ -108,9 +110,9 @@ __device__ __forceinline__ void tr_issue2(uint32_t addr, i16x4 (&x)[8]) {
       : "v"(addr), "i"(OFF), "i"(OFF + 8 * RB), "i"(OFF + 64), "i"(OFF + 8 * RB + 64));
   x[4] = x[5] = x[6] = x[7] = i16x4{0, 0, 0, 0};
 }
-template <int D, int OFF, int RB>
+template <int D, int OFF, int RB, int R2 = 8 * RB>
 __device__ __forceinline__ void tr_issue(uint32_t addr, i16x4 (&x)[8]) {
-  if constexpr (D == 128) tr_issue4<OFF, RB>(addr, x);
+  if constexpr (D == 128) tr_issue4<OFF, RB, R2>(addr, x);
   else tr_issue2<OFF, RB>(addr, x);
 }
 // Wait until at most N LDS reads of this wave are outstanding; the values in
@@ -834,6 +836,17 @@ struct Pair {
   static_assert(RB == 19 * 16 && RPW >= 3, "copy geometry");
   static_assert(NBUF * BUF + XBYTES + 64 <= 160 * 1024, "LDS");
   static_assert(NW * 32 * 32 * 4 <= XBYTES, "the store staging fits the hand-over area");
+  // Q / dO tiles are read both ways: 16-byte reads of 16 consecutive query
+  // rows (S = Q K^T, dP = dO V^T) and transposing reads of 4 consecutive
+  // rows x 64 bytes per 32 lanes (dV^T += dO^T P, dK^T += Q^T dS).  Query
+  // row r of a tile sits at row position perm(r): within each group of 16
+  // rows the 4 x 4 transpose (r = 4 m + i at 4 i + m).  Any 16 consecutive
+  // rows then still take 16 distinct positions modulo 16, and 4 consecutive
+  // rows 4 m .. 4 m + 3 take positions m, m + 4, m + 8, m + 12, whose 64-byte
+  // windows of a 304-byte row are 64 bytes apart modulo the 256 bytes of
+  // the LDS banks: both reads are free of bank conflicts.  perm is its own
+  // inverse.
+  __host__ __device__ static constexpr int perm(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 };
 
 // Eight 16-byte LDS reads at OFF + 32 ks (k-step ks of a 128-wide row, the
@@ -881,9 +894,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
   const int64_t ld = (int64_t)H * D;
   const float c2 = a.scale_log2;
 
-  // This lane's part of a transposed read (see lds_operand_tr).
+  // This lane's part of a transposed read (see lds_operand_tr): row g * 4 +
+  // (trs >> 2) of a group of 16 sits at position C::perm of it, and the
+  // rows 8 further at 2 positions further.
   const int trs = l & 15;
-  const uint32_t tr_lane = (uint32_t)((g * 4 + (trs >> 2)) * RB + (((((l >> 4) & 1) << 4) + ((trs & 3) << 2)) << 1));
+  const uint32_t tr_lane =
+      (uint32_t)(C::perm(g * 4 + (trs >> 2)) * RB + (((((l >> 4) & 1) << 4) + ((trs & 3) << 2)) << 1));
+  constexpr int TR2 = 2 * RB;
 
   const int64_t t0 = zigzag_tile(0, slot, a.P);
   if (t0 >= T) return;
@@ -925,23 +942,29 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     return p;
   };
 
-  // The block stream, as in dkdv_kernel: each wave copies its 8 rows of Q
-  // and of dO (three padded rows per copy) and one row-term array (even
-  // waves -lse / scale, odd waves -delta) of the block two ahead.
-  const uint16_t* j_q = a.q;
-  const uint16_t* j_d = a.q;
+  // The block stream, as in dkdv_kernel: each wave fills its 8 row
+  // positions of the Q and dO tiles (three padded rows per copy) and copies
+  // one row-term array (even waves -lse / scale, odd waves -delta) of the
+  // block two ahead.  The copies read through buffer resources over the
+  // block's rows that exist (rows past the last query read as zeros); the
+  // source row of each position (C::perm) is fixed per lane and copy.
+  __amdgpu_buffer_rsrc_t j_rq = make_rsrc(a.q, 0), j_rd = make_rsrc(a.q, 0);
   const u32x4* j_v = reinterpret_cast<const u32x4*>(a.term_l);
   uint32_t j_lds = 0, j_ldw = 0;
-  int j_last = 0, j_n = 0;
-  const PadRowCopy pc;
+  int j_n = 0;
+  const uint32_t rstride = (uint32_t)(qs * 2);
+  uint32_t cvoff[C::CPT];
+#pragma unroll
+  for (int k = 0; k < C::CPT; ++k)
+    cvoff[k] = (uint32_t)C::perm(wave * C::RPW + PadRowCopy::start(k, C::RPW) + (int)PadRowCopy::lane_row(l)) * rstride +
+               PadRowCopy::lane_byte(l);
   auto issue_rows = [&](int k0, int k1) {
     if (j_n == 0) return;
 #pragma unroll
     for (int k = k0; k < k1; ++k) {
       const int R = PadRowCopy::start(k % C::CPT, C::RPW);
-      const uint32_t voff = pc.voff(R, j_last, (uint32_t)(qs * 2));
-      if (k < C::CPT) dma_copy16(j_q, voff, j_ldw + R * RB);
-      else dma_copy16(j_d, voff, j_ldw + C::OFF_DO + R * RB);
+      if (k < C::CPT) dma_copy16_buf(j_rq, cvoff[k % C::CPT], 0, j_ldw + R * RB);
+      else dma_copy16_buf(j_rd, cvoff[k % C::CPT], 0, j_ldw + C::OFF_DO + R * RB);
     }
   };
   auto issue_vec = [&]() {
@@ -965,14 +988,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     const int gi = cur ? cur_gi : 0;
     const int j = cur ? cp.m_first + cur_jb : np.m_first;
     const int nq_ = cur ? cp.nq : np.nq;
-    const int base_row = min(j * QB + wave * C::RPW, nq_ - 1);
-    const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(qs * 2);
-    j_q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>((cur ? cp.qb : np.qb) + gi * hs_qd) + roff);
-    j_d = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>((cur ? cp.db : np.db) + gi * hs_qd) + roff);
+    // the block's rows that exist, up to the one past it (the last copy's
+    // overhang)
+    const int rows = max(0, min(nq_ - j * QB, QB + 1));
+    const uint64_t roff = (uint64_t)(uint32_t)(j * QB) * rstride;
+    j_rq = make_rsrc(reinterpret_cast<const char*>((cur ? cp.qb : np.qb) + gi * hs_qd) + roff, rows * (int)rstride);
+    j_rd = make_rsrc(reinterpret_cast<const char*>((cur ? cp.db : np.db) + gi * hs_qd) + roff, rows * (int)rstride);
     j_v = (cur ? cp.vb : np.vb) + gi * hs_row + (int64_t)min(j * QB + l, nq_ - 1) * sld;
     j_lds = lds_addr(smem[ring_iss]);
     j_ldw = j_lds + wave * C::RPW * RB;
-    j_last = nq_ - 1 - base_row;
     j_n = C::IPS;
     // (value selects, not a branch over which counter to bump: the latter
     // becomes an increment through a selected address, which puts the
@@ -1081,7 +1105,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     const bf16x8 ones3 = __builtin_bit_cast(bf16x8, g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
     // Lane bases: this lane's query row and chunk g of the role's row tile,
     // its row term, and its 16-byte slots of the hand-over area.
-    const uint32_t row_lane = (uint32_t)(lc * RB + g * 16) + (grad ? (uint32_t)C::OFF_DO : 0u);
+    const uint32_t row_lane = (uint32_t)(C::perm(lc) * RB + g * 16) + (grad ? (uint32_t)C::OFF_DO : 0u);
     const uint32_t tm_lane = (uint32_t)(lc * 16) + (grad ? (uint32_t)C::OFF_TD : (uint32_t)C::OFF_TL);
     u32x2* const xw = reinterpret_cast<u32x2*>(xchg) + (kgrp * 4) * WAVE + l;  // + ((xs * 2 + s) * NG * 4 + i4) * WAVE
 
@@ -1184,8 +1208,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
         constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
         const u32x2* xr = reinterpret_cast<const u32x2*>(xchg) + (((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l;
         i16x4 x0[8], x1[8];
-        tr_issue<D, OF0, RB>(tbr, x0);
-        tr_issue<D, OF1, RB>(tbr, x1);
+        tr_issue<D, OF0, RB, TR2>(tbr, x0);
+        tr_issue<D, OF1, RB, TR2>(tbr, x1);
         // gradient wave: dS of register group i4 = P (fp16, from the score
         // wave's lanes) times dP'
         auto ds4 = [&](int i4, float (&d4)[4]) __attribute__((always_inline)) {
@@ -1242,10 +1266,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
           // reads and their wait in one statement: on this rare path the
           // compiler may move registers freely
           bf16x8 y[4];
-          lds_operand_tr_x4(tbr + OF0 + 0 * RB, tbr + OF0 + 8 * RB, y);
+          lds_operand_tr_x4(tbr + OF0, tbr + OF0 + TR2, y);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(y[dt], __builtin_bit_cast(bf16x8, lo[0]), acc[dt]);
-          lds_operand_tr_x4(tbr + OF1 + 0 * RB, tbr + OF1 + 8 * RB, y);
+          lds_operand_tr_x4(tbr + OF1, tbr + OF1 + TR2, y);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(y[dt], __builtin_bit_cast(bf16x8, lo[1]), acc[dt]);
         }
