@@ -189,3 +189,73 @@ def make_workload(w, seed: int | None = None, device="cpu", with_dout: bool = Tr
         t["v"] = t["v"][:, :w.kv_heads].contiguous()
     t["workload"] = w
     return t
+
+
+# MXFP8 inputs ("Low-precision (MXFP8) attention"): random E4M3 element codes
+# and E8M0 scale codes, drawn directly as integers (no quantization happens
+# here).  Element magnitude codes are uniform over exponent fields 4..8
+# (values 2^-3 .. 3.75) with a random sign; scale codes are 125..127 (scales
+# 1/4, 1/2, 1).  V comes transposed, [H_kv, d, T_pad] with T_pad = T rounded
+# up to 64 and zero codes past T, its scales per 32 keys of the packed index,
+# [H_kv, T_pad / 32, d].
+MX_CODE_LO, MX_CODE_HI = 0x20, 0x47
+MX_SCALE_LO, MX_SCALE_HI = 125, 127
+
+
+def _mx_codes(shape, gen, device):
+    mag = torch.randint(MX_CODE_LO, MX_CODE_HI + 1, shape, generator=gen, device=device, dtype=torch.int32)
+    sign = torch.randint(0, 2, shape, generator=gen, device=device, dtype=torch.int32) * 0x80
+    return (mag | sign).to(torch.uint8)
+
+
+def _mx_scales(shape, gen, device):
+    return torch.randint(MX_SCALE_LO, MX_SCALE_HI + 1, shape, generator=gen, device=device,
+                         dtype=torch.int32).to(torch.uint8)
+
+
+def make_mx_tensors(lengths, H: int, H_kv: int, d: int, Lq: int, broadcast_q: bool, seed: int = 0,
+                    device="cpu"):
+    """Seeded MXFP8 inputs: q8 / q_scale, k8 / k_scale, vt8 / vt_scale (uint8
+    codes) and offsets.  Layouts: q8 [H, Lq, d] (broadcast) or [T, H, d],
+    q_scale the same with d / 32; k8 [T, H_kv, d], k_scale [T, H_kv, d / 32];
+    vt8 [H_kv, d, T_pad], vt_scale [H_kv, T_pad / 32, d]."""
+    if torch is None:  # pragma: no cover
+        raise RuntimeError("torch is required to build tensors")
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    T_pad = max(64, -(-T // 64) * 64)
+    dev = torch.device(device)
+    gens = []
+    for i in range(6):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed * 6007 + 7919 * (i + 1))
+        gens.append(g)
+    nb = d // 32
+    q_shape = (H, Lq, d) if broadcast_q else (T, H, d)
+    vt8 = _mx_codes((H_kv, d, T_pad), gens[4], dev)
+    vt8[:, :, T:] = 0
+    return {
+        "offsets": torch.from_numpy(off).to(dev),
+        "q8": _mx_codes(q_shape, gens[0], dev),
+        "q_scale": _mx_scales(q_shape[:-1] + (nb,), gens[1], dev),
+        "k8": _mx_codes((T, H_kv, d), gens[2], dev),
+        "k_scale": _mx_scales((T, H_kv, nb), gens[3], dev),
+        "vt8": vt8,
+        "vt_scale": _mx_scales((H_kv, T_pad // 32, d), gens[5], dev),
+        "lengths": lengths,
+        "total_len": T,
+        "t_pad": T_pad,
+    }
+
+
+def make_mx_workload(w, seed: int | None = None, device="cpu"):
+    """MXFP8 inputs for a named workload's shapes (seed: the workload's index)."""
+    if not isinstance(w, Workload):
+        w = workload(w)
+    if seed is None:
+        seed = WORKLOADS.index(w)
+    lengths = draw_lengths(w.lengths, w.B, seed)
+    t = make_mx_tensors(lengths, w.H, w.kv_heads, w.d, w.Lq, w.broadcast_q, seed, device)
+    t["workload"] = w
+    return t
