@@ -158,6 +158,7 @@ LABEL_SYMBOLS = {
     "dq_kernel": ("dq_kernel", "dq_bcast_kernel"),
     "dq_reduce": ("dq_reduce",),
     "group_sum_kernel": ("group_sum_kernel",),
+    "fwd_mx_kernel": ("fwd_mx_kernel",),
 }
 # Counter passes of the counters summary (rocprofv3 collects each pass in a
 # run of its own; at most 8 SQ and 2 GRBM counters per pass).
@@ -233,13 +234,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
             continue
         kf, kw = sum(fv) / len(fv), sum(wv) / len(wv)
         path = os.path.join(PROFILE_DIR, f"traffic_{label}_{workload}.txt")
+        mode = " --mxfp8" if label == "fwd_mx_kernel" else ""
         with open(path, "w") as f:
             f.write(f"# HBM traffic of {label} ({', '.join(LABEL_SYMBOLS[label])}) on {workload}, "
                     "from rocprofv3 FETCH_SIZE and WRITE_SIZE\n")
             f.write("# commands (MI355X; one counter per run):\n")
             for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
                 f.write(f"#   cd /tmp && rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/pmc_{ctr} "
-                        f"-o pmc -- python -u $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
+                        f"-o pmc -- python -u $REPO/bench.py --workload {workload}{mode} --steps 2 --warmup 1 "
                         f"--no-cpu-baseline --copy-calibration-mib {copy_bytes >> 20}\n")
             f.write(f"#   python bench.py --summarize-pmc <fetch csv> <write csv> --workload {workload}\n")
             f.write(f"# calibration: plain copy of {copy_bytes} bytes read {copy_fetch:.0f} FETCH bytes and "
@@ -255,22 +257,23 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
     return paths
 
 
-def summarize_stats(stats_csv: str, bench_json: str, workload: str) -> str:
+def summarize_stats(stats_csv: str, bench_json: str, workload: str, mxfp8: bool = False) -> str:
     """Write profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace
     --stats run of bench.py and the JSON line of a plain bench.py run."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     b = json.load(open(bench_json))
     c = b["config"]
-    path = os.path.join(PROFILE_DIR, f"kernels_{workload}.md")
-    lines = [f"# rocprofv3 kernel statistics, {workload} (B={c['B']}, H={c['H']}, H_kv={c['H_kv']}, d={c['d']}, "
-             f"Lq={c['Lq']}, causal={c['causal']}, broadcast_q={c['broadcast_q']})", "",
+    mode = " --mxfp8" if mxfp8 else ""
+    path = os.path.join(PROFILE_DIR, f"kernels_{workload}{'_mxfp8' if mxfp8 else ''}.md")
+    lines = [f"# rocprofv3 kernel statistics, {workload}{' MXFP8 forward' if mxfp8 else ''} (B={c['B']}, H={c['H']}, "
+             f"H_kv={c['H_kv']}, d={c['d']}, Lq={c['Lq']}, causal={c['causal']}, broadcast_q={c['broadcast_q']})", "",
              "Commands (MI355X, one GPU; `$REPO` is the repository root):", "", "```",
              "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             f"-d $REPO/gpurun_out/stats_{workload} -o stats -- python -u $REPO/bench.py --workload {workload} "
+             f"-d $REPO/gpurun_out/stats_{workload} -o stats -- python -u $REPO/bench.py --workload {workload}{mode} "
              "--steps 10 --warmup 2 --no-cpu-baseline",
-             f"python bench.py --workload {workload} --no-cpu-baseline > bench.json",
-             f"python bench.py --summarize-stats <stats_kernel_stats.csv> bench.json --workload {workload}",
+             f"python bench.py --workload {workload}{mode} --no-cpu-baseline > bench.json",
+             f"python bench.py --summarize-stats <stats_kernel_stats.csv> bench.json --workload {workload}{mode}",
              "```", "", "| kernel | calls | avg (us) | total (ms) | % |", "|---|---|---|---|---|"]
     for r in rows:
         n = r["Name"].replace("|", "/")
@@ -278,46 +281,56 @@ def summarize_stats(stats_csv: str, bench_json: str, workload: str) -> str:
             n = n[:90] + "..."
         lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
-    lines += ["", f"HIP-event timing inside the bench run (`bench.py --steps {b['steps']} --warmup {b['warmup']}`):", ""]
-    for k, v in b["kernels"].items():
-        lines.append(f"- {k}: {v['launches']} launches, avg {v['avg_ms']} ms"
-                     + (f", {v['gbs']} GB/s algorithmic" if "gbs" in v else ""))
+    lines += ["", f"HIP-event timing inside the bench run (`bench.py{mode} --steps {b['steps']} "
+                  f"--warmup {b['warmup']}`):", ""]
     r = b["roofline"]
-    lines += ["", f"Step: {b['value']} useful TFLOP/s ({b['pct_of_peak'] * 100:.1f}% of "
-                  f"{b['device']['bf16_peak_tflops']} TFLOP/s), {b['ms_per_step']} ms; forward {b['fwd']['ms']} ms "
-                  f"({b['fwd']['tflops']} TFLOP/s), backward {b['bwd']['ms']} ms ({b['bwd']['tflops']} TFLOP/s).",
-              f"Dominant kernel {r['kernel']}: {r['achieved']} {r['unit']} of {r['peak']} "
-              f"({r['frac'] * 100:.1f}%), traffic {r['traffic']}.", ""]
+    if mxfp8:
+        k = b["kernel"]
+        lines.append(f"- {k['name']}: avg {k['avg_ms']} ms, {k['tflops']} useful TFLOP/s "
+                     f"({k['pct_of_fp8_peak'] * 100:.1f}% of the dense FP8 peak), {k['gbs']} GB/s algorithmic")
+        lines += ["", f"Forward call: {b['value']} useful TFLOP/s, {b['ms_per_step']} ms (schedule and kernel).",
+                  f"Roofline: {r['achieved']} {r['unit']} of {r['peak']} ({r['frac'] * 100:.1f}%), "
+                  f"traffic {r['traffic']}.", ""]
+    else:
+        for k, v in b["kernels"].items():
+            lines.append(f"- {k}: {v['launches']} launches, avg {v['avg_ms']} ms"
+                         + (f", {v['gbs']} GB/s algorithmic" if "gbs" in v else ""))
+        lines += ["", f"Step: {b['value']} useful TFLOP/s ({b['pct_of_peak'] * 100:.1f}% of "
+                      f"{b['device']['bf16_peak_tflops']} TFLOP/s), {b['ms_per_step']} ms; forward {b['fwd']['ms']} "
+                      f"ms ({b['fwd']['tflops']} TFLOP/s), backward {b['bwd']['ms']} ms ({b['bwd']['tflops']} TFLOP/s).",
+                  f"Dominant kernel {r['kernel']}: {r['achieved']} {r['unit']} of {r['peak']} "
+                  f"({r['frac'] * 100:.1f}%), traffic {r['traffic']}.", ""]
     with open(path, "w") as f:
         f.write("\n".join(lines))
     return path
 
 
-def summarize_counters(csvs, workload: str, cus: int = 256) -> str:
+def summarize_counters(csvs, workload: str, cus: int = 256, mxfp8: bool = False) -> str:
     """Write profiles/counters_<workload>.md from the COUNTER_PASSES runs:
     per kernel, the mean of each counter over its dispatches and the ratios
     read from them."""
     rows, _ = counter_rows(csvs)
-    path = os.path.join(PROFILE_DIR, f"counters_{workload}.md")
+    mode = " --mxfp8" if mxfp8 else ""
+    path = os.path.join(PROFILE_DIR, f"counters_{workload}{'_mxfp8' if mxfp8 else ''}.md")
     simds = cus * SIMD_PER_CU
-    lines = [f"# Hardware counters per kernel, {workload} (MI355X)", "",
+    lines = [f"# Hardware counters per kernel, {workload}{' MXFP8 forward' if mxfp8 else ''} (MI355X)", "",
              "Commands (one rocprofv3 run per counter pass; `$REPO` is the repository root):", "", "```"]
     for i, ps in enumerate(COUNTER_PASSES):
         lines.append(f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {ps} --output-format csv "
-                     f"-d $REPO/gpurun_out/ctr_p{i} -o pmc -- python -u $REPO/bench.py --workload {workload} "
+                     f"-d $REPO/gpurun_out/ctr_p{i} -o pmc -- python -u $REPO/bench.py --workload {workload}{mode} "
                      "--steps 2 --warmup 1 --no-cpu-baseline")
     lines += [f"python bench.py --summarize-counters <the {len(COUNTER_PASSES)} counter_collection.csv files> "
-              f"--workload {workload}", "```", "",
+              f"--workload {workload}{mode}", "```", "",
               "Ratios:",
               f"- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} x {simds} SIMDs); "
-              f"GRBM_GUI_ACTIVE counts every XCD's cycles. SQ_VALU_MFMA_BUSY_CYCLES = {MFMA_CYCLES} x "
-              "SQ_INSTS_MFMA, one 32x32x16 bf16 product per 32 cycles of a SIMD.",
+              f"GRBM_GUI_ACTIVE counts every XCD's cycles. In the bf16 kernels SQ_VALU_MFMA_BUSY_CYCLES = "
+              f"{MFMA_CYCLES} x SQ_INSTS_MFMA, one 32x32x16 bf16 product per 32 cycles of a SIMD.",
               "- LDS conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles the LDS stalls on "
               "bank conflicts, of the cycles it is busy with indexed access).",
               "- LDS cycles per instruction = SQ_LDS_IDX_ACTIVE / SQ_INSTS_LDS.",
               "- VALU / MFMA co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES.",
               "- wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave cycles spent in s_waitcnt).", ""]
-    order = [k for k in ("fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "dq_reduce",
+    order = [k for k in ("fwd_kernel", "fwd_mx_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "dq_reduce",
                          "delta_exact_kernel", "group_sum_kernel") if k in rows]
     ratio_hdr = "| kernel | MFMA busy | LDS conflict share | LDS cycles / instr | VALU-MFMA co-issue | wait share | VALU / MFMA instr |"
     lines += [ratio_hdr, "|" + "---|" * 7]
@@ -415,6 +428,103 @@ def cpu_baseline(t, w, scale, seconds: float):
             "seconds": round(el, 2), "sequences": b}
 
 
+# ---------------------------------------------------------------- MXFP8 ----
+FP8_MFMA_FLOP_PER_CLK_PER_CU = 8192  # dense E4M3 (twice bf16)
+
+
+def mx_algorithmic_bytes(lengths, H: int, H_kv: int, d: int, Lq: int, broadcast_q: bool) -> int:
+    """The MXFP8 forward's bytes per launch: K and V codes once (1 byte per
+    element) with their scales (K: one per 32 head-dim elements; V: one per
+    32 keys of the padded packed index), Q codes and scales once, O (bf16)
+    and lse (fp32) written once."""
+    T = int(np.asarray(lengths).sum())
+    B = len(lengths)
+    t_pad = max(64, -(-T // 64) * 64)
+    kv = T * H_kv * d + T * H_kv * (d // 32) + H_kv * d * t_pad + H_kv * (t_pad // 32) * d
+    q_rows = H * Lq if broadcast_q else T * H
+    rows = B * H * Lq if broadcast_q else T * H
+    return kv + q_rows * (d + d // 32) + rows * (2 * d + 4)
+
+
+def bench_mxfp8(args) -> int:
+    """The MXFP8 forward on a workload's shapes (random E4M3 / E8M0 codes):
+    K timed calls by the host clock, then an instrumented run of K calls for
+    the kernel's own time.  Prints one JSON line of its own."""
+    import torch
+    import workloads as wl
+    import jagged_flashattention_fwd_amd as jfa
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    peak8 = cus * FP8_MFMA_FLOP_PER_CLK_PER_CU * PEAK_SCLK_GHZ * 1e9 / 1e12
+    w = wl.workload(args.workload)
+    if w.d != 128 or w.window:
+        print(f"--mxfp8 needs d = 128 and no window ({w.name})", file=sys.stderr)
+        return 2
+    t = wl.make_mx_workload(w, device=dev)
+    lengths, T = t["lengths"], t["total_len"]
+    H, H_kv, d, Lq, B = w.H, w.kv_heads, w.d, w.Lq, w.B
+    bq, causal = w.broadcast_q, w.causal
+    if bq:
+        out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, dev, H_kv=H_kv)
+
+    def fwd():
+        jfa.jfa_fwd_mxfp8(t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["vt8"], t["vt_scale"], t["offsets"],
+                          B, H, H_kv, Lq, d, w.scale, causal, bq, out, lse, T, ws)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    jfa.jfa_timing_enable(8 * args.steps + 8)
+    jfa.jfa_timing_reset()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    kt = jfa.kernel_times()
+    jfa.jfa_timing_enable(0)
+    n, kms = kt["fwd_mx_kernel"]
+    avg = kms / n
+    fl, _ = useful_flops(lengths, H, d, Lq, causal, bq, 0)
+    nbytes = mx_algorithmic_bytes(lengths, H, H_kv, d, Lq, bq)
+    ktf = fl / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "useful TFLOP/s, MXFP8 forward (E4M3 operands, E8M0 block scales)",
+        "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3", "data": "synthetic (random E4M3 / E8M0 codes)",
+        "config": {"workload": w.name, "B": B, "H": H, "H_kv": H_kv, "d": d, "Lq": Lq, "causal": causal,
+                   "broadcast_q": bq, "total_len": T, "accumulate": "fp32", "out": "bf16"},
+        "timing": "value and ms_per_step: host clock over the K timed calls (schedule and kernel); kernel: "
+                  "hipEvents on the launch stream over a second run of K calls",
+        "kernel": {"name": "fwd_mx_kernel", "avg_ms": round(avg, 4), "tflops": round(ktf, 1),
+                   "pct_of_fp8_peak": round(ktf / peak8, 4), "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(ktf, 1), "peak": round(peak8, 1), "unit": "TFLOP/s",
+                     "frac": round(ktf / peak8, 4), "traffic": measured_traffic("fwd_mx_kernel", w.name),
+                     "algorithmic_bytes": nbytes, "useful_flops": fl},
+    }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n * 4
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------- main ----
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -431,11 +541,13 @@ def main(argv=None):
                     help="write the traffic summaries under profiles/ from two counter runs and exit")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="write profiles/counters_<workload>.md from the counter-pass runs and exit")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="measure the MXFP8 forward on the workload's shapes instead (its own JSON line)")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
                     help="write profiles/kernels_<workload>.md from a --kernel-trace --stats run and exit")
     args = ap.parse_args(argv)
     if args.summarize_stats:
-        print(summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.workload))
+        print(summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.workload, args.mxfp8))
         return 0
     if args.summarize_pmc:
         for p in summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
@@ -443,12 +555,14 @@ def main(argv=None):
             print(p)
         return 0
     if args.summarize_counters:
-        print(summarize_counters(args.summarize_counters, args.workload))
+        print(summarize_counters(args.summarize_counters, args.workload, mxfp8=args.mxfp8))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library runs on a single MI355X).", file=sys.stderr)
         return 2
+    if args.mxfp8:
+        return bench_mxfp8(args)
 
     import torch
     import workloads as wl

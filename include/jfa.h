@@ -133,6 +133,38 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
                const float* lse, const void* dout, float* dq, float* dk, float* dv, int64_t total_len,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* MXFP8 forward ("Optimizing Jagged Flash Attention with TLX",
+ * "Low-precision (MXFP8) attention": both products take block-scaled FP8
+ * operands, E4M3 elements with one E8M0 scale per 32 elements along the
+ * product's reduction dimension, and the softmax output P is quantized to
+ * FP8 on the fly).  d = 128 only (JFA_ERR_UNSUPPORTED otherwise); no
+ * sliding window.  Inputs are uint8 codes (OCP MX formats: E4M3 with bias
+ * 7, no infinities, 0x7F / 0xFF NaN; E8M0 code c = 2^(c - 127)):
+ *   q8        broadcast [H, Lq, 128], self [total_len, H, 128]   (16-byte aligned)
+ *   q_scale   q8's shape with 128 -> 4: block j = elements 32j .. 32j+31 (4-byte aligned)
+ *   k8        [total_len, H_kv, 128], k_scale [total_len, H_kv, 4]
+ *   vt8       V transposed, [H_kv, 128, T_pad], T_pad = jfa_mxfp8_t_pad(total_len)
+ *             (total_len rounded up to 64; columns past total_len are read as
+ *             keys of no sequence and may hold anything finite)
+ *   vt_scale  [H_kv, T_pad / 32, 128]: one scale per 32 keys of the packed
+ *             key index (block j = packed keys 32j .. 32j+31, which may span
+ *             two sequences) and head-dim element
+ * P is quantized per query row and per 32-key block of that same packed
+ * index: with b the block's largest P (keys outside the row's visible set
+ * have P = 0), scale 2^(floor(log2 b) - 8), elements P / scale rounded to
+ * the nearest E4M3 (ties to even) and capped at 448.  The softmax
+ * statistics are not quantized: O = (quantized P) V / l with l the sum of
+ * P, and lse = log sum exp(scale * q.k) as in jfa_fwd.  out, lse, offsets,
+ * the workspace (jfa_workspace_size_gqa with pass 0), the modes and the
+ * error rules are those of jfa_fwd_ex. */
+int jfa_fwd_mxfp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale, const void* vt8,
+                  const void* vt_scale, const int64_t* offsets, int B, int H, int H_kv, int Lq, int d, float scale,
+                  int causal, int broadcast_q, void* out, float* lse, int64_t total_len, void* workspace,
+                  size_t workspace_bytes, void* stream);
+/* Keys per row of the MXFP8 forward's transposed V for a packed length
+ * (total_len rounded up to a multiple of 64, at least 64); -1 if negative. */
+int64_t jfa_mxfp8_t_pad(int64_t total_len);
+
 /* Allocation-free forward, for callers that cannot allocate device memory
  * or pass a workspace (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): jfa_fwd_ex without the workspace

@@ -43,6 +43,11 @@ _SIGS = {
     "jfa_fwd_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
                                    _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "jfa_fwd_mxfp8": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                 _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
+                                 _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                 _c.c_size_t, _c.c_void_p]),
+    "jfa_mxfp8_t_pad": (_c.c_int64, [_c.c_int64]),
     "jfa_schedule_params": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_int),
                                        _c.POINTER(_c.c_int)]),
     "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -135,6 +140,18 @@ def jfa_fwd_noalloc(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, 
     _check(lib().jfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, H_kv, Lq, d, float(scale),
                                  int(causal), int(window), int(broadcast_q), _ptr(out), _ptr(lse),
                                  int(total_len), _stream(stream)), "jfa_fwd_noalloc")
+
+
+def jfa_fwd_mxfp8(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, B, H, H_kv, Lq, d, scale, causal,
+                  broadcast_q, out, lse, total_len, workspace, stream=None):
+    _check(lib().jfa_fwd_mxfp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt8), _ptr(vt_scale),
+                               _ptr(offsets), B, H, H_kv, Lq, d, float(scale), int(causal), int(broadcast_q),
+                               _ptr(out), _ptr(lse), int(total_len), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_fwd_mxfp8")
+
+
+def jfa_mxfp8_t_pad(total_len) -> int:
+    return int(lib().jfa_mxfp8_t_pad(int(total_len)))
 
 
 def jfa_schedule_params(pass_, causal, broadcast_q, d):
@@ -254,3 +271,22 @@ def attention_bwd(q, k, v, offsets, scale, causal, broadcast_q, out, lse, dout, 
     jfa_bwd_ex(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, dout, dq, dk,
                dv, T, ws)
     return dq, dk, dv
+
+
+def attention_fwd_mxfp8(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, scale, causal=False, broadcast_q=True,
+                        ws=None):
+    """(out bf16, lse fp32) of the MXFP8 forward on uint8 E4M3 / E8M0 codes;
+    see include/jfa.h (jfa_fwd_mxfp8) for layouts."""
+    import torch
+    B, H, H_kv, Lq, d, T = _shape_args(q8, k8, offsets, broadcast_q)
+    if broadcast_q:
+        out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=k8.device)
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=k8.device)
+    else:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=k8.device)
+        lse = torch.empty((T, H), dtype=torch.float32, device=k8.device)
+    if ws is None:
+        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 0, k8.device, H_kv)
+    jfa_fwd_mxfp8(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q,
+                  out, lse, T, ws)
+    return out, lse

@@ -264,6 +264,10 @@ size_t jfa_workspace_size(int64_t total_len, int B, int H, int Lq, int d, int ca
 namespace jfa {
 namespace {
 
+// Keys per row of the MXFP8 forward's transposed V: total_len rounded up to
+// a whole 64-key step (at least one).
+int64_t mxfp8_t_pad(int64_t total_len) { return total_len <= 0 ? 64 : (total_len + 63) / 64 * 64; }
+
 // Argument checks shared by the forward entry points (everything but the
 // workspace).
 int check_fwd_args(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
@@ -338,6 +342,60 @@ int jfa_fwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
   return fwd_launch(q, k, v, offsets, B, H, H_kv, Lq, d, scale, causal, window, broadcast_q, out, lse, total_len,
                     static_cast<char*>(workspace), lay, P, st);
 }
+
+int jfa_fwd_mxfp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale, const void* vt8,
+                  const void* vt_scale, const int64_t* offsets, int B, int H, int H_kv, int Lq, int d, float scale,
+                  int causal, int broadcast_q, void* out, float* lse, int64_t total_len, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!q_scale || !k_scale || !vt_scale) return JFA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q_scale) & 3) || (reinterpret_cast<uintptr_t>(k_scale) & 3) ||
+      (reinterpret_cast<uintptr_t>(vt_scale) & 3))
+    return JFA_ERR_INVALID_ARG;
+  int rc = check_fwd_args(q8, k8, vt8, offsets, B, H, H_kv, Lq, d, scale, causal, 0, broadcast_q, out, lse,
+                          total_len);
+  if (rc != JFA_OK) return rc;
+  if (d != 128) return JFA_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace)) return JFA_ERR_INVALID_ARG;
+  if (!broadcast_q) Lq = 0;
+  int P = 0;
+  rc = workers(0, &P);
+  if (rc != JFA_OK) return rc;
+  const Layout lay = layout(0, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    rc = check_offsets_sync(offsets, B, total_len, st);
+    if (rc != JFA_OK) return rc;
+  }
+  const Schedule s = schedule_at(static_cast<char*>(workspace), lay.sched_a, lay.cap_a);
+  SchedArgs sa{offsets, total_len, B, H, Lq, broadcast_q ? 1 : 0, 0, fwd_block_rows(), H / H_kv};
+  if (launch_schedule(sa, s, st) != hipSuccess) return JFA_ERR_HIP;
+  FwdMxArgs fa;
+  fa.q8 = static_cast<const uint8_t*>(q8);
+  fa.q_scale = static_cast<const uint8_t*>(q_scale);
+  fa.k8 = static_cast<const uint8_t*>(k8);
+  fa.k_scale = static_cast<const uint8_t*>(k_scale);
+  fa.vt8 = static_cast<const uint8_t*>(vt8);
+  fa.vt_scale = static_cast<const uint8_t*>(vt_scale);
+  fa.offsets = offsets;
+  fa.out = static_cast<uint16_t*>(out);
+  fa.lse = lse;
+  fa.tiles = s.tiles;
+  fa.n_tiles = s.n_tiles;
+  fa.tile_ctr = reinterpret_cast<unsigned int*>(s.n_tiles + 1);
+  fa.total_len = total_len;
+  fa.t_pad = mxfp8_t_pad(total_len);
+  fa.B = B; fa.H = H; fa.Lq = Lq;
+  fa.Hkv = H_kv; fa.G = H / H_kv;
+  fa.scale_log2 = scale * 1.4426950408889634f;
+  fa.causal = causal ? 1 : 0;
+  fa.broadcast_q = broadcast_q ? 1 : 0;
+  fa.P = P;
+  if (launch_fwd_mx(fa, st) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
+}
+
+int64_t jfa_mxfp8_t_pad(int64_t total_len) { return total_len < 0 ? -1 : mxfp8_t_pad(total_len); }
 
 int jfa_fwd_noalloc(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
                     int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,

@@ -75,6 +75,31 @@ struct FwdArgs {
 };
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
+// MXFP8 forward (d = 128): E4M3 codes and E8M0 scale codes, layouts as in
+// jfa_fwd_mxfp8.
+struct FwdMxArgs {
+  const uint8_t* q8;
+  const uint8_t* q_scale;
+  const uint8_t* k8;
+  const uint8_t* k_scale;
+  const uint8_t* vt8;
+  const uint8_t* vt_scale;
+  const int64_t* offsets;
+  uint16_t* out;
+  float* lse;
+  const TileRec* tiles;
+  const int64_t* n_tiles;
+  unsigned int* tile_ctr;
+  int64_t total_len;
+  int64_t t_pad;  // keys per V^T row: total_len rounded up to 64
+  int B, H, Lq;
+  int Hkv, G;
+  float scale_log2;
+  int causal, broadcast_q;
+  int P;
+};
+hipError_t launch_fwd_mx(const FwdMxArgs& a, hipStream_t stream);
+
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;

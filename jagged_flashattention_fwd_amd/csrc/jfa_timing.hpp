@@ -15,6 +15,7 @@ enum KernelId {
   K_DQ,
   K_DELTA_EXACT,
   K_GROUP_SUM,
+  K_FWD_MX,
   K_COUNT
 };
 

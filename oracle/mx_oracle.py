@@ -112,23 +112,25 @@ def block_scale_exponent(amax: float):
 
 def quantize_block(p: np.ndarray):
     """One MX block of non-negative values: (dequantized values, scale
-    exponent or None for an all-zero block, fragile flags)."""
+    exponent or None for an all-zero block, dev).  dev[j] is how far element
+    j's dequantized value can move if its input, or the block maximum, is
+    off by a relative FRAGILE_REL (the other side of a rounding boundary or
+    of a power of two): 0 where the decision is robust."""
     p = np.asarray(p, dtype=np.float64)
     amax = float(p.max()) if p.size else 0.0
     if amax == 0.0:
-        return np.zeros_like(p), None, np.zeros(p.shape, dtype=bool)
+        return np.zeros_like(p), None, np.zeros_like(p)
     se = block_scale_exponent(amax)
-    r = p / 2.0 ** se
-    q = quantize_e4m3(r) * 2.0 ** se
-    # fragile: r near a rounding midpoint, or amax near a power of two (the
-    # scale exponent itself could change)
-    j = np.clip(np.searchsorted(_MIDS, np.minimum(r, E4M3_MAX)), 1, len(_MIDS) - 1)
-    near = np.minimum(np.abs(r - _MIDS[j]) / _MIDS[j], np.abs(r - _MIDS[j - 1]) / _MIDS[j - 1])
-    frag = (near < FRAGILE_REL) & (r > 0)
-    l2 = math.log2(amax)
-    if abs(l2 - round(l2)) < FRAGILE_REL:
-        frag[:] = p > 0
-    return q, se, frag
+    q = quantize_e4m3(p / 2.0 ** se) * 2.0 ** se
+    dev = np.zeros_like(p)
+    for f_max in (1.0 - FRAGILE_REL, 1.0, 1.0 + FRAGILE_REL):
+        se_alt = block_scale_exponent(amax * f_max)
+        for f in (1.0 - FRAGILE_REL, 1.0 + FRAGILE_REL):
+            alt = quantize_e4m3(p * f / 2.0 ** se_alt) * 2.0 ** se_alt
+            dev = np.maximum(dev, np.abs(alt - q))
+    # inputs moved by FRAGILE_REL move robust outputs by at most that much too
+    dev = np.where(dev <= 2.0 * FRAGILE_REL * np.abs(q), 0.0, dev)
+    return q, se, dev
 
 
 def dequantize_rows(x8, scale8) -> np.ndarray:
@@ -149,14 +151,16 @@ def dequantize_vt(vt8, vt_scale, total_len: int) -> np.ndarray:
 def sequence_forward(q, k, v, s0: int, scale: float, causal: bool):
     """One (sequence, head): q [n_q, d], k, v [L, d] float64 (dequantized),
     s0 = the sequence's first packed key index.  Returns (o [n_q, d],
-    lse [n_q], fragile [n_q]: rows with a fragile quantization decision)."""
+    lse [n_q], allow [n_q, d]): allow bounds how far o can move when a
+    fragile quantization decision (see quantize_block) goes the other way,
+    sum over those keys of dev |v| / l; 0 where every decision is robust."""
     n_q, d = q.shape
     L = k.shape[0]
     o = np.zeros((n_q, d))
     lse = np.full(n_q, -np.inf)
-    fragile = np.zeros(n_q, dtype=bool)
+    allow = np.zeros((n_q, d))
     if L == 0 or n_q == 0:
-        return o, lse, fragile
+        return o, lse, allow
     x = (q @ k.T) * (scale / math.log(2.0))                  # scores in log2 units
     vis = np.ones((n_q, L), dtype=bool)
     if causal:
@@ -172,21 +176,21 @@ def sequence_forward(q, k, v, s0: int, scale: float, causal: bool):
         p = np.exp2(xi - ref)
         l = float(p.sum())
         phat = np.zeros_like(p)
+        dev = np.zeros_like(p)
         for b in np.unique(blocks[cols]):
             sel = blocks[cols] == b
-            qb, _, fb = quantize_block(p[sel])
-            phat[sel] = qb
-            fragile[i] |= bool(fb.any())
+            phat[sel], _, dev[sel] = quantize_block(p[sel])
         o[i] = (phat @ v[cols]) / l
+        allow[i] = (dev @ np.abs(v[cols])) / l
         lse[i] = (ref + math.log2(l)) * math.log(2.0)
-    return o, lse, fragile
+    return o, lse, allow
 
 
 def jagged_forward(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, scale: float, causal: bool,
                    broadcast_q: bool, H_kv: int | None = None):
-    """MXFP8 forward over a packed batch.  Returns (out, lse, fragile) with
-    out / lse in the bf16 path's layouts (float64) and fragile a bool array
-    of lse's shape."""
+    """MXFP8 forward over a packed batch.  Returns (out, lse, allow) with
+    out / lse in the bf16 path's layouts (float64) and allow of out's shape
+    (see sequence_forward)."""
     offsets = np.asarray(offsets, dtype=np.int64)
     B = len(offsets) - 1
     T = int(offsets[-1])
@@ -201,11 +205,10 @@ def jagged_forward(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, scale: floa
         Lq = Q.shape[1]
         out = np.zeros((B, H, Lq, d))
         lse = np.full((B, H, Lq), -np.inf)
-        frag = np.zeros((B, H, Lq), dtype=bool)
     else:
         out = np.zeros((T, H, d))
         lse = np.full((T, H), -np.inf)
-        frag = np.zeros((T, H), dtype=bool)
+    frag = np.zeros_like(out)
     for b in range(B):
         s0, s1 = int(offsets[b]), int(offsets[b + 1])
         for h in range(H):

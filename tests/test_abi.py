@@ -24,14 +24,15 @@ def lib():
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "jfa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(jfa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(jfa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_calls():
     assert _declared_functions() == sorted([
         "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_kernel_name", "jfa_schedule_params",
         "jfa_status_string", "jfa_timing_enable", "jfa_timing_read", "jfa_timing_reset",
-        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex", "jfa_debug_schedule_ex", "jfa_fwd_noalloc"])
+        "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex", "jfa_debug_schedule_ex", "jfa_fwd_noalloc",
+        "jfa_fwd_mxfp8", "jfa_mxfp8_t_pad"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -176,3 +177,25 @@ def test_noalloc_forward_host_checks(lib):
     assert call(H_kv=3) == 1
     # 1000 heads x (8192 sequences + 2^30 / 256 rows) tiles: far beyond the 16 MiB scratch
     assert call(B=8192, H=1000, H_kv=1000, T=1 << 30) == 3
+
+
+def test_mxfp8_forward_host_checks(lib):
+    """jfa_fwd_mxfp8 rejects bad arguments before any HIP call: missing or
+    misaligned scale arrays, a head dim other than 128, the forward's own
+    checks, a missing workspace."""
+    vp = ctypes.c_void_p
+
+    def call(qs=FAKE, ks=FAKE, vs=FAKE, d=128, q=FAKE, H_kv=2, scale=0.1, ws=FAKE):
+        return lib.jfa_fwd_mxfp8(vp(q), vp(qs), vp(FAKE), vp(ks), vp(FAKE), vp(vs), vp(FAKE), 2, 2, H_kv, 8, d,
+                                 scale, 0, 1, vp(FAKE), vp(FAKE), 10, vp(ws), 1 << 20, None)
+    assert call(qs=0) == 1 and call(ks=0) == 1 and call(vs=0) == 1
+    assert call(qs=FAKE + 1) == 1 and call(ks=FAKE + 2) == 1 and call(vs=FAKE + 3) == 1
+    assert call(q=0) == 1 and call(q=FAKE + 8) == 1
+    assert call(d=64) == 2 and call(d=96) == 2
+    assert call(H_kv=3) == 1 and call(scale=math.inf) == 1
+    assert call(ws=0) == 1 and call(ws=FAKE + 4) == 1
+
+
+def test_mxfp8_t_pad(lib):
+    assert [lib.jfa_mxfp8_t_pad(n) for n in (0, 1, 63, 64, 65, 1000)] == [64, 64, 64, 64, 128, 1024]
+    assert lib.jfa_mxfp8_t_pad(-5) == -1

@@ -76,8 +76,8 @@ def test_block_rule_closed_forms():
     # smallest subnormal step rounds to zero; 2^-16 is two steps, exact
     q, _, _ = mo.quantize_block(np.array([1.0, 2.0 ** -20, 2.0 ** -16]))
     assert np.array_equal(q, [1.0, 0.0, 2.0 ** -16])
-    q, se, fr = mo.quantize_block(np.zeros(5))
-    assert se is None and not q.any() and not fr.any()
+    q, se, dev = mo.quantize_block(np.zeros(5))
+    assert se is None and not q.any() and not dev.any()
 
 
 def test_block_quantization_scales_with_powers_of_two():
@@ -92,17 +92,18 @@ def test_block_quantization_scales_with_powers_of_two():
         assert np.array_equal(q1, q0 * 2.0 ** k)
 
 
-def test_fragile_flags_midpoints_not_grid_points():
-    # 1.0625 is the midpoint of 1 and 1.125 (in units of a scale of 2^-8 x 256)
-    base = np.array([1.9, 1.0625 * 1.0])
-    _, _, fr = mo.quantize_block(base)
-    # with amax 1.9 the scale is 2^-8, so 1.0625 maps to 272 = 1.0625 * 256: a midpoint
-    assert fr[1] and not fr[0]
-    _, _, fr = mo.quantize_block(np.array([1.9, 1.3]))
-    assert not fr.any()
-    # amax at a power of two: the scale choice itself is fragile
-    _, _, fr = mo.quantize_block(np.array([2.0 * (1 - 2.0 ** -20), 0.3]))
-    assert fr.all()
+def test_fragile_decisions_and_their_deviation():
+    # with amax 1.9 the scale is 2^-8, and 1.0625 maps to 272, the midpoint
+    # of 256 and 288: it rounds to 1.0 (the even code) or, moved up, to
+    # 1.125, one step of 2^-3 away
+    q, _, dev = mo.quantize_block(np.array([1.9, 1.0625]))
+    assert q[1] == 1.0 and dev[1] == 0.125 and dev[0] == 0.0
+    _, _, dev = mo.quantize_block(np.array([1.9, 1.3]))
+    assert not dev.any()
+    # amax just below a power of two: the scale could be the next one up,
+    # where 2 - 2^-20 no longer saturates (1.75 -> 2)
+    q, _, dev = mo.quantize_block(np.array([2.0 * (1 - 2.0 ** -20), 0.3]))
+    assert q[0] == 1.75 and dev[0] == 0.25
 
 
 def test_exact_p_reduces_to_plain_attention():
@@ -114,11 +115,11 @@ def test_exact_p_reduces_to_plain_attention():
         q = rng.standard_normal((L, d))
         k = np.zeros((L, d))
         v = rng.standard_normal((L, d))
-        o, lse, fr = mo.sequence_forward(q, k, v, 17, 0.1, causal)
+        o, lse, allow = mo.sequence_forward(q, k, v, 17, 0.1, causal)
         ro, rl, _ = jo.sequence_forward(q, k, v, 0.1, causal, 0)
-        # (every block maximum is exactly 1, a power of two: flagged fragile,
-        # since a float32 value just below it would take the next scale down)
-        assert fr.all()
+        # every block maximum is exactly 1, a power of two: a float32 value
+        # just below it would take the next scale down and saturate at 0.875
+        assert (allow > 0).all()
         np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
 
