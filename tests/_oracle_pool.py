@@ -2,9 +2,8 @@
 per-(sequence, head) functions, unchanged, spread over a process pool, and
 error statistics accumulated over every element of each output tensor.
 
-TEST INFRASTRUCTURE.  The pool only distributes calls of
-oracle.jfa_oracle.sequence_forward / sequence_backward; the arithmetic is
-the oracle's.  Workers are spawned (no fork of a process that holds a GPU
+TEST INFRASTRUCTURE.  The pool only distributes calls of the oracle's
+per-(sequence, head) functions; the arithmetic is the oracle's.  Workers are spawned (no fork of a process that holds a GPU
 context) with one BLAS thread each, and take the most expensive items first.
 """
 from __future__ import annotations
@@ -41,6 +40,33 @@ def run_items(items, cost):
         ctx = mp.get_context("spawn")
         with ctx.Pool(pool_size()) as pool:
             for i, res in zip(order, pool.imap(_item, [items[i] for i in order], chunksize=1)):
+                yield i, res
+    finally:
+        for k, v in keep.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _call(args):
+    module, fn, fargs = args
+    import importlib
+    return getattr(importlib.import_module(module), fn)(*fargs)
+
+
+def run_calls(module: str, fn: str, arg_lists, cost):
+    """Yields (index, result) of module.fn(*arg_lists[i]) for every i, most
+    expensive first, in the same pool (an oracle function, unchanged)."""
+    order = sorted(range(len(arg_lists)), key=lambda i: -cost[i])
+    keep = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in keep:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(pool_size()) as pool:
+            work = [(module, fn, arg_lists[i]) for i in order]
+            for i, res in zip(order, pool.imap(_call, work, chunksize=4)):
                 yield i, res
     finally:
         for k, v in keep.items():

@@ -259,3 +259,100 @@ def make_mx_workload(w, seed: int | None = None, device="cpu"):
     t = make_mx_tensors(lengths, w.H, w.kv_heads, w.d, w.Lq, w.broadcast_q, seed, device)
     t["workload"] = w
     return t
+
+
+def _tile_encodings(codes, tiles, n: int, n_pad: int):
+    """Row and column encodings of one tensor given as E4M3 codes [..., n, d]
+    and one E8M0 code per 32 x 32 tile, [..., n_pad / 32, d / 32]: the row
+    encoding's scales [..., n, d / 32] and the transposed codes [..., d, n_pad]
+    (zero past n) with scales [..., n_pad / 32, d].  Both dequantize to the
+    same values."""
+    row_scale = tiles.repeat_interleave(32, dim=-2)[..., :n, :]
+    col_codes = torch.zeros(codes.shape[:-2] + (codes.shape[-1], n_pad), dtype=torch.uint8, device=codes.device)
+    col_codes[..., :n] = codes.transpose(-1, -2)
+    col_scale = tiles.repeat_interleave(32, dim=-1)
+    return row_scale.contiguous(), col_codes.contiguous(), col_scale.contiguous()
+
+
+def make_mx_bwd_tensors(lengths, H: int, H_kv: int, d: int, Lq: int, broadcast_q: bool, seed: int = 0,
+                        consistent: bool = True, device="cpu"):
+    """Seeded MXFP8 inputs of the forward and the backward: every encoding of
+    Q, K, V and dO (layouts in oracle/mx_oracle.py's header) and offsets.
+
+    consistent=True: each tensor is one set of E4M3 codes with one E8M0 scale
+    per 32 x 32 tile (32 positions of its query / key axis by 32 head-dim
+    elements), so that its row-wise and its transposed, axis-blocked encoding
+    hold the same values, as two quantizations of one tensor would nearly.
+    consistent=False: every encoding drawn on its own (codes and scales), so
+    that a kernel reading one encoding in place of another differs."""
+    if torch is None:  # pragma: no cover
+        raise RuntimeError("torch is required to build tensors")
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    B = len(lengths)
+    T_pad = max(64, -(-T // 64) * 64)
+    Lq_pad = max(64, -(-Lq // 64) * 64) if broadcast_q else 0
+    dev = torch.device(device)
+    gens = []
+    for i in range(16):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed * 7001 + 104729 * (i + 1))
+        gens.append(g)
+    nb = d // 32
+    out = {"offsets": torch.from_numpy(off).to(dev), "lengths": lengths, "total_len": T, "t_pad": T_pad,
+           "lq_pad": Lq_pad}
+
+    def packed(name, heads, gi):
+        # [T, heads, d] row encoding; transposed [heads, d, T_pad] along the packed index
+        codes = _mx_codes((heads, T, d), gens[gi], dev)
+        if consistent:
+            tiles = _mx_scales((heads, T_pad // 32, nb), gens[gi + 1], dev)
+            rs, cc, cs = _tile_encodings(codes, tiles, T, T_pad)
+        else:
+            rs = _mx_scales((heads, T, nb), gens[gi + 1], dev)
+            cc = _mx_codes((heads, d, T_pad), gens[gi + 2], dev)
+            cc[:, :, T:] = 0
+            cs = _mx_scales((heads, T_pad // 32, d), gens[gi + 3], dev)
+        out[name + "8"] = codes.permute(1, 0, 2).contiguous()
+        out[name + "_scale"] = rs.permute(1, 0, 2).contiguous()
+        out[name + "t8"] = cc
+        out[name + "t_scale"] = cs
+
+    def dense(name, lead, gi):
+        # [*lead, Lq, d] row encoding; transposed [*lead, d, Lq_pad] from query 0
+        codes = _mx_codes(lead + (Lq, d), gens[gi], dev)
+        if consistent:
+            tiles = _mx_scales(lead + (Lq_pad // 32, nb), gens[gi + 1], dev)
+            rs, cc, cs = _tile_encodings(codes, tiles, Lq, Lq_pad)
+        else:
+            rs = _mx_scales(lead + (Lq, nb), gens[gi + 1], dev)
+            cc = _mx_codes(lead + (d, Lq_pad), gens[gi + 2], dev)
+            cc[..., Lq:] = 0
+            cs = _mx_scales(lead + (Lq_pad // 32, d), gens[gi + 3], dev)
+        out[name + "8"] = codes
+        out[name + "_scale"] = rs
+        out[name + "t8"] = cc
+        out[name + "t_scale"] = cs
+
+    packed("k", H_kv, 0)
+    packed("v", H_kv, 4)
+    if broadcast_q:
+        dense("q", (H,), 8)
+        dense("do", (B, H), 12)
+    else:
+        packed("q", H, 8)
+        packed("do", H, 12)
+    return out
+
+
+def make_mx_bwd_workload(w, seed: int | None = None, consistent: bool = True, device="cpu"):
+    """make_mx_bwd_tensors for a named workload's shapes (seed: the workload's index)."""
+    if not isinstance(w, Workload):
+        w = workload(w)
+    if seed is None:
+        seed = WORKLOADS.index(w)
+    lengths = draw_lengths(w.lengths, w.B, seed)
+    t = make_mx_bwd_tensors(lengths, w.H, w.kv_heads, w.d, w.Lq, w.broadcast_q, seed, consistent, device)
+    t["workload"] = w
+    return t
