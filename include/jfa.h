@@ -162,8 +162,53 @@ int jfa_fwd_mxfp8(const void* q8, const void* q_scale, const void* k8, const voi
                   int causal, int broadcast_q, void* out, float* lse, int64_t total_len, void* workspace,
                   size_t workspace_bytes, void* stream);
 /* Keys per row of the MXFP8 forward's transposed V for a packed length
- * (total_len rounded up to a multiple of 64, at least 64); -1 if negative. */
+ * (total_len rounded up to a multiple of 64, at least 64); -1 if negative.
+ * The same rounding gives Lq_pad for the MXFP8 backward's broadcast Q^T. */
 int64_t jfa_mxfp8_t_pad(int64_t total_len);
+
+/* MXFP8 backward (the same page gives the variant for both directions):
+ * every product takes block-scaled FP8 operands blocked along its own
+ * reduction dimension, so each tensor comes in the encodings its products
+ * need, and P and dS are quantized on the fly.  With S = scale Q K^T,
+ * P = exp(S - lse), dP = dO V^T, delta = rowsum(dO o O), dS = P o (dP - delta):
+ *   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
+ * where S and dP read the row-wise Q, K, dO, V (blocks of 32 along d), dV
+ * and dK the query-blocked dO and Q, dQ the key-blocked K; delta uses the
+ * row-wise dO and `out` as stored.  P and dS are quantized per key column
+ * in blocks of 32 queries for dV and dK, dS per query row in blocks of 32
+ * keys of the packed index for dQ, each block with the rule of
+ * jfa_fwd_mxfp8 (scale 2^(floor(log2 amax) - 8), nearest E4M3, ties to
+ * even, capped at +-448).  d = 128 only; no sliding window.  Inputs (uint8
+ * codes; codes 16-byte aligned, scales 4-byte aligned):
+ *   q8, q_scale      row-wise Q, as in jfa_fwd_mxfp8
+ *   qt8, qt_scale    Q blocked along the queries, transposed:
+ *                    broadcast [H, 128, Lq_pad], scales [H, Lq_pad / 32, 128]
+ *                    (Lq_pad = jfa_mxfp8_t_pad(Lq), blocks from query 0);
+ *                    self [H, 128, T_pad], scales [H, T_pad / 32, 128]
+ *                    (blocks of the packed index)
+ *   k8, k_scale      row-wise K, as in jfa_fwd_mxfp8
+ *   kt8, kt_scale    K blocked along the keys, transposed: [H_kv, 128, T_pad],
+ *                    scales [H_kv, T_pad / 32, 128] (the layout of vt8)
+ *   v8, v_scale      row-wise V: [total_len, H_kv, 128], [total_len, H_kv, 4]
+ *   do8, do_scale    row-wise dO: broadcast [B, H, Lq, 128], [B, H, Lq, 4];
+ *                    self [total_len, H, 128], [total_len, H, 4]
+ *   dot8, dot_scale  dO blocked along the queries, transposed: broadcast
+ *                    [B, H, 128, Lq_pad], [B, H, Lq_pad / 32, 128]; self
+ *                    [H, 128, T_pad], [H, T_pad / 32, 128]
+ * Padding columns of the transposed encodings may hold anything finite.
+ * out (bf16) and lse are the MXFP8 forward's outputs; dq, dk, dv are fp32 in
+ * the layouts of jfa_bwd_ex (dk, dv [total_len, H_kv, 128], each summed over
+ * its query heads; broadcast dq summed over the sequences).  Any finite scale
+ * is accepted.  The workspace is that of jfa_bwd_ex:
+ * jfa_workspace_size_gqa(total_len, B, H, H_kv, Lq, 128, causal,
+ * broadcast_q, 1) bytes.  Offsets, modes and error rules as in jfa_bwd_ex. */
+int jfa_bwd_mxfp8(const void* q8, const void* q_scale, const void* qt8, const void* qt_scale, const void* k8,
+                  const void* k_scale, const void* kt8, const void* kt_scale, const void* v8,
+                  const void* v_scale, const void* do8, const void* do_scale, const void* dot8,
+                  const void* dot_scale, const int64_t* offsets, int B, int H, int H_kv, int Lq, int d,
+                  float scale, int causal, int broadcast_q, const void* out, const float* lse, float* dq,
+                  float* dk, float* dv, int64_t total_len, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* Allocation-free forward, for callers that cannot allocate device memory
  * or pass a workspace (code under HIP graph capture, tight serving loops,

@@ -48,6 +48,10 @@ _SIGS = {
                                  _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                  _c.c_size_t, _c.c_void_p]),
     "jfa_mxfp8_t_pad": (_c.c_int64, [_c.c_int64]),
+    "jfa_bwd_mxfp8": (_c.c_int, [_c.c_void_p] * 15 + [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
+                                                      _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                                      _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                                      _c.c_size_t, _c.c_void_p]),
     "jfa_schedule_params": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_int),
                                        _c.POINTER(_c.c_int)]),
     "jfa_debug_schedule": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -148,6 +152,19 @@ def jfa_fwd_mxfp8(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, B, H, H_kv, 
                                _ptr(offsets), B, H, H_kv, Lq, d, float(scale), int(causal), int(broadcast_q),
                                _ptr(out), _ptr(lse), int(total_len), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "jfa_fwd_mxfp8")
+
+
+def jfa_bwd_mxfp8(t, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, dq, dk, dv, total_len,
+                  workspace, stream=None):
+    """t: the uint8 encodings by their header names (q8, q_scale, qt8,
+    qt_scale, k8, k_scale, kt8, kt_scale, v8, v_scale, do8, do_scale, dot8,
+    dot_scale)."""
+    enc = [_ptr(t[n]) for n in ("q8", "q_scale", "qt8", "qt_scale", "k8", "k_scale", "kt8", "kt_scale", "v8",
+                                "v_scale", "do8", "do_scale", "dot8", "dot_scale")]
+    _check(lib().jfa_bwd_mxfp8(*enc, _ptr(offsets), B, H, H_kv, Lq, d, float(scale), int(causal),
+                               int(broadcast_q), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                               int(total_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)), "jfa_bwd_mxfp8")
 
 
 def jfa_mxfp8_t_pad(total_len) -> int:
@@ -290,3 +307,20 @@ def attention_fwd_mxfp8(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, scale,
     jfa_fwd_mxfp8(q8, q_scale, k8, k_scale, vt8, vt_scale, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q,
                   out, lse, T, ws)
     return out, lse
+
+
+def attention_bwd_mxfp8(t, offsets, scale, causal, broadcast_q, out, lse, ws=None):
+    """(dq, dk, dv) fp32 of the MXFP8 backward; t holds the uint8 encodings
+    by their header names (include/jfa.h, jfa_bwd_mxfp8), out / lse are the
+    MXFP8 forward's outputs."""
+    import torch
+    q8, k8 = t["q8"], t["k8"]
+    B, H, H_kv, Lq, d, T = _shape_args(q8, k8, offsets, broadcast_q)
+    dev = k8.device
+    dq = torch.empty(q8.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty((T, H_kv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((T, H_kv, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(T, B, H, Lq, d, causal, broadcast_q, 1, dev, H_kv)
+    jfa_bwd_mxfp8(t, offsets, B, H, H_kv, Lq, d, scale, causal, broadcast_q, out, lse, dq, dk, dv, T, ws)
+    return dq, dk, dv

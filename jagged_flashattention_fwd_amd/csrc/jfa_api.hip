@@ -397,6 +397,96 @@ int jfa_fwd_mxfp8(const void* q8, const void* q_scale, const void* k8, const voi
 
 int64_t jfa_mxfp8_t_pad(int64_t total_len) { return total_len < 0 ? -1 : mxfp8_t_pad(total_len); }
 
+int jfa_bwd_mxfp8(const void* q8, const void* q_scale, const void* qt8, const void* qt_scale, const void* k8,
+                  const void* k_scale, const void* kt8, const void* kt_scale, const void* v8,
+                  const void* v_scale, const void* do8, const void* do_scale, const void* dot8,
+                  const void* dot_scale, const int64_t* offsets, int B, int H, int H_kv, int Lq, int d,
+                  float scale, int causal, int broadcast_q, const void* out, const float* lse, float* dq,
+                  float* dk, float* dv, int64_t total_len, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const void* codes[] = {q8, qt8, k8, kt8, v8, do8, dot8, out, dq, dk, dv, workspace};
+  const void* scales[] = {q_scale, qt_scale, k_scale, kt_scale, v_scale, do_scale, dot_scale, lse};
+  for (const void* p : codes)
+    if (!p || !aligned16(p)) return JFA_ERR_INVALID_ARG;
+  for (const void* p : scales)
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 3)) return JFA_ERR_INVALID_ARG;
+  if (!offsets || (reinterpret_cast<uintptr_t>(offsets) & 7)) return JFA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return JFA_ERR_INVALID_ARG;
+  int rc = check_sizes(total_len, B, H, Lq, d, broadcast_q);
+  if (rc != JFA_OK) return rc;
+  rc = check_heads(H, H_kv);
+  if (rc != JFA_OK) return rc;
+  if (d != 128) return JFA_ERR_UNSUPPORTED;
+  if (!broadcast_q) Lq = 0;
+  int P = 0;
+  rc = workers(1, &P);
+  if (rc != JFA_OK) return rc;
+  const Layout lay = layout(1, total_len, B, H, H_kv, Lq, d, broadcast_q, P);
+  if (workspace_bytes < lay.total) return JFA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    rc = check_offsets_sync(offsets, B, total_len, st);
+    if (rc != JFA_OK) return rc;
+  }
+  char* ws = static_cast<char*>(workspace);
+  const Schedule sk = schedule_at(ws, lay.sched_a, lay.cap_a);
+  SchedArgs sa{offsets, total_len, B, H_kv, Lq, broadcast_q ? 1 : 0, 1, MX_BK, H / H_kv};
+  sa.kv_tiles = 1;
+  if (launch_schedule(sa, sk, st) != hipSuccess) return JFA_ERR_HIP;
+  Schedule sq{};
+  if (!broadcast_q) {
+    sq = schedule_at(ws, lay.sched_b, lay.cap_b);
+    SchedArgs sb{offsets, total_len, B, H, Lq, 0, 0, MX_BM, H / H_kv};
+    if (launch_schedule(sb, sq, st) != hipSuccess) return JFA_ERR_HIP;
+  }
+  BwdMxArgs ba;
+  ba.q8 = static_cast<const uint8_t*>(q8);
+  ba.q_scale = static_cast<const uint8_t*>(q_scale);
+  ba.qt8 = static_cast<const uint8_t*>(qt8);
+  ba.qt_scale = static_cast<const uint8_t*>(qt_scale);
+  ba.k8 = static_cast<const uint8_t*>(k8);
+  ba.k_scale = static_cast<const uint8_t*>(k_scale);
+  ba.kt8 = static_cast<const uint8_t*>(kt8);
+  ba.kt_scale = static_cast<const uint8_t*>(kt_scale);
+  ba.v8 = static_cast<const uint8_t*>(v8);
+  ba.v_scale = static_cast<const uint8_t*>(v_scale);
+  ba.do8 = static_cast<const uint8_t*>(do8);
+  ba.do_scale = static_cast<const uint8_t*>(do_scale);
+  ba.dot8 = static_cast<const uint8_t*>(dot8);
+  ba.dot_scale = static_cast<const uint8_t*>(dot_scale);
+  ba.offsets = offsets;
+  ba.out = static_cast<const uint16_t*>(out);
+  ba.lse = lse;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.delta = reinterpret_cast<float*>(ws + lay.delta);
+  ba.lse2 = reinterpret_cast<float*>(ws + lay.lse2);
+  ba.dq_part = broadcast_q ? reinterpret_cast<float*>(ws + lay.dq_part) : nullptr;
+  ba.seq_order = sk.order;
+  ba.dq_qblocks = 0;
+  ba.dq_chunks = 0;
+  if (broadcast_q) dq_split(B, H, Lq, P, &ba.dq_qblocks, &ba.dq_chunks);
+  ba.ktiles = sk.tiles;
+  ba.n_ktiles = sk.n_tiles;
+  ba.ktile_ctr = reinterpret_cast<unsigned int*>(sk.n_tiles + 1);
+  ba.qtiles = broadcast_q ? nullptr : sq.tiles;
+  ba.n_qtiles = broadcast_q ? nullptr : sq.n_tiles;
+  ba.qtile_ctr = broadcast_q ? nullptr : reinterpret_cast<unsigned int*>(sq.n_tiles + 1);
+  ba.total_len = total_len;
+  ba.t_pad = mxfp8_t_pad(total_len);
+  ba.lq_pad = broadcast_q ? (int)mxfp8_t_pad(Lq) : 0;
+  ba.B = B; ba.H = H; ba.Lq = Lq;
+  ba.Hkv = H_kv; ba.G = H / H_kv;
+  ba.scale = scale;
+  ba.scale_log2 = scale * 1.4426950408889634f;
+  ba.causal = causal ? 1 : 0;
+  ba.broadcast_q = broadcast_q ? 1 : 0;
+  ba.P = P;
+  if (launch_bwd_mx(ba, st) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
+}
+
 int jfa_fwd_noalloc(const void* q, const void* k, const void* v, const int64_t* offsets, int B, int H, int H_kv,
                     int Lq, int d, float scale, int causal, int window, int broadcast_q, void* out, float* lse,
                     int64_t total_len, void* stream) {

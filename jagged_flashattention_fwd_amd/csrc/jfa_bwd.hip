@@ -808,29 +808,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
         JFA_TIMED_LAUNCH(K_DQ, st, (dq_kernel<D, DQ_BM_BCAST / 32, false, true>), dim3(items), dim3(DQ_BM_BCAST * 2), 0, st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t n = (int64_t)a.H * a.Lq * D;
-    int np2 = 1;
-    while (np2 < a.dq_chunks) np2 <<= 1;
-    const dim3 grid((unsigned)((n + 255) / 256));
-#define JFA_DQ_REDUCE(NPV)                                                                                   \
-  case NPV:                                                                                                  \
-    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce<NPV>, grid, dim3(256), 0, st, a.dq_part, a.dq, a.H, a.Lq, D, \
-                     DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale);                                       \
-    break;
-    switch (np2) {
-      JFA_DQ_REDUCE(1)
-      JFA_DQ_REDUCE(2)
-      JFA_DQ_REDUCE(4)
-      JFA_DQ_REDUCE(8)
-      JFA_DQ_REDUCE(16)
-      JFA_DQ_REDUCE(32)
-      JFA_DQ_REDUCE(64)
-      JFA_DQ_REDUCE(128)
-      JFA_DQ_REDUCE(256)
-      default: return hipErrorInvalidValue;
-    }
-#undef JFA_DQ_REDUCE
-    return hipGetLastError();
+    return launch_dq_reduce(a.dq_part, a.dq, a.H, a.Lq, D, DQ_BM_BCAST, a.dq_qblocks, a.dq_chunks, a.scale, st);
   }
   // Tiles of 256 rows: 8 waves, two per SIMD, as in the forward.
   if (a.causal)
@@ -850,6 +828,34 @@ hipError_t launch_group_sum(const float* src, float* dst, int64_t total_len, int
   const int blocks = (int)(want < 4096 ? want : 4096);
   JFA_TIMED_LAUNCH(K_GROUP_SUM, stream, group_sum_kernel, dim3(blocks), dim3(256), 0, stream,
                    reinterpret_cast<const f32x4*>(src), reinterpret_cast<f32x4*>(dst), n, Hkv, H / Hkv, d / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_reduce(const float* part, float* dq, int H, int Lq, int d, int BM, int n_qb, int NC,
+                            float scale, hipStream_t st) {
+  const int64_t n = (int64_t)H * Lq * d;
+  if (n == 0) return hipSuccess;
+  int np2 = 1;
+  while (np2 < NC) np2 <<= 1;
+  const dim3 grid((unsigned)((n + 255) / 256));
+#define JFA_DQ_REDUCE(NPV)                                                                                     \
+  case NPV:                                                                                                    \
+    JFA_TIMED_LAUNCH(K_DQ_REDUCE, st, dq_reduce<NPV>, grid, dim3(256), 0, st, part, dq, H, Lq, d, BM, n_qb, NC, \
+                     scale);                                                                                   \
+    break;
+  switch (np2) {
+    JFA_DQ_REDUCE(1)
+    JFA_DQ_REDUCE(2)
+    JFA_DQ_REDUCE(4)
+    JFA_DQ_REDUCE(8)
+    JFA_DQ_REDUCE(16)
+    JFA_DQ_REDUCE(32)
+    JFA_DQ_REDUCE(64)
+    JFA_DQ_REDUCE(128)
+    JFA_DQ_REDUCE(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef JFA_DQ_REDUCE
   return hipGetLastError();
 }
 

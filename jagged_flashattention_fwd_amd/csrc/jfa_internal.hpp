@@ -100,6 +100,50 @@ struct FwdMxArgs {
 };
 hipError_t launch_fwd_mx(const FwdMxArgs& a, hipStream_t stream);
 
+// MXFP8 backward (d = 128): E4M3 / E8M0 codes of every encoding, layouts as
+// in jfa_bwd_mxfp8.
+struct BwdMxArgs {
+  const uint8_t* q8;  const uint8_t* q_scale;    // row-wise
+  const uint8_t* qt8; const uint8_t* qt_scale;   // query-blocked, transposed
+  const uint8_t* k8;  const uint8_t* k_scale;    // row-wise
+  const uint8_t* kt8; const uint8_t* kt_scale;   // key-blocked, transposed
+  const uint8_t* v8;  const uint8_t* v_scale;    // row-wise
+  const uint8_t* do8; const uint8_t* do_scale;   // row-wise
+  const uint8_t* dot8; const uint8_t* dot_scale; // query-blocked, transposed
+  const int64_t* offsets;
+  const uint16_t* out;    // the forward's O (bf16)
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;           // [rows] scratch
+  float* lse2;            // [rows] scratch: lse * log2(e)
+  float* dq_part;         // broadcast-mode dQ partials, as in BwdArgs
+  const int* seq_order;
+  int dq_qblocks, dq_chunks;
+  const TileRec* ktiles;  // key tiles of MX_BK keys per (sequence, key / value head)
+  const int64_t* n_ktiles;
+  unsigned int* ktile_ctr;
+  const TileRec* qtiles;  // self mode: query tiles of MX_BM rows
+  const int64_t* n_qtiles;
+  unsigned int* qtile_ctr;
+  int64_t total_len;
+  int64_t t_pad;          // total_len rounded up to 64
+  int lq_pad;             // broadcast: Lq rounded up to 64
+  int B, H, Lq;
+  int Hkv, G;
+  float scale, scale_log2;
+  int causal, broadcast_q;
+  int P;
+};
+constexpr int MX_BK = 128;  // keys per tile of the MXFP8 dK / dV kernel: 4 waves x 32
+constexpr int MX_BM = 256;  // query rows per tile of the MXFP8 dQ kernel: 8 waves x 32
+hipError_t launch_bwd_mx(const BwdMxArgs& a, hipStream_t stream);
+// dq[h][q][:] = scale * the sum over the NC partials of (h, q-block), as
+// the broadcast dQ of the bf16 backward (jfa_bwd.hip).
+hipError_t launch_dq_reduce(const float* part, float* dq, int H, int Lq, int d, int BM, int n_qb, int NC,
+                            float scale, hipStream_t stream);
+
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -7,13 +7,7 @@
 // fly.  Here the products are
 //   S^T  = K Q^T    v_mfma_scale_f32_32x32x64_f8f6f4, reduction over d
 //   O^T += V^T P^T  the same instruction, reduction over 64 keys
-// Operand layout of that instruction (checked on the device): row m of an
-// operand lives in lanes m and m + 32, 32 bytes each; bytes 0-15 of both
-// lanes are one 32-element block, scaled by lane m's scale byte, bytes 16-31
-// of both the next block, scaled by lane m + 32's.  Only the pairing of byte
-// positions between the two operands matters, so lane m + 32 g holds
-// elements 16 g .. 16 g + 15 of each of its two blocks.  The output has the
-// 32 x 32 fp32 layout of the bf16 product.
+// (operand layout in jfa_mx.hpp).
 //
 // Inputs (one reading of the page, which gives none): Q and K rows as E4M3
 // with one scale per 32 head-dim elements; V transposed, [H_kv, d, T_pad]
@@ -34,12 +28,11 @@
 
 #include "jfa_device.hpp"
 #include "jfa_internal.hpp"
+#include "jfa_mx.hpp"
 #include "jfa_timing.hpp"
 
 namespace jfa {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 struct Mx {
   static constexpr int NW = 8, BN = 64, BM = NW * 32, D = 128, NBUF = 4, DEP = 2;
@@ -59,35 +52,6 @@ struct Mx {
   static_assert(NBUF * BUF <= 160 * 1024, "LDS");
   static_assert(DEP * IPS + NST <= 63, "vector-memory counter");
 };
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 4 bytes per lane from byte soff + voff of the resource into LDS at
-// lds + 4 * lane (buffer_load_dword ... lds); out-of-range lanes write zeros.
-__device__ __forceinline__ void dma_copy4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds" ::"v"(voff), "s"(rs),
-               "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ i32x8 lds_read32x2(const char* p0, const char* p1) {
-  const u32x4 a = *reinterpret_cast<const u32x4*>(p0);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(p1);
-  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-}
-
-template <int SA, int SB>
-__device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SA, sa, SB, sb);
-}
-
-// Two floats to two E4M3 codes in byte pair HI of `old` (nearest, ties to
-// even; callers keep the values within +-448).
-template <bool HI>
-__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b, uint32_t old) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
-}
 
 template <bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, const TileRec* __restrict__ tiles) {

@@ -31,7 +31,8 @@ Timer g_timer;
 
 const char* const kNames[K_COUNT] = {"sched_sort_scan", "sched_expand", "sched_dump", "fwd_kernel",
                                      "delta_kernel",    "dkdv_kernel",  "dq_reduce",  "dq_kernel",
-                                     "delta_exact_kernel", "group_sum_kernel", "fwd_mx_kernel"};
+                                     "delta_exact_kernel", "group_sum_kernel", "fwd_mx_kernel",
+                                     "delta_mx_kernel", "dkdv_mx_kernel", "dq_mx_kernel"};
 
 void release_all() {
   for (hipEvent_t e : g_timer.events) (void)hipEventDestroy(e);

@@ -16,6 +16,9 @@ enum KernelId {
   K_DELTA_EXACT,
   K_GROUP_SUM,
   K_FWD_MX,
+  K_DELTA_MX,
+  K_DKDV_MX,
+  K_DQ_MX,
   K_COUNT
 };
 

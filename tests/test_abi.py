@@ -32,7 +32,7 @@ def test_header_declares_expected_calls():
         "jfa_bwd", "jfa_debug_schedule", "jfa_fwd", "jfa_kernel_name", "jfa_schedule_params",
         "jfa_status_string", "jfa_timing_enable", "jfa_timing_read", "jfa_timing_reset",
         "jfa_workspace_size", "jfa_workspace_size_gqa", "jfa_fwd_ex", "jfa_bwd_ex", "jfa_debug_schedule_ex", "jfa_fwd_noalloc",
-        "jfa_fwd_mxfp8", "jfa_mxfp8_t_pad"])
+        "jfa_fwd_mxfp8", "jfa_mxfp8_t_pad", "jfa_bwd_mxfp8"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -199,3 +199,27 @@ def test_mxfp8_forward_host_checks(lib):
 def test_mxfp8_t_pad(lib):
     assert [lib.jfa_mxfp8_t_pad(n) for n in (0, 1, 63, 64, 65, 1000)] == [64, 64, 64, 64, 128, 1024]
     assert lib.jfa_mxfp8_t_pad(-5) == -1
+
+
+def test_mxfp8_backward_host_checks(lib):
+    """jfa_bwd_mxfp8 rejects bad arguments before any HIP call: any missing
+    or misaligned encoding, scale array or output, a head dim other than
+    128, heads that do not split, a non-finite scale."""
+    vp = ctypes.c_void_p
+
+    def call(over=None, d=128, H_kv=2, scale=0.1):
+        ptrs = [FAKE] * 15 + [FAKE] * 5 + [FAKE]  # 14 encodings, offsets; out, lse, dq, dk, dv; workspace
+        for i, v in (over or {}).items():
+            ptrs[i] = v
+        enc, offs, outs, ws = ptrs[:14], ptrs[14], ptrs[15:20], ptrs[20]
+        return lib.jfa_bwd_mxfp8(*[vp(x) for x in enc], vp(offs), 2, 2, H_kv, 8, d, scale, 0, 1,
+                                 *[vp(x) for x in outs], 10, vp(ws), 1 << 30, None)
+    for i in range(21):
+        assert call({i: 0}) == 1, i
+    for i in (0, 2, 4, 6, 8, 10, 12, 15, 17, 18, 19, 20):   # codes, out, dq, dk, dv, workspace: 16 bytes
+        assert call({i: FAKE + 4}) == 1, i
+    for i in (1, 3, 5, 7, 9, 11, 13, 16):                    # scale arrays, lse: 4 bytes
+        assert call({i: FAKE + 2}) == 1, i
+    assert call({14: FAKE + 4}) == 1                         # offsets: 8 bytes
+    assert call(d=64) == 2 and call(d=96) == 2
+    assert call(H_kv=3) == 1 and call(scale=math.nan) == 1 and call(scale=-math.inf) == 1
