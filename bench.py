@@ -159,6 +159,9 @@ LABEL_SYMBOLS = {
     "dq_reduce": ("dq_reduce",),
     "group_sum_kernel": ("group_sum_kernel",),
     "fwd_mx_kernel": ("fwd_mx_kernel",),
+    "delta_mx_kernel": ("delta_mx_kernel",),
+    "dkdv_mx_kernel": ("dkdv_mx_kernel",),
+    "dq_mx_kernel": ("dq_mx_kernel",),
 }
 # Counter passes of the counters summary (rocprofv3 collects each pass in a
 # run of its own; at most 8 SQ and 2 GRBM counters per pass).
@@ -214,7 +217,7 @@ def counter_rows(paths):
     return out, copy
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int):
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int, mxfp8: bool = False):
     """Write profiles/traffic_<kernel>_<workload>.txt for every timed kernel
     from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).
     Each counter is scaled by bytes-moved / counter-reading of the plain
@@ -233,8 +236,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
         if not fv or not wv:
             continue
         kf, kw = sum(fv) / len(fv), sum(wv) / len(wv)
-        path = os.path.join(PROFILE_DIR, f"traffic_{label}_{workload}.txt")
-        mode = " --mxfp8" if label == "fwd_mx_kernel" else ""
+        path = os.path.join(PROFILE_DIR, f"traffic_{label}_{workload}{'_mxfp8' if mxfp8 else ''}.txt")
+        mode = " --mxfp8" if mxfp8 else ""
         with open(path, "w") as f:
             f.write(f"# HBM traffic of {label} ({', '.join(LABEL_SYMBOLS[label])}) on {workload}, "
                     "from rocprofv3 FETCH_SIZE and WRITE_SIZE\n")
@@ -243,7 +246,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
                 f.write(f"#   cd /tmp && rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/pmc_{ctr} "
                         f"-o pmc -- python -u $REPO/bench.py --workload {workload}{mode} --steps 2 --warmup 1 "
                         f"--no-cpu-baseline --copy-calibration-mib {copy_bytes >> 20}\n")
-            f.write(f"#   python bench.py --summarize-pmc <fetch csv> <write csv> --workload {workload}\n")
+            f.write(f"#   python bench.py --summarize-pmc <fetch csv> <write csv> --workload {workload}{mode}\n")
             f.write(f"# calibration: plain copy of {copy_bytes} bytes read {copy_fetch:.0f} FETCH bytes and "
                     f"{copy_write:.0f} WRITE bytes\n")
             f.write(f"fetch_scale: {f_scale:.4f}\n")
@@ -266,7 +269,7 @@ def summarize_stats(stats_csv: str, bench_json: str, workload: str, mxfp8: bool 
     c = b["config"]
     mode = " --mxfp8" if mxfp8 else ""
     path = os.path.join(PROFILE_DIR, f"kernels_{workload}{'_mxfp8' if mxfp8 else ''}.md")
-    lines = [f"# rocprofv3 kernel statistics, {workload}{' MXFP8 forward' if mxfp8 else ''} (B={c['B']}, H={c['H']}, "
+    lines = [f"# rocprofv3 kernel statistics, {workload}{' MXFP8 step' if mxfp8 else ''} (B={c['B']}, H={c['H']}, "
              f"H_kv={c['H_kv']}, d={c['d']}, Lq={c['Lq']}, causal={c['causal']}, broadcast_q={c['broadcast_q']})", "",
              "Commands (MI355X, one GPU; `$REPO` is the repository root):", "", "```",
              "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
@@ -285,12 +288,14 @@ def summarize_stats(stats_csv: str, bench_json: str, workload: str, mxfp8: bool 
                   f"--warmup {b['warmup']}`):", ""]
     r = b["roofline"]
     if mxfp8:
-        k = b["kernel"]
-        lines.append(f"- {k['name']}: avg {k['avg_ms']} ms, {k['tflops']} useful TFLOP/s "
-                     f"({k['pct_of_fp8_peak'] * 100:.1f}% of the dense FP8 peak), {k['gbs']} GB/s algorithmic")
-        lines += ["", f"Forward call: {b['value']} useful TFLOP/s, {b['ms_per_step']} ms (schedule and kernel).",
-                  f"Roofline: {r['achieved']} {r['unit']} of {r['peak']} ({r['frac'] * 100:.1f}%), "
-                  f"traffic {r['traffic']}.", ""]
+        for k, v in b["kernels"].items():
+            lines.append(f"- {k}: {v['launches']} launches, avg {v['avg_ms']} ms, {v['gbs']} GB/s algorithmic"
+                         + (f", {v['tflops']} useful TFLOP/s ({v['pct_of_fp8_peak'] * 100:.1f}% of the dense FP8 "
+                            "peak)" if "tflops" in v else ""))
+        lines += ["", f"Step: {b['value']} useful TFLOP/s, {b['ms_per_step']} ms; forward {b['fwd']['ms']} ms "
+                      f"({b['fwd']['tflops']} TFLOP/s), backward {b['bwd']['ms']} ms ({b['bwd']['tflops']} TFLOP/s).",
+                  f"Dominant kernel {r['kernel']}: {r['achieved']} {r['unit']} of {r['peak']} "
+                  f"({r['frac'] * 100:.1f}%), traffic {r['traffic']}.", ""]
     else:
         for k, v in b["kernels"].items():
             lines.append(f"- {k}: {v['launches']} launches, avg {v['avg_ms']} ms"
@@ -313,7 +318,7 @@ def summarize_counters(csvs, workload: str, cus: int = 256, mxfp8: bool = False)
     mode = " --mxfp8" if mxfp8 else ""
     path = os.path.join(PROFILE_DIR, f"counters_{workload}{'_mxfp8' if mxfp8 else ''}.md")
     simds = cus * SIMD_PER_CU
-    lines = [f"# Hardware counters per kernel, {workload}{' MXFP8 forward' if mxfp8 else ''} (MI355X)", "",
+    lines = [f"# Hardware counters per kernel, {workload}{' MXFP8 step' if mxfp8 else ''} (MI355X)", "",
              "Commands (one rocprofv3 run per counter pass; `$REPO` is the repository root):", "", "```"]
     for i, ps in enumerate(COUNTER_PASSES):
         lines.append(f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {ps} --output-format csv "
@@ -330,8 +335,9 @@ def summarize_counters(csvs, workload: str, cus: int = 256, mxfp8: bool = False)
               "- LDS cycles per instruction = SQ_LDS_IDX_ACTIVE / SQ_INSTS_LDS.",
               "- VALU / MFMA co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES.",
               "- wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave cycles spent in s_waitcnt).", ""]
-    order = [k for k in ("fwd_kernel", "fwd_mx_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "dq_reduce",
-                         "delta_exact_kernel", "group_sum_kernel") if k in rows]
+    order = [k for k in ("fwd_kernel", "fwd_mx_kernel", "delta_kernel", "delta_mx_kernel", "dkdv_kernel",
+                         "dkdv_mx_kernel", "dq_kernel", "dq_mx_kernel", "dq_reduce", "delta_exact_kernel",
+                         "group_sum_kernel") if k in rows]
     ratio_hdr = "| kernel | MFMA busy | LDS conflict share | LDS cycles / instr | VALU-MFMA co-issue | wait share | VALU / MFMA instr |"
     lines += [ratio_hdr, "|" + "---|" * 7]
 
@@ -432,24 +438,45 @@ def cpu_baseline(t, w, scale, seconds: float):
 FP8_MFMA_FLOP_PER_CLK_PER_CU = 8192  # dense E4M3 (twice bf16)
 
 
-def mx_algorithmic_bytes(lengths, H: int, H_kv: int, d: int, Lq: int, broadcast_q: bool) -> int:
-    """The MXFP8 forward's bytes per launch: K and V codes once (1 byte per
-    element) with their scales (K: one per 32 head-dim elements; V: one per
-    32 keys of the padded packed index), Q codes and scales once, O (bf16)
-    and lse (fp32) written once."""
+def mx_algorithmic_bytes(kernel: str, lengths, H: int, H_kv: int, d: int, Lq: int, broadcast_q: bool,
+                         P: int = 256) -> int:
+    """Bytes an MXFP8 kernel must move per launch: every input encoding it
+    reads once (E4M3 codes, 1 byte per element, with their E8M0 scales, one
+    byte per 32 elements) and every output written once."""
     T = int(np.asarray(lengths).sum())
     B = len(lengths)
     t_pad = max(64, -(-T // 64) * 64)
-    kv = T * H_kv * d + T * H_kv * (d // 32) + H_kv * d * t_pad + H_kv * (t_pad // 32) * d
+    enc = d + d // 32                              # one row-wise or transposed encoding, per row
+    kv_rows = T * H_kv * enc                       # K or V, row-wise
+    kv_t = H_kv * d * t_pad + H_kv * (t_pad // 32) * d   # K^T or V^T
     q_rows = H * Lq if broadcast_q else T * H
     rows = B * H * Lq if broadcast_q else T * H
-    return kv + q_rows * (d + d // 32) + rows * (2 * d + 4)
+    if kernel == "fwd_mx_kernel":                 # Q, K, V^T in; O (bf16), lse out
+        return kv_rows + kv_t + q_rows * enc + rows * (2 * d + 4)
+    if kernel == "delta_mx_kernel":               # O, dO, lse in; delta, lse * log2(e) out
+        return rows * (2 * d + enc + 4) + rows * 8
+    if kernel == "dkdv_mx_kernel":                # K, V, Q and Q^T, dO and dO^T, lse, delta in; dK, dV (fp32) out
+        return 2 * kv_rows + 2 * q_rows * enc + 2 * rows * enc + rows * 8 + 2 * T * H_kv * d * 4
+    if kernel == "dq_mx_kernel":                  # K, V, K^T, Q, dO, lse, delta in; dQ or the partials out
+        b = 2 * kv_rows + kv_t + q_rows * enc + rows * (enc + 8)
+        if broadcast_q:
+            n_qb, nc = dq_split(B, H, Lq, P)
+            return b + H * n_qb * nc * 256 * d * 4
+        return b + T * H * d * 4
+    if kernel == "dq_reduce":
+        n_qb, nc = dq_split(B, H, Lq, P)
+        return H * n_qb * nc * 256 * d * 4 + H * Lq * d * 4
+    return 0
+
+
+MX_KERNELS = ("fwd_mx_kernel", "delta_mx_kernel", "dkdv_mx_kernel", "dq_mx_kernel", "dq_reduce")
 
 
 def bench_mxfp8(args) -> int:
-    """The MXFP8 forward on a workload's shapes (random E4M3 / E8M0 codes):
-    K timed calls by the host clock, then an instrumented run of K calls for
-    the kernel's own time.  Prints one JSON line of its own."""
+    """The MXFP8 step (forward, then backward) on a workload's shapes, from
+    random E4M3 / E8M0 codes in every encoding: K timed steps by the host
+    clock, then an instrumented run of K steps for each kernel's own time.
+    Prints one JSON line of its own."""
     import torch
     import workloads as wl
     import jagged_flashattention_fwd_amd as jfa
@@ -462,56 +489,102 @@ def bench_mxfp8(args) -> int:
     if w.d != 128 or w.window:
         print(f"--mxfp8 needs d = 128 and no window ({w.name})", file=sys.stderr)
         return 2
-    t = wl.make_mx_workload(w, device=dev)
+    t = wl.make_mx_bwd_workload(w, device=dev)
     lengths, T = t["lengths"], t["total_len"]
     H, H_kv, d, Lq, B = w.H, w.kv_heads, w.d, w.Lq, w.B
     bq, causal = w.broadcast_q, w.causal
     if bq:
         out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+        dq = torch.empty((H, Lq, d), dtype=torch.float32, device=dev)
     else:
         out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, dev, H_kv=H_kv)
+        dq = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((T, H_kv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws_f = jfa.workspace(T, B, H, Lq, d, causal, bq, 0, dev, H_kv=H_kv)
+    ws_b = jfa.workspace(T, B, H, Lq, d, causal, bq, 1, dev, H_kv=H_kv)
 
     def fwd():
         jfa.jfa_fwd_mxfp8(t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["vt8"], t["vt_scale"], t["offsets"],
-                          B, H, H_kv, Lq, d, w.scale, causal, bq, out, lse, T, ws)
+                          B, H, H_kv, Lq, d, w.scale, causal, bq, out, lse, T, ws_f)
+
+    def bwd():
+        jfa.jfa_bwd_mxfp8(t, t["offsets"], B, H, H_kv, Lq, d, w.scale, causal, bq, out, lse, dq, dk, dv, T, ws_b)
+
+    def step():
+        fwd()
+        bwd()
 
     for _ in range(args.warmup):
-        fwd()
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        fwd()
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    jfa.jfa_timing_enable(8 * args.steps + 8)
+    # instrumented run: the forward's and the backward's calls, and each kernel
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    jfa.jfa_timing_enable(16 * args.steps + 16)
     jfa.jfa_timing_reset()
-    for _ in range(args.steps):
+    for e in ev:
+        e[0].record(s)
         fwd()
+        e[1].record(s)
+        bwd()
+        e[2].record(s)
     torch.cuda.synchronize()
     kt = jfa.kernel_times()
     jfa.jfa_timing_enable(0)
-    n, kms = kt["fwd_mx_kernel"]
-    avg = kms / n
-    fl, _ = useful_flops(lengths, H, d, Lq, causal, bq, 0)
-    nbytes = mx_algorithmic_bytes(lengths, H, H_kv, d, Lq, bq)
-    ktf = fl / (avg * 1e-3) / 1e12
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    fl, bfl = useful_flops(lengths, H, d, Lq, causal, bq, 0)
+    kflops = {"fwd_mx_kernel": fl, "dkdv_mx_kernel": bfl * 8 // 10, "dq_mx_kernel": bfl * 2 // 10 + fl}
+    kernels = {}
+    for name in MX_KERNELS:
+        n, kms = kt.get(name, (0, 0.0))
+        if not n:
+            continue
+        nbytes = mx_algorithmic_bytes(name, lengths, H, H_kv, d, Lq, bq, cus)
+        e = {"launches": n, "avg_ms": round(kms / n, 4), "gbs": round(nbytes / (kms / n * 1e-3) / 1e9, 1),
+             "algorithmic_bytes": nbytes}
+        if name in kflops:
+            tf = kflops[name] / (kms / n * 1e-3) / 1e12
+            e["tflops"] = round(tf, 1)
+            e["pct_of_fp8_peak"] = round(tf / peak8, 4)
+        kernels[name] = e
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    kd = kernels[dom]
+    t_hbm = kd["algorithmic_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = kflops.get(dom, 0) / (peak8 * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": round(peak8, 1), "unit": "TFLOP/s",
+                "frac": round(kd["tflops"] / peak8, 4)}
+    roof.update({"kernel": dom, "traffic": measured_traffic(dom, w.name + "_mxfp8"),
+                 "algorithmic_bytes": kd["algorithmic_bytes"], "useful_flops": kflops.get(dom, 0)})
+    tot = fl + bfl
     res = {
-        "metric": "useful TFLOP/s, MXFP8 forward (E4M3 operands, E8M0 block scales)",
-        "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": "useful TFLOP/s, MXFP8 step: forward + backward (E4M3 operands, E8M0 block scales)",
+        "value": round(tot / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "e4m3", "data": "synthetic (random E4M3 / E8M0 codes)",
+        "vs_baseline": None, "dtype": "e4m3", "data": "synthetic (random E4M3 / E8M0 codes, every encoding)",
         "config": {"workload": w.name, "B": B, "H": H, "H_kv": H_kv, "d": d, "Lq": Lq, "causal": causal,
-                   "broadcast_q": bq, "total_len": T, "accumulate": "fp32", "out": "bf16"},
-        "timing": "value and ms_per_step: host clock over the K timed calls (schedule and kernel); kernel: "
-                  "hipEvents on the launch stream over a second run of K calls",
-        "kernel": {"name": "fwd_mx_kernel", "avg_ms": round(avg, 4), "tflops": round(ktf, 1),
-                   "pct_of_fp8_peak": round(ktf / peak8, 4), "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "mfma", "achieved": round(ktf, 1), "peak": round(peak8, 1), "unit": "TFLOP/s",
-                     "frac": round(ktf / peak8, 4), "traffic": measured_traffic("fwd_mx_kernel", w.name),
-                     "algorithmic_bytes": nbytes, "useful_flops": fl},
+                   "broadcast_q": bq, "total_len": T, "accumulate": "fp32", "out": "bf16", "grads": "fp32"},
+        "timing": "value and ms_per_step: host clock over the K timed steps; fwd / bwd and kernels: hipEvents "
+                  "on the launch stream over a second, instrumented run of K steps",
+        "fwd": {"ms": round(f_ms, 4), "tflops": round(fl / (f_ms * 1e-3) / 1e12, 1),
+                "pct_of_fp8_peak": round(fl / (f_ms * 1e-3) / 1e12 / peak8, 4)},
+        "bwd": {"ms": round(b_ms, 4), "tflops": round(bfl / (b_ms * 1e-3) / 1e12, 1),
+                "pct_of_fp8_peak": round(bfl / (b_ms * 1e-3) / 1e12 / peak8, 4)},
+        "kernels": kernels,
+        "roofline": roof,
+        "device": {"cus": cus, "fp8_peak_tflops": round(peak8, 1), "hbm_peak_gbs": HBM_PEAK_GBS},
     }
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -542,7 +615,8 @@ def main(argv=None):
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="write profiles/counters_<workload>.md from the counter-pass runs and exit")
     ap.add_argument("--mxfp8", action="store_true",
-                    help="measure the MXFP8 forward on the workload's shapes instead (its own JSON line)")
+                    help="measure the MXFP8 step (forward + backward) on the workload's shapes instead "
+                         "(its own JSON line)")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
                     help="write profiles/kernels_<workload>.md from a --kernel-trace --stats run and exit")
     args = ap.parse_args(argv)
@@ -551,7 +625,7 @@ def main(argv=None):
         return 0
     if args.summarize_pmc:
         for p in summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
-                               (args.copy_calibration_mib or 1024) << 20):
+                               (args.copy_calibration_mib or 1024) << 20, args.mxfp8):
             print(p)
         return 0
     if args.summarize_counters:
