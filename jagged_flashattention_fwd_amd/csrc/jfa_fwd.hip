@@ -928,6 +928,9 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       else last(std::false_type{}, j, sa);
     }
 
+    // A tile without steps has no barrier after the waves read s_next,
+    // which wave 0 rewrites at the next tile start.
+    if (DYN_FWD && g_cmp == g_first) barrier_lds();
     // Tile end: the next tile's Q rows, then this tile's O and lse.
     if (has_nxt) load_q(np);
     store_out(cp, nq);

@@ -371,6 +371,9 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
     for (int j = cp.lead; j < cp.n_plain; ++j) kv_step(j, std::false_type{});
     for (int j = max(cp.n_plain, cp.lead); j < n_kv; ++j) kv_step(j, std::true_type{});
 
+    // a tile without steps has no barrier after the waves read s_next,
+    // which wave 0 rewrites at the next tile start
+    if (g_cmp == g_first) barrier_lds();
     // the next tile's Q rows, then this tile's stores
     if (has_nxt) load_q(np);
     store_out(cp, nq);

@@ -103,7 +103,10 @@ __global__ __launch_bounds__(256) void delta_mx_kernel(const uint16_t* __restric
 
 // ------------------------------------------------------------- dK / dV --
 struct MxB {
-  static constexpr int NW = 4, BQ = 64, BK = NW * 32, D = 128, NBUF = 3, DEP = 2;
+  // Waves w and w + 4 form a pair over the same 32 keys: wave w takes the
+  // step's first 32 queries and accumulates dV, wave w + 4 the other 32 and
+  // dK; each hands its partner the quantized operand the partner needs.
+  static constexpr int NW = 8, BQ = 64, BK = NW / 2 * 32, D = 128, NBUF = 3, DEP = 2;
   static constexpr int RW = BQ / NW, TW = D / NW;  // Q / dO rows and transposed rows copied per wave
   static constexpr int NRC = (RW + 6) / 7, NTC = (TW + 11) / 12;  // copies per wave of each
   static_assert(RW >= 7 && TW >= 12, "copy geometry");
@@ -122,11 +125,13 @@ struct MxB {
   // Copies per wave per step: Q, dO, Q^T, dO^T, and one dword copy each of
   // the four scale arrays, lse and delta.
   static constexpr int IPS = 2 * NRC + 2 * NTC + 6;
-  static constexpr int NST = 2 * 4 * 4;  // stores per wave at a tile end: dK and dV, 4 pieces per head-dim tile
+  static constexpr int NST = 4 * 4;  // stores per wave at a tile end: dV or dK, 4 pieces per head-dim tile
   static_assert(BUF % 16 == 0, "buffer alignment");
   static_assert(NBUF * BUF <= 160 * 1024, "LDS");
   static_assert(NBUF >= DEP + 1, "a buffer is refilled only after every wave has left it");
-  static constexpr int NKV = 10;          // loads of a tile's K / V operands
+  static_assert(NW * 32 * 144 <= BUF, "the store staging fits one ring buffer");
+  static_assert(NBUF == DEP + 1, "the buffer of the last computed step is the free one at a tile end");
+  static constexpr int NKV = 12;          // loads of a tile's K / V operands and of the next tile record
   // At a tile end at most one step's copies stay in flight before the next
   // tile's K / V loads and this tile's stores are issued.
   static_assert(DEP * IPS <= 63 && IPS + NKV + NST <= 63, "vector-memory counter");
@@ -146,8 +151,13 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
   constexpr int NW = C::NW, RW = C::RW, TW = C::TW, NRC = C::NRC, NTC = C::NTC;
   __shared__ __attribute__((aligned(16))) char smem[NBUF][C::BUF];
 
+  __shared__ __attribute__((aligned(16))) u32x4 xw[NW][WAVE];  // operand words handed to the partner
+  __shared__ uint32_t xc[NW][WAVE];                           // and their block scale codes
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int role = wave / (NW / 2);  // 0: queries 0..31 of a step, dV; 1: queries 32..63, dK
+  const int kw = wave % (NW / 2);    // key group of the pair
   const int l = tid % WAVE, g = l / 32, lc = l % 32;
   const int slot = logical_slot(blockIdx.x, a.P);
   const int64_t T = *a.n_ktiles;
@@ -281,7 +291,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
   i32x8 kop[2], vop[2];
   uint32_t ksc = 0, vsc = 0;
   auto load_kv = [&](const Tp& p) {
-    int key = p.k0 + wave * 32 + lc;
+    int key = p.k0 + kw * 32 + lc;
     key = key < p.L ? key : 0;
     const int64_t row = (p.s0 + key) * Hkv + p.hk;
     const uint8_t* kr = a.k8 + row * D;
@@ -295,45 +305,58 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
     vsc = *reinterpret_cast<const uint32_t*>(a.v_scale + row * 4) >> (8 * g);
   };
 
-  f32x16 dva[4], dka[4];
-  // dK = scale dK^T acc and dV of a tile: NST bounded buffer stores per wave
-  auto store_out = [&](const Tp& p, bool live) {
-    const int k0 = p.k0 + wave * 32;
+  f32x16 acc[4];  // dV^T (role 0) or dK^T (role 1) of this wave's 32 keys
+  // dV, or dK = scale dK^T acc, of a tile: NST bounded buffer stores per
+  // wave.  Each 32-key x 32-element piece goes through `stage` (this wave's
+  // 32 rows of 144 bytes in a free ring buffer) so that every store writes
+  // whole 128-byte runs of 8 keys, not 32-byte pieces of 32 keys.
+  auto store_out = [&](const Tp& p, bool live, char* stage) {
+    const int k0 = p.k0 + kw * 32;
     const int nv = live ? max(0, min(p.L - k0, 32)) : 0;
     const uint32_t kstride = (uint32_t)Hkv * D * 4;
     const int64_t row0 = (p.s0 + k0) * Hkv + p.hk;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.dk + row0 * D, nv * (int)kstride);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.dv + row0 * D, nv * (int)kstride);
-    const float sc = a.scale;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((role ? a.dk : a.dv) + row0 * D, nv * (int)kstride);
+    const float sc = role ? a.scale : 1.f;
+    const int rk = l >> 3, rc = l & 7;  // read-back: key rk of 8, 16-byte chunk rc
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt) {
+      if (live) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const uint32_t off = (uint32_t)lc * kstride + (uint32_t)(dt * 32 + i4 * 8 + g * 4) * 4u;
-        f32x4 vk, vv;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vk[e] = dka[dt][i4 * 4 + e] * sc;
-          vv[e] = dva[dt][i4 * 4 + e];
+          for (int e = 0; e < 4; ++e) v[e] = acc[dt][i4 * 4 + e] * sc;
+          *reinterpret_cast<f32x4*>(stage + lc * 144 + (i4 * 8 + g * 4) * 4) = v;
         }
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, vk), rk, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, vv), rv, off, 0, 0);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = r * 8 + rk;
+        const u32x4 v = live ? *reinterpret_cast<const u32x4*>(stage + kr * 144 + rc * 16) : u32x4{};
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)kr * kstride + (uint32_t)(dt * 128 + rc * 16), 0, 0);
+      }
+    }
   };
 
   Tp cp = tparams(a.ktiles[t0]);
   load_kv(cp);
-  store_out(cp, false);  // stores that write nothing: every tile start sees NST stores after its K / V loads
+  // The record of the tile after the next, loaded by lane 0 of wave 0 one
+  // tile ahead and handed to every wave through LDS at the tile start, so
+  // that no wave waits for it there.
+  __shared__ TileRec s_rec;
+  TileRec nrec{};
+  {
+    const int64_t t1 = zigzag_tile(1, slot, a.P);
+    if (wave == 0 && l == 0 && t1 < T) nrec = a.ktiles[t1];
+  }
+  store_out(cp, false, nullptr);  // stores that write nothing: every tile start sees NST stores after its loads
 
   __shared__ int s_next;
   unsigned int fetched = 0;
   for (int64_t pass = 0;; ++pass) {
     const int nsteps = cp.nj * G;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      dva[dt] = f32x16{};
-      dka[dt] = f32x16{};
-    }
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
     {
       const int need = min(DEP, nsteps);
       if (iss_cur < need) {
@@ -343,19 +366,22 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         wait_vmcnt<NST>();
       }
     }
-    if (pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
+    if (wave == 0 && l == 0) {
+      if (pass > 0) s_next = (int)fetched;
+      s_rec = nrec;
+    }
     barrier_lds();
     const int64_t tn = pass == 0 ? zigzag_tile(1, slot, a.P)
                                  : 2 * (int64_t)a.P + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
     const bool has_nxt = tn < T;
     if (has_nxt && wave == 0 && l == 0) fetched = atomicAdd(a.ktile_ctr, 1u);
-    const Tp np = has_nxt ? tparams(a.ktiles[tn]) : cp;
+    const Tp np = has_nxt ? tparams(s_rec) : cp;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) asm volatile("" : "+v"(kop[kk]), "+v"(vop[kk]));
     asm volatile("" : "+v"(ksc), "+v"(vsc));
     const int g_first = g_cmp;
-    const int key = cp.k0 + wave * 32 + lc;           // this lane's key (local)
-    const bool wave_live = cp.k0 + wave * 32 < cp.L;  // the wave has a key of the sequence
+    const int key = cp.k0 + kw * 32 + lc;           // this lane's key (local)
+    const bool wave_live = cp.k0 + kw * 32 < cp.L;  // the pair has a key of the sequence
     const int64_t base = BCAST ? 0 : cp.s0;
 
     auto step = [&](int j, auto masked_tag) {
@@ -365,14 +391,12 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
       issue_next(cp, np, has_nxt);
       const char* buf = smem[(uint32_t)g_cmp % NBUF];
       ++g_cmp;
-      if (!wave_live) return;
       const int qbase = (int)((int64_t)j * BQ - base);  // local index of the step's first query
-      uint32_t pw[8], dw[8];
-      uint32_t psc = 127, dsc = 127;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        // S and dP for 32 queries x this wave's 32 keys: lane (key, g) holds
-        // query rows qt * 32 + (i / 4) * 8 + 4 g + i % 4
+      const int qt = role;
+      uint32_t wq[4], wd[4], cpq = 127, cdq = 127;
+      if (wave_live) {
+        // S and dP for queries qt * 32 .. qt * 32 + 31 x this pair's 32 keys:
+        // lane (key, g) holds query rows qt * 32 + (i / 4) * 8 + 4 g + i % 4
         const char* qr = buf + C::OFF_Q + (qt * 32 + lc) * RB;
         const char* dr = buf + C::OFF_DO + (qt * 32 + lc) * RB;
         const uint32_t qsw = *reinterpret_cast<const uint32_t*>(buf + C::OFF_QS + (qt * 32 + lc) * 4) >> (8 * g);
@@ -400,35 +424,39 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
             ds[i] = pv * (dp[i] - dl[e]);
           }
         }
-        uint32_t wq[4], wd[4], cpq, cdq;
         quantize_block32<false>(p, wq, &cpq);
         quantize_block32<true>(ds, wd, &cdq);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pw[qt * 4 + w] = wq[w];
-          dw[qt * 4 + w] = wd[w];
-        }
-        psc = g == qt ? cpq : psc;
-        dsc = g == qt ? cdq : dsc;
+        // the partner accumulates with the other product's operand: role 0
+        // hands over its dS block, role 1 its P block
+        xw[wave][l] = role ? u32x4{wq[0], wq[1], wq[2], wq[3]} : u32x4{wd[0], wd[1], wd[2], wd[3]};
+        xc[wave][l] = role ? cpq : cdq;
       }
-      const i32x8 pop = i32x8{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
-                              (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-      const i32x8 dop = i32x8{(int)dw[0], (int)dw[1], (int)dw[2], (int)dw[3],
-                              (int)dw[4], (int)dw[5], (int)dw[6], (int)dw[7]};
-      // dV^T += dO^T P and dK^T += Q^T dS over the step's 64 queries, 4
-      // head-dim tiles of 32
-      uint32_t uts = 0, qts = 0;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        uts |= (uint32_t)(*reinterpret_cast<const uint8_t*>(buf + C::OFF_DOTS + g * D + dt * 32 + lc)) << (8 * dt);
-        qts |= (uint32_t)(*reinterpret_cast<const uint8_t*>(buf + C::OFF_QTS + g * D + dt * 32 + lc)) << (8 * dt);
+      barrier_lds();
+      if (!wave_live) return;
+      const u32x4 xo = xw[wave ^ (NW / 2)][l];
+      const uint32_t xcode = xc[wave ^ (NW / 2)][l];
+      // role 0: dV^T += dO^T P with P of both query blocks; role 1: dK^T +=
+      // Q^T dS.  Block 0 is the role-0 wave's, block 1 the role-1 wave's;
+      // lane half g takes block g's scale.
+      i32x8 bop;
+      uint32_t bsc;
+      if (role == 0) {
+        bop = i32x8{(int)wq[0], (int)wq[1], (int)wq[2], (int)wq[3], (int)xo[0], (int)xo[1], (int)xo[2], (int)xo[3]};
+        bsc = g == 0 ? cpq : xcode;
+      } else {
+        bop = i32x8{(int)xo[0], (int)xo[1], (int)xo[2], (int)xo[3], (int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+        bsc = g == 0 ? xcode : cdq;
       }
+      const int off_a = role ? C::OFF_QT : C::OFF_DOT;
+      const int off_s = role ? C::OFF_QTS : C::OFF_DOTS;
+      uint32_t asc = 0;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        asc |= (uint32_t)(*reinterpret_cast<const uint8_t*>(buf + off_s + g * D + dt * 32 + lc)) << (8 * dt);
       static_for<0, 4>([&](auto dt_tag) {
         constexpr int dt = decltype(dt_tag)::value;
-        const char* ur = buf + C::OFF_DOT + (dt * 32 + lc) * TB;
-        const char* tr = buf + C::OFF_QT + (dt * 32 + lc) * TB;
-        dva[dt] = mfma_mx<dt, 0>(lds_read32x2(ur + 16 * g, ur + 32 + 16 * g), pop, dva[dt], (int)uts, (int)psc);
-        dka[dt] = mfma_mx<dt, 0>(lds_read32x2(tr + 16 * g, tr + 32 + 16 * g), dop, dka[dt], (int)qts, (int)dsc);
+        const char* ar = buf + off_a + (dt * 32 + lc) * TB;
+        acc[dt] = mfma_mx<dt, 0>(lds_read32x2(ar + 16 * g, ar + 32 + 16 * g), bop, acc[dt], (int)asc, (int)bsc);
       });
     };
     for (int gi = 0; gi < G; ++gi)
@@ -438,9 +466,18 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         else step(j, std::true_type{});
       }
 
+    // s_next and s_rec are rewritten at the next tile start: a tile without
+    // steps has no barrier of its own after the waves read them
+    if (nsteps == 0) barrier_lds();
     wait_vmcnt<IPS>();
-    if (has_nxt) load_kv(np);
-    store_out(cp, true);
+    if (has_nxt) {
+      load_kv(np);
+      const int64_t t2 = 2 * (int64_t)a.P + fetched;  // the tile after np
+      if (wave == 0 && l == 0 && t2 < T) nrec = a.ktiles[t2];
+    }
+    // the last computed step's buffer is free once every wave has left it
+    barrier_lds();
+    store_out(cp, true, smem[(uint32_t)(g_cmp + NBUF - 1) % NBUF] + wave * 32 * 144);
     if (!has_nxt) break;
     cp = np;
     iss_cur = iss_nxt;
