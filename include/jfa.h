@@ -156,7 +156,8 @@ int jfa_bwd_ex(const void* q, const void* k, const void* v, const int64_t* offse
  * statistics are not quantized: O = (quantized P) V / l with l the sum of
  * P, and lse = log sum exp(scale * q.k) as in jfa_fwd.  out, lse, offsets,
  * the workspace (jfa_workspace_size_gqa with pass 0), the modes and the
- * error rules are those of jfa_fwd_ex. */
+ * error rules are those of jfa_fwd_ex; total_len above 2^26 (T_pad past
+ * (2^31 - 1) / 32) returns JFA_ERR_UNSUPPORTED. */
 int jfa_fwd_mxfp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale, const void* vt8,
                   const void* vt_scale, const int64_t* offsets, int B, int H, int H_kv, int Lq, int d, float scale,
                   int causal, int broadcast_q, void* out, float* lse, int64_t total_len, void* workspace,
@@ -201,7 +202,8 @@ int64_t jfa_mxfp8_t_pad(int64_t total_len);
  * its query heads; broadcast dq summed over the sequences).  Any finite scale
  * is accepted.  The workspace is that of jfa_bwd_ex:
  * jfa_workspace_size_gqa(total_len, B, H, H_kv, Lq, 128, causal,
- * broadcast_q, 1) bytes.  Offsets, modes and error rules as in jfa_bwd_ex. */
+ * broadcast_q, 1) bytes.  Offsets, modes and error rules as in jfa_bwd_ex;
+ * the total_len limit of jfa_fwd_mxfp8 applies. */
 int jfa_bwd_mxfp8(const void* q8, const void* q_scale, const void* qt8, const void* qt_scale, const void* k8,
                   const void* k_scale, const void* kt8, const void* kt_scale, const void* v8,
                   const void* v_scale, const void* do8, const void* do_scale, const void* dot8,

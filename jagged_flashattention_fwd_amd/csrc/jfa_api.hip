@@ -355,6 +355,9 @@ int jfa_fwd_mxfp8(const void* q8, const void* q_scale, const void* k8, const voi
                           total_len);
   if (rc != JFA_OK) return rc;
   if (d != 128) return JFA_ERR_UNSUPPORTED;
+  // The MXFP8 kernels bound their copies of transposed rows with 32-bit
+  // byte counts of up to 17 rows of T_pad keys.
+  if (mxfp8_t_pad(total_len) > (int64_t)(INT32_MAX / 32)) return JFA_ERR_UNSUPPORTED;
   if (!workspace || !aligned16(workspace)) return JFA_ERR_INVALID_ARG;
   if (!broadcast_q) Lq = 0;
   int P = 0;
@@ -417,6 +420,9 @@ int jfa_bwd_mxfp8(const void* q8, const void* q_scale, const void* qt8, const vo
   rc = check_heads(H, H_kv);
   if (rc != JFA_OK) return rc;
   if (d != 128) return JFA_ERR_UNSUPPORTED;
+  // The MXFP8 kernels bound their copies of transposed rows with 32-bit
+  // byte counts of up to 17 rows of T_pad keys.
+  if (mxfp8_t_pad(total_len) > (int64_t)(INT32_MAX / 32)) return JFA_ERR_UNSUPPORTED;
   if (!broadcast_q) Lq = 0;
   int P = 0;
   rc = workers(1, &P);

@@ -194,6 +194,9 @@ def test_mxfp8_forward_host_checks(lib):
     assert call(d=64) == 2 and call(d=96) == 2
     assert call(H_kv=3) == 1 and call(scale=math.inf) == 1
     assert call(ws=0) == 1 and call(ws=FAKE + 4) == 1
+    # transposed rows past (2^31 - 1) / 32 keys
+    assert lib.jfa_fwd_mxfp8(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 2, 2, 2, 8, 128,
+                             0.1, 0, 1, vp(FAKE), vp(FAKE), 1 << 27, vp(FAKE), 1 << 40, None) == 2
 
 
 def test_mxfp8_t_pad(lib):
@@ -223,3 +226,6 @@ def test_mxfp8_backward_host_checks(lib):
     assert call({14: FAKE + 4}) == 1                         # offsets: 8 bytes
     assert call(d=64) == 2 and call(d=96) == 2
     assert call(H_kv=3) == 1 and call(scale=math.nan) == 1 and call(scale=-math.inf) == 1
+    ptrs = [vp(FAKE)] * 15
+    assert lib.jfa_bwd_mxfp8(*ptrs, 2, 2, 2, 8, 128, 0.1, 0, 1, *[vp(FAKE)] * 5, 1 << 27, vp(FAKE), 1 << 40,
+                             None) == 2
