@@ -463,6 +463,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
   }
 }
 
+// Row position of row r of a tile stored with the 4 x 4 transpose within each
+// group of 16 rows (its own inverse).
+__device__ __forceinline__ int kperm_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Broadcast dQ, d = 128.  One workgroup per (head, 256-row query block,
 // chunk); its K/V steps form one stream over the chunk's sequences, copied DEP
 // steps ahead across sequence boundaries and issued from inside the S^T / dP^T
@@ -549,13 +553,23 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     return q;
   };
 
-  // ---- the step stream (as in the forward).
+  // ---- the step stream (as in the forward).  The K tile is read both ways
+  // (16-byte reads of 16 consecutive key rows for S^T, transposing reads of
+  // 4 rows for dQ^T += K^T dS^T): key row r of a step sits at row position
+  // perm(r), the 4 x 4 transpose within each group of 16 rows, which keeps
+  // both reads free of bank conflicts with 304-byte rows (as the Q / dO
+  // tiles of the dK / dV kernel).  Position p of a copy takes key row
+  // perm(p) of the step, fixed per lane and copy; V is read one way only.
   int g_iss = 0, g_cmp = 0, iss_cur = 0, iss_nxt = 0;
   const uint16_t* j_k = a.k;
   const uint16_t* j_v = a.v;
   uint32_t j_kd = 0, j_vd = 0;
-  int j_last = 0;
+  int j_last = 0, j_lastk = 0;
   bool j_on = false;
+  int kperm[C::CPT];
+#pragma unroll
+  for (int k = 0; k < C::CPT; ++k)
+    kperm[k] = kperm_row(wave * RPW + PadRowCopy::start(k, RPW) + (int)PadRowCopy::lane_row(l));
   auto prep_next = [&](const Sq& cp, const Sq& np, bool has_nxt) {
     const int nn = has_nxt ? np.n_kv - np.j0 : 0;
     const bool cur = iss_cur < cp.n_kv - cp.j0;
@@ -564,11 +578,14 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
     const int L_ = cur ? cp.L : np.L;
     const int j = cur ? cp.j0 + iss_cur : np.j0 + iss_nxt;
     const int base_row = min(j * BN + wave * RPW, L_ - 1);
-    // byte offset of the row within the sequence (a 32 x 32-bit product)
+    // byte offsets of rows within the sequence (32 x 32-bit products); K from
+    // the step's first row (j BN < L), V from this wave's first
     const uint64_t roff = (uint64_t)(uint32_t)base_row * (uint32_t)(ld * 2);
-    j_k = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + roff);
+    const uint64_t koff = (uint64_t)(uint32_t)(j * BN) * (uint32_t)(ld * 2);
+    j_k = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + koff);
     j_v = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(cur ? cp.vb : np.vb) + roff);
     j_last = L_ - 1 - base_row;
+    j_lastk = L_ - 1 - j * BN;
     const int buf = (int)((uint32_t)g_iss % NBUF);
     j_kd = lds_addr(smem[buf][0]) + wave * RPW * RB;
     j_vd = lds_addr(smem[buf][1]) + wave * RPW * RB;
@@ -581,9 +598,12 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
 #pragma unroll
     for (int k = k0; k < k1; ++k) {
       const int R = PadRowCopy::start(k % C::CPT, RPW);
-      const uint32_t vo = pc.voff(R, j_last, (uint32_t)(ld * 2));
-      if (k < C::CPT) dma_copy16(j_k, vo, j_kd + R * RB);
-      else dma_copy16(j_v, vo, j_vd + R * RB);
+      if (k < C::CPT) {
+        const uint32_t vo = (uint32_t)min(kperm[k], j_lastk) * (uint32_t)(ld * 2) + pc.byte;
+        dma_copy16(j_k, vo, j_kd + R * RB);
+      } else {
+        dma_copy16(j_v, pc.voff(R, j_last, (uint32_t)(ld * 2)), j_vd + R * RB);
+      }
     }
   };
 
@@ -661,15 +681,15 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
           f32x16 sacc = f32x16{}, dpacc = f32x16{};
           // K / V operands of k-step ks + 1 are read before the products of
           // k-step ks.
-          bf16x8 kc = lds_read16(Ks, tile_off<D>(kt * 32 + lc, g));
+          const int kpos = kperm_row(kt * 32 + lc);  // row position of this lane's key
+          bf16x8 kc = lds_read16(Ks, tile_off<D>(kpos, g));
           bf16x8 vc = lds_read16(Vs, tile_off<D>(kt * 32 + lc, g));
           static_for<0, KS>([&](auto ks_tag) {
             constexpr int ks = decltype(ks_tag)::value;
             bf16x8 kn, vn;
             if constexpr (ks + 1 < KS) {
-              const int off = tile_off<D>(kt * 32 + lc, (ks + 1) * 2 + g);
-              kn = lds_read16(Ks, off);
-              vn = lds_read16(Vs, off);
+              kn = lds_read16(Ks, tile_off<D>(kpos, (ks + 1) * 2 + g));
+              vn = lds_read16(Vs, tile_off<D>(kt * 32 + lc, (ks + 1) * 2 + g));
             }
             sacc = mfma32(kc, qreg[ks], sacc);
             dpacc = mfma32(vc, doreg[ks], dpacc);
@@ -686,9 +706,10 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
           // the dS arithmetic.
           uint32_t ta[2];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) ta[hh] = lds_addr(Ks + tile_off_col4<D>(kt * 32 + hh * 16 + g * 4 + jj, cq));
+          for (int hh = 0; hh < 2; ++hh) ta[hh] = lds_addr(Ks + tile_off_col4<D>(kperm_row(kt * 32 + hh * 16 + g * 4 + jj), cq));
+          // rows r and r + 8 (r < 8 within its group) sit 2 positions apart
           i16x4 xk[2][4];
-          tr4_issue<0>(ta[0], ta[0] + 8 * RB, xk[0]);
+          tr4_issue<0>(ta[0], ta[0] + 2 * RB, xk[0]);
           // C layout: lane owns query qi; register i is key
           // k0 + kt*32 + 8*(i/4) + 4g + i%4.
           float dsf[16];
@@ -723,7 +744,7 @@ __global__ __launch_bounds__(DQ_BM_BCAST * 2, 1) void dq_bcast_kernel(BwdArgs a)
             constexpr int hh = pc >> 1, hf = pc & 1;
             if constexpr (pc + 1 < 4) {
               constexpr int nh = (pc + 1) >> 1, nf = (pc + 1) & 1;
-              tr4_issue<nf * 128>(ta[nh], ta[nh] + 8 * RB, xk[(pc + 1) & 1]);
+              tr4_issue<nf * 128>(ta[nh], ta[nh] + 2 * RB, xk[(pc + 1) & 1]);
               tr4_wait<4>(xk[pc & 1]);
             } else {
               tr4_wait<0>(xk[pc & 1]);
