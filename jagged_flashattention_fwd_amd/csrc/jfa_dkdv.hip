@@ -1314,9 +1314,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
           // more than one block ahead of the fronts.
           if (i < nb) {
             prep_next(cp, np, has_nxt);
-            issue_now();
+            issue_rows(0, C::CPT);  // Q rows and row terms now, dO rows after the back:
+            issue_vec();            // a workgroup's 56 copies queue behind each other
           }
           back(smem[ring_back], (i - 1) & 1);
+          if (i < nb) issue_rows(C::CPT, 2 * C::CPT);
         }
         if (i < nb) {
           front(masked_tag, m, smem[ring_cmp], i & 1);
