@@ -218,7 +218,10 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
   int g_iss = 0, g_cmp = 0, iss_cur = 0, iss_nxt = 0;
   const int64_t qt_bytes = (int64_t)H * D * tpad;
   const int64_t dot_bytes = BCAST ? (int64_t)a.B * H * D * tpad : (int64_t)H * D * tpad;
-  auto issue_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
+  // part 0: the row copies and the small ones (after a step's first
+  // barrier), 1: the transposed rows (after its second), 2: both.  Splitting
+  // keeps a workgroup's 112 copies from queueing behind each other at once.
+  auto issue_next = [&](const Tp& cp, const Tp& np, bool has_nxt, int part) {
     const int ncur = cp.nj * G, nnxt = np.nj * G;
     const bool cur = iss_cur < ncur;
     if (!(cur || (has_nxt && iss_nxt < nnxt))) return;
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
     const int64_t sc_q = ((int64_t)h * nqb + 2 * j) * D + wave * (2 * D / NW);
     const int64_t sc_d = BCAST ? (((int64_t)p.b * H + h) * nqb + 2 * j) * D + wave * (2 * D / NW) : sc_q;
     const uint32_t buf = lds_addr(smem[(uint32_t)g_iss % NBUF]);
-    {
+    if (part != 1) {
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8 + qrow * D, nrow * (int)rstride);
       const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.do8 + drow * D, nrow * (int)rstride);
       const uint32_t qd = buf + C::OFF_Q + wave * RW * RB, dd = buf + C::OFF_DO + wave * RW * RB;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         dma_copy16_buf(rd, voff_r, (uint32_t)r * rstride, dd + r * RB);
       }
     }
-    {
+    if (part != 0) {
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qt8 + qt_off, (int)min(qt_bytes - qt_off, (int64_t)(TW + 1) * tpad));
       const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dot8 + dot_off, (int)min(dot_bytes - dot_off, (int64_t)(TW + 1) * tpad));
       const uint32_t qd = buf + C::OFF_QT + wave * TW * TB, dd = buf + C::OFF_DOT + wave * TW * TB;
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         dma_copy16_buf(rd, voff_t, (uint32_t)r * tpad, dd + r * TB);
       }
     }
-    if (l < RW) {
+    if (part != 1 && l < RW) {
       const uint32_t so = (uint32_t)l * sstride, sb = (uint32_t)wave * RW * 4;
       dma_copy4_buf(make_rsrc(a.q_scale + qrow * 4, nsc * (int)sstride), so, 0, buf + C::OFF_QS + sb);
       dma_copy4_buf(make_rsrc(a.do_scale + drow * 4, nsc * (int)sstride), so, 0, buf + C::OFF_DOS + sb);
@@ -274,6 +277,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
       dma_copy4_buf(make_rsrc(a.qt_scale + sc_q, 2 * D / NW), (uint32_t)l * 4, 0, buf + C::OFF_QTS + sb);
       dma_copy4_buf(make_rsrc(a.dot_scale + sc_d, 2 * D / NW), (uint32_t)l * 4, 0, buf + C::OFF_DOTS + sb);
     }
+    if (part == 0) return;
     if (cur) ++iss_cur;
     else ++iss_nxt;
     ++g_iss;
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
     {
       const int need = min(DEP, nsteps);
       if (iss_cur < need) {
-        while (iss_cur < need) issue_next(cp, cp, false);
+        while (iss_cur < need) issue_next(cp, cp, false, 2);
         wait_vmcnt<0>();
       } else {
         wait_vmcnt<NST>();
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
       constexpr bool MASKED = decltype(masked_tag)::value;
       if (g_cmp != g_first) wait_step(g_cmp);
       barrier_lds();
-      issue_next(cp, np, has_nxt);
+      issue_next(cp, np, has_nxt, 0);
       const char* buf = smem[(uint32_t)g_cmp % NBUF];
       ++g_cmp;
       const int qbase = (int)((int64_t)j * BQ - base);  // local index of the step's first query
@@ -432,6 +436,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         xc[wave][l] = role ? cpq : cdq;
       }
       barrier_lds();
+      issue_next(cp, np, has_nxt, 1);
       if (!wave_live) return;
       const u32x4 xo = xw[wave ^ (NW / 2)][l];
       const uint32_t xcode = xc[wave ^ (NW / 2)][l];
