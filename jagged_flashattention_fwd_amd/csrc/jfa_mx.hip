@@ -135,17 +135,21 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
     else ++iss_nxt;
     ++g_iss;
   };
-  auto issue_copies = [&]() {
+  auto issue_copies = [&](int part) {  // 0: K and scales, 1: V^T
     if (!j_on) return;
-    const uint32_t kd = j_buf + C::OFF_K + wave * 8 * C::K_RB;
-    dma_copy16_buf(j_rk, voff_k, 0, kd);
-    dma_copy16_buf(j_rk, voff_k, kstride, kd + C::K_RB);
-    const uint32_t vd = j_buf + C::OFF_V + wave * 16 * C::V_RB;
-    dma_copy16_buf(j_rv, voff_v, 0, vd);
-    dma_copy16_buf(j_rv, voff_v, 4 * tpad, vd + 4 * C::V_RB);
-    if (l < 8) {
-      dma_copy4_buf(j_rks, (uint32_t)l * Hkv * 4, 0, j_buf + C::OFF_KS + wave * 32);
-      dma_copy4_buf(j_rvs, (uint32_t)l * 4, 0, j_buf + C::OFF_VS + wave * 32);
+    if (part != 1) {
+      const uint32_t kd = j_buf + C::OFF_K + wave * 8 * C::K_RB;
+      dma_copy16_buf(j_rk, voff_k, 0, kd);
+      dma_copy16_buf(j_rk, voff_k, kstride, kd + C::K_RB);
+      if (l < 8) {
+        dma_copy4_buf(j_rks, (uint32_t)l * Hkv * 4, 0, j_buf + C::OFF_KS + wave * 32);
+        dma_copy4_buf(j_rvs, (uint32_t)l * 4, 0, j_buf + C::OFF_VS + wave * 32);
+      }
+    }
+    if (part != 0) {
+      const uint32_t vd = j_buf + C::OFF_V + wave * 16 * C::V_RB;
+      dma_copy16_buf(j_rv, voff_v, 0, vd);
+      dma_copy16_buf(j_rv, voff_v, 4 * tpad, vd + 4 * C::V_RB);
     }
   };
   auto wait_step = [&](int gi) {
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
       if (iss_cur < need) {
         while (iss_cur < need) {
           prep_next(cp, cp, false);
-          issue_copies();
+          issue_copies(2);
         }
         wait_vmcnt<0>();
       } else {
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
       if (g_cmp != g_first) wait_step(g_cmp);
       barrier_lds();
       prep_next(cp, np, has_nxt);
-      issue_copies();
+      issue_copies(0);
       const char* buf = smem[(uint32_t)g_cmp % NBUF];
       const int kbase = (cp.J0 + j) * BN - (int)s0;  // local index of the step's first key
 
@@ -296,6 +300,7 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
           sacc[kt][i] = x;
           mt = fmaxf(mt, x);
         }
+      issue_copies(1);
       mt = max_across_halves(mt);
       // the running maximum moves in whole numbers, and only past a slack of 8
       if (__builtin_expect(__any(mt > m2 + 8.f), 0)) {

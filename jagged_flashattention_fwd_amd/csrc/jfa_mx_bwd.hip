@@ -586,7 +586,9 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
 
   int g_iss = 0, g_cmp = 0, iss_cur = 0, iss_nxt = 0;
   const int64_t kt_bytes = (int64_t)Hkv * D * tpad;
-  auto issue_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
+  // part 0: K and V rows and their scales (after the step's barrier), 1: the
+  // K^T rows and scales (after the first key half's dS), 2: both.
+  auto issue_next = [&](const Tp& cp, const Tp& np, bool has_nxt, int part) {
     const bool cur = iss_cur < cp.n_kv;
     if (!(cur || (has_nxt && iss_nxt < np.n_kv))) return;
     const Tp& p = cur ? cp : np;
@@ -600,18 +602,25 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k8 + row * D, nrow * (int)kstride);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v8 + row * D, nrow * (int)kstride);
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(a.kt8 + t_off, (int)min(kt_bytes - t_off, (int64_t)(17 * tpad)));
-    const uint32_t kd = buf + C::OFF_K + wave * 8 * RB;
-    dma_copy16_buf(rk, voff_k, 0, kd);
-    dma_copy16_buf(rk, voff_k, kstride, kd + RB);
-    const uint32_t vd = buf + C::OFF_V + wave * 8 * RB;
-    dma_copy16_buf(rv, voff_k, 0, vd);
-    dma_copy16_buf(rv, voff_k, kstride, vd + RB);
+    if (part != 1) {
+      const uint32_t kd = buf + C::OFF_K + wave * 8 * RB;
+      dma_copy16_buf(rk, voff_k, 0, kd);
+      dma_copy16_buf(rk, voff_k, kstride, kd + RB);
+      const uint32_t vd = buf + C::OFF_V + wave * 8 * RB;
+      dma_copy16_buf(rv, voff_k, 0, vd);
+      dma_copy16_buf(rv, voff_k, kstride, vd + RB);
+      if (l < 8) {
+        dma_copy4_buf(make_rsrc(a.k_scale + row * 4, nsc * Hkv * 4), (uint32_t)l * Hkv * 4, 0,
+                      buf + C::OFF_KS + wave * 32);
+        dma_copy4_buf(make_rsrc(a.v_scale + row * 4, nsc * Hkv * 4), (uint32_t)l * Hkv * 4, 0,
+                      buf + C::OFF_VS + wave * 32);
+      }
+    }
+    if (part == 0) return;
     const uint32_t td = buf + C::OFF_KT + wave * 16 * TB;
     dma_copy16_buf(rt, voff_t, 0, td);
     dma_copy16_buf(rt, voff_t, 4 * tpad, td + 4 * TB);
     if (l < 8) {
-      dma_copy4_buf(make_rsrc(a.k_scale + row * 4, nsc * Hkv * 4), (uint32_t)l * Hkv * 4, 0, buf + C::OFF_KS + wave * 32);
-      dma_copy4_buf(make_rsrc(a.v_scale + row * 4, nsc * Hkv * 4), (uint32_t)l * Hkv * 4, 0, buf + C::OFF_VS + wave * 32);
       dma_copy4_buf(make_rsrc(a.kt_scale + ((int64_t)p.hk * nbk + 2 * J) * D + wave * 32, 32), (uint32_t)l * 4, 0,
                     buf + C::OFF_KTS + wave * 32);
     }
@@ -706,7 +715,7 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
     {
       const int need = min(DEP, n_kv);
       if (iss_cur < need) {
-        while (iss_cur < need) issue_next(cp, cp, false);
+        while (iss_cur < need) issue_next(cp, cp, false, 2);
         wait_vmcnt<0>();
       } else if (BCAST) {
         wait_vmcnt<0>();
@@ -737,7 +746,7 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       if (g_cmp != g_first) wait_step(g_cmp);
       barrier_lds();
-      issue_next(cp, np, has_nxt);
+      issue_next(cp, np, has_nxt, 0);
       const char* buf = smem[(uint32_t)g_cmp % NBUF];
       const int kbase = (cp.J0 + j) * BN - (int)s0;
       uint32_t sw[8];
@@ -768,6 +777,7 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) sw[kt * 4 + q] = w[q];
         ssc = g == kt ? code : ssc;
+        if (kt == 0) issue_next(cp, np, has_nxt, 1);
       }
       const i32x8 sop = i32x8{(int)sw[0], (int)sw[1], (int)sw[2], (int)sw[3],
                               (int)sw[4], (int)sw[5], (int)sw[6], (int)sw[7]};
