@@ -208,3 +208,58 @@ def test_mx_backward_prod_bcast_sampled(jfa):
     for h, ri in rows.items():
         for r, i in enumerate(ri):
             _compare(f"prod_bcast dq head {h} row {i}", dq[h, i], ref[h][r], allow[h][r])
+
+
+def test_mx_forward_backward_long_causal_sampled(jfa):
+    """long_causal_8k's shapes (64 sequences of logU[128, 8192] keys, 16
+    heads, self mode, causal) at full size, forward and backward in the
+    launch configuration the bench times: every output finite; three
+    sequences (the shortest and two near 1.5K keys), two heads each, against
+    the oracle.  The backward reads O and lse of the sampled rows from the
+    oracle's MXFP8 forward and the library's own forward elsewhere (rows of
+    other sequences do not enter these sequences' gradients)."""
+    w = wl.workload("long_causal_8k")
+    print("mx long_causal_8k: generating", flush=True)
+    t = wl.make_mx_bwd_workload(w, device="cuda:0")
+    scale = w.scale
+    dev = torch.device("cuda:0")
+    out, lse = jfa.attention_fwd_mxfp8(t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["vt8"], t["vt_scale"],
+                                       t["offsets"], scale, True, False)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    a = _np(t)
+    off = a["offsets"]
+    L = np.diff(off)
+    seqs = [int(np.argmin(L))] + [int(b) for b in np.argsort(np.abs(L - 1500))[:2]]
+    heads = [0, 11]
+    Qr = mo.dequantize_rows(a["q8"], a["q_scale"])
+    Kr = mo.dequantize_rows(a["k8"], a["k_scale"])
+    Vc = mo.dequantize_vt(a["vt8"], a["vt_scale"], t["total_len"])
+    out_in, lse_in = out.clone(), lse.clone()
+    ref_f = {}
+    for b in seqs:
+        s0, s1 = int(off[b]), int(off[b + 1])
+        for h in heads:
+            o, ls, allow = mo.sequence_forward(Qr[s0:s1, h], Kr[s0:s1, h], Vc[s0:s1, h], s0, scale, True)
+            _compare(f"long_causal_8k fwd seq {b} (L={s1 - s0}) head {h} O", out[s0:s1, h].float().cpu().double().numpy(),
+                     o, allow)
+            lerr = float(np.max(np.abs(lse[s0:s1, h].cpu().double().numpy() - ls)))
+            assert lerr <= 2e-2, f"lse {lerr:.3e}"
+            out_in[s0:s1, h] = torch.from_numpy(o).to(torch.bfloat16).to(dev)
+            lse_in[s0:s1, h] = torch.from_numpy(ls).to(torch.float32).to(dev)
+    print("mx long_causal_8k: backward", flush=True)
+    g = {n: t[n] for n in ENC}
+    dq, dk, dv = jfa.attention_bwd_mxfp8(g, t["offsets"], scale, True, False, out_in, lse_in)
+    torch.cuda.synchronize()
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(x).all()), f"{name} has non-finite values"
+    o64 = out_in.float().cpu().double().numpy()
+    l64 = lse_in.cpu().double().numpy()
+    deq = mo.dequantize_backward_inputs(a, False)
+    for b in seqs:
+        s0, s1 = int(off[b]), int(off[b + 1])
+        for h in heads:
+            r = mo.backward_item(a, deq, o64, l64, b, h, scale, True, False)
+            for i, (name, x) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+                _compare(f"long_causal_8k seq {b} (L={s1 - s0}) head {h} {name}",
+                         x[s0:s1, h].cpu().double().numpy(), r[i], r[3 + i])
