@@ -369,7 +369,13 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   const int64_t T = *a.n_tiles;
   const int H = a.H, Lq = a.Lq;
   const int64_t ld = (int64_t)a.Hkv * D;  // K / V row stride (elements)
-  const float c2 = a.scale_log2;
+  // A negative scale is folded into Q: the sign bits of the Q operand are
+  // flipped at its load, so that every score below is (-q) k with the
+  // scale's magnitude, and the softmax keeps one form (the row maximum of
+  // the raw scores).  The products are exact; the matrix unit's sums of
+  // them may round differently from those of q k, within the same error.
+  const float c2 = __builtin_fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   // This lane's source byte offset within a K copy (304-byte rows in LDS)
   // and a V copy (320-byte rows), relative to the copy's first row.
   const uint32_t rstride = (uint32_t)(ld * 2);
@@ -413,15 +419,23 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   // The prepared step: buffer resources over this wave's K and V source
   // rows of it (the rows that exist, at most RPW + 1: a copy's overhang
   // reaches one row past the run; rows past the sequence end read as
-  // zeros), its ring buffer, and whether there is one.
+  // zeros) and its ring buffer.  Past the stream's last step the copies
+  // still go out, over empty ranges (they read nothing and at most write
+  // zeros into the ring buffer the next step would take, which no wave
+  // reads again), so that no branch splits the code they sit in.
   __amdgpu_buffer_rsrc_t j_rk = make_rsrc(a.k, 0), j_rv = make_rsrc(a.v, 0);
   uint32_t j_kd = 0, j_vd = 0;
-  bool j_on = false;
   auto prep_next = [&](const Tp& cp, const Tp& np, bool has_nxt) {
     const int nn = has_nxt ? np.n_kv - np.j0 : 0;
     const bool cur = iss_cur < cp.n_kv - cp.j0;
-    j_on = cur || iss_nxt < nn;
-    if (!j_on) return;
+    const int buf = (int)((uint32_t)g_iss % NBUF);
+    j_kd = lds_addr(smem_k[buf]) + wave * RPW * RB;
+    j_vd = lds_addr(smem_v[buf]) + wave * RPW * RBV;
+    if (!(cur || iss_nxt < nn)) {
+      j_rk = make_rsrc(a.k, 0);
+      j_rv = make_rsrc(a.v, 0);
+      return;
+    }
     const int L_ = cur ? cp.L : np.L;
     const int j = cur ? cp.j0 + iss_cur : np.j0 + iss_nxt;
     const int base_row = j * BN + wave * RPW;
@@ -430,9 +444,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     const uint64_t roff = (uint64_t)(uint32_t)base_row * rstride;
     j_rk = make_rsrc(reinterpret_cast<const char*>(cur ? cp.kb : np.kb) + roff, rows * (int)rstride);
     j_rv = make_rsrc(reinterpret_cast<const char*>(cur ? cp.vb : np.vb) + roff, rows * (int)rstride);
-    const int buf = (int)((uint32_t)g_iss % NBUF);
-    j_kd = lds_addr(smem_k[buf]) + wave * RPW * RB;
-    j_vd = lds_addr(smem_v[buf]) + wave * RPW * RBV;
     if (cur) ++iss_cur;
     else ++iss_nxt;
     ++g_iss;
@@ -440,7 +451,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
   // Copies [k0, k1) of the prepared step (K for k < CPT, V after); the
   // copy's first row goes into the scalar offset.
   auto issue_copies = [&](int k0, int k1) {
-    if (!j_on) return;
 #pragma unroll
     for (int k = k0; k < k1; ++k) {
       const int R = PadRowCopy::start(k % C::CPT, RPW);
@@ -460,8 +470,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       qi = qi < nq ? qi : p.q0 < nq ? p.q0 : 0;
       const uint16_t* qrow = BCAST ? a.q + ((int64_t)p.h * Lq + qi) * D : a.q + ((p.s0 + qi) * H + p.h) * (int64_t)D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qreg[s][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8));
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] ^= qsign;
+        qreg[s][ks] = __builtin_bit_cast(bf16x8, x);
+      }
     }
   };
 
@@ -591,8 +605,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // causal diagonal steps take the masked body.
     // S^T = K Q^T of stream step gi into sacc; the K operand of k-step
     // ks + 1 is read before the products of k-step ks, and hook(ks) runs
-    // after them.
-    auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook) {
+    // after them; the prepared step's copies go out between the k-steps
+    // when COPY is true.
+    auto s_phase = [&](int gi, f32x16 (&sacc)[2][QS], auto&& hook, auto copy_tag) {
+      constexpr bool COPY = decltype(copy_tag)::value;
       const char* Ks = smem_k[(uint32_t)gi % NBUF];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -613,7 +629,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
 #pragma unroll
           for (int s = 0; s < QS; ++s) sacc[kt][s] = mfma32(ka[kt], qreg[s][ks], sacc[kt][s]);
         constexpr int PER = (2 * C::CPT + KS - 1) / KS;
-        issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
+        if constexpr (COPY) issue_copies(ks * PER, min((ks + 1) * PER, 2 * C::CPT));
         hook(ks_tag);
         if constexpr (ks + 1 < KS) {
           ka[0] = kn[0];
@@ -686,16 +702,15 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
         // ---- S^T = K Q^T : two 32-key subtiles x QS query subtiles; the
         // next step's copies are issued between the k-steps.
         f32x16 sacc[2][QS];
-        s_phase(g_cmp, sacc, [](auto) {});
+        s_phase(g_cmp, sacc, [](auto) {}, std::true_type{});
         // ---- online softmax, one query per lane (both halves of a row agree).
         uint32_t pk[2][2][QS][4];  // [kt][k-half][s][bf16 pairs]
 #pragma unroll
         for (int s = 0; s < QS; ++s) {
           const int qi = wq0 + s * 32 + lc;
           // Row maximum in exp2 units.  Unmasked steps reduce the raw
-          // scores (the maximum for a non-negative scale, the minimum for a
-          // negative one) and fold the scale into the exponent's fma below;
-          // masked steps scale first and set masked scores to -inf.
+          // scores and fold the scale into the exponent's fma below; masked
+          // steps scale first and set masked scores to -inf.
           float mt;
           if constexpr (MASKED) {
             mt = -INFINITY;
@@ -712,21 +727,12 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
               }
             mt = max_across_halves(mt);
           } else {
-            if (c2 >= 0.f) {
-              float r = -INFINITY;
+            float r = -INFINITY;
 #pragma unroll
-              for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) r = fmaxf(r, sacc[kt][s][i]);
-              mt = max_across_halves(r) * c2;
-            } else {
-              float r = INFINITY;
-#pragma unroll
-              for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) r = fminf(r, sacc[kt][s][i]);
-              mt = min_across_halves(r) * c2;
-            }
+              for (int i = 0; i < 16; ++i) r = fmaxf(r, sacc[kt][s][i]);
+            mt = max_across_halves(r) * c2;
           }
           const bool need = mt > m2[s] + RESCALE_SLACK;
           if (__builtin_expect(__any(need), 0)) {
@@ -810,14 +816,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
               sacc[kt][s][i] = x;
               r = fmaxf(r, x);
             }
-          } else if (c2 >= 0.f) {
+          } else {
             r = kt == 0 ? -INFINITY : rmax[s];
 #pragma unroll
             for (int i = 0; i < 16; ++i) r = fmaxf(r, sacc[kt][s][i]);
-          } else {
-            r = kt == 0 ? INFINITY : rmax[s];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) r = fminf(r, sacc[kt][s][i]);
           }
           rmax[s] = r;
         }
@@ -828,7 +830,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
         for (int s = 0; s < QS; ++s) {
           float mt;
           if constexpr (MASKED) mt = max_across_halves(rmax[s]);
-          else mt = (c2 >= 0.f ? max_across_halves(rmax[s]) : min_across_halves(rmax[s])) * c2;
+          else mt = max_across_halves(rmax[s]) * c2;
           const bool need = mt > m2[s] + RESCALE_SLACK;
           if (__builtin_expect(__any(need), 0)) {
             const float alpha = need ? fast_exp2(m2[s] - mt) : 1.f;
@@ -886,7 +888,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
           }
           if constexpr (ks >= 2 && ks < 6) sm_exp(F{}, sa, (ks - 2) >> 1, (ks - 2) & 1, pk);
           if constexpr (ks == 6) sm_sum();
-        });
+        }, std::true_type{});
         pv_phase(gj, pk);
         ++g_cmp;
       };
@@ -909,8 +911,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
       // prologue: step 0's S products, with no copies (each tile issues
       // one copy step per iteration and one in its last step)
       barrier_lds();
-      j_on = false;
-      s_phase(g_first, sa, [](auto) {});
+      s_phase(g_first, sa, [](auto) {}, std::false_type{});
       int j = 0;
       for (; j + 2 < n_kv; j += 2) {
         iter(j, sa, sb);
@@ -934,7 +935,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void fwd_kernel_dma(FwdArgs a, const 
     // Tile end: the next tile's Q rows, then this tile's O and lse.
     if (has_nxt) load_q(np);
     store_out(cp, nq);
-    if (!has_nxt) break;
+    if (!has_nxt) {
+      wait_vmcnt<0>();  // no copy into LDS outlives the workgroup
+      break;
+    }
     cp = np;
     iss_cur = iss_nxt;
     iss_nxt = 0;
