@@ -331,15 +331,16 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
         bm = max_across_halves(bm);
         const uint32_t be = __float_as_uint(bm) >> 23;  // biased exponent of the block maximum
         const bool live = be >= 27u;                      // maximum at least 2^-100, else the block is 0
-        const float inv = live ? __uint_as_float((262u - be) << 23) : 0.f;  // 2^(8 - floor(log2 bm))
-        const uint32_t code = live ? be - 8u : 127u;                          // E8M0 of 2^(floor(log2 bm) - 8)
+        const float cap = live ? mx_block_cap(be) : 0.f;  // 448 times the block scale, before the division
+        const float scale = live ? mx_block_scale(be) : 1.f;
+        const uint32_t code = live ? be - 8u : 127u;      // E8M0 of 2^(floor(log2 bm) - 8)
         pscale = g == kt ? code : pscale;
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float* v = p + 4 * q;
-          uint32_t x = cvt_e4m3x2<false>(fminf(v[0] * inv, 448.f), fminf(v[1] * inv, 448.f), 0u);
-          w[q] = cvt_e4m3x2<true>(fminf(v[2] * inv, 448.f), fminf(v[3] * inv, 448.f), x);
+          uint32_t x = cvt_e4m3x2_scaled<false>(fminf(v[0], cap), fminf(v[1], cap), scale, 0u);
+          w[q] = cvt_e4m3x2_scaled<true>(fminf(v[2], cap), fminf(v[3], cap), scale, x);
         }
         // lo = keys 4g + {0..3, 8..11}, hi = keys 16 + 4g + {0..3, 8..11}:
         // the lower half takes the upper half's lo, the upper half the

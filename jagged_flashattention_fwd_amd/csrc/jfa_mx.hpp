@@ -44,12 +44,24 @@ __device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SA, sa, SB, sb);
 }
 
-// Two floats to two E4M3 codes in byte pair HI of `old` (nearest, ties to
-// even; callers keep the values within +-448).
+// a / 2^k and b / 2^k as two E4M3 codes in byte pair HI of `old`, with k
+// the exponent of `scale` (only the scale's exponent counts: a scale of 3
+// acts as 2), in one instruction (v_cvt_scalef32_pk_fp8_f32: nearest, ties
+// to even, E4M3 denormals kept, no saturation: past 464 * 2^k the code is
+// NaN, so callers keep |a|, |b| within 448 * 2^k).
 template <bool HI>
-__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b, uint32_t old) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+__device__ __forceinline__ uint32_t cvt_e4m3x2_scaled(float a, float b, float scale, uint32_t old) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2, old), a, b, scale, HI);
+  return __builtin_bit_cast(uint32_t, r);
 }
+
+// Of a block whose largest magnitude has biased exponent be (the block is
+// live: be >= 27): the scale 2^(floor(log2 amax) - 8) as a float, and the cap
+// 448 times it, 1.75 * 2^floor(log2 amax), applied before the division (exact:
+// the division is by a power of two).
+__device__ __forceinline__ float mx_block_scale(uint32_t be) { return __uint_as_float((be - 8u) << 23); }
+__device__ __forceinline__ float mx_block_cap(uint32_t be) { return __uint_as_float((be << 23) | 0x600000u); }
 
 // One 32-element MX block held as 16 floats in each of two lanes (lane n
 // and n + 32: the product output layout above, rows (i / 4) * 8 + 4 g +
@@ -67,17 +79,19 @@ __device__ __forceinline__ void quantize_block32(const float (&x)[16], uint32_t 
   am = max_across_halves(am);
   const uint32_t be = __float_as_uint(am) >> 23;  // biased exponent of the block maximum
   const bool live = be >= 27u;
-  const float inv = live ? __uint_as_float((262u - be) << 23) : 0.f;  // 2^(8 - floor(log2 amax))
-  *code = live ? be - 8u : 127u;                                     // E8M0 of 2^(floor(log2 amax) - 8)
+  // a dead block: every element capped to 0
+  const float cap = live ? mx_block_cap(be) : 0.f;
+  const float scale = live ? mx_block_scale(be) : 1.f;
+  *code = live ? be - 8u : 127u;  // E8M0 of 2^(floor(log2 amax) - 8)
   uint32_t c[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float* v = x + 4 * q;
     float a[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = SIGNED ? fminf(fmaxf(v[e] * inv, -448.f), 448.f) : fminf(v[e] * inv, 448.f);
+    for (int e = 0; e < 4; ++e) a[e] = SIGNED ? __builtin_amdgcn_fmed3f(v[e], -cap, cap) : fminf(v[e], cap);
     const float a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
-    c[q] = cvt_e4m3x2<true>(a2, a3, cvt_e4m3x2<false>(a0, a1, 0u));
+    c[q] = cvt_e4m3x2_scaled<true>(a2, a3, scale, cvt_e4m3x2_scaled<false>(a0, a1, scale, 0u));
   }
   // c[q] holds rows 8 q + 4 g + {0..3} (q = 0, 1: first 16, q = 2, 3: the
   // others): the lower half takes the upper half's first words, the upper
