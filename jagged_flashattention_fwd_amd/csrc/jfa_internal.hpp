@@ -116,7 +116,7 @@ struct BwdMxArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;           // [rows] scratch
+  float* delta;           // [rows] scratch: -delta (the dP products start from it)
   float* lse2;            // [rows] scratch: lse * log2(e)
   float* dq_part;         // broadcast-mode dQ partials, as in BwdArgs
   const int* seq_order;

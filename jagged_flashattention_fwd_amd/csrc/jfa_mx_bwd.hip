@@ -63,8 +63,10 @@ __device__ __forceinline__ uint32_t trow_voff(int l, uint32_t stride) {
 }
 
 // ---------------------------------------------------------------- delta --
-// delta = sum over d of dequant(dO) o O, and lse * log2(e), per query row.
-// Eight threads per row of 128, 16 elements (half a scale block) each.
+// -delta, delta = sum over d of dequant(dO) o O, and lse * log2(e), per
+// query row (the dP products of both kernels below start from -delta, so
+// that dS = P o dP' takes no subtraction).  Eight threads per row of 128,
+// 16 elements (half a scale block) each.
 __global__ __launch_bounds__(256) void delta_mx_kernel(const uint16_t* __restrict__ out,
                                                        const uint8_t* __restrict__ do8,
                                                        const uint8_t* __restrict__ do_scale,
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void delta_mx_kernel(const uint16_t* __restric
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
     if (c == 0) {
-      delta[row] = acc;
+      delta[row] = -acc;
       lse2[row] = lse[row] * LOG2E;
     }
   }
@@ -120,7 +122,7 @@ struct MxB {
   static constexpr int OFF_QTS = OFF_DOS + BQ * 4;         // Q^T scales [2 query blocks][128 d]
   static constexpr int OFF_DOTS = OFF_QTS + 2 * D;         // dO^T scales
   static constexpr int OFF_L = OFF_DOTS + 2 * D;           // lse * log2(e) [64]
-  static constexpr int OFF_DL = OFF_L + BQ * 4;            // delta [64]
+  static constexpr int OFF_DL = OFF_L + BQ * 4;            // -delta [64]
   static constexpr int BUF = OFF_DL + BQ * 4;
   // Copies per wave per step: Q, dO, Q^T, dO^T, and one dword copy each of
   // the four scale arrays, lse and delta.
@@ -405,16 +407,23 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         const char* dr = buf + C::OFF_DO + (qt * 32 + lc) * RB;
         const uint32_t qsw = *reinterpret_cast<const uint32_t*>(buf + C::OFF_QS + (qt * 32 + lc) * 4) >> (8 * g);
         const uint32_t dsw = *reinterpret_cast<const uint32_t*>(buf + C::OFF_DOS + (qt * 32 + lc) * 4) >> (8 * g);
+        // dP' = dP - delta: the products start from the rows' -delta
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(buf + C::OFF_DL + (qt * 32 + r * 8 + 4 * g) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[r * 4 + e] = nd[e];
+        }
         f32x16 s = mfma_mx<0, 0>(lds_read32x2(qr + 16 * g, qr + 32 + 16 * g), kop[0], f32x16{}, (int)qsw, (int)ksc);
         s = mfma_mx<2, 2>(lds_read32x2(qr + 64 + 16 * g, qr + 96 + 16 * g), kop[1], s, (int)qsw, (int)ksc);
-        f32x16 dp = mfma_mx<0, 0>(lds_read32x2(dr + 16 * g, dr + 32 + 16 * g), vop[0], f32x16{}, (int)dsw, (int)vsc);
+        dp = mfma_mx<0, 0>(lds_read32x2(dr + 16 * g, dr + 32 + 16 * g), vop[0], dp, (int)dsw, (int)vsc);
         dp = mfma_mx<2, 2>(lds_read32x2(dr + 64 + 16 * g, dr + 96 + 16 * g), vop[1], dp, (int)dsw, (int)vsc);
         float p[16], ds[16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = qt * 32 + r * 8 + 4 * g;
           const f32x4 lv = *reinterpret_cast<const f32x4*>(buf + C::OFF_L + row * 4);
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(buf + C::OFF_DL + row * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = r * 4 + e;
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
               pv = ok ? pv : 0.f;
             }
             p[i] = pv;
-            ds[i] = pv * (dp[i] - dl[e]);
+            ds[i] = pv * dp[i];
           }
         }
         quantize_block32<false>(p, wq, &cpq);
@@ -639,7 +648,7 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
   // queries read the block's first row; they are never stored.
   i32x8 qop[2], dop[2];
   uint32_t qsc = 0, dsc = 0;
-  float lq2 = 0.f, dlt = 0.f;
+  float lq2 = 0.f, dlt = 0.f;  // lse * log2(e) and -delta of this lane's row
   auto load_q = [&](const Tp& p) {
     const int nq = BCAST ? Lq : p.L;
     int qi = p.q0 + wave * 32 + lc;
@@ -740,6 +749,11 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) asm volatile("" : "+v"(qop[kk]), "+v"(dop[kk]));
     asm volatile("" : "+v"(qsc), "+v"(dsc), "+v"(lq2), "+v"(dlt));
+    // dP' = dP - delta of this lane's row: the dP products of every step
+    // start from it
+    f32x16 ndel;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndel[i] = dlt;
     const int g_first = g_cmp;
 
     auto kv_step = [&](int j, auto masked_tag) {
@@ -759,7 +773,7 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
         const uint32_t vsw = *reinterpret_cast<const uint32_t*>(buf + C::OFF_VS + (kt * 32 + lc) * 4) >> (8 * g);
         f32x16 s = mfma_mx<0, 0>(lds_read32x2(kr + 16 * g, kr + 32 + 16 * g), qop[0], f32x16{}, (int)ksw, (int)qsc);
         s = mfma_mx<2, 2>(lds_read32x2(kr + 64 + 16 * g, kr + 96 + 16 * g), qop[1], s, (int)ksw, (int)qsc);
-        f32x16 dp = mfma_mx<0, 0>(lds_read32x2(vr + 16 * g, vr + 32 + 16 * g), dop[0], f32x16{}, (int)vsw, (int)dsc);
+        f32x16 dp = mfma_mx<0, 0>(lds_read32x2(vr + 16 * g, vr + 32 + 16 * g), dop[0], ndel, (int)vsw, (int)dsc);
         dp = mfma_mx<2, 2>(lds_read32x2(vr + 64 + 16 * g, vr + 96 + 16 * g), dop[1], dp, (int)vsw, (int)dsc);
         float ds[16];
 #pragma unroll
@@ -770,7 +784,7 @@ __global__ __launch_bounds__(MxQ::NW * WAVE, 1) void dq_mx_kernel(BwdMxArgs a) {
             const bool ok = key >= 0 && key < L && (!CAUSAL || key <= qrow);
             pv = ok ? pv : 0.f;
           }
-          ds[i] = pv * (dp[i] - dlt);
+          ds[i] = pv * dp[i];
         }
         uint32_t w[4], code;
         quantize_block32<true>(ds, w, &code);
