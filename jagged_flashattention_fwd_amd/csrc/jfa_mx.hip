@@ -66,7 +66,11 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
   const int64_t T = *a.n_tiles;
   const int H = a.H, Lq = a.Lq, Hkv = a.Hkv;
   const int64_t total = a.total_len;
-  const float c2 = a.scale_log2;
+  // A negative scale is folded into Q: the sign bits of its E4M3 codes flip
+  // at its load (exact), so that every score below is (-q) k with the
+  // scale's magnitude and the softmax keeps one form.
+  const float c2 = __builtin_fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80808080u : 0u;
 
   const int64_t t0 = zigzag_tile(0, slot, a.P);
   if (t0 >= T) return;
@@ -173,7 +177,8 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
     for (int kk = 0; kk < 2; ++kk) {
       const u32x4 x0 = *reinterpret_cast<const u32x4*>(qr + 64 * kk + 16 * g);
       const u32x4 x1 = *reinterpret_cast<const u32x4*>(qr + 64 * kk + 32 + 16 * g);
-      qop[kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      qop[kk] = i32x8{(int)(x0[0] ^ qsign), (int)(x0[1] ^ qsign), (int)(x0[2] ^ qsign), (int)(x0[3] ^ qsign),
+                      (int)(x1[0] ^ qsign), (int)(x1[1] ^ qsign), (int)(x1[2] ^ qsign), (int)(x1[3] ^ qsign)};
     }
     qsc = *reinterpret_cast<const uint32_t*>(a.q_scale + row * 4) >> (8 * g);
   };
@@ -285,23 +290,28 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
         sacc[kt] = mfma_mx<0, 0>(k0, qop[0], f32x16{}, (int)ksw, (int)qsc);
         sacc[kt] = mfma_mx<2, 2>(k1, qop[1], sacc[kt], (int)ksw, (int)qsc);
       }
-      // ---- row maximum (log2 units), masked keys at -inf
+      // ---- row maximum (log2 units).  Unmasked steps reduce the raw scores
+      // and fold the scale into the exponent's fma below; masked steps scale
+      // first and set masked keys to -inf.
       float mt = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float x = sacc[kt][i] * c2;
           if constexpr (MASKED) {
+            float x = sacc[kt][i] * c2;
             const int key = kbase + kt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
             const bool ok = key >= 0 && key < L && (!CAUSAL || key <= qrow);
             x = ok ? x : -INFINITY;
+            sacc[kt][i] = x;
+            mt = fmaxf(mt, x);
+          } else {
+            mt = fmaxf(mt, sacc[kt][i]);
           }
-          sacc[kt][i] = x;
-          mt = fmaxf(mt, x);
         }
       issue_copies(1);
       mt = max_across_halves(mt);
+      if constexpr (!MASKED) mt *= c2;
       // the running maximum moves in whole numbers, and only past a slack of 8
       if (__builtin_expect(__any(mt > m2 + 8.f), 0)) {
         if (mt > m2 + 8.f) {
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(Mx::NW * WAVE, 1) void fwd_mx_kernel(FwdMxArgs a, c
         float bm = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(sacc[kt][i] - mref);
+          p[i] = MASKED ? fast_exp2(sacc[kt][i] - mref) : fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -mref));
           ls += p[i];
           bm = fmaxf(bm, p[i]);
         }
