@@ -101,12 +101,14 @@ __global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Sch
   // wave, then the totals of the waves before.
   const int per = (B + SORT_THREADS - 1) / SORT_THREADS;
   const int r0 = tid * per, r1 = min(B, r0 + per);
+  // a sequence's length comes back out of its key (every length is at
+  // most total_len, below 2^31)
+  auto len_of = [](unsigned long long key) { return (int64_t)(0xffffffffull - (key >> 32)); };
   int64_t local = 0;
   for (int r = r0; r < r1; ++r) {
     const int b = (int)(keys[r] & 0xffffffffull);
     s.order[r] = b;
-    int64_t s0;
-    local += tiles_of(seq_range(a.offsets, b, a.total_len, &s0), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
+    local += tiles_of(len_of(keys[r]), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
   }
   const int lane = tid % WAVE, wv = tid / WAVE;
   int64_t incl = local;
@@ -126,9 +128,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sched_sort_scan(SchedArgs a, Sch
   int64_t run = before + incl - local;  // exclusive prefix of this chunk
   for (int r = r0; r < r1; ++r) {
     s.cum[r] = run < s.max_tiles ? run : s.max_tiles;
-    const int b = (int)(keys[r] & 0xffffffffull);
-    int64_t s0;
-    run += tiles_of(seq_range(a.offsets, b, a.total_len, &s0), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
+    run += tiles_of(len_of(keys[r]), a.H, a.Lq, a.broadcast_q, a.pass, a.blk);
   }
   if (tid == SORT_THREADS - 1) {
     const int64_t T = total < s.max_tiles ? total : s.max_tiles;
