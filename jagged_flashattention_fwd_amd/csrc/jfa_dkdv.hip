@@ -5,6 +5,10 @@
 // "2-CTA collaborative MMA (backward)"; the tiles follow the K/V-outer,
 // dense-Q-inner loop of "Scheduling jagged tiles across SMs").
 //
+// d = 64 runs dkdv_kernel, described here; d = 128 runs dkdv_pair_kernel (its
+// own description below), which splits each 32-key group's work between two
+// waves of one SIMD.
+//
 // dkdv_kernel is persistent.  A tile is 128 keys of one (sequence, head); each
 // of the 4 waves keeps its 32 keys' K and V rows in registers as MFMA
 // operands and accumulates their dK^T / dV^T.  Query blocks of 64 rows (Q, dO

@@ -19,17 +19,20 @@
 // even, capped at 448).  The softmax scale multiplies dK and dQ.
 //
 // Kernels, in launch order:
-//   delta_mx_kernel  delta and lse * log2(e) per query row.
+//   delta_mx_kernel  -delta (the dP products below start from it) and
+//                    lse * log2(e) per query row.
 //   dkdv_mx_kernel   persistent over tiles of 128 keys of one (sequence,
-//                    key / value head), four waves with one wave per SIMD
-//                    (two would not hold the two float32 accumulators of 32
-//                    keys x 128 beside the operands): each wave holds 32
-//                    keys' row-wise K
-//                    and V in registers and streams the group's query heads
-//                    in steps of 64 queries through LDS (row-wise Q and dO,
-//                    query-blocked Q^T and dO^T, their scales, lse and
-//                    delta).  A lane owns one key, so the quantization along
-//                    the queries is a per-lane block of the score layout.
+//                    key / value head), eight waves in four pairs of 32
+//                    keys, two waves per SIMD: both waves of a pair hold the
+//                    keys' row-wise K and V in registers, one takes the
+//                    first 32 queries of each step and accumulates dV, the
+//                    other the last 32 and accumulates dK, and each hands its
+//                    partner the quantized block the partner's product
+//                    needs.  The group's query heads stream in steps of 64
+//                    queries through LDS (row-wise Q and dO, query-blocked
+//                    Q^T and dO^T, their scales, lse and -delta).  A lane
+//                    owns one key, so the quantization along the queries is
+//                    a per-lane block of the score layout.
 //   dq_mx_kernel     the forward's structure: a lane owns one query row,
 //                    keys stream in steps of 64 of the packed index (row-wise
 //                    K and V, key-blocked K^T).  Self mode: persistent over
