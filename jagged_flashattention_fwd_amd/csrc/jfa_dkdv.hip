@@ -810,16 +810,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, const TileRec* 
 // SIMD and one's vector work runs beside the other's matrix products:
 //   score wave (waves 0-3):    K rows of its keys; S = Q K^T (+ the -lse /
 //                              scale row terms), P = exp2(c S'), masked;
-//                              P to LDS; dV^T += dO^T P.
+//                              P to LDS; dV += P^T dO.
 //   gradient wave (waves 4-7): V rows of the same keys; dP = dO V^T (+ the
 //                              -delta row terms); after P arrives,
-//                              dS = P o dP', dK^T += Q^T dS.
+//                              dS = P o dP', dK += dS^T Q.
 // P passes lane to lane (both waves own the same key per lane and the same
-// query rows per register), through a 32 KB area that also stages the tile's
-// dK / dV stores.  Each wave holds one operand set (K or V) and one fp32
-// accumulator (dV or dK), half of dkdv_kernel's, so that it fits in the 256
-// registers of a wave sharing its SIMD.  Per block: the ring barrier, the
-// scores and products of both subtiles, the hand-over barrier, then dV or dK.
+// query rows per register), through a 32 KB area.  Each wave holds one
+// operand set (K or V) and one fp32 accumulator (dV or dK, key by d, so that
+// its stores write whole 128-byte rows straight from the registers), half of
+// dkdv_kernel's, so that it fits in the 256 registers of a wave sharing its
+// SIMD.  The iterations are software-pipelined (the back of one block beside
+// the front of the next) in one stream across tiles: between two tiles a
+// transition runs the back of one tile's last block beside the front of the
+// next tile's first, and the finished tile's stores drain during the next
+// iteration.
 struct Pair {
   static constexpr int NW = 8, NG = 4;  // waves; key groups of 32 keys (one score + one gradient wave each)
   static constexpr int QB = BWD_QB, BN = BWD_BN, D = 128, KS = 8, DT = 4;
@@ -839,10 +843,9 @@ struct Pair {
   static constexpr int XBYTES = 2 * 2 * NG * 4 * WAVE * 8;
   static_assert(RB == 19 * 16 && RPW >= 3, "copy geometry");
   static_assert(NBUF * BUF + XBYTES + 64 <= 160 * 1024, "LDS");
-  static_assert(NW * 32 * 32 * 4 <= XBYTES, "the store staging fits the hand-over area");
   // Q / dO tiles are read both ways: 16-byte reads of 16 consecutive query
   // rows (S = Q K^T, dP = dO V^T) and transposing reads of 4 consecutive
-  // rows x 64 bytes per 32 lanes (dV^T += dO^T P, dK^T += Q^T dS).  Query
+  // rows x 64 bytes per 32 lanes (dV += P^T dO, dK += dS^T Q).  Query
   // row r of a tile sits at row position perm(r): within each group of 16
   // rows the 4 x 4 transpose (r = 4 m + i at 4 i + m).  Any 16 consecutive
   // rows then still take 16 distinct positions modulo 16, and 4 consecutive
@@ -1033,336 +1036,405 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
     for (int ks = 0; ks < KS; ++ks) kvraw[ks] = *reinterpret_cast<const u32x4*>(r + ks * 16);
   };
 
-  // dV (score wave) or scale * dK (gradient wave) of this wave's keys:
-  // each 32 x 32 chunk is transposed through the wave's 4 KB of the
-  // hand-over area (16-byte chunks XOR-swizzled by key; every wave has read
-  // its P when this runs) and leaves as whole 128-byte segments of 8 keys;
-  // bounded buffer stores, 4 * DT per wave.
+  // dV (score wave) or scale * dK (gradient wave) of this wave's keys.  The
+  // accumulators hold them key by d: register 4 i4 + e of head-dim tile dt
+  // is key 8 i4 + 4 g + e of the wave's 32 at d = 32 dt + lc, so each
+  // 4-byte store writes two whole 128-byte runs (lanes 0-31 one key, lanes
+  // 32-63 the key 4 further); bounded buffer stores (keys past the sequence
+  // end are dropped), 16 * DT per wave.  A store's byte offset is this
+  // lane's part (key kgrp * 32 + 4 g, d = lc) plus the register's, added per
+  // store, so that the whole offset stays in the lane operand, which the
+  // range check covers; st_base hides the lane part from loop-invariant
+  // hoisting, which would keep all the sums live.
+  const uint32_t st_lane = (uint32_t)(((kgrp * 32 + 4 * g) * a.Hkv * D + lc) * 4);
+  auto st_base = [&]() {
+    uint32_t b = st_lane;
+    asm volatile("" : "+v"(b));
+    return b;
+  };
   auto store_acc = [&](const Tp& p, int nvalid, const f32x16 (&acc)[DT]) {
     const int64_t row0 = (p.s0 + p.k0) * a.Hkv + p.hk;  // dK / dV are [total_len, H_kv, d]
     const int nrec = nvalid * a.Hkv * D * 4;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc((grad ? a.dk : a.dv) + row0 * D, nrec);
     const float mul = grad ? a.scale : 1.0f;
-    char* const st = xchg + wave * 4096;
-    auto row_at = [&](int kr) { return reinterpret_cast<float*>(st + kr * 128); };
-    const int rk8 = l >> 3, rc = l & 7;
+    const uint32_t sb = st_base();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        f32x4 v;
+      for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[dt][i4 * 4 + e] * mul;
-        *reinterpret_cast<f32x4*>(row_at(lc) + (((2 * i4 + g) ^ (lc & 7)) << 2)) = v;
-      }
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[dt][i4 * 4 + e] * mul), rs,
+                                                sb + (uint32_t)(((8 * i4 + e) * a.Hkv * D + dt * 32) * 4), 0, 0);
+  };
+  // Zero dV / dK for a tile without query blocks: 16-byte stores of whole
+  // 128-byte runs (lane l: key l / 8 of each group of 8, chunk l % 8).
+  auto store_zero = [&](const Tp& p, int nvalid) {
+    const int64_t row0 = (p.s0 + p.k0) * a.Hkv + p.hk;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((grad ? a.dk : a.dv) + row0 * D, nvalid * a.Hkv * D * 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = r * 8 + rk8;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(row_at(kr) + ((rc ^ (kr & 7)) << 2));
-        const int off = ((kgrp * 32 + kr) * a.Hkv * D + dt * 32 + rc * 4) * 4;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
-      }
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rs,
+                                               (uint32_t)(((kgrp * 32 + r * 8 + (l >> 3)) * a.Hkv * D + dt * 32 + (l & 7) * 4) * 4), 0, 0);
   };
 
   Tp cp = tparams(tiles[t0]);
-  load_rows(cp);
-  {
-    f32x16 z[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
-    store_acc(cp, 0, z);  // stores that write nothing: the first tile start waits like every later one
-  }
 
   constexpr bool DYN = CAUSAL || !BCAST;
   __shared__ int s_next;
   unsigned int fetched = 0;
-  for (int64_t pass = 0;; ++pass) {
-    const int64_t tn0 = zigzag_tile(pass + 1, slot, a.P);
-    bool has_nxt = !DYN && tn0 < T;
-    Tp np = has_nxt ? tparams(tiles[tn0]) : cp;
-    auto handoff = [&]() {
-      if constexpr (DYN) {
-        const int64_t tn = pass == 0 ? tn0 : 2 * (int64_t)a.P + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
-        has_nxt = tn < T;
-        if (has_nxt && wave == 0 && l == 0) fetched = atomicAdd(a.ktile_ctr, 1u);
-        if (has_nxt) np = tparams(tiles[tn]);
-      }
-    };
-    int vm_last = 0;
-    const int L = cp.L;
-    const int k0 = cp.k0;
-    const int kw = k0 + kgrp * 32 + lc;  // this lane's key
-    const bool key_ok = kw < L;
-    const int nq = BCAST ? Lq : L;
-    const int m_first = cp.m_first, m_end = cp.m_end;
-    const int nbh = cp.nbh, nb = cp.nb;  // blocks per query head; of the whole stream
-    const int m_diag = CAUSAL ? (k0 + BN - 1 + QB - 1) / QB : 0;
-    const bool tile_partial = k0 + BN > L || a.window > 0;
-    const int m_full = nq / QB;
+  // The tile after the current one, known from the current tile's start.
+  Tp np = cp;
+  bool has_nxt = false;
+  // At the start barrier of the tile of pass p: its successor (static
+  // zigzag, or past the first two passes the hand-out counter, whose next
+  // value one lane fetches now and passes on at the next tile start).
+  auto start_duties = [&](int64_t p) {
+    const int64_t tn0 = zigzag_tile(p + 1, slot, a.P);
+    if constexpr (DYN) {
+      const int64_t tn = p == 0 ? tn0 : 2 * (int64_t)a.P + (uint32_t)__builtin_amdgcn_readfirstlane(s_next);
+      has_nxt = tn < T;
+      if (has_nxt && wave == 0 && l == 0) fetched = atomicAdd(a.ktile_ctr, 1u);
+      if (has_nxt) np = tparams(tiles[tn]);
+    } else {
+      has_nxt = tn0 < T;
+      if (has_nxt) np = tparams(tiles[tn0]);
+    }
+  };
 
-    bf16x8 kv[KS];
-    f32x16 acc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-    // B operand of the row-term k-step: ones in k-slots 0..2.
-    const bf16x8 ones3 = __builtin_bit_cast(bf16x8, g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
-    // Lane bases: this lane's query row and chunk g of the role's row tile,
-    // its row term, and its 16-byte slots of the hand-over area.
-    const uint32_t row_lane = (uint32_t)(C::perm(lc) * RB + g * 16) + (grad ? (uint32_t)C::OFF_DO : 0u);
-    const uint32_t tm_lane = (uint32_t)(lc * 16) + (grad ? (uint32_t)C::OFF_TD : (uint32_t)C::OFF_TL);
-    u32x2* const xw = reinterpret_cast<u32x2*>(xchg) + (kgrp * 4) * WAVE + l;  // + ((xs * 2 + s) * NG * 4 + i4) * WAVE
+  // A tile's lane and loop values: this lane's key, the query rows, and per
+  // query head the blocks [0, u0) and [u1, nbh) that take the masked front.
+  struct Tv {
+    int kw, nq, nb, nbh, m_first, u0, u1;
+    bool key_ok;
+  };
+  auto tvals = [&](const Tp& p) {
+    Tv v;
+    v.kw = p.k0 + kgrp * 32 + lc;
+    v.key_ok = v.kw < p.L;
+    v.nq = p.nq;
+    v.nb = p.nb;
+    v.nbh = p.nbh;
+    v.m_first = p.m_first;
+    const int m_diag = CAUSAL ? (p.k0 + BN - 1 + QB - 1) / QB : 0;
+    const bool tile_partial = p.k0 + BN > p.L || a.window > 0;
+    const int m_full = p.nq / QB;
+    v.u0 = tile_partial ? p.nbh : CAUSAL ? min(max(m_diag, p.m_first), p.m_end) - p.m_first : 0;
+    v.u1 = tile_partial ? p.nbh : max(v.u0, min(m_full, p.m_end) - p.m_first);
+    return v;
+  };
 
-    // Carried from one iteration to the next, in one register array for
-    // both roles: the score wave's P of the block just scored as packed
-    // bf16 B operands (carry[8 s + 4 hh + k], subtile s, pair hh) and their
-    // rounded remainders (carry[16 + ...]), plus the largest value per
-    // subtile; the gradient wave's dP' of that block (carry[16 s + i] as
-    // fp32 bits).
-    uint32_t carry[32];
-    float pmaxc[2] = {0.f, 0.f};
+  bf16x8 kv[KS];
+  f32x16 acc[DT];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) carry[i] = 0u;
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // B operand of the row-term k-step: ones in k-slots 0..2.
+  const bf16x8 ones3 = __builtin_bit_cast(bf16x8, g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+  // Lane bases: this lane's query row and chunk g of the role's row tile,
+  // its row term, and its 16-byte slots of the hand-over area.
+  const uint32_t row_lane = (uint32_t)(C::perm(lc) * RB + g * 16) + (grad ? (uint32_t)C::OFF_DO : 0u);
+  const uint32_t tm_lane = (uint32_t)(lc * 16) + (grad ? (uint32_t)C::OFF_TD : (uint32_t)C::OFF_TL);
+  u32x2* const xw = reinterpret_cast<u32x2*>(xchg) + (kgrp * 4) * WAVE + l;  // + ((xs * 2 + s) * NG * 4 + i4) * WAVE
 
-    // Front of an iteration: S (score wave) or dP (gradient wave) of block
-    // m, each subtile from its row-term k-step and KS k-steps of LDS rows
-    // (three reads ahead) against the registers.  The score wave turns S
-    // into P, writes it to hand-over area xs for the gradient wave and keeps
-    // it packed; the gradient wave keeps dP'.
-    auto front = [&](auto masked_tag, int m, const char* buf, int xs) __attribute__((always_inline)) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      const uint32_t lb = lds_addr(buf);
-      f32x16 sc[2];
-      // score wave: P of register group I4 of subtile S_ (rows S_ * 32 + 8 I4 + 4 g + e)
-      auto p_rows = [&](auto s_tag, auto i4_tag) __attribute__((always_inline)) {
-        constexpr int S_ = decltype(s_tag)::value, I4 = decltype(i4_tag)::value;
-        const int r = S_ * 32 + I4 * 8 + g * 4;
-        float p4[4];
+  // Carried from one iteration to the next, in one register array for
+  // both roles: the score wave's P of the block just scored as packed
+  // bf16 B operands (carry[8 s + 4 hh + k], subtile s, pair hh) and their
+  // rounded remainders (carry[16 + ...]), plus the largest value per
+  // subtile; the gradient wave's dP' of that block (carry[16 s + i] as
+  // fp32 bits).
+  uint32_t carry[32];
+  float pmaxc[2] = {0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv = fast_exp2(sc[S_][I4 * 4 + e] * c2);
-          if constexpr (MASKED) {
-            const int row = m * QB + r + e;
-            bool ok = key_ok && row < nq;
-            if constexpr (CAUSAL) ok = ok && kw <= row && (a.window <= 0 || kw > row - a.window);
-            pv = ok ? pv : 0.f;
-          }
-          p4[e] = pv;
-          pmaxc[S_] = fmaxf(pmaxc[S_], pv);
+  for (int i = 0; i < 32; ++i) carry[i] = 0u;
+
+  // Front of an iteration: S (score wave) or dP (gradient wave) of block
+  // m, each subtile from its row-term k-step and KS k-steps of LDS rows
+  // (three reads ahead) against the registers.  The score wave turns S
+  // into P, writes it to hand-over area xs for the gradient wave and keeps
+  // it packed; the gradient wave keeps dP'.
+  auto front = [&](auto masked_tag, const Tv& tv, int m, const char* buf, int xs) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const uint32_t lb = lds_addr(buf);
+    f32x16 sc[2];
+    // score wave: P of register group I4 of subtile S_ (rows S_ * 32 + 8 I4 + 4 g + e)
+    auto p_rows = [&](auto s_tag, auto i4_tag) __attribute__((always_inline)) {
+      constexpr int S_ = decltype(s_tag)::value, I4 = decltype(i4_tag)::value;
+      const int r = S_ * 32 + I4 * 8 + g * 4;
+      float p4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pv = fast_exp2(sc[S_][I4 * 4 + e] * c2);
+        if constexpr (MASKED) {
+          const int row = m * QB + r + e;
+          bool ok = tv.key_ok && row < tv.nq;
+          if constexpr (CAUSAL) ok = ok && tv.kw <= row && (a.window <= 0 || tv.kw > row - a.window);
+          pv = ok ? pv : 0.f;
         }
-        xw[((xs * 2 + S_) * C::NG * 4 + I4) * WAVE] = u32x2{pack_f16x2(p4[0], p4[1]), pack_f16x2(p4[2], p4[3])};
-        const uint32_t h0 = pack_bf16x2(p4[0], p4[1]), h1 = pack_bf16x2(p4[2], p4[3]);
-        constexpr int c = 8 * S_ + 4 * (I4 >> 1) + (I4 & 1) * 2;
-        carry[c] = h0;
-        carry[c + 1] = h1;
-        carry[16 + c] = bf16x2_residual(p4[0], p4[1], h0);
-        carry[16 + c + 1] = bf16x2_residual(p4[2], p4[3], h1);
-      };
-      using Z = std::integral_constant<int, 0>;
-      using O = std::integral_constant<int, 1>;
-      if (!grad) pmaxc[0] = pmaxc[1] = 0.f;
-      static_for<0, 2>([&](auto s_tag) {
-        constexpr int s = decltype(s_tag)::value;
-        constexpr int LA = 3;  // row reads in flight ahead of the products
-        u32x4 rw[KS], tmv;
-        const uint32_t rb = lb + row_lane;
-        lds_read16_issue<s * 32 * 16>(lb + tm_lane, tmv);
-        static_for<0, LA>([&](auto k_tag) {
-          constexpr int k = decltype(k_tag)::value;
-          lds_read16_issue<s * 32 * RB + 32 * k>(rb, rw[k]);
-        });
-        lgkm_wait1<LA>(tmv);
-        sc[s] = mfma32(__builtin_bit_cast(bf16x8, tmv), ones3, f32x16{});
-        static_for<0, KS>([&](auto ks_tag) {
-          constexpr int ks = decltype(ks_tag)::value;
-          // reads issued after this k-step's: ks + 1 .. ks + LA - 1 (and any
-          // hand-over writes, which only make the wait conservative)
-          lgkm_wait1<(KS - 1 - ks < LA - 1 ? KS - 1 - ks : LA - 1)>(rw[ks]);
-          if constexpr (ks + LA < KS) lds_read16_issue<s * 32 * RB + 32 * (ks + LA)>(rb, rw[ks + LA]);
-          sc[s] = mfma32(__builtin_bit_cast(bf16x8, rw[ks]), kv[ks], sc[s]);
-          if constexpr (s == 1 && (ks & 1)) {
-            // score wave: P of subtile 0 beside subtile 1's products
-            if (!grad) p_rows(Z{}, std::integral_constant<int, (ks >> 1)>{});
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
+        p4[e] = pv;
+        pmaxc[S_] = fmaxf(pmaxc[S_], pv);
+      }
+      xw[((xs * 2 + S_) * C::NG * 4 + I4) * WAVE] = u32x2{pack_f16x2(p4[0], p4[1]), pack_f16x2(p4[2], p4[3])};
+      const uint32_t h0 = pack_bf16x2(p4[0], p4[1]), h1 = pack_bf16x2(p4[2], p4[3]);
+      constexpr int c = 8 * S_ + 4 * (I4 >> 1) + (I4 & 1) * 2;
+      carry[c] = h0;
+      carry[c + 1] = h1;
+      carry[16 + c] = bf16x2_residual(p4[0], p4[1], h0);
+      carry[16 + c + 1] = bf16x2_residual(p4[2], p4[3], h1);
+    };
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
+    if (!grad) pmaxc[0] = pmaxc[1] = 0.f;
+    static_for<0, 2>([&](auto s_tag) {
+      constexpr int s = decltype(s_tag)::value;
+      constexpr int LA = 3;  // row reads in flight ahead of the products
+      u32x4 rw[KS], tmv;
+      const uint32_t rb = lb + row_lane;
+      lds_read16_issue<s * 32 * 16>(lb + tm_lane, tmv);
+      static_for<0, LA>([&](auto k_tag) {
+        constexpr int k = decltype(k_tag)::value;
+        lds_read16_issue<s * 32 * RB + 32 * k>(rb, rw[k]);
       });
-      if (!grad) {
-        static_for<0, 4>([&](auto i4_tag) { p_rows(O{}, i4_tag); });
+      lgkm_wait1<LA>(tmv);
+      sc[s] = mfma32(__builtin_bit_cast(bf16x8, tmv), ones3, f32x16{});
+      static_for<0, KS>([&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        // reads issued after this k-step's: ks + 1 .. ks + LA - 1 (and any
+        // hand-over writes, which only make the wait conservative)
+        lgkm_wait1<(KS - 1 - ks < LA - 1 ? KS - 1 - ks : LA - 1)>(rw[ks]);
+        if constexpr (ks + LA < KS) lds_read16_issue<s * 32 * RB + 32 * (ks + LA)>(rb, rw[ks + LA]);
+        sc[s] = mfma32(__builtin_bit_cast(bf16x8, rw[ks]), kv[ks], sc[s]);
+        if constexpr (s == 1 && (ks & 1)) {
+          // score wave: P of subtile 0 beside subtile 1's products
+          if (!grad) p_rows(Z{}, std::integral_constant<int, (ks >> 1)>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+    if (!grad) {
+      static_for<0, 4>([&](auto i4_tag) { p_rows(O{}, i4_tag); });
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        carry[i] = __float_as_uint(sc[0][i]);
+        carry[16 + i] = __float_as_uint(sc[1][i]);
+      }
+    }
+  };
+
+  // Back of an iteration: dV += P^T dO (score wave) or dK += dS^T Q
+  // (gradient wave, dS = P o dP' with P from hand-over area xs) of the
+  // block before, one instruction stream for both: the packed P or dS (its
+  // registers read as the A operand give P^T / dS^T, a key per row) times
+  // transposed reads of the dO or Q tile at the query rows of its k-slots
+  // (pair hh: rows s * 32 + 16 hh + 4 g + {0..3, 8..11}) as the B operand,
+  // so that the accumulator holds key rows by d columns.  Where a subtile
+  // holds a value above its threshold the rounded remainders are multiplied
+  // in as well.
+  auto back = [&](const char* buf, int xs) __attribute__((always_inline)) {
+    const uint32_t tbr = lds_addr(buf) + tr_lane + (grad ? 0u : (uint32_t)C::OFF_DO);
+    static_for<0, 2>([&](auto s_tag) {
+      constexpr int s = decltype(s_tag)::value;
+      constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
+      const u32x2* xr = reinterpret_cast<const u32x2*>(xchg) + (((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l;
+      i16x4 x0[8], x1[8];
+      tr_issue<D, OF0, RB, TR2>(tbr, x0);
+      tr_issue<D, OF1, RB, TR2>(tbr, x1);
+      // gradient wave: dS of register group i4 = P (fp16, from the score
+      // wave's lanes) times dP'
+      auto ds4 = [&](int i4, float (&d4)[4]) __attribute__((always_inline)) {
+        const u32x2 pv = xr[i4 * WAVE];
+        const float pf[4] = {f16_lo(pv[0]), f16_hi(pv[0]), f16_lo(pv[1]), f16_hi(pv[1])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d4[e] = pf[e] * __uint_as_float(carry[16 * s + i4 * 4 + e]);
+      };
+      uint32_t op[2][4];
+      bool big;
+      if (grad) {
+        float dsmax = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float d4[4];
+          ds4(i4, d4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dsmax = fmaxf(dsmax, fabsf(d4[e]));
+          op[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(d4[0], d4[1]);
+          op[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(d4[2], d4[3]);
+        }
+        big = dsmax > SPLIT_DS;
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          carry[i] = __float_as_uint(sc[0][i]);
-          carry[16 + i] = __float_as_uint(sc[1][i]);
-        }
-      }
-    };
-
-    // Back of an iteration: dV^T += dO^T P (score wave) or dK^T += Q^T dS
-    // (gradient wave, dS = P o dP' with P from hand-over area xs) of the
-    // block before, one instruction stream for both: the A operands are
-    // transposed reads of the dO or Q tile at the query rows of the packed
-    // operand's k-slots (pair hh: rows s * 32 + 16 hh + 4 g + {0..3,
-    // 8..11}).  Where a subtile holds a value above its threshold the
-    // rounded remainders are multiplied in as well.
-    auto back = [&](const char* buf, int xs) __attribute__((always_inline)) {
-      const uint32_t tbr = lds_addr(buf) + tr_lane + (grad ? 0u : (uint32_t)C::OFF_DO);
-      static_for<0, 2>([&](auto s_tag) {
-        constexpr int s = decltype(s_tag)::value;
-        constexpr int OF0 = (s * 32) * RB, OF1 = (s * 32 + 16) * RB;
-        const u32x2* xr = reinterpret_cast<const u32x2*>(xchg) + (((xs * 2 + s) * C::NG + kgrp) * 4) * WAVE + l;
-        i16x4 x0[8], x1[8];
-        tr_issue<D, OF0, RB, TR2>(tbr, x0);
-        tr_issue<D, OF1, RB, TR2>(tbr, x1);
-        // gradient wave: dS of register group i4 = P (fp16, from the score
-        // wave's lanes) times dP'
-        auto ds4 = [&](int i4, float (&d4)[4]) __attribute__((always_inline)) {
-          const u32x2 pv = xr[i4 * WAVE];
-          const float pf[4] = {f16_lo(pv[0]), f16_hi(pv[0]), f16_lo(pv[1]), f16_hi(pv[1])};
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d4[e] = pf[e] * __uint_as_float(carry[16 * s + i4 * 4 + e]);
-        };
-        uint32_t op[2][4];
-        bool big;
+          for (int k = 0; k < 4; ++k) op[hh][k] = carry[8 * s + 4 * hh + k];
+        big = pmaxc[s] > SPLIT_P;
+      }
+      const bf16x8 o0 = __builtin_bit_cast(bf16x8, u32x4{op[0][0], op[0][1], op[0][2], op[0][3]});
+      const bf16x8 o1 = __builtin_bit_cast(bf16x8, u32x4{op[1][0], op[1][1], op[1][2], op[1][3]});
+      tr_wait<2 * DT>(x0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(o0, tr_operand(x0, dt), acc[dt]);
+      tr_wait<0>(x1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(o1, tr_operand(x1, dt), acc[dt]);
+      if (__builtin_expect(__any(big), 0)) {
+        u32x4 lo[2];
         if (grad) {
-          float dsmax = 0.f;
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             float d4[4];
             ds4(i4, d4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dsmax = fmaxf(dsmax, fabsf(d4[e]));
-            op[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(d4[0], d4[1]);
-            op[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(d4[2], d4[3]);
+            lo[i4 >> 1][(i4 & 1) * 2] = bf16x2_residual(d4[0], d4[1], op[i4 >> 1][(i4 & 1) * 2]);
+            lo[i4 >> 1][(i4 & 1) * 2 + 1] = bf16x2_residual(d4[2], d4[3], op[i4 >> 1][(i4 & 1) * 2 + 1]);
           }
-          big = dsmax > SPLIT_DS;
         } else {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) op[hh][k] = carry[8 * s + 4 * hh + k];
-          big = pmaxc[s] > SPLIT_P;
+            for (int k = 0; k < 4; ++k) lo[hh][k] = carry[16 + 8 * s + 4 * hh + k];
         }
-        const bf16x8 o0 = __builtin_bit_cast(bf16x8, u32x4{op[0][0], op[0][1], op[0][2], op[0][3]});
-        const bf16x8 o1 = __builtin_bit_cast(bf16x8, u32x4{op[1][0], op[1][1], op[1][2], op[1][3]});
-        tr_wait<2 * DT>(x0);
+        // reads and their wait in one statement: on this rare path the
+        // compiler may move registers freely
+        bf16x8 y[4];
+        lds_operand_tr_x4(tbr + OF0, tbr + OF0 + TR2, y);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_operand(x0, dt), o0, acc[dt]);
-        tr_wait<0>(x1);
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(__builtin_bit_cast(bf16x8, lo[0]), y[dt], acc[dt]);
+        lds_operand_tr_x4(tbr + OF1, tbr + OF1 + TR2, y);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_operand(x1, dt), o1, acc[dt]);
-        if (__builtin_expect(__any(big), 0)) {
-          u32x4 lo[2];
-          if (grad) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              float d4[4];
-              ds4(i4, d4);
-              lo[i4 >> 1][(i4 & 1) * 2] = bf16x2_residual(d4[0], d4[1], op[i4 >> 1][(i4 & 1) * 2]);
-              lo[i4 >> 1][(i4 & 1) * 2 + 1] = bf16x2_residual(d4[2], d4[3], op[i4 >> 1][(i4 & 1) * 2 + 1]);
-            }
-          } else {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-              for (int k = 0; k < 4; ++k) lo[hh][k] = carry[16 + 8 * s + 4 * hh + k];
-          }
-          // reads and their wait in one statement: on this rare path the
-          // compiler may move registers freely
-          bf16x8 y[4];
-          lds_operand_tr_x4(tbr + OF0, tbr + OF0 + TR2, y);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(y[dt], __builtin_bit_cast(bf16x8, lo[0]), acc[dt]);
-          lds_operand_tr_x4(tbr + OF1, tbr + OF1 + TR2, y);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(y[dt], __builtin_bit_cast(bf16x8, lo[1]), acc[dt]);
-        }
-      });
-    };
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(__builtin_bit_cast(bf16x8, lo[1]), y[dt], acc[dt]);
+      }
+    });
+  };
 
-    // The operand registers are taken here, outside the loops, so that the
-    // compiler's wait for their loads happens once per tile.
+  // The operand registers are taken where a first front needs them, so that
+  // the compiler's wait for their loads happens once per tile.
+  auto take_kv = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       asm volatile("" : "+v"(kvraw[ks]));
       kv[ks] = __builtin_bit_cast(bf16x8, kvraw[ks]);
     }
-    if (nb > 0) {
-      // Iteration i (0 <= i <= nb): the back of block i - 1, then the front
-      // of block i.  Blocks stream one ahead: block i + 1 is copied during
-      // iteration i into the ring buffer that block i - 2 left, so the ring
-      // holds the back's block, the front's block and the copies in flight.
-      {
-        if (iss_cur < 1) {
-          prep_next(cp, cp, false);  // this tile's first block
-          issue_now();
-          wait_vmcnt<0>();
-        } else {
-          static_assert(4 * DT <= 63, "store count");
-          wait_vmcnt<4 * DT>();
-        }
-        if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
-        barrier_lds();
-        handoff();
-        prep_next(cp, np, has_nxt);
-        issue_now();
-      }
-      int ring_back = 0;
-      // iteration i; its front is block m (of the stream's current query head)
-      auto iter = [&](auto masked_tag, int i, int m) __attribute__((always_inline)) {
-        if (i > 0) {
-          wait_vmcnt<0>();  // this wave's copies of block i
-          barrier_lds();    // every wave's copies landed; block i - 2's buffer and hand-over area free
-          // Block i + 1 (the next tile's first block at i = nb - 1); the
-          // last iteration copies nothing, so that the stream never runs
-          // more than one block ahead of the fronts.
-          if (i < nb) {
-            prep_next(cp, np, has_nxt);
-            issue_rows(0, C::CPT);  // Q rows and row terms now, dO rows after the back:
-            issue_vec();            // a workgroup's 56 copies queue behind each other
-          }
-          back(smem[ring_back], (i - 1) & 1);
-          if (i < nb) issue_rows(C::CPT, 2 * C::CPT);
-        }
-        if (i < nb) {
-          front(masked_tag, m, smem[ring_cmp], i & 1);
-          ring_back = ring_cmp;  // the next iteration's back reads this block
-          ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
-        }
-      };
-      // iterations [i0, i1) whose fronts take one mask variant (a loop per
-      // variant keeps register allocation to one body at a time)
-      // iterations [i0, i1) of the head whose blocks start at iteration hb
-      auto run = [&](auto masked_tag, int i0, int i1, int hb) __attribute__((always_inline)) {
-        for (int i = i0; i < i1; ++i) iter(masked_tag, i, m_first + (i - hb));
-      };
-      // per query head: blocks [0, u0) and [u1, nbh) take the masked front
-      const int u0 = tile_partial ? nbh : CAUSAL ? min(max(m_diag, m_first), m_end) - m_first : 0;
-      const int u1 = tile_partial ? nbh : max(u0, min(m_full, m_end) - m_first);
-      for (int i0 = 0; i0 < nb; i0 += nbh) {
-        run(std::true_type{}, i0, i0 + u0, i0);
-        run(std::false_type{}, i0 + u0, i0 + u1, i0);
-        run(std::true_type{}, i0 + u1, i0 + nbh, i0);
-      }
-      iter(std::false_type{}, nb, 0);  // the last back
-    } else {
-      if (DYN && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
-      if (DYN) barrier_lds();
-      handoff();
-    }
+  };
+  // The front of a tile's first block (query head 0, block m_first).
+  auto front_first = [&](const Tv& tv, const char* buf, int xs) __attribute__((always_inline)) {
+    if (tv.u0 > 0 || tv.u1 <= 0) front(std::true_type{}, tv, tv.m_first, buf, xs);
+    else front(std::false_type{}, tv, tv.m_first, buf, xs);
+  };
 
-    // Tile end: the next tile's operand rows, then (once every wave has
-    // read its P) this tile's stores through the hand-over area.
-    if (has_nxt) load_rows(np);
+  // One stream of iterations across tiles.  Iteration i of a tile runs the
+  // back of block i - 1 and then the front of block i, with one barrier per
+  // iteration; blocks stream one ahead through a ring of 3 buffers, so the
+  // ring holds the back's block, the front's block and the copies in
+  // flight.  Between two tiles one transition runs the back of the first
+  // tile's last block beside the front of the next tile's first block (the
+  // next tile's start: its successor, the copies of its second block); each
+  // wave issues the first tile's stores right after that back, and they
+  // drain during the front and the next iteration.  Hand-over areas
+  // alternate by iteration across tiles.
+  int ring_back = 0;
+  int xlast = 1;       // hand-over area of the last front
+  Tp pv = cp;          // the tile whose last back is pending
+  bool pend = false;   // ... if any
+  bool cv = true;      // cp is a tile to start
+  for (int64_t pass = 0;; ++pass) {
+    // ---- transition: the back of pv's last block (pend), the start of cp (cv)
+    const Tv tv = tvals(cp);
+    const bool fr = cv && tv.nb > 0;
+    if (fr) load_rows(cp);                // the last front has used the rows it replaces
+    asm volatile("" ::: "memory");        // the row loads stay ahead of the wait that counts them
+    bool own0 = false;
+    if (fr && iss_cur < 1) {
+      prep_next(cp, cp, false);           // cp's first block, not issued yet (the first tile's,
+      issue_now();                        // or one after a tile without blocks)
+      own0 = true;
+    }
+    // this wave's copies of cp's first block, issued before the row loads
+    // (and any stores), or just now
+    if (own0 || !fr) wait_vmcnt<0>();
+    else wait_vmcnt<KS>();
+    if constexpr (!DYN) {
+      if (cv) start_duties(pass);
+    }
+    if (DYN && cv && pass > 0 && wave == 0 && l == 0) s_next = (int)fetched;
     barrier_lds();
-    store_acc(cp, min(L - k0, BN), acc);
-    if (!has_nxt) break;
-    // the next tile's first block may already be issued
-    cur_gi = iss_nxt > 0 && np.nbh == 1 ? 1 : 0;
-    cur_jb = iss_nxt > 0 && np.nbh > 1 ? 1 : 0;
-    cp = np;
-    iss_cur = iss_nxt;
-    iss_nxt = 0;
+    if (cv) {
+      if constexpr (DYN) start_duties(pass);
+      prep_next(cp, np, has_nxt);         // cp's second block, or the next tile's first
+      issue_now();
+    }
+    if (pend) {
+      back(smem[ring_back], xlast);
+      store_acc(pv, min(pv.L - pv.k0, BN), acc);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+    }
+    if (fr) {
+      take_kv();
+      front_first(tv, smem[ring_cmp], xlast ^ 1);
+      xlast ^= 1;
+      ring_back = ring_cmp;
+      ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
+    } else {
+      // (a definition on this path too, so that the rows of the tile before
+      // are dead during the back above)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kv[ks] = bf16x8{};
+    }
+    const bool stores_out = pend;
+    if (!cv) break;
+    // every wave has read the hand-out index before wave 0 writes the next
+    // one (a tile of two or more blocks has iteration barriers in between)
+    if (DYN && tv.nb <= 1) barrier_lds();
+
+    if (tv.nb == 0) {
+      store_zero(cp, min(cp.L - cp.k0, BN));  // a tile without query blocks
+      pend = false;
+    } else {
+      const int nb = tv.nb, nbh = tv.nbh;
+      // iteration i (1 <= i < nb); its front is block m of the stream's current query head
+      auto iter = [&](auto masked_tag, int i, int m) __attribute__((always_inline)) {
+        // this wave's copies of block i (issued at the transition before
+        // the 16 * DT stores of the tile before, when i = 1)
+        static_assert(16 * DT >= 63, "wait count");
+        if (i == 1 && stores_out) wait_vmcnt<63>();
+        else wait_vmcnt<0>();
+        barrier_lds();  // every wave's copies landed; block i - 2's buffer and hand-over area free
+        // Block i + 1 (the next tile's first block at i = nb - 1)
+        prep_next(cp, np, has_nxt);
+        issue_rows(0, C::CPT);  // Q rows and row terms now, dO rows after the back:
+        issue_vec();            // a workgroup's 56 copies queue behind each other
+        back(smem[ring_back], xlast);
+        issue_rows(C::CPT, 2 * C::CPT);
+        front(masked_tag, tv, m, smem[ring_cmp], xlast ^ 1);
+        xlast ^= 1;
+        ring_back = ring_cmp;  // the next iteration's back reads this block
+        ring_cmp = ring_cmp == NBUF - 1 ? 0 : ring_cmp + 1;
+      };
+      // iterations [max(i0, 1), i1) of the head whose blocks start at
+      // iteration hb (a loop per mask variant keeps register allocation to
+      // one body at a time)
+      auto run = [&](auto masked_tag, int i0, int i1, int hb) __attribute__((always_inline)) {
+        for (int i = max(i0, 1); i < i1; ++i) iter(masked_tag, i, tv.m_first + (i - hb));
+      };
+      for (int i0 = 0; i0 < nb; i0 += nbh) {
+        run(std::true_type{}, i0, i0 + tv.u0, i0);
+        run(std::false_type{}, i0 + tv.u0, i0 + tv.u1, i0);
+        run(std::true_type{}, i0 + tv.u1, i0 + nbh, i0);
+      }
+      pend = true;
+    }
+    pv = cp;
+    cv = has_nxt;
+    if (cv) {
+      // the stream's position moves on to the next tile, whose first block
+      // may already be issued
+      cur_gi = iss_nxt > 0 && np.nbh == 1 ? 1 : 0;
+      cur_jb = iss_nxt > 0 && np.nbh > 1 ? 1 : 0;
+      iss_cur = iss_nxt;
+      iss_nxt = 0;
+      cp = np;
+    }
   }
 }
 
