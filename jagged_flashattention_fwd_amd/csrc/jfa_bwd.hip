@@ -200,7 +200,11 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
     const int jj = (l & 15) >> 2, cq = ((l >> 4) & 1) * 16 + (l & 3) * 4;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // dP^T starts from -delta (a lane's registers all belong to its query
+      // row), so that dS^T = P^T o dP' takes no subtraction.
+      f32x16 sacc = f32x16{}, dpacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dpacc[i] = -del;
       // K / V operands of k-step ks + 1 are read before the products of
       // k-step ks.
       bf16x8 kc = lds_read16(Ks, tile_off<D>(kt * 32 + lc, g));
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dq_kernel(BwdArgs a) {
           const bool ok = key < L && (!CAUSAL || (key <= qi && (a.window <= 0 || key > qi - a.window)));
           pv = ok ? pv : 0.f;
         }
-        dsf[i] = pv * (dpacc[i] - del);
+        dsf[i] = pv * dpacc[i];
         dsmax = fmaxf(dsmax, fabsf(dsf[i]));
       }
       // dQ sums dS over many keys (all keys of a chunk of sequences in
