@@ -130,16 +130,15 @@ struct MxB {
   // Copies per wave per step: Q, dO, Q^T, dO^T, and one dword copy each of
   // the four scale arrays, lse and delta.
   static constexpr int IPS = 2 * NRC + 2 * NTC + 6;
-  static constexpr int NST = 4 * 4;  // stores per wave at a tile end: dV or dK, 4 pieces per head-dim tile
+  static constexpr int NST = 4 * 16;  // stores per wave at a tile end: dV or dK, 16 per head-dim tile
+  static constexpr int NST_WAIT = NST < 63 ? NST : 63;
   static_assert(BUF % 16 == 0, "buffer alignment");
   static_assert(NBUF * BUF <= 160 * 1024, "LDS");
   static_assert(NBUF >= DEP + 1, "a buffer is refilled only after every wave has left it");
-  static_assert(NW * 32 * 144 <= BUF, "the store staging fits one ring buffer");
-  static_assert(NBUF == DEP + 1, "the buffer of the last computed step is the free one at a tile end");
   static constexpr int NKV = 12;          // loads of a tile's K / V operands and of the next tile record
   // At a tile end at most one step's copies stay in flight before the next
   // tile's K / V loads and this tile's stores are issued.
-  static_assert(DEP * IPS <= 63 && IPS + NKV + NST <= 63, "vector-memory counter");
+  static_assert(DEP * IPS <= 63 && IPS + NKV <= 63, "vector-memory counter");
 };
 
 // Two 16-byte global reads forming one lane's 32 operand bytes.
@@ -152,7 +151,7 @@ __device__ __forceinline__ i32x8 ld32x2(const uint8_t* p0, const uint8_t* p1) {
 template <bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a) {
   using C = MxB;
-  constexpr int BQ = C::BQ, BK = C::BK, D = C::D, NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS, NST = C::NST;
+  constexpr int BQ = C::BQ, BK = C::BK, D = C::D, NBUF = C::NBUF, DEP = C::DEP, IPS = C::IPS, NST_WAIT = C::NST_WAIT;
   constexpr int NW = C::NW, RW = C::RW, TW = C::TW, NRC = C::NRC, NTC = C::NTC;
   __shared__ __attribute__((aligned(16))) char smem[NBUF][C::BUF];
 
@@ -314,37 +313,33 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
     vsc = *reinterpret_cast<const uint32_t*>(a.v_scale + row * 4) >> (8 * g);
   };
 
-  f32x16 acc[4];  // dV^T (role 0) or dK^T (role 1) of this wave's 32 keys
-  // dV, or dK = scale dK^T acc, of a tile: NST bounded buffer stores per
-  // wave.  Each 32-key x 32-element piece goes through `stage` (this wave's
-  // 32 rows of 144 bytes in a free ring buffer) so that every store writes
-  // whole 128-byte runs of 8 keys, not 32-byte pieces of 32 keys.
-  auto store_out = [&](const Tp& p, bool live, char* stage) {
+  // dV (role 0) or dK (role 1) of this wave's 32 keys, key by d: the
+  // quantized operand of the products is their A side (a key per row, the
+  // scaled product's A and B layouts being the same), so register
+  // 4 i4 + e of head-dim tile dt is key 8 i4 + 4 g + e at d = 32 dt + lc.
+  f32x16 acc[4];
+  // dV, or dK = scale * acc, of a tile: NST bounded buffer stores per wave,
+  // each writing two whole 128-byte rows (lanes 0-31 one key, lanes 32-63
+  // the key 4 further) straight from the registers.  The whole byte offset
+  // stays in the lane operand, which the range check covers; the asm hides
+  // the lane part from loop-invariant hoisting.
+  auto store_out = [&](const Tp& p, bool live) {
     const int k0 = p.k0 + kw * 32;
     const int nv = live ? max(0, min(p.L - k0, 32)) : 0;
     const uint32_t kstride = (uint32_t)Hkv * D * 4;
     const int64_t row0 = (p.s0 + k0) * Hkv + p.hk;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc((role ? a.dk : a.dv) + row0 * D, nv * (int)kstride);
     const float sc = role ? a.scale : 1.f;
-    const int rk = l >> 3, rc = l & 7;  // read-back: key rk of 8, 16-byte chunk rc
+    uint32_t sb = (uint32_t)(4 * g) * kstride + (uint32_t)lc * 4;
+    asm volatile("" : "+v"(sb));
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      if (live) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 v;
+      for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[dt][i4 * 4 + e] * sc;
-          *reinterpret_cast<f32x4*>(stage + lc * 144 + (i4 * 8 + g * 4) * 4) = v;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = r * 8 + rk;
-        const u32x4 v = live ? *reinterpret_cast<const u32x4*>(stage + kr * 144 + rc * 16) : u32x4{};
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)kr * kstride + (uint32_t)(dt * 128 + rc * 16), 0, 0);
-      }
-    }
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(live ? acc[dt][i4 * 4 + e] * sc : 0.f), ro,
+                                                sb + (uint32_t)(8 * i4 + e) * kstride + (uint32_t)(dt * 128), 0, 0);
   };
 
   Tp cp = tparams(a.ktiles[t0]);
@@ -358,7 +353,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
     const int64_t t1 = zigzag_tile(1, slot, a.P);
     if (wave == 0 && l == 0 && t1 < T) nrec = a.ktiles[t1];
   }
-  store_out(cp, false, nullptr);  // stores that write nothing: every tile start sees NST stores after its loads
+  store_out(cp, false);  // stores that write nothing: every tile start sees NST stores after its loads
 
   __shared__ int s_next;
   unsigned int fetched = 0;
@@ -372,7 +367,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
         while (iss_cur < need) issue_next(cp, cp, false, 2);
         wait_vmcnt<0>();
       } else {
-        wait_vmcnt<NST>();
+        wait_vmcnt<NST_WAIT>();  // (at most 63: the counter's range; waiting for more is safe)
       }
     }
     if (wave == 0 && l == 0) {
@@ -452,9 +447,10 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
       if (!wave_live) return;
       const u32x4 xo = xw[wave ^ (NW / 2)][l];
       const uint32_t xcode = xc[wave ^ (NW / 2)][l];
-      // role 0: dV^T += dO^T P with P of both query blocks; role 1: dK^T +=
-      // Q^T dS.  Block 0 is the role-0 wave's, block 1 the role-1 wave's;
-      // lane half g takes block g's scale.
+      // role 0: dV += P^T dO with P of both query blocks; role 1: dK +=
+      // dS^T Q (the quantized P or dS as the A operand, dO^T or Q^T rows as
+      // the B operand).  Block 0 is the role-0 wave's, block 1 the role-1
+      // wave's; lane half g takes block g's scale.
       i32x8 bop;
       uint32_t bsc;
       if (role == 0) {
@@ -473,7 +469,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
       static_for<0, 4>([&](auto dt_tag) {
         constexpr int dt = decltype(dt_tag)::value;
         const char* ar = buf + off_a + (dt * 32 + lc) * TB;
-        acc[dt] = mfma_mx<dt, 0>(lds_read32x2(ar + 16 * g, ar + 32 + 16 * g), bop, acc[dt], (int)asc, (int)bsc);
+        acc[dt] = mfma_mx<0, dt>(bop, lds_read32x2(ar + 16 * g, ar + 32 + 16 * g), acc[dt], (int)bsc, (int)asc);
       });
     };
     for (int gi = 0; gi < G; ++gi)
@@ -492,9 +488,7 @@ __global__ __launch_bounds__(MxB::NW * WAVE, 1) void dkdv_mx_kernel(BwdMxArgs a)
       const int64_t t2 = 2 * (int64_t)a.P + fetched;  // the tile after np
       if (wave == 0 && l == 0 && t2 < T) nrec = a.ktiles[t2];
     }
-    // the last computed step's buffer is free once every wave has left it
-    barrier_lds();
-    store_out(cp, true, smem[(uint32_t)(g_cmp + NBUF - 1) % NBUF] + wave * 32 * 144);
+    store_out(cp, true);
     if (!has_nxt) break;
     cp = np;
     iss_cur = iss_nxt;
