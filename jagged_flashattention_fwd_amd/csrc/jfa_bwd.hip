@@ -44,22 +44,51 @@ constexpr float SPLIT_DS = 0.25f;
 // Rows of d elements; D/8 threads per row, 16 bytes each.  Also writes the
 // row's lse in base-2 units (lse * log2(e)), the form the dQ kernels read, and
 // the row terms (row_terms) of -lse / scale and -delta that the dK/dV kernel
-// folds into its score products.
+// folds into its score products.  Broadcast rows whose delta the exact pass
+// (delta_exact_kernel, after this one) writes are not read here.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
                                                     const float* __restrict__ lse,
                                                     float* __restrict__ delta, float* __restrict__ lse2,
                                                     u32x4* __restrict__ term_l, u32x4* __restrict__ term_d,
-                                                    float inv_scale, int64_t rows) {
+                                                    float inv_scale, int64_t rows, const int64_t* __restrict__ offsets,
+                                                    int64_t total_len, int HLq, int Lq, int causal) {
   constexpr int TPR = D / 8;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // Broadcast rows (HLq > 0) whose delta the exact pass writes (sequences of
+  // 1 .. BWD_BN keys; with the causal mask also the first BWD_BN query rows
+  // of every sequence) skip the O / dO reads.  A row's flag is found one
+  // iteration ahead, so that its offsets read overlaps the row before.
+  auto exact_row = [&](int64_t row) {
+    if (HLq <= 0 || row >= rows) return false;
+    // (32-bit division where the row index fits: the 64-bit one costs
+    // several times more)
+    int b, q;
+    if (rows <= 0x7fffffffll) {
+      const uint32_t r32 = (uint32_t)row;
+      b = (int)(r32 / (uint32_t)HLq);
+      q = (int)(r32 % (uint32_t)Lq);
+    } else {
+      b = (int)(row / HLq);
+      q = (int)(row % Lq);
+    }
+    int64_t s0;
+    const int64_t L = seq_range(offsets, b, total_len, &s0);
+    return L > 0 && (L <= BWD_BN || (causal && q < BWD_BN));
+  };
+  bool exact_nxt = exact_row(gtid / TPR);
   for (int64_t e = gtid; e < rows * TPR; e += stride) {
     const int64_t row = e / TPR;
     const int c = (int)(e % TPR);
-    const u32x4 o = *reinterpret_cast<const u32x4*>(out + row * D + c * 8);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + c * 8);
+    const bool exact = exact_nxt;
+    u32x4 o = u32x4{0u, 0u, 0u, 0u}, g = u32x4{0u, 0u, 0u, 0u};
+    if (!exact) {
+      o = *reinterpret_cast<const u32x4*>(out + row * D + c * 8);
+      g = *reinterpret_cast<const u32x4*>(dout + row * D + c * 8);
+    }
+    exact_nxt = exact_row((e + stride) / TPR);
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -69,10 +98,12 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
     if (c == 0) {
-      delta[row] = acc;
       lse2[row] = lse[row] * LOG2E;
       term_l[row] = row_terms(-lse[row] * inv_scale);
-      term_d[row] = row_terms(-acc);
+      if (!exact) {
+        delta[row] = acc;
+        term_d[row] = row_terms(-acc);
+      }
     }
   }
 }
@@ -813,7 +844,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const int blocks = (int)(want < 4096 ? want : 4096);
     JFA_TIMED_LAUNCH(K_DELTA, st, (delta_kernel<D>), dim3(blocks), dim3(256), 0, st, a.out, a.dout, a.lse, a.delta,
                      a.lse2, reinterpret_cast<u32x4*>(a.term_l), reinterpret_cast<u32x4*>(a.term_d),
-                     1.0f / a.scale, rows);
+                     1.0f / a.scale, rows, a.offsets, a.total_len, a.broadcast_q ? a.H * a.Lq : 0, a.Lq, a.causal);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

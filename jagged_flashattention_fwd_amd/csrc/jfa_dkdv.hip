@@ -1447,70 +1447,96 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a, const Tile
 // them, so their P is large too, and dQ sums such rows over every sequence.
 // (Self-attention rows are not summed across sequences; their error stays
 // within the bar, and the pass would cost a workgroup per (sequence, head).)
-// One workgroup: 128 query rows of one (sequence, head); wave w takes
-// rows 32w .. 32w+31 with the transposed score layout S^T = K Q^T (lane ->
-// query, registers -> keys), so each lane sums its registers and the two
-// halves of the wave are added.
+// A workgroup takes query rows 128 z .. 128 z + 127 (z = blockIdx.z) of one
+// head for each sequence it visits: in causal broadcast mode for z = 0 one
+// sequence per workgroup, otherwise a walk over the short sequences from
+// the end of the length-sorted order.  Wave w takes rows 32w .. 32w+31
+// with the transposed score layout S^T = K Q^T (lane -> query, registers
+// -> keys), so each lane sums its registers and the two halves of the wave
+// are added.
 template <int D, bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
-  const int b = blockIdx.x, h = blockIdx.y;
-  int64_t s0;
-  const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
-  if (L == 0 || (L > BWD_BN && !(CAUSAL && BCAST && blockIdx.z == 0))) return;
   static_assert(BWD_BN == 128, "the causal rows of block 0 see keys below 128 only");
-  const int Lk = min(L, BWD_BN);  // keys any row of this workgroup sees
+  const int h = blockIdx.y;
   const int H = a.H, Lq = a.Lq;
-  const int nq = BCAST ? Lq : L;
   const int wave = threadIdx.x / WAVE, l = threadIdx.x % WAVE, g = l / 32, lc = l % 32;
   const int qw = blockIdx.z * 128 + wave * 32;
-  if (qw >= nq) return;
-  const int q = qw + lc;
-  const int qc = min(q, nq - 1);
-  const uint16_t* qrow = BCAST ? a.q + ((int64_t)h * Lq + qc) * D : a.q + ((s0 + qc) * H + h) * (int64_t)D;
-  const int64_t ri = BCAST ? ((int64_t)b * H + h) * Lq + qc : (s0 + qc) * H + h;
-  const uint16_t* dorow = a.dout + ri * D;
-  bf16x8 qr[KS], dr[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8));
-    dr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dorow + ks * 16 + g * 8));
-  }
-  const float ls2 = a.lse2[ri];
-  const float c2 = a.scale_log2;
-  float acc = 0.f;
-  for (int kt = 0; kt * 32 < Lk; ++kt) {
-    const int key = min(kt * 32 + lc, Lk - 1);
-    const uint16_t* kr = a.k + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
-    const uint16_t* vr = a.v + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
-    f32x16 st = f32x16{}, dpt = f32x16{};
+  // Rows of sequence b: query block blockIdx.z against its first Lk keys.
+  auto rows_of = [&](int b, int L, int64_t s0) {
+    const int Lk = min(L, BWD_BN);  // keys any row of this workgroup sees
+    const int nq = BCAST ? Lq : L;
+    if (qw >= nq) return;
+    const int q = qw + lc;
+    const int qc = min(q, nq - 1);
+    const uint16_t* qrow = BCAST ? a.q + ((int64_t)h * Lq + qc) * D : a.q + ((s0 + qc) * H + h) * (int64_t)D;
+    const int64_t ri = BCAST ? ((int64_t)b * H + h) * Lq + qc : (s0 + qc) * H + h;
+    const uint16_t* dorow = a.dout + ri * D;
+    bf16x8 qr[KS], dr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + ks * 16 + g * 8));
-      const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vr + ks * 16 + g * 8));
-      st = mfma32(ka, qr[ks], st);
-      dpt = mfma32(va, dr[ks], dpt);
+      qr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8));
+      dr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dorow + ks * 16 + g * 8));
     }
+    const float ls2 = a.lse2[ri];
+    const float c2 = a.scale_log2;
+    float acc = 0.f;
+    for (int kt = 0; kt * 32 < Lk; ++kt) {
+      const int key = min(kt * 32 + lc, Lk - 1);
+      const uint16_t* kr = a.k + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
+      const uint16_t* vr = a.v + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
+      f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-      bool ok = kk < Lk;
-      if (CAUSAL) ok = ok && kk <= q && (a.window <= 0 || kk > q - a.window);
-      const float p = ok ? fast_exp2(st[i] * c2 - ls2) : 0.f;
-      acc += p * dpt[i];
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + ks * 16 + g * 8));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vr + ks * 16 + g * 8));
+        st = mfma32(ka, qr[ks], st);
+        dpt = mfma32(va, dr[ks], dpt);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+        bool ok = kk < Lk;
+        if (CAUSAL) ok = ok && kk <= q && (a.window <= 0 || kk > q - a.window);
+        const float p = ok ? fast_exp2(st[i] * c2 - ls2) : 0.f;
+        acc += p * dpt[i];
+      }
     }
+    acc = sum_across_halves(acc);
+    if (g == 0 && q < nq) {
+      a.delta[ri] = acc;
+      reinterpret_cast<u32x4*>(a.term_d)[ri] = row_terms(-acc);
+    }
+  };
+  if (CAUSAL && BCAST && blockIdx.z == 0) {
+    // every sequence: the first 128 query rows see keys below 128 only
+    const int b = blockIdx.x;
+    int64_t s0;
+    const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
+    if (L > 0) rows_of(b, L, s0);
+    return;
   }
-  acc = sum_across_halves(acc);
-  if (g == 0 && q < nq) {
-    a.delta[ri] = acc;
-    reinterpret_cast<u32x4*>(a.term_d)[ri] = row_terms(-acc);
+  // The sequences of at most BWD_BN keys sit at the end of the
+  // length-sorted order (longest first): workgroup x takes ranks
+  // B - 1 - x, B - 1 - x - gridDim.x, ... until a longer sequence.
+  for (int r = a.B - 1 - (int)blockIdx.x; r >= 0; r -= (int)gridDim.x) {
+    const int b = a.seq_order[r];
+    int64_t s0;
+    const int L = (int)seq_range(a.offsets, b, a.total_len, &s0);
+    if (L > BWD_BN) break;
+    if (L > 0) rows_of(b, L, s0);
   }
 }
+
+constexpr int DELTA_EXACT_WG = 256;  // workgroups per (head, query block) over the short sequences
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
   const int nqb = a.broadcast_q ? (a.Lq + 127) / 128 : 1;
-  const dim3 eg((unsigned)a.B, (unsigned)a.H, (unsigned)nqb);
+  // causal broadcast: a workgroup per sequence (every sequence's first query
+  // block); otherwise workgroups walk the short sequences of the sorted order
+  const int gx = a.broadcast_q && a.causal ? a.B : min(a.B, DELTA_EXACT_WG);
+  const dim3 eg((unsigned)gx, (unsigned)a.H, (unsigned)nqb);
   if (a.broadcast_q) {
     if (a.causal) JFA_TIMED_LAUNCH(K_DELTA_EXACT, st, (delta_exact_kernel<D, true, true>), eg, dim3(256), 0, st, a);
     else JFA_TIMED_LAUNCH(K_DELTA_EXACT, st, (delta_exact_kernel<D, false, true>), eg, dim3(256), 0, st, a);
