@@ -1481,17 +1481,33 @@ __global__ __launch_bounds__(256) void delta_exact_kernel(BwdArgs a) {
     const float ls2 = a.lse2[ri];
     const float c2 = a.scale_log2;
     float acc = 0.f;
-    for (int kt = 0; kt * 32 < Lk; ++kt) {
+    // K and V of each 32-key half are loaded one half ahead, so that a
+    // sequence's key halves cost one load latency, not one each
+    u32x4 kn[KS], vn[KS];
+    auto load_kv = [&](int kt) {
       const int key = min(kt * 32 + lc, Lk - 1);
       const uint16_t* kr = a.k + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
       const uint16_t* vr = a.v + ((s0 + key) * a.Hkv + h / a.G) * (int64_t)D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kn[ks] = *reinterpret_cast<const u32x4*>(kr + ks * 16 + g * 8);
+        vn[ks] = *reinterpret_cast<const u32x4*>(vr + ks * 16 + g * 8);
+      }
+    };
+    load_kv(0);
+    for (int kt = 0; kt * 32 < Lk; ++kt) {
+      bf16x8 kc[KS], vc[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kc[ks] = __builtin_bit_cast(bf16x8, kn[ks]);
+        vc[ks] = __builtin_bit_cast(bf16x8, vn[ks]);
+      }
+      if ((kt + 1) * 32 < Lk) load_kv(kt + 1);
       f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + ks * 16 + g * 8));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vr + ks * 16 + g * 8));
-        st = mfma32(ka, qr[ks], st);
-        dpt = mfma32(va, dr[ks], dpt);
+        st = mfma32(kc[ks], qr[ks], st);
+        dpt = mfma32(vc[ks], dr[ks], dpt);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
